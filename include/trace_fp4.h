@@ -1,0 +1,203 @@
+/*
+ * trace_fp4.h — C ABI of the rollout-guided FP4 fake-quantization library
+ * (MI355X / gfx950).
+ *
+ * The operations follow "TRACE: Rollout-Guided Quantization-Aware Training
+ * for FP4 Reinforcement Learning of MoE Language Models" (arXiv 2610.07767),
+ * cited below by section of its reader-view page.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Tensors. A tensor is a contiguous row-major [rows, cols] array of bf16 bit
+ * patterns (uint16_t). Blocks run along the last dimension: B = 16 elements
+ * for NVFP4, 32 for MXFP4, and cols must be a multiple of B. N = rows * cols.
+ * Block j covers elements [j*B, (j+1)*B) of the flattened tensor.
+ *
+ * Pointers. Every pointer argument is a DEVICE pointer owned by the caller;
+ * nothing is retained after the call returns. Input arrays are only read.
+ * bf16 arrays must be 16-byte aligned; code planes 4-byte aligned; global
+ * scales 4-byte aligned; the statistics accumulator and workspace 8-byte
+ * aligned. Other planes have no alignment requirement. When N == 0 the data
+ * pointers may be NULL.
+ *
+ * Planes written or read by the calls:
+ *   codes   uint8[N/2]  E2M1 codes, code = sign << 3 | k, k the 3-bit magnitude
+ *                       index (magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6); element
+ *                       2i in the low nibble of byte i, 2i+1 in the high one.
+ *   mbits   uint8[N/8]  one bit per element, the mantissa bit k & 1; element
+ *                       8i+j in bit j of byte i (LSB first).
+ *   scales  uint8[N/B]  NVFP4: E4M3 (bias 7, OCP "fn") block scale; MXFP4:
+ *                       E8M0 block scale (byte = E + 127). One byte per block,
+ *                       block order. Bytes read by a call must be valid
+ *                       non-negative finite values (E4M3 <= 0x7E, E8M0 <= 254);
+ *                       otherwise results are unspecified (memory-safe).
+ *   gscale  float32[2]  NVFP4 only: [0] = the FP32 global scale S,
+ *                       [1] = the tensor amax A it came from.
+ *
+ * Scaling (NVFP4). A = max|x| over the tensor; S = 2688 / A (1 if A == 0,
+ * at most FLT_MAX). Per block with max a: u = (a / 6) * S, e = E4M3 of
+ * min(u, 448) rounded to nearest even; decode factor d = e / S, encode factor
+ * r = min(S / e, FLT_MAX), both 0 when e == 0. The normalized value of an
+ * element is t = |x| * r. Binary32 arithmetic, each operation rounded, no
+ * fused multiply-add. (Paper §3.1 "Key Design", Fig. 4(a): the same global
+ * and block scales; Algorithm 1 prose: s combines block and global scales.)
+ *
+ * Scaling (MXFP4). E = clamp(floor(log2 a) - 2, -127, 127), -127 for an
+ * all-zero block; t = |x| * 2^-E, d = 2^E. (Paper §4.3, MXFP4 variants.)
+ *
+ * Rounding. RTN rounds t to the nearest E2M1 magnitude, ties to the even
+ * index, saturating at 6. Every code and output keeps its input's sign bit
+ * (a negative value that rounds to zero gives code 0x8 and bf16 -0.0). The
+ * dequantized output is y = sign * bf16(v(k) * d), bf16 rounded to nearest
+ * even. (Paper §3.1 "Motivation": FP4 fake quantization in the forward pass.)
+ *
+ * Global scale source (quantize_rtn, encode_guidance). For NVFP4 exactly one
+ * of gscale_in / gscale_out is non-NULL: gscale_in points at a caller-chosen
+ * S (its [0] is read); gscale_out receives {S, A} computed from the tensor.
+ * For MXFP4 both must be NULL.
+ *
+ * Streams and errors. Every call validates its arguments on the host before
+ * any HIP call, then enqueues its kernels on `stream` (a hipStream_t; NULL is
+ * the null stream) and returns without synchronizing. Calls allocate no
+ * memory. Results are bit-deterministic. A call that returns an error has
+ * enqueued nothing, except TRACE_ELAUNCH, which reports a HIP error seen at
+ * launch. Calls are reentrant and may run concurrently on different streams
+ * when their buffers are disjoint.
+ */
+#ifndef TRACE_FP4_H
+#define TRACE_FP4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TRACE_ABI_VERSION 1
+
+enum trace_fmt { TRACE_FMT_NVFP4 = 0, TRACE_FMT_MXFP4 = 1 };
+
+enum trace_status {
+  TRACE_OK = 0,
+  TRACE_EINVAL = -1,  /* NULL required pointer, bad fmt/bits/flag, bad gscale combination */
+  TRACE_ESHAPE = -2,  /* negative size, cols % B != 0, N overflow, workspace too small */
+  TRACE_EALIGN = -3,  /* a pointer misses its alignment */
+  TRACE_EALIAS = -4,  /* an output overlaps an input or another output */
+  TRACE_EDEVICE = -5, /* no current gfx950 device */
+  TRACE_ELAUNCH = -6  /* HIP reported an error when the kernels were enqueued */
+};
+
+/* TRACE_ABI_VERSION of the built library. */
+int trace_abi_version(void);
+
+/* Static name of a status code ("TRACE_OK", ...); "unknown status" otherwise. */
+const char* trace_status_str(int status);
+
+/*
+ * quantize_rtn — vanilla FP4 fake quantization of one tensor with its own
+ * scales (paper §3.1 "Motivation": QAT fake quantization; Fig. 4(a): RTN).
+ *
+ *   x       in   bf16[N]
+ *   codes   out  uint8[N/2]      E2M1 codes of RTN(t)
+ *   scales  out  uint8[N/B]      block scales
+ *   gscale_in / gscale_out       see "Global scale source"
+ *   y_opt   out  bf16[N] or NULL dequantized output y
+ */
+int quantize_rtn(int fmt, int64_t rows, int64_t cols, const uint16_t* x,
+                 const float* gscale_in, uint8_t* codes, uint8_t* scales,
+                 float* gscale_out, uint16_t* y_opt, void* stream);
+
+/*
+ * encode_guidance — rollout side: quantize with RTN and emit the guidance
+ * record (paper §3.2 "Key Design", Fig. 6; §4.2 "Rollout Efficiency": one
+ * mantissa bit plus the amortized block scale, 1.5 bits per element for
+ * NVFP4; Algorithm 1 prose: packed low-bit rollout codes plus the rollout
+ * scales).
+ *
+ *   bits    1: guide = mbits uint8[N/8] (mantissa bit of each rollout code)
+ *           4: guide = codes uint8[N/2] (the full signed rollout codes, the
+ *              full-information record of §3.1)
+ *   x_rollout      in   bf16[N]
+ *   guide          out  see bits
+ *   scales         out  uint8[N/B]
+ *   gscale_in / gscale_out     see "Global scale source"
+ *   y_rollout_opt  out  bf16[N] or NULL, the rollout's own dequantized output
+ */
+int encode_guidance(int fmt, int bits, int64_t rows, int64_t cols,
+                    const uint16_t* x_rollout, const float* gscale_in,
+                    uint8_t* guide, uint8_t* scales, float* gscale_out,
+                    uint16_t* y_rollout_opt, void* stream);
+
+/*
+ * decode_guidance — training side, compact record: Reconstruct (Algorithm 1
+ * prose). For each element, t = |x_train| * r under the ROLLOUT block scale;
+ * the reference index is the E2M1 magnitude nearest t whose mantissa bit
+ * equals the rollout bit, ties toward the larger magnitude; its sign is the
+ * training sign. A rollout block whose scale is zero gives t = 0.
+ *
+ *   x_train   in   bf16[N]
+ *   mbits     in   uint8[N/8]   from encode_guidance(bits=1)
+ *   scales    in   uint8[N/B]   rollout block scales
+ *   gscale    in   float[>=1]   NVFP4: rollout S at [0]; MXFP4: must be NULL
+ *   ref_codes out  uint8[N/2]
+ */
+int decode_guidance(int fmt, int64_t rows, int64_t cols, const uint16_t* x_train,
+                    const uint8_t* mbits, const uint8_t* scales, const float* gscale,
+                    uint8_t* ref_codes, void* stream);
+
+/*
+ * guided_fake_quant — training side, rollout-guided rounding (paper §3.1
+ * "Key Design", Eq. 2 prose; Algorithm 1 prose: BracketFP4 then the candidate
+ * nearest the reference, STE forward value). Under the ROLLOUT scales,
+ * t = |x_train| * r is bracketed by its two neighbouring E2M1 magnitudes
+ * {q-, q+} (a single one when t is a codeword or t >= 6) and one is chosen:
+ *
+ *   bits 0  RTN (the q_RTN of the local guarantee, §3.1); guide must be NULL
+ *   bits 1  the candidate nearest the Reconstruct reference (decode fused);
+ *           guide = mbits uint8[N/8]
+ *   bits 4  the candidate nearest the exact rollout codeword, both signed
+ *           (candidates carry the training sign); guide = codes uint8[N/2]
+ *
+ *   x_train    in   bf16[N]
+ *   guide      in   see bits
+ *   scales     in   uint8[N/B]   rollout block scales
+ *   gscale     in   float[>=1]   NVFP4: rollout S at [0]; MXFP4: must be NULL
+ *   y          out  bf16[N]      sign(x_train) * bf16(v(k) * d_rollout)
+ *   codes_opt  out  uint8[N/2] or NULL, the chosen codes
+ */
+int guided_fake_quant(int fmt, int bits, int64_t rows, int64_t cols,
+                      const uint16_t* x_train, const uint8_t* guide,
+                      const uint8_t* scales, const float* gscale, uint16_t* y,
+                      uint8_t* codes_opt, void* stream);
+
+/*
+ * discrepancy_stats — the sums behind the train–rollout discrepancy
+ * measures (paper §3.1 "Motivation", Eq. 1; "Key Design", Fig. 4(b):
+ * D_FP4, D_BF16 and the relative excess (D_FP4 - D_BF16) / D_BF16).
+ *
+ *   n          number of elements in each of the four arrays
+ *   x_t, x_r   in  bf16[n]  training / rollout inputs
+ *   y_t, y_r   in  bf16[n]  training / rollout FP4 outputs
+ *   acc3       out float64[3] = {SB, SF, count}: SB = sum (x_t - x_r)^2,
+ *              SF = sum (y_t - y_r)^2, count = n. accumulate = 0 overwrites,
+ *              1 adds to the previous contents (a per-layer sum over chunks).
+ *   work       scratch device memory of at least
+ *              trace_stats_workspace_bytes(n) bytes, 8-byte aligned; its
+ *              contents on entry do not matter and are left undefined.
+ *   work_bytes size of `work`
+ *
+ * Sums are taken in float64 in a fixed order (determined by n alone), so the
+ * result is bit-identical from run to run.
+ */
+int discrepancy_stats(int64_t n, const uint16_t* x_t, const uint16_t* x_r,
+                      const uint16_t* y_t, const uint16_t* y_r, double* acc3,
+                      int accumulate, void* work, int64_t work_bytes, void* stream);
+
+/* Bytes of workspace discrepancy_stats needs for n elements (>= 16). */
+int64_t trace_stats_workspace_bytes(int64_t n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TRACE_FP4_H */

@@ -1,0 +1,157 @@
+"""The C-ABI library loads without a GPU, exports every call the header
+declares, and rejects bad arguments on the host before any HIP call.
+
+No test here may reach a kernel launch: every call below fails validation,
+except the EDEVICE check, which only runs when no GPU is visible.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from precision_rl_nvfp4_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "trace_fp4.h")
+
+A = 0x100000            # a fake, 16-byte-aligned "device" address; never dereferenced
+B = 0x200000
+C = 0x300000
+D = 0x400000
+E = 0x500000
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?\w[\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M)) - {"if"}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _abi.load()
+
+
+def test_library_builds_are_present():
+    assert os.path.exists(_abi.LIB_PATH), "run __graft_entry__.build() first"
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert {"quantize_rtn", "encode_guidance", "decode_guidance", "guided_fake_quant",
+            "discrepancy_stats", "trace_abi_version", "trace_status_str",
+            "trace_stats_workspace_bytes"} <= names
+    raw = ctypes.CDLL(_abi.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+    assert set(_abi.SIGNATURES) == names
+
+
+def test_version_and_status_strings(lib):
+    assert lib.trace_abi_version() == 1
+    for code, name in [(0, "TRACE_OK"), (-1, "TRACE_EINVAL"), (-2, "TRACE_ESHAPE"),
+                       (-3, "TRACE_EALIGN"), (-4, "TRACE_EALIAS"), (-5, "TRACE_EDEVICE"),
+                       (-6, "TRACE_ELAUNCH"), (7, "unknown status")]:
+        assert _abi.status_str(code) == name
+
+
+def test_workspace_size(lib):
+    assert lib.trace_stats_workspace_bytes(0) == 16
+    assert lib.trace_stats_workspace_bytes(8192 * 2048) == 16 * 1024
+    assert lib.trace_stats_workspace_bytes(-1) == 0
+
+
+# quantize_rtn(fmt, rows, cols, x, gin, codes, scales, gout, y, stream)
+@pytest.mark.parametrize("args,status", [
+    ((2, 4, 32, A, None, B, C, D, None, None), _abi.EINVAL),          # bad fmt
+    ((0, 4, 24, A, None, B, C, D, None, None), _abi.ESHAPE),          # cols % 16
+    ((1, 4, 48, A, None, B, C, None, None, None), _abi.ESHAPE),       # cols % 32
+    ((0, -1, 32, A, None, B, C, D, None, None), _abi.ESHAPE),         # negative rows
+    ((0, 2 ** 40, 2 ** 20, A, None, B, C, D, None, None), _abi.ESHAPE),  # N overflow guard
+    ((0, 4, 32, A, None, B, C, None, None, None), _abi.EINVAL),       # NVFP4 needs a gscale
+    ((0, 4, 32, A, E, B, C, D, None, None), _abi.EINVAL),             # both gscale_in and out
+    ((1, 4, 32, A, E, B, C, None, None, None), _abi.EINVAL),          # MXFP4 takes no gscale
+    ((0, 4, 32, None, None, B, C, D, None, None), _abi.EINVAL),       # NULL x
+    ((0, 4, 32, A, None, None, C, D, None, None), _abi.EINVAL),       # NULL codes
+    ((0, 4, 32, A + 8, None, B, C, D, None, None), _abi.EALIGN),      # x not 16-B aligned
+    ((0, 4, 32, A, None, B + 2, C, D, None, None), _abi.EALIGN),      # codes not 4-B aligned
+    ((0, 4, 32, A, None, B, C, D, A + 16, None), _abi.EALIAS),        # y overlaps x
+    ((0, 4, 32, A, None, B, B + 8, D, None, None), _abi.EALIAS),      # scales overlap codes
+    ((0, 4, 32, A, None, B, C, A + 4, None, None), _abi.EALIAS),      # gscale_out inside x
+])
+def test_quantize_rtn_rejects(lib, args, status):
+    assert lib.quantize_rtn(*args) == status
+
+
+# encode_guidance(fmt, bits, rows, cols, x, gin, guide, scales, gout, y, stream)
+@pytest.mark.parametrize("args,status", [
+    ((0, 2, 4, 32, A, None, B, C, D, None, None), _abi.EINVAL),       # bits 2
+    ((0, 0, 4, 32, A, None, B, C, D, None, None), _abi.EINVAL),       # bits 0
+    ((0, 4, 4, 32, A, None, B + 1, C, D, None, None), _abi.EALIGN),   # code plane alignment
+    ((0, 1, 4, 32, A, None, B, B + 8, D, None, None), _abi.EALIAS),   # bit plane is 16 B here
+    ((0, 1, 4, 32, A, None, A + 100, C, D, None, None), _abi.EALIAS),
+])
+def test_encode_guidance_rejects(lib, args, status):
+    assert lib.encode_guidance(*args) == status
+
+
+# decode_guidance(fmt, rows, cols, x, mbits, scales, gscale, ref, stream)
+@pytest.mark.parametrize("args,status", [
+    ((0, 4, 32, A, B, C, None, D, None), _abi.EINVAL),               # NVFP4 needs rollout S
+    ((1, 4, 32, A, B, C, E, D, None), _abi.EINVAL),                  # MXFP4 takes none
+    ((0, 4, 32, A, None, C, E, D, None), _abi.EINVAL),               # NULL mbits
+    ((0, 4, 32, A, B, C, E, None, None), _abi.EINVAL),               # NULL output
+    ((0, 4, 32, A, B, C, E, D + 1, None), _abi.EALIGN),
+    ((0, 4, 32, A, B, C, E, B, None), _abi.EALIAS),                  # output on the bits
+])
+def test_decode_guidance_rejects(lib, args, status):
+    assert lib.decode_guidance(*args) == status
+
+
+# guided_fake_quant(fmt, bits, rows, cols, x, guide, scales, gscale, y, codes, stream)
+@pytest.mark.parametrize("args,status", [
+    ((0, 3, 4, 32, A, B, C, E, D, None, None), _abi.EINVAL),          # bits 3
+    ((0, 0, 4, 32, A, B, C, E, D, None, None), _abi.EINVAL),          # bits 0 takes no guide
+    ((0, 1, 4, 32, A, None, C, E, D, None, None), _abi.EINVAL),       # bits 1 needs a guide
+    ((0, 1, 4, 32, A, B, C, E, None, None, None), _abi.EINVAL),       # NULL y
+    ((0, 4, 4, 32, A, B + 2, C, E, D, None, None), _abi.EALIGN),      # code guide alignment
+    ((0, 1, 4, 32, A, B, C, E, D + 8, None, None), _abi.EALIGN),      # y alignment
+    ((0, 1, 4, 32, A, B, C, E, A, None, None), _abi.EALIAS),          # in-place y over x
+    ((0, 1, 4, 32, A, B, C, E, D, D + 64, None), _abi.EALIAS),        # codes inside y
+    ((0, 1, 4, 32, A, B, C, E, D, C, None), _abi.EALIAS),             # codes over scales
+])
+def test_guided_fake_quant_rejects(lib, args, status):
+    assert lib.guided_fake_quant(*args) == status
+
+
+# discrepancy_stats(n, xt, xr, yt, yr, acc, accumulate, work, work_bytes, stream)
+@pytest.mark.parametrize("args,status", [
+    ((64, A, B, C, D, E, 2, E + 64, 16, None), _abi.EINVAL),          # accumulate flag
+    ((-5, A, B, C, D, E, 0, E + 64, 16, None), _abi.ESHAPE),
+    ((64, A, B, C, D, None, 0, E + 64, 16, None), _abi.EINVAL),
+    ((64, A, B, C, D, E, 0, None, 16, None), _abi.EINVAL),
+    ((64, A, B, C, D, E, 0, E + 64, 8, None), _abi.ESHAPE),           # workspace too small
+    ((64, A + 2, B, C, D, E, 0, E + 64, 16, None), _abi.EALIGN),
+    ((64, A, B, C, D, E + 4, 0, E + 64, 16, None), _abi.EALIGN),
+    ((64, A, B, C, D, A + 8, 0, E + 64, 16, None), _abi.EALIAS),      # acc inside x_t
+    ((64, A, B, C, D, E, 0, E + 8, 16, None), _abi.EALIAS),           # work over acc
+])
+def test_discrepancy_stats_rejects(lib, args, status):
+    assert lib.discrepancy_stats(*args) == status
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is visible: valid calls would launch")
+def test_valid_call_without_gpu_is_edevice(lib):
+    assert lib.quantize_rtn(0, 4, 32, A, None, B, C, D, None, None) == _abi.EDEVICE
+    assert lib.guided_fake_quant(1, 1, 4, 32, A, B, C, None, D, None, None) == _abi.EDEVICE
+    assert lib.discrepancy_stats(64, A, B, C, D, E, 0, E + 64, 16, None) == _abi.EDEVICE
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_abi, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_abi, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        _abi.load()

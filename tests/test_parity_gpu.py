@@ -1,0 +1,292 @@
+"""GPU parity: every entry point against the CPU oracle, bit for bit, on
+seeded inputs at sizes the oracle finishes in seconds. Sizes span several
+workgroup tiles (8,192 elements each) and end in a ragged tail.
+
+The statistics are compared within 1e-6 relative (the oracle sums in float64
+in a different order)."""
+
+import numpy as np
+import pytest
+import torch
+
+import precision_rl_nvfp4_amd as tq
+import synthetic as syn
+from oracle import formats, fp4 as ofp4
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+
+NV, MX = tq.NVFP4, tq.MXFP4
+
+
+def _pair(rows, cols, seed, mx=False):
+    if mx:
+        xt, xr = syn.mxfp4_pair(rows=rows, cols=cols, frac=0.01)
+    else:
+        xt, xr = syn.activation_pair(rows, cols, (90, seed))
+    return syn.bits_u16(xt), syn.bits_u16(xr)
+
+
+SHAPES = [  # (rows, cols): one block, sub-tile, ragged multi-tile, tiny workload, KV rows
+    (1, 32), (7, 96), (37, 2048), (256, 2048), (333, 256),
+]
+
+
+@pytest.mark.parametrize("fmt", [NV, MX])
+@pytest.mark.parametrize("rows,cols", SHAPES)
+def test_quantize_rtn(fmt, rows, cols):
+    G.say(f"quantize_rtn fmt={fmt} shape=({rows},{cols})")
+    xt, _ = _pair(rows, cols, rows, mx=(fmt == MX and cols % 32 == 0))
+    G.check_quantize(xt, rows, cols, fmt)
+
+
+@pytest.mark.parametrize("fmt", [NV, MX])
+@pytest.mark.parametrize("bits", [1, 4])
+@pytest.mark.parametrize("rows,cols", SHAPES)
+def test_encode_guidance(fmt, bits, rows, cols):
+    G.say(f"encode_guidance fmt={fmt} bits={bits} shape=({rows},{cols})")
+    _, xr = _pair(rows, cols, rows + 1, mx=(fmt == MX))
+    G.check_encode(xr, rows, cols, fmt, bits)
+
+
+@pytest.mark.parametrize("fmt", [NV, MX])
+@pytest.mark.parametrize("bits", [0, 1, 4])
+@pytest.mark.parametrize("rows,cols", SHAPES)
+def test_guided_fake_quant(fmt, bits, rows, cols):
+    G.say(f"guided_fake_quant fmt={fmt} bits={bits} shape=({rows},{cols})")
+    xt, xr = _pair(rows, cols, rows + 2, mx=(fmt == MX))
+    G.check_guided(xt, xr, rows, cols, fmt, bits, with_codes=True)
+    G.check_guided(xt, xr, rows, cols, fmt, bits, with_codes=False)
+
+
+@pytest.mark.parametrize("fmt", [NV, MX])
+@pytest.mark.parametrize("rows,cols", SHAPES)
+def test_decode_guidance(fmt, rows, cols):
+    G.say(f"decode_guidance fmt={fmt} shape=({rows},{cols})")
+    xt, xr = _pair(rows, cols, rows + 3, mx=(fmt == MX))
+    G.check_decode(xt, xr, rows, cols, fmt)
+
+
+def test_quantize_without_y_and_with_given_scale():
+    G.say("quantize_rtn given S / no y")
+    xt, _ = _pair(64, 2048, 5)
+    G.check_quantize(xt, 64, 2048, NV, with_y=False)
+    for s in (1.0, 0.37, 1e-3, 3.0e4):
+        G.check_quantize(xt, 64, 2048, NV, gscale=np.float32(s))
+
+
+def test_empty_tensors():
+    G.say("empty tensors")
+    x = torch.empty(0, 2048, dtype=torch.bfloat16, device=G.DEV)
+    q = tq.quantize_rtn(x, NV)
+    assert G.f32(q.gscale).tolist() == [1.0, 0.0]
+    g = tq.encode_guidance(x, MX, 1)
+    y, c = tq.guided_fake_quant(x, g, with_codes=True)
+    assert y.numel() == 0 and c.numel() == 0
+    acc = tq.discrepancy_stats(x, x, x, x)
+    assert acc.cpu().tolist() == [0.0, 0.0, 0.0]
+
+
+def _edge_tensor():
+    """Blocks that exercise the scale corner cases: zero blocks, E4M3
+    subnormal and zero scales next to a huge anchor, signed zeros, exact
+    codewords, the largest bf16 values."""
+    f = np.zeros((16, 64), np.float32)
+    f[0, 0] = 3.0e38                         # tensor amax near the bf16 top
+    f[1, :16] = np.linspace(-1e34, 1e34, 16)  # scale e in the subnormal range
+    f[1, 16:32] = 1e33                        # e = 0: zero block
+    f[2, :] = -0.0
+    f[3, :16] = np.array([6, 4, 3, 2, 1.5, 1, .5, 0, -6, -4, -3, -2, -1.5, -1, -.5, -0.0]) * 1e36
+    f[4, :] = np.linspace(-3e38, 3e38, 64)
+    f[5, :32] = 2.0 ** -133                  # bf16 subnormals
+    b = formats.f32_to_bf16(f)
+    b[2, :] = 0x8000
+    b[5, 32:] = np.arange(1, 33, dtype=np.uint16)   # more subnormal patterns
+    return b.reshape(-1)
+
+
+@pytest.mark.parametrize("fmt", [NV, MX])
+def test_scale_corner_cases(fmt):
+    G.say(f"scale corner cases fmt={fmt}")
+    b = _edge_tensor()
+    G.check_quantize(b, 16, 64, fmt)
+    for bits in (1, 4):
+        G.check_encode(b, 16, 64, fmt, bits)
+    b2 = b.copy()
+    b2[::3] ^= 0x0001                        # perturb the training side a little
+    for bits in (0, 1, 4):
+        G.check_guided(b2, b, 16, 64, fmt, bits)
+    G.check_decode(b2, b, 16, 64, fmt)
+
+
+def test_tiny_amax_clamps_global_scale():
+    G.say("tiny amax")
+    b = np.zeros(64, np.uint16)
+    b[:8] = np.arange(1, 9)                   # largest value is the 8th bf16 subnormal
+    G.check_quantize(b, 2, 32, NV)
+    o = ofp4.quantize_rtn(NV, b)
+    assert o["gscale"] == formats.FLT_MAX
+
+
+def _enumeration_members():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    f = formats.bf16_to_f32(bits)
+    return bits[np.isfinite(f) & (np.abs(f) <= 6.0)]
+
+
+def test_enumerate_bf16_members_unit_scale():
+    """Every finite bf16 value with |x| <= 6 as a non-max block member under
+    S = 1, e = 1 (and under MXFP4, E = 0): all five calls, GPU vs oracle."""
+    G.say("enumeration: block members")
+    members = _enumeration_members()
+    per = 15
+    nblk = -(-members.size // per)
+    nblk += nblk % 2 == 0                    # anchor block + members: an even block count
+    x = np.zeros((nblk + 1, 16), np.uint16)
+    x[0, 0] = formats.f32_to_bf16(np.array([2688.0], np.float32))[0]
+    x[1:, 0] = formats.f32_to_bf16(np.array([6.0], np.float32))[0]
+    flat = np.zeros(nblk * per, np.uint16)
+    flat[: members.size] = members
+    x[1:, 1:] = flat.reshape(nblk, per)
+    rows = (nblk + 1) // 2
+    xb = x.reshape(-1)
+    assert xb.size == rows * 32
+    G.check_quantize(xb, rows, 32, NV)
+    G.check_quantize(xb, rows, 32, MX)
+    rng = np.random.default_rng(0)
+    for _ in range(2):
+        # rollout side: the same blocks with members replaced by random codewords
+        xr = xb.copy()
+        pick = rng.integers(0, 16, xr.size)
+        vals = np.array([0, .5, 1, 1.5, 2, 3, 4, 6, -0.0, -.5, -1, -1.5, -2, -3, -4, -6], np.float32)
+        keep = np.zeros(xr.size, bool)
+        keep[0::16] = True
+        xr = np.where(keep, xr, formats.f32_to_bf16(vals[pick]))
+        for fmt in (NV, MX):
+            for bits in (0, 1, 4):
+                G.check_guided(xb, xr, rows, 32, fmt, bits)
+            G.check_decode(xb, xr, rows, 32, fmt)
+
+
+def test_enumerate_bf16_block_max():
+    """Every positive finite bf16 value as the max of its block, under three
+    tensor anchors (the amax sets S): E4M3 normal, subnormal and zero scales,
+    and the FLT_MAX clamp of S all occur."""
+    G.say("enumeration: block max")
+    pos = np.arange(1, 0x7F80, dtype=np.uint16)
+    blocks = np.zeros((pos.size, 16), np.uint16)
+    blocks[:, 0] = pos
+    blocks[:, 1] = pos >> 1                     # a smaller member
+    blocks[:, 2] = (pos - 1) | 0x8000           # a negative member
+    for anchor in (0x7F7F, 0x4F00, 0x3F80):     # ~3.4e38, 2^31, 1.0
+        keep = pos <= anchor
+        xb = np.concatenate([[anchor], np.zeros(15, np.uint16), blocks[keep].reshape(-1)]).astype(np.uint16)
+        pad = (-xb.size) % 32
+        xb = np.concatenate([xb, np.zeros(pad, np.uint16)])
+        rows = xb.size // 32
+        G.check_quantize(xb, rows, 32, NV)
+        G.check_quantize(xb, rows, 32, MX)
+
+
+def test_guided_guarantee_on_gpu_outputs():
+    """§3.1: on every element, |y_guided - y_r| <= |y_RTN(rollout scale) - y_r|
+    with full-information guidance."""
+    G.say("guarantee on GPU outputs")
+    xt, xr = _pair(256, 2048, 77)
+    t, r = G.to_dev(xt, 256, 2048), G.to_dev(xr, 256, 2048)
+    g = tq.encode_guidance(r, NV, 4, with_y=True)
+    yg, _ = tq.guided_fake_quant(t, g, bits=4)
+    yn, _ = tq.guided_fake_quant(t, g, bits=0)
+    dg = (yg.float() - g.y.float()).abs()
+    dn = (yn.float() - g.y.float()).abs()
+    assert bool((dg <= dn).all())
+    assert float(dg.sum()) < float(dn.sum())
+
+
+def test_stats_vs_oracle_and_deterministic():
+    G.say("discrepancy_stats")
+    for rows, cols in [(1, 16), (37, 2048), (256, 2048), (4096, 2048)]:
+        xt, xr = _pair(rows, cols, 11)
+        t, r = G.to_dev(xt, rows, cols), G.to_dev(xr, rows, cols)
+        q_t = tq.quantize_rtn(t, NV)
+        q_r = tq.quantize_rtn(r, NV)
+        acc = tq.discrepancy_stats(t, r, q_t.y, q_r.y)
+        acc2 = tq.discrepancy_stats(t, r, q_t.y, q_r.y)
+        assert torch.equal(acc, acc2)
+        sb, sf, n = ofp4.discrepancy_stats(xt, xr, G.bits_of(q_t.y), G.bits_of(q_r.y))
+        a = acc.cpu().numpy()
+        assert a[2] == n
+        assert abs(a[0] - sb) <= 1e-6 * abs(sb)
+        assert abs(a[1] - sf) <= 1e-6 * abs(sf)
+        # accumulate over two halves equals one call
+        half = rows * cols // 2
+        if half % 8 == 0 and half > 0:
+            fl = [v.reshape(-1) for v in (t, r, q_t.y, q_r.y)]
+            acc3 = tq.discrepancy_stats(*(v[:half] for v in fl))
+            tq.discrepancy_stats(*(v[half:] for v in fl), acc=acc3, accumulate=True)
+            b = acc3.cpu().numpy()
+            assert b[2] == n and abs(b[0] - sb) <= 1e-6 * sb and abs(b[1] - sf) <= 1e-6 * sf
+
+
+def test_stats_ragged_lengths():
+    G.say("discrepancy_stats ragged")
+    rng = np.random.default_rng(3)
+    for n in (1, 7, 9, 8191, 100003):
+        arrs = [formats.f32_to_bf16(rng.normal(size=n).astype(np.float32)) for _ in range(4)]
+        devs = [torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).to(G.DEV) for a in arrs]
+        acc = tq.discrepancy_stats(*devs).cpu().numpy()
+        sb, sf, cnt = ofp4.discrepancy_stats(*arrs)
+        assert acc[2] == cnt and abs(acc[0] - sb) <= 1e-6 * sb and abs(acc[1] - sf) <= 1e-6 * sf
+
+
+def test_outputs_deterministic():
+    G.say("determinism")
+    xt, xr = _pair(256, 2048, 21)
+    t, r = G.to_dev(xt, 256, 2048), G.to_dev(xr, 256, 2048)
+    outs = []
+    for _ in range(2):
+        g = tq.encode_guidance(r, NV, 1, with_y=True)
+        y, c = tq.guided_fake_quant(t, g, with_codes=True)
+        outs.append([G.u8(g.guide), G.u8(g.scales), G.bits_of(g.y), G.bits_of(y), G.u8(c)])
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+
+
+def test_writes_stay_in_bounds():
+    """Canary bytes around every output survive each call."""
+    G.say("canaries")
+    rows, cols = 37, 2048
+    xt, xr = _pair(rows, cols, 31)
+    t, r = G.to_dev(xt, rows, cols), G.to_dev(xr, rows, cols)
+    n = rows * cols
+    PAD = 4096
+
+    def guarded(nbytes, dtype=torch.uint8):
+        raw = torch.full((nbytes + 2 * PAD,), 0xA5, dtype=torch.uint8, device=G.DEV)
+        return raw, raw[PAD:PAD + nbytes].view(dtype)
+
+    def intact(raw, nbytes):
+        h = raw.cpu().numpy()
+        return bool((h[:PAD] == 0xA5).all() and (h[PAD + nbytes:] == 0xA5).all())
+
+    for fmt in (NV, MX):
+        B = 16 if fmt == NV else 32
+        rc, codes = guarded(n // 2)
+        rs, scales = guarded(n // B)
+        ry, yb = guarded(2 * n)
+        rg, gs = guarded(8)
+        tq.quantize_rtn(t, fmt, codes=codes.view(rows, cols // 2), scales=scales.view(rows, cols // B),
+                        gscale_out=gs.view(torch.float32) if fmt == NV else None,
+                        y=yb.view(torch.bfloat16).view(rows, cols))
+        torch.cuda.synchronize()
+        assert intact(rc, n // 2) and intact(rs, n // B) and intact(ry, 2 * n) and intact(rg, 8)
+        rb, bits = guarded(n // 8)
+        g = tq.encode_guidance(r, fmt, 1, guide=bits.view(rows, cols // 8))
+        ry2, y2 = guarded(2 * n)
+        rc2, c2 = guarded(n // 2)
+        tq.guided_fake_quant(t, g, with_codes=True, y=y2.view(torch.bfloat16).view(rows, cols),
+                             codes=c2.view(rows, cols // 2))
+        rr, refc = guarded(n // 2)
+        tq.decode_guidance(t, g, ref_codes=refc.view(rows, cols // 2))
+        torch.cuda.synchronize()
+        assert intact(rb, n // 8) and intact(ry2, 2 * n) and intact(rc2, n // 2) and intact(rr, n // 2)
