@@ -1,0 +1,349 @@
+#!/usr/bin/env python3
+"""Throughput of the rollout-guided FP4 hot path on one MI355X.
+
+Workload: the long-trajectory stream. 20 guided (deepest) MoE layers x 17
+chunks of 8,192 tokens x 2,048 hidden, bf16 train/rollout pairs (8K prompt +
+128K response = 139,264 tokens per layer), NVFP4 with one FP32 global scale
+per chunk. A step is one pass of the whole path over that batch, one call per
+layer and side (the 17 chunks of a layer are the call's global-scale groups):
+
+  rollout side   encode_guidance(bits=1): per-chunk amax -> global scale,
+                 E4M3 block scales, RTN codes, the packed mantissa-bit plane
+  training side  guided_fake_quant_stats(bits=1): Reconstruct + BracketFP4 +
+                 selection + bf16 dequantization -> y_t, and in the same pass
+                 the layer's sums of (x_t - x_r)^2 and (y_t - y_r)^2 (y_r the
+                 rollout's RTN output, recomputed from x_r)
+
+Inputs are seeded synthetic tensors drawn on the GPU (no model, no dataset);
+they are resident in HBM before the timed region starts. Every kernel runs
+through the C ABI of libtrace_fp4.so; the binding only passes pointers.
+
+Prints one JSON line. ``roofline`` covers the call with the largest share of
+step time, from HIP events recorded on the launch stream around each phase;
+``kernels`` also reports plain guided_fake_quant (no statistics) timed the same
+way outside the step; ``cpu_baseline`` times the CPU oracle on a bounded
+sample of the same workload in a process pool.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD public specification
+HIDDEN = 2048
+CHUNK = 8192
+NV = 0
+
+# Algorithmic bytes per element (one read of every input, one write of every
+# output; the per-chunk global scales add 8 bytes per 16.8M elements), NVFP4,
+# 1-bit guidance.
+BPE = {
+    "encode_guidance": 2 + 1 / 8 + 1 / 16,                 # x_r in; mantissa bits, scales out
+    "guided_fake_quant_stats": 2 + 2 + 1 / 8 + 1 / 16 + 2,  # x_t, x_r, bits, scales in; y_t out
+    "guided_fake_quant": 2 + 1 / 8 + 1 / 16 + 2,           # x_t, bits, scales in; y_t out
+}
+# rocprofv3 kernel names of each call's main kernel.
+KERNEL_NAME = {
+    "encode_guidance": "quantize_kernel",
+    "guided_fake_quant_stats": "guided_kernel",
+    "guided_fake_quant": "guided_kernel",
+}
+KERNEL_SRC = os.path.join(ROOT, "precision_rl_nvfp4_amd", "csrc", "trace_fp4_kernels.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=20, help="guided layers (deepest first)")
+    ap.add_argument("--chunks", type=int, default=17, help="8192-token chunks per layer")
+    ap.add_argument("--cpu-workers", type=int, default=0, help="0: usable cores, at most 16")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle wall time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the plain guided_fake_quant timing")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain device copy of known size (counter calibration)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------- workload
+
+class Workload:
+    """All chunks of the stream, resident in HBM, as [layers, chunks*8192, 2048]."""
+
+    def __init__(self, torch, syn, layers, chunks, dev):
+        self.layers, self.chunks = layers, chunks
+        self.rows = chunks * CHUNK
+        self.n = self.rows * HIDDEN                      # elements per layer call
+        shape = (layers, self.rows, HIDDEN)
+        self.xt = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        self.xr = torch.empty_like(self.xt)
+        for li, layer in enumerate(syn.GUIDED_LAYERS[:layers]):
+            sigma = syn.stream_sigma(layer, dev)
+            for c in range(chunks):
+                xt, xr = syn.stream_pair(layer, c, dev, sigma=sigma)
+                self.xt[li, c * CHUNK:(c + 1) * CHUNK].copy_(xt)
+                self.xr[li, c * CHUNK:(c + 1) * CHUNK].copy_(xr)
+                del xt, xr
+        self.guide = torch.empty((layers, self.rows, HIDDEN // 8), dtype=torch.uint8, device=dev)
+        self.scales = torch.empty((layers, self.rows, HIDDEN // 16), dtype=torch.uint8, device=dev)
+        self.gscale = torch.empty((layers, chunks, 2), dtype=torch.float32, device=dev)
+        self.yt = torch.empty_like(self.xt)
+        self.acc = torch.zeros((layers, 3), dtype=torch.float64, device=dev)
+
+    def bytes_resident(self):
+        ts = [self.xt, self.xr, self.guide, self.scales, self.gscale, self.yt, self.acc]
+        return sum(t.numel() * t.element_size() for t in ts)
+
+
+def build_phases(lib, w, stream, qwork, swork):
+    """Argument tuples of every ABI call, grouped by phase."""
+    qb, sb = qwork.numel() * qwork.element_size(), swork.numel() * swork.element_size()
+    enc, gst, gfq = [], [], []
+    for i in range(w.layers):
+        p = lambda t: t[i].data_ptr()  # noqa: E731
+        enc.append((NV, 1, w.rows, HIDDEN, CHUNK, p(w.xr), None, p(w.guide), p(w.scales),
+                    p(w.gscale), None, qwork.data_ptr(), qb, stream))
+        gst.append((NV, 1, w.rows, HIDDEN, CHUNK, p(w.xt), p(w.xr), p(w.guide), p(w.scales),
+                    p(w.gscale), p(w.yt), None, p(w.acc), 0, swork.data_ptr(), sb, stream))
+        gfq.append((NV, 1, w.rows, HIDDEN, CHUNK, p(w.xt), p(w.guide), p(w.scales), p(w.gscale),
+                    p(w.yt), None, stream))
+    step = [("encode_guidance", lib.encode_guidance, enc),
+            ("guided_fake_quant_stats", lib.guided_fake_quant_stats, gst)]
+    extra = [("guided_fake_quant", lib.guided_fake_quant, gfq)]
+    return step, extra
+
+
+def run_phases(phases, events=None):
+    for j, (name, fn, calls) in enumerate(phases):
+        if events is not None:
+            events[j].record()
+        for a in calls:
+            st = fn(*a)
+            if st != 0:
+                raise RuntimeError(f"{name} returned {st}")
+    if events is not None:
+        events[len(phases)].record()
+
+
+def timed(torch, phases, steps):
+    """Run `steps` passes with events around each phase; returns (wall s, per-phase ms lists)."""
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        run_phases(phases, evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [[evs[k][j].elapsed_time(evs[k][j + 1]) for k in range(steps)] for j in range(len(phases))]
+    return wall, per
+
+
+def kernel_entry(name, ms_list, calls, n):
+    steps = len(ms_list)
+    ms = sum(ms_list)
+    per_call_us = ms * 1e3 / (steps * calls)
+    algo = BPE[name] * n
+    gbs = algo / (per_call_us * 1e-6) / 1e9
+    return {"avg_us_per_call": round(per_call_us, 2), "calls_per_pass": calls,
+            "elements_per_call": n, "algorithmic_bytes_per_call": int(algo),
+            "GB_s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "Gelem_s": round(n / (per_call_us * 1e-6) / 1e9, 1),
+            "phase_ms_per_pass": round(ms / steps, 3)}
+
+
+# ---------------------------------------------------------------- counters
+
+def read_traffic(kernel):
+    """HBM bytes per launch of ``kernel`` from the committed rocprofv3 --pmc
+    summary, or None when there is none or the kernel source changed since
+    the counters were taken."""
+    path = os.path.join(PROFILES, f"{kernel}_stream_nvfp4_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    if fields.get("kernel_source_sha256") != src_hash:
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------- CPU baseline
+
+def _oracle_unit(args):
+    import numpy as np
+    from oracle import fp4 as ofp4
+    bt, br = args
+    e = ofp4.encode_guidance(ofp4.NVFP4, 1, br)
+    g = ofp4.guided_fake_quant(ofp4.NVFP4, 1, bt, e["guide"], e["scales"], e["gscale"])
+    ofp4.discrepancy_stats(bt, br, g["y"], e["y"])
+    return int(np.asarray(bt).size)
+
+
+def cpu_baseline(torch, w, workers, target_s):
+    """The oracle, as it stands, over 1024-token slices of the streamed
+    workload (each slice taken as one tensor with its own global scale),
+    through the same encode -> guided -> discrepancy path, in rounds of one
+    slice per worker process until about `target_s` seconds have passed."""
+    import multiprocessing as mp
+
+    import numpy as np
+    rows = 1024
+
+    def slice_bits(t, layer, r0):
+        return t[layer, r0:r0 + rows].contiguous().view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1)
+
+    ctx = mp.get_context("spawn")
+    elems, rounds, j = 0, 0, 0
+    with ctx.Pool(workers) as pool:
+        pool.map(_oracle_unit, [(np.zeros(32, np.uint16), np.zeros(32, np.uint16))] * workers)  # warm
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < target_s and rounds < 64:
+            jobs = []
+            for _ in range(workers):
+                layer = j % w.layers
+                r0 = ((j * 37) % (w.rows // rows)) * rows
+                jobs.append((slice_bits(w.xt, layer, r0), slice_bits(w.xr, layer, r0)))
+                j += 1
+            elems += sum(pool.map(_oracle_unit, jobs, chunksize=1))
+            rounds += 1
+        wall = time.perf_counter() - t0
+    return {
+        "value": round(elems / wall / 1e9, 6),
+        "unit": "Gelem/s",
+        "cores": workers,
+        "kind": "oracle",
+        "sample": (f"{rounds * workers} slices of {rows} tokens x {HIDDEN} from the streamed workload "
+                   f"({elems} elements per side), each one NVFP4 tensor: encode(bits=1) -> "
+                   f"guided(bits=1) -> discrepancy sums; {workers} worker processes, {rounds} rounds, "
+                   f"{wall:.1f} s wall"),
+    }
+
+
+# ---------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) is not supported: "
+              "the path has no cross-GPU step to run", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synthetic as syn
+    from precision_rl_nvfp4_amd import _abi
+
+    lib = _abi.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"bench: generating {args.layers} layers x {args.chunks} chunks of [{CHUNK}, {HIDDEN}] pairs")
+    t0 = time.perf_counter()
+    w = Workload(torch, syn, args.layers, args.chunks, dev)
+    qn = int(lib.trace_quant_workspace_bytes(NV, w.rows, HIDDEN, CHUNK))
+    sn = int(lib.trace_guided_stats_workspace_bytes(NV, w.rows, HIDDEN, CHUNK))
+    qwork = torch.empty(max(qn // 8, 1), dtype=torch.float64, device=dev)
+    swork = torch.empty(max(sn // 8, 1), dtype=torch.float64, device=dev)
+    torch.cuda.synchronize()
+    log(f"bench: workload ready in {time.perf_counter() - t0:.1f} s, "
+        f"{w.bytes_resident() / 2**30:.1f} GiB resident")
+
+    stream = torch.cuda.current_stream(dev)
+    step, extra = build_phases(lib, w, stream.cuda_stream, qwork, swork)
+
+    for i in range(args.warmup):
+        run_phases(step)
+        torch.cuda.synchronize()
+        log(f"bench: warmup step {i + 1}/{args.warmup} done")
+
+    wall, per = timed(torch, step, args.steps)
+    log(f"bench: {args.steps} timed steps in {wall:.3f} s")
+    acc = w.acc.cpu().tolist()               # sums of the last step
+
+    kernels = {name: kernel_entry(name, per[j], len(calls), w.n) for j, (name, _, calls) in enumerate(step)}
+    if not args.no_extra:
+        run_phases(extra)
+        _, per_x = timed(torch, extra, max(3, args.steps // 2))
+        kernels["guided_fake_quant"] = kernel_entry("guided_fake_quant", per_x[0], len(extra[0][2]), w.n)
+        kernels["guided_fake_quant"]["note"] = "timed outside the step (no statistics)"
+        log("bench: plain guided_fake_quant timed")
+
+    elems_step = w.layers * w.n
+    ms_step = wall * 1e3 / args.steps
+    dom = max((k for k, _, _ in step), key=lambda k: kernels[k]["phase_ms_per_pass"])
+    d = kernels[dom]
+    roofline = {"bound": "hbm", "achieved": d["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": d["frac_of_peak"], "traffic": read_traffic(KERNEL_NAME[dom]), "kernel": dom,
+                "algorithmic_bytes_per_launch": d["algorithmic_bytes_per_call"],
+                "avg_launch_us": d["avg_us_per_call"]}
+    rel = [((sf - sb) / sb) if sb > 0 else math.nan for sb, sf, _ in acc]
+
+    if args.copy_probe:
+        src = torch.empty(2**30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"bench: copy probe, 5 x {src.numel()} bytes device-to-device")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        try:
+            aff = len(os.sched_getaffinity(0))
+        except AttributeError:
+            aff = os.cpu_count() or 1
+        workers = args.cpu_workers or max(1, min(16, aff))
+        log(f"bench: cpu baseline (oracle) on {workers} workers")
+        cpu = cpu_baseline(torch, w, workers, args.cpu_seconds)
+
+    out = {
+        "metric": "guided FP4 fake-quant Gelem/s + achieved HBM GB/s (% of peak), 1 GPU",
+        "value": round(elems_step * args.steps / wall / 1e9, 2),
+        "unit": "Gelem/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "stream_nvfp4_136k_tokens", "layers": w.layers, "chunks": w.chunks,
+                   "chunk_tokens": CHUNK, "hidden": HIDDEN, "format": "nvfp4", "guide_bits": 1,
+                   "elements_per_side_per_step": elems_step},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "step_GB_s": round(sum(BPE[k] for k, _, _ in step) * elems_step / (ms_step * 1e-3) / 1e9, 1),
+        "rel_excess_mse_guided_per_layer": [round(r, 6) for r in rel],
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

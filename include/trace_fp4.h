@@ -13,12 +13,19 @@
  * for NVFP4, 32 for MXFP4, and cols must be a multiple of B. N = rows * cols.
  * Block j covers elements [j*B, (j+1)*B) of the flattened tensor.
  *
+ * Global-scale groups (NVFP4). group_rows > 0 splits the rows into
+ * G = rows / group_rows consecutive groups (group_rows must divide rows), each
+ * quantized as its own tensor with its own FP32 global scale; group_rows == 0
+ * means one group holding every row (G = 1). This lets one call cover, e.g.,
+ * all 8192-token chunks of a streamed layer. For MXFP4 (no global scale) the
+ * grouping has no effect on the results.
+ *
  * Pointers. Every pointer argument is a DEVICE pointer owned by the caller;
  * nothing is retained after the call returns. Input arrays are only read.
  * bf16 arrays must be 16-byte aligned; code planes 4-byte aligned; global
- * scales 4-byte aligned; the statistics accumulator and workspace 8-byte
- * aligned. Other planes have no alignment requirement. When N == 0 the data
- * pointers may be NULL.
+ * scales 4-byte aligned; workspaces and float64 accumulators 8-byte aligned.
+ * Other planes have no alignment requirement. When N == 0 the data pointers
+ * may be NULL.
  *
  * Planes written or read by the calls:
  *   codes   uint8[N/2]  E2M1 codes, code = sign << 3 | k, k the 3-bit magnitude
@@ -31,11 +38,11 @@
  *                       block order. Bytes read by a call must be valid
  *                       non-negative finite values (E4M3 <= 0x7E, E8M0 <= 254);
  *                       otherwise results are unspecified (memory-safe).
- *   gscale  float32[2]  NVFP4 only: [0] = the FP32 global scale S,
- *                       [1] = the tensor amax A it came from.
+ *   gscale  float32[2G] NVFP4 only: for group g, [2g] = the FP32 global scale
+ *                       S, [2g+1] = the group amax A it came from.
  *
- * Scaling (NVFP4). A = max|x| over the tensor; S = 2688 / A (1 if A == 0,
- * at most FLT_MAX). Per block with max a: u = (a / 6) * S, e = E4M3 of
+ * Scaling (NVFP4). A = max|x| over the group; S = 2688 / A (1 if A == 0, at
+ * most FLT_MAX). Per block with max a: u = (a / 6) * S, e = E4M3 of
  * min(u, 448) rounded to nearest even; decode factor d = e / S, encode factor
  * r = min(S / e, FLT_MAX), both 0 when e == 0. The normalized value of an
  * element is t = |x| * r. Binary32 arithmetic, each operation rounded, no
@@ -52,9 +59,10 @@
  * even. (Paper §3.1 "Motivation": FP4 fake quantization in the forward pass.)
  *
  * Global scale source (quantize_rtn, encode_guidance). For NVFP4 exactly one
- * of gscale_in / gscale_out is non-NULL: gscale_in points at a caller-chosen
- * S (its [0] is read); gscale_out receives {S, A} computed from the tensor.
- * For MXFP4 both must be NULL.
+ * of gscale_in / gscale_out is non-NULL: gscale_in holds a caller-chosen S
+ * per group (read at [2g]); gscale_out receives {S, A} per group computed from
+ * the tensor, and then `work` must hold trace_quant_workspace_bytes(...)
+ * bytes. For MXFP4 both must be NULL (and work may be NULL).
  *
  * Streams and errors. Every call validates its arguments on the host before
  * any HIP call, then enqueues its kernels on `stream` (a hipStream_t; NULL is
@@ -62,7 +70,8 @@
  * memory. Results are bit-deterministic. A call that returns an error has
  * enqueued nothing, except TRACE_ELAUNCH, which reports a HIP error seen at
  * launch. Calls are reentrant and may run concurrently on different streams
- * when their buffers are disjoint.
+ * when their buffers (workspaces included) are disjoint. Workspace contents
+ * on entry do not matter and are left undefined.
  */
 #ifndef TRACE_FP4_H
 #define TRACE_FP4_H
@@ -73,14 +82,15 @@
 extern "C" {
 #endif
 
-#define TRACE_ABI_VERSION 1
+#define TRACE_ABI_VERSION 2
 
 enum trace_fmt { TRACE_FMT_NVFP4 = 0, TRACE_FMT_MXFP4 = 1 };
 
 enum trace_status {
   TRACE_OK = 0,
   TRACE_EINVAL = -1,  /* NULL required pointer, bad fmt/bits/flag, bad gscale combination */
-  TRACE_ESHAPE = -2,  /* negative size, cols % B != 0, N overflow, workspace too small */
+  TRACE_ESHAPE = -2,  /* negative size, cols % B != 0, group_rows not dividing rows, N overflow,
+                         workspace too small */
   TRACE_EALIGN = -3,  /* a pointer misses its alignment */
   TRACE_EALIAS = -4,  /* an output overlaps an input or another output */
   TRACE_EDEVICE = -5, /* no current gfx950 device */
@@ -93,19 +103,33 @@ int trace_abi_version(void);
 /* Static name of a status code ("TRACE_OK", ...); "unknown status" otherwise. */
 const char* trace_status_str(int status);
 
+/* Workspace bytes quantize_rtn / encode_guidance need to derive the global
+ * scales from the amax (NVFP4 with gscale_out); 0 for MXFP4. -1 for an
+ * invalid shape. */
+int64_t trace_quant_workspace_bytes(int fmt, int64_t rows, int64_t cols, int64_t group_rows);
+
+/* Workspace bytes guided_fake_quant_stats needs. -1 for an invalid shape. */
+int64_t trace_guided_stats_workspace_bytes(int fmt, int64_t rows, int64_t cols,
+                                           int64_t group_rows);
+
+/* Workspace bytes discrepancy_stats needs for n elements (>= 16). */
+int64_t trace_stats_workspace_bytes(int64_t n);
+
 /*
- * quantize_rtn — vanilla FP4 fake quantization of one tensor with its own
- * scales (paper §3.1 "Motivation": QAT fake quantization; Fig. 4(a): RTN).
+ * quantize_rtn — vanilla FP4 fake quantization of one tensor (or of each
+ * group) with its own scales (paper §3.1 "Motivation": QAT fake
+ * quantization; Fig. 4(a): RTN).
  *
  *   x       in   bf16[N]
  *   codes   out  uint8[N/2]      E2M1 codes of RTN(t)
  *   scales  out  uint8[N/B]      block scales
  *   gscale_in / gscale_out       see "Global scale source"
  *   y_opt   out  bf16[N] or NULL dequantized output y
+ *   work, work_bytes             see "Global scale source"
  */
-int quantize_rtn(int fmt, int64_t rows, int64_t cols, const uint16_t* x,
-                 const float* gscale_in, uint8_t* codes, uint8_t* scales,
-                 float* gscale_out, uint16_t* y_opt, void* stream);
+int quantize_rtn(int fmt, int64_t rows, int64_t cols, int64_t group_rows, const uint16_t* x,
+                 const float* gscale_in, uint8_t* codes, uint8_t* scales, float* gscale_out,
+                 uint16_t* y_opt, void* work, int64_t work_bytes, void* stream);
 
 /*
  * encode_guidance — rollout side: quantize with RTN and emit the guidance
@@ -120,13 +144,13 @@ int quantize_rtn(int fmt, int64_t rows, int64_t cols, const uint16_t* x,
  *   x_rollout      in   bf16[N]
  *   guide          out  see bits
  *   scales         out  uint8[N/B]
- *   gscale_in / gscale_out     see "Global scale source"
+ *   gscale_in / gscale_out, work   see "Global scale source"
  *   y_rollout_opt  out  bf16[N] or NULL, the rollout's own dequantized output
  */
-int encode_guidance(int fmt, int bits, int64_t rows, int64_t cols,
-                    const uint16_t* x_rollout, const float* gscale_in,
-                    uint8_t* guide, uint8_t* scales, float* gscale_out,
-                    uint16_t* y_rollout_opt, void* stream);
+int encode_guidance(int fmt, int bits, int64_t rows, int64_t cols, int64_t group_rows,
+                    const uint16_t* x_rollout, const float* gscale_in, uint8_t* guide,
+                    uint8_t* scales, float* gscale_out, uint16_t* y_rollout_opt, void* work,
+                    int64_t work_bytes, void* stream);
 
 /*
  * decode_guidance — training side, compact record: Reconstruct (Algorithm 1
@@ -138,12 +162,12 @@ int encode_guidance(int fmt, int bits, int64_t rows, int64_t cols,
  *   x_train   in   bf16[N]
  *   mbits     in   uint8[N/8]   from encode_guidance(bits=1)
  *   scales    in   uint8[N/B]   rollout block scales
- *   gscale    in   float[>=1]   NVFP4: rollout S at [0]; MXFP4: must be NULL
+ *   gscale    in   float[2G]    NVFP4: rollout S of group g at [2g]; MXFP4: NULL
  *   ref_codes out  uint8[N/2]
  */
-int decode_guidance(int fmt, int64_t rows, int64_t cols, const uint16_t* x_train,
-                    const uint8_t* mbits, const uint8_t* scales, const float* gscale,
-                    uint8_t* ref_codes, void* stream);
+int decode_guidance(int fmt, int64_t rows, int64_t cols, int64_t group_rows,
+                    const uint16_t* x_train, const uint8_t* mbits, const uint8_t* scales,
+                    const float* gscale, uint8_t* ref_codes, void* stream);
 
 /*
  * guided_fake_quant — training side, rollout-guided rounding (paper §3.1
@@ -161,14 +185,36 @@ int decode_guidance(int fmt, int64_t rows, int64_t cols, const uint16_t* x_train
  *   x_train    in   bf16[N]
  *   guide      in   see bits
  *   scales     in   uint8[N/B]   rollout block scales
- *   gscale     in   float[>=1]   NVFP4: rollout S at [0]; MXFP4: must be NULL
+ *   gscale     in   float[2G]    NVFP4: rollout S of group g at [2g]; MXFP4: NULL
  *   y          out  bf16[N]      sign(x_train) * bf16(v(k) * d_rollout)
  *   codes_opt  out  uint8[N/2] or NULL, the chosen codes
  */
-int guided_fake_quant(int fmt, int bits, int64_t rows, int64_t cols,
-                      const uint16_t* x_train, const uint8_t* guide,
-                      const uint8_t* scales, const float* gscale, uint16_t* y,
-                      uint8_t* codes_opt, void* stream);
+int guided_fake_quant(int fmt, int bits, int64_t rows, int64_t cols, int64_t group_rows,
+                      const uint16_t* x_train, const uint8_t* guide, const uint8_t* scales,
+                      const float* gscale, uint16_t* y, uint8_t* codes_opt, void* stream);
+
+/*
+ * guided_fake_quant_stats — guided_fake_quant plus, in the same pass over
+ * the data, the discrepancy sums of discrepancy_stats(x_train, x_rollout, y,
+ * y_rollout), where y_rollout is the rollout's RTN output under the same
+ * rollout scales (what encode_guidance writes to y_rollout_opt); it is
+ * recomputed from x_rollout instead of being read. Paper §3.1 Eq. 1 and
+ * Fig. 4(b) (D_BF16, D_FP4 and the relative excess).
+ *
+ *   x_rollout  in   bf16[N], the rollout input the record was encoded from
+ *   acc3, accumulate           as in discrepancy_stats
+ *   work, work_bytes           trace_guided_stats_workspace_bytes(...) bytes
+ *   other arguments            as in guided_fake_quant
+ *
+ * The sums equal discrepancy_stats' within 5 * 2^-24 relative (binary32
+ * squares of single pairs, exact binary64 fallback outside a safe range); the
+ * summation order is fixed by the shape, so results are bit-deterministic.
+ */
+int guided_fake_quant_stats(int fmt, int bits, int64_t rows, int64_t cols, int64_t group_rows,
+                            const uint16_t* x_train, const uint16_t* x_rollout,
+                            const uint8_t* guide, const uint8_t* scales, const float* gscale,
+                            uint16_t* y, uint8_t* codes_opt, double* acc3, int accumulate,
+                            void* work, int64_t work_bytes, void* stream);
 
 /*
  * discrepancy_stats — the sums behind the train–rollout discrepancy
@@ -181,20 +227,16 @@ int guided_fake_quant(int fmt, int bits, int64_t rows, int64_t cols,
  *   acc3       out float64[3] = {SB, SF, count}: SB = sum (x_t - x_r)^2,
  *              SF = sum (y_t - y_r)^2, count = n. accumulate = 0 overwrites,
  *              1 adds to the previous contents (a per-layer sum over chunks).
- *   work       scratch device memory of at least
- *              trace_stats_workspace_bytes(n) bytes, 8-byte aligned; its
- *              contents on entry do not matter and are left undefined.
+ *   work       trace_stats_workspace_bytes(n) bytes of device memory
  *   work_bytes size of `work`
  *
- * Sums are taken in float64 in a fixed order (determined by n alone), so the
- * result is bit-identical from run to run.
+ * Each sum is within 5 * 2^-24 relative of the exact value (see
+ * guided_fake_quant_stats) and taken in a fixed order determined by n alone,
+ * so the result is bit-identical from run to run.
  */
 int discrepancy_stats(int64_t n, const uint16_t* x_t, const uint16_t* x_r,
                       const uint16_t* y_t, const uint16_t* y_r, double* acc3,
                       int accumulate, void* work, int64_t work_bytes, void* stream);
-
-/* Bytes of workspace discrepancy_stats needs for n elements (>= 16). */
-int64_t trace_stats_workspace_bytes(int64_t n);
 
 #ifdef __cplusplus
 }

@@ -6,14 +6,17 @@ runs in the library's HIP kernels. The calls and their sources in the paper
 ("TRACE: Rollout-Guided Quantization-Aware Training for FP4 Reinforcement
 Learning of MoE Language Models", arXiv 2610.07767):
 
-    quantize_rtn        vanilla FP4 fake quantization (§3.1, Fig. 4(a))
-    encode_guidance     rollout-side guidance record (§3.2, §4.2; Algorithm 1)
-    decode_guidance     Reconstruct (Algorithm 1)
-    guided_fake_quant   rollout-guided rounding (§3.1 "Key Design")
-    discrepancy_stats   D_BF16 / D_FP4 sums (§3.1, Fig. 4(b))
+    quantize_rtn             vanilla FP4 fake quantization (§3.1, Fig. 4(a))
+    encode_guidance          rollout-side guidance record (§3.2, §4.2; Algorithm 1)
+    decode_guidance          Reconstruct (Algorithm 1)
+    guided_fake_quant        rollout-guided rounding (§3.1 "Key Design")
+    guided_fake_quant_stats  the same plus the discrepancy sums in one pass
+    discrepancy_stats        D_BF16 / D_FP4 sums (§3.1, Fig. 4(b))
 
 Tensors are bf16 [rows, cols] on a gfx950 device, contiguous, with cols a
-multiple of the block size (16 for NVFP4, 32 for MXFP4).
+multiple of the block size (16 for NVFP4, 32 for MXFP4). ``group_rows`` > 0
+gives every ``group_rows`` consecutive rows their own FP32 global scale
+(NVFP4); 0 means one scale for the whole tensor.
 """
 
 from __future__ import annotations
@@ -27,8 +30,9 @@ from . import _abi
 from ._abi import MXFP4, NVFP4, TraceError, load, status_str  # noqa: F401
 
 __all__ = ["NVFP4", "MXFP4", "TraceError", "Quantized", "Guidance", "quantize_rtn",
-           "encode_guidance", "decode_guidance", "guided_fake_quant", "discrepancy_stats",
-           "stats_workspace", "derived_metrics", "fmt_id", "BLOCK"]
+           "encode_guidance", "decode_guidance", "guided_fake_quant", "guided_fake_quant_stats",
+           "discrepancy_stats", "stats_workspace", "quant_workspace", "guided_stats_workspace",
+           "derived_metrics", "fmt_id", "BLOCK"]
 
 BLOCK = {NVFP4: 16, MXFP4: 32}
 
@@ -44,7 +48,7 @@ def fmt_id(fmt) -> int:
 class Quantized(NamedTuple):
     codes: torch.Tensor            # uint8 [rows, cols/2]
     scales: torch.Tensor           # uint8 [rows, cols/B]
-    gscale: Optional[torch.Tensor]  # float32 [2] = {S, A} (NVFP4) or None
+    gscale: Optional[torch.Tensor]  # float32 [G, 2] = {S, A} per group (NVFP4) or None
     y: Optional[torch.Tensor]      # bf16 [rows, cols] or None
 
 
@@ -53,12 +57,17 @@ class Guidance(NamedTuple):
     bits: int
     guide: torch.Tensor            # uint8 [rows, cols/8] (bits=1) or [rows, cols/2] (bits=4)
     scales: torch.Tensor           # uint8 [rows, cols/B]
-    gscale: Optional[torch.Tensor]  # float32 [2] (NVFP4) or None
+    gscale: Optional[torch.Tensor]  # float32 [G, 2] (NVFP4) or None
     y: Optional[torch.Tensor]      # the rollout's own dequantized bf16 output, or None
+    group_rows: int = 0
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
+
+
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
 
 
 def _stream(t: torch.Tensor) -> int:
@@ -77,6 +86,12 @@ def _check_x(x: torch.Tensor, name: str = "x") -> tuple[int, int]:
     return x.shape[0], x.shape[1]
 
 
+def _groups(rows: int, group_rows: int) -> int:
+    if group_rows < 0 or (group_rows > 0 and rows % group_rows):
+        raise ValueError(f"group_rows={group_rows} must be 0 or divide rows={rows}")
+    return rows // group_rows if group_rows > 0 else 1
+
+
 def _empty(shape, dtype, like: torch.Tensor, out: Optional[torch.Tensor]):
     if out is not None:
         if tuple(out.shape) != tuple(shape) or out.dtype != dtype or not out.is_contiguous():
@@ -85,43 +100,77 @@ def _empty(shape, dtype, like: torch.Tensor, out: Optional[torch.Tensor]):
     return torch.empty(shape, dtype=dtype, device=like.device)
 
 
-def quantize_rtn(x: torch.Tensor, fmt="nvfp4", gscale: Optional[torch.Tensor] = None,
-                 with_y: bool = True, codes=None, scales=None, gscale_out=None, y=None) -> Quantized:
-    """RTN FP4 fake quantization of x with its own scales. For NVFP4 the global
-    scale comes from the tensor amax unless ``gscale`` (a device float tensor
-    whose [0] is S) is given."""
-    f = fmt_id(fmt)
+def _workspace(nbytes: int, device, work: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    if nbytes < 0:
+        raise ValueError("invalid shape")
+    if work is not None:
+        return work
+    if nbytes == 0:
+        return None
+    return torch.empty((nbytes + 7) // 8, dtype=torch.float64, device=device)
+
+
+def quant_workspace(fmt, rows: int, cols: int, group_rows: int = 0, device="cuda"):
+    """Workspace tensor for quantize_rtn / encode_guidance with scales from the amax."""
+    n = int(load().trace_quant_workspace_bytes(fmt_id(fmt), rows, cols, group_rows))
+    return _workspace(n, device, None)
+
+
+def guided_stats_workspace(fmt, rows: int, cols: int, group_rows: int = 0, device="cuda"):
+    n = int(load().trace_guided_stats_workspace_bytes(fmt_id(fmt), rows, cols, group_rows))
+    return _workspace(n, device, None)
+
+
+def stats_workspace(n: int, device) -> torch.Tensor:
+    nbytes = int(load().trace_stats_workspace_bytes(int(n)))
+    return torch.empty(max(nbytes // 8, 2), dtype=torch.float64, device=device)
+
+
+def _rtn_call(name, x, f, bits, group_rows, gscale, plane_shape, with_y, plane, scales,
+              gscale_out, y, work):
     rows, cols = _check_x(x)
-    codes = _empty((rows, cols // 2), torch.uint8, x, codes)
+    G = _groups(rows, group_rows)
+    plane = _empty(plane_shape, torch.uint8, x, plane)
     scales = _empty((rows, cols // BLOCK[f]), torch.uint8, x, scales)
     if f == NVFP4 and gscale is None:
-        gscale_out = _empty((2,), torch.float32, x, gscale_out)
+        gscale_out = _empty((G, 2), torch.float32, x, gscale_out)
+        need = int(load().trace_quant_workspace_bytes(f, rows, cols, group_rows))
+        work = _workspace(need, x.device, work)
     else:
         gscale_out = None
+        work = None
     y = _empty((rows, cols), torch.bfloat16, x, y) if with_y else None
-    _abi.call("quantize_rtn", f, rows, cols, _ptr(x), _ptr(gscale), _ptr(codes), _ptr(scales),
-              _ptr(gscale_out), _ptr(y), _stream(x))
-    return Quantized(codes, scales, gscale if gscale is not None else gscale_out, y)
+    head = [f] if bits is None else [f, int(bits)]
+    _abi.call(name, *head, rows, cols, group_rows, _ptr(x), _ptr(gscale), _ptr(plane), _ptr(scales),
+              _ptr(gscale_out), _ptr(y), _ptr(work), _nbytes(work), _stream(x))
+    return plane, scales, (gscale if gscale is not None else gscale_out), y
+
+
+def quantize_rtn(x: torch.Tensor, fmt="nvfp4", gscale: Optional[torch.Tensor] = None,
+                 with_y: bool = True, group_rows: int = 0, codes=None, scales=None,
+                 gscale_out=None, y=None, work=None) -> Quantized:
+    """RTN FP4 fake quantization of x with its own scales. For NVFP4 the global
+    scale of each group comes from its amax unless ``gscale`` (a device float
+    tensor holding S of group g at flat index 2g) is given."""
+    f = fmt_id(fmt)
+    rows, cols = _check_x(x)
+    c, s, g, yy = _rtn_call("quantize_rtn", x, f, None, group_rows, gscale, (rows, cols // 2),
+                            with_y, codes, scales, gscale_out, y, work)
+    return Quantized(c, s, g, yy)
 
 
 def encode_guidance(x_rollout: torch.Tensor, fmt="nvfp4", bits: int = 1,
                     gscale: Optional[torch.Tensor] = None, with_y: bool = False,
-                    guide=None, scales=None, gscale_out=None, y=None) -> Guidance:
+                    group_rows: int = 0, guide=None, scales=None, gscale_out=None, y=None,
+                    work=None) -> Guidance:
     """Rollout side: RTN-quantize and emit the guidance record (bits=1: the
     mantissa-bit plane; bits=4: the full code plane) plus the scales."""
     f = fmt_id(fmt)
     rows, cols = _check_x(x_rollout, "x_rollout")
     gcols = cols // 8 if bits == 1 else cols // 2
-    guide = _empty((rows, gcols), torch.uint8, x_rollout, guide)
-    scales = _empty((rows, cols // BLOCK[f]), torch.uint8, x_rollout, scales)
-    if f == NVFP4 and gscale is None:
-        gscale_out = _empty((2,), torch.float32, x_rollout, gscale_out)
-    else:
-        gscale_out = None
-    y = _empty((rows, cols), torch.bfloat16, x_rollout, y) if with_y else None
-    _abi.call("encode_guidance", f, int(bits), rows, cols, _ptr(x_rollout), _ptr(gscale),
-              _ptr(guide), _ptr(scales), _ptr(gscale_out), _ptr(y), _stream(x_rollout))
-    return Guidance(f, int(bits), guide, scales, gscale if gscale is not None else gscale_out, y)
+    c, s, g, yy = _rtn_call("encode_guidance", x_rollout, f, bits, group_rows, gscale,
+                            (rows, gcols), with_y, guide, scales, gscale_out, y, work)
+    return Guidance(f, int(bits), c, s, g, yy, int(group_rows))
 
 
 def decode_guidance(x_train: torch.Tensor, g: Guidance, ref_codes=None) -> torch.Tensor:
@@ -130,9 +179,20 @@ def decode_guidance(x_train: torch.Tensor, g: Guidance, ref_codes=None) -> torch
         raise ValueError("decode_guidance takes a bits=1 record")
     rows, cols = _check_x(x_train, "x_train")
     ref_codes = _empty((rows, cols // 2), torch.uint8, x_train, ref_codes)
-    _abi.call("decode_guidance", g.fmt, rows, cols, _ptr(x_train), _ptr(g.guide), _ptr(g.scales),
-              _ptr(g.gscale), _ptr(ref_codes), _stream(x_train))
+    _abi.call("decode_guidance", g.fmt, rows, cols, g.group_rows, _ptr(x_train), _ptr(g.guide),
+              _ptr(g.scales), _ptr(g.gscale), _ptr(ref_codes), _stream(x_train))
     return ref_codes
+
+
+def _guided_common(x_train, g, bits, with_codes, y, codes):
+    b = g.bits if bits is None else int(bits)
+    if b not in (0, g.bits):
+        raise ValueError(f"record holds bits={g.bits}, asked for bits={b}")
+    rows, cols = _check_x(x_train, "x_train")
+    y = _empty((rows, cols), torch.bfloat16, x_train, y)
+    codes = _empty((rows, cols // 2), torch.uint8, x_train, codes) if with_codes else None
+    guide = None if b == 0 else g.guide
+    return b, rows, cols, y, codes, guide
 
 
 def guided_fake_quant(x_train: torch.Tensor, g: Guidance, bits: Optional[int] = None,
@@ -140,21 +200,33 @@ def guided_fake_quant(x_train: torch.Tensor, g: Guidance, bits: Optional[int] = 
     """Training side: rollout-guided rounding under the rollout scales.
     ``bits`` defaults to the record's (1 or 4); 0 gives RTN under the rollout
     scales. Returns (y, codes or None)."""
-    b = g.bits if bits is None else int(bits)
-    rows, cols = _check_x(x_train, "x_train")
-    y = _empty((rows, cols), torch.bfloat16, x_train, y)
-    codes = _empty((rows, cols // 2), torch.uint8, x_train, codes) if with_codes else None
-    guide = None if b == 0 else g.guide
-    if b not in (0, g.bits):
-        raise ValueError(f"record holds bits={g.bits}, asked for bits={b}")
-    _abi.call("guided_fake_quant", g.fmt, b, rows, cols, _ptr(x_train), _ptr(guide), _ptr(g.scales),
-              _ptr(g.gscale), _ptr(y), _ptr(codes), _stream(x_train))
+    b, rows, cols, y, codes, guide = _guided_common(x_train, g, bits, with_codes, y, codes)
+    _abi.call("guided_fake_quant", g.fmt, b, rows, cols, g.group_rows, _ptr(x_train), _ptr(guide),
+              _ptr(g.scales), _ptr(g.gscale), _ptr(y), _ptr(codes), _stream(x_train))
     return y, codes
 
 
-def stats_workspace(n: int, device) -> torch.Tensor:
-    nbytes = int(load().trace_stats_workspace_bytes(int(n)))
-    return torch.empty(max(nbytes // 8, 2), dtype=torch.float64, device=device)
+def guided_fake_quant_stats(x_train: torch.Tensor, x_rollout: torch.Tensor, g: Guidance,
+                            bits: Optional[int] = None, with_codes: bool = False,
+                            acc: Optional[torch.Tensor] = None, accumulate: bool = False,
+                            y=None, codes=None, work=None):
+    """guided_fake_quant plus {SB, SF, n} against the rollout (whose RTN output
+    under the record's scales is recomputed from x_rollout). Returns
+    (y, codes or None, acc float64[3])."""
+    b, rows, cols, y, codes, guide = _guided_common(x_train, g, bits, with_codes, y, codes)
+    _check_x(x_rollout, "x_rollout")
+    if tuple(x_rollout.shape) != (rows, cols):
+        raise ValueError("x_rollout must have x_train's shape")
+    if acc is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs an acc tensor")
+        acc = torch.empty(3, dtype=torch.float64, device=x_train.device)
+    need = int(load().trace_guided_stats_workspace_bytes(g.fmt, rows, cols, g.group_rows))
+    work = _workspace(need, x_train.device, work)
+    _abi.call("guided_fake_quant_stats", g.fmt, b, rows, cols, g.group_rows, _ptr(x_train),
+              _ptr(x_rollout), _ptr(guide), _ptr(g.scales), _ptr(g.gscale), _ptr(y), _ptr(codes),
+              _ptr(acc), 1 if accumulate else 0, _ptr(work), _nbytes(work), _stream(x_train))
+    return y, codes, acc
 
 
 def discrepancy_stats(x_t, x_r, y_t, y_r, acc: Optional[torch.Tensor] = None,
@@ -171,7 +243,7 @@ def discrepancy_stats(x_t, x_r, y_t, y_r, acc: Optional[torch.Tensor] = None,
     if work is None:
         work = stats_workspace(n, x_t.device)
     _abi.call("discrepancy_stats", n, _ptr(x_t), _ptr(x_r), _ptr(y_t), _ptr(y_r), _ptr(acc),
-              1 if accumulate else 0, _ptr(work), work.numel() * 8, _stream(x_t))
+              1 if accumulate else 0, _ptr(work), _nbytes(work), _stream(x_t))
     return acc
 
 

@@ -22,12 +22,23 @@ _vp = ctypes.c_void_p
 SIGNATURES = {
     "trace_abi_version": (_int, []),
     "trace_status_str": (ctypes.c_char_p, [_int]),
-    "quantize_rtn": (_int, [_int, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
-    "encode_guidance": (_int, [_int, _int, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
-    "decode_guidance": (_int, [_int, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
-    "guided_fake_quant": (_int, [_int, _int, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
-    "discrepancy_stats": (_int, [_i64, _vp, _vp, _vp, _vp, _vp, _int, _vp, _i64, _vp]),
+    "trace_quant_workspace_bytes": (_i64, [_int, _i64, _i64, _i64]),
+    "trace_guided_stats_workspace_bytes": (_i64, [_int, _i64, _i64, _i64]),
     "trace_stats_workspace_bytes": (_i64, [_i64]),
+    # fmt, rows, cols, group_rows, x, gscale_in, codes, scales, gscale_out, y, work, work_bytes, stream
+    "quantize_rtn": (_int, [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp]),
+    # fmt, bits, rows, cols, group_rows, x_r, gscale_in, guide, scales, gscale_out, y_r, work, work_bytes, stream
+    "encode_guidance": (_int, [_int, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp]),
+    # fmt, rows, cols, group_rows, x_t, mbits, scales, gscale, ref_codes, stream
+    "decode_guidance": (_int, [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
+    # fmt, bits, rows, cols, group_rows, x_t, guide, scales, gscale, y, codes, stream
+    "guided_fake_quant": (_int, [_int, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    # fmt, bits, rows, cols, group_rows, x_t, x_r, guide, scales, gscale, y, codes, acc3, accumulate,
+    # work, work_bytes, stream
+    "guided_fake_quant_stats": (_int, [_int, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       _vp, _int, _vp, _i64, _vp]),
+    # n, x_t, x_r, y_t, y_r, acc3, accumulate, work, work_bytes, stream
+    "discrepancy_stats": (_int, [_i64, _vp, _vp, _vp, _vp, _vp, _int, _vp, _i64, _vp]),
 }
 
 _lib = None

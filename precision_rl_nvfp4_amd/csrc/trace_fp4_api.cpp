@@ -2,10 +2,11 @@
 // then kernel launches on the caller's stream. The operations and their
 // sources in the paper are documented in include/trace_fp4.h.
 //
-// Validation order: (1) scalars (fmt, bits, flags, sizes), (2) NULL checks,
-// (3) alignment, (4) aliasing of outputs against every other buffer, (5) the
-// current device must be gfx950. Steps 1-4 make no HIP call, so every error
-// path short of EDEVICE is testable on a machine without a GPU.
+// Validation order: (1) scalars (fmt, bits, flags, sizes, grouping), (2) NULL
+// checks, (3) workspace sizes, (4) alignment, (5) aliasing of outputs against
+// every other buffer, (6) the current device must be gfx950. Steps 1-5 make
+// no HIP call, so every error path short of EDEVICE is testable on a machine
+// without a GPU.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -30,11 +31,12 @@ bool overlaps(const Range& a, const Range& b) {
 }
 
 // Every output must be disjoint from every input and from the other outputs.
-bool any_alias(const Range* outs, int n_out, const Range* ins, int n_in) {
-  for (int i = 0; i < n_out; ++i) {
-    for (int j = 0; j < n_in; ++j)
+template <int NO, int NI>
+bool any_alias(const Range (&outs)[NO], const Range (&ins)[NI]) {
+  for (int i = 0; i < NO; ++i) {
+    for (int j = 0; j < NI; ++j)
       if (overlaps(outs[i], ins[j])) return true;
-    for (int j = i + 1; j < n_out; ++j)
+    for (int j = i + 1; j < NO; ++j)
       if (overlaps(outs[i], outs[j])) return true;
   }
   return false;
@@ -46,14 +48,27 @@ int block_of(int fmt) { return fmt == TRACE_FMT_NVFP4 ? 16 : 32; }
 
 bool valid_fmt(int fmt) { return fmt == TRACE_FMT_NVFP4 || fmt == TRACE_FMT_MXFP4; }
 
-// N = rows * cols with cols % B == 0 and no overflow; the limit keeps every
-// byte offset (2N) and unit index inside int64 with room to spare.
-int shape_n(int fmt, int64_t rows, int64_t cols, int64_t* n) {
-  if (rows < 0 || cols < 0) return TRACE_ESHAPE;
+// A validated call shape: N elements in G groups of upg units.
+struct CallShape {
+  int64_t n;
+  tfp4::Shape sh;
+};
+
+// N = rows * cols with cols % B == 0, group_rows dividing rows, and every
+// launch grid (tiles of kTileUnits units; amax partials) inside 2^31 workgroups.
+int shape_of(int fmt, int64_t rows, int64_t cols, int64_t group_rows, CallShape* out) {
+  if (rows < 0 || cols < 0 || group_rows < 0) return TRACE_ESHAPE;
   if (cols % block_of(fmt) != 0) return TRACE_ESHAPE;
-  const int64_t kMaxElems = (int64_t)1 << 50;
+  if (group_rows > 0 && rows % group_rows != 0) return TRACE_ESHAPE;
+  const int64_t kMaxElems = (int64_t)1 << 44;
   if (cols != 0 && rows > kMaxElems / cols) return TRACE_ESHAPE;
-  *n = rows * cols;
+  const int64_t grows = group_rows > 0 ? group_rows : rows;
+  out->n = rows * cols;
+  out->sh.groups = group_rows > 0 ? rows / group_rows : 1;
+  out->sh.upg = grows * cols / tfp4::kUnitElems;
+  const int64_t tiles = (out->sh.upg + tfp4::kTileUnits - 1) / tfp4::kTileUnits;
+  if (out->sh.groups > 0 && (tiles > INT32_MAX / out->sh.groups || out->sh.groups > INT32_MAX / tfp4::kPartMax))
+    return TRACE_ESHAPE;
   return TRACE_OK;
 }
 
@@ -77,45 +92,43 @@ int check_device() {
 
 int launched(hipError_t e) { return e == hipSuccess ? TRACE_OK : TRACE_ELAUNCH; }
 
-// Checks shared by quantize_rtn and encode_guidance. `plane_bytes` is the
-// size of the code or bit plane.
-int check_rtn_args(int fmt, int64_t n, const uint16_t* x, const float* gin, const uint8_t* plane,
-                   int64_t plane_bytes, uint32_t plane_align, const uint8_t* scales,
-                   const float* gout, const uint16_t* y) {
+// Shared by quantize_rtn and encode_guidance. `plane_bytes` is the size of
+// the code or bit plane, `plane_align` its alignment.
+int run_rtn(int fmt, int plane_mode, int64_t rows, int64_t cols, int64_t group_rows,
+            const uint16_t* x, const float* gin, uint8_t* plane, int64_t plane_div,
+            uint32_t plane_align, uint8_t* scales, float* gout, uint16_t* y, void* work,
+            int64_t work_bytes, void* stream) {
+  CallShape cs;
+  int st = shape_of(fmt, rows, cols, group_rows, &cs);
+  if (st != TRACE_OK) return st;
+  const int64_t n = cs.n, G = cs.sh.groups;
   if (fmt == TRACE_FMT_NVFP4) {
     if ((gin == nullptr) == (gout == nullptr)) return TRACE_EINVAL;
   } else if (gin != nullptr || gout != nullptr) {
     return TRACE_EINVAL;
   }
   if (n > 0 && (x == nullptr || plane == nullptr || scales == nullptr)) return TRACE_EINVAL;
+  const bool need_work = gout != nullptr && n > 0;
+  const int64_t wneed = need_work ? tfp4::quant_work_bytes(cs.sh) : 0;
+  if (need_work && work == nullptr) return TRACE_EINVAL;
+  if (work_bytes < wneed) return TRACE_ESHAPE;
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(plane, plane_align) || !aligned(gin, 4) ||
-      !aligned(gout, 4))
+      !aligned(gout, 4) || (need_work && !aligned(work, 8)))
     return TRACE_EALIGN;
-  const Range ins[] = {{x, 2 * n}, {gin, 4}};
-  const Range outs[] = {{plane, plane_bytes}, {scales, n / block_of(fmt)}, {gout, 8}, {y, 2 * n}};
-  if (any_alias(outs, 4, ins, 2)) return TRACE_EALIAS;
-  return TRACE_OK;
-}
-
-int run_rtn(int fmt, int plane_mode, int64_t n, const uint16_t* x, const float* gin, uint8_t* plane,
-            uint8_t* scales, float* gout, uint16_t* y, void* stream) {
-  int st = check_device();
+  const Range ins[] = {{x, 2 * n}, {gin, 8 * G}};
+  const Range outs[] = {{plane, n / plane_div}, {scales, n / block_of(fmt)}, {gout, 8 * G},
+                        {y, 2 * n}, {need_work ? work : nullptr, wneed}};
+  if (any_alias(outs, ins)) return TRACE_EALIAS;
+  st = check_device();
   if (st != TRACE_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t units = n / tfp4::kUnitElems;
-  if (fmt == TRACE_FMT_NVFP4 && gout != nullptr) {
-    hipError_t e = tfp4::launch_global_scale(x, units, gout, s);
-    if (e != hipSuccess) return TRACE_ELAUNCH;
-    return launched(tfp4::launch_quantize(fmt, plane_mode, true, x, units, gout, plane, scales, y, s));
-  }
-  return launched(tfp4::launch_quantize(fmt, plane_mode, false, x, units, const_cast<float*>(gin),
-                                        plane, scales, y, s));
+  return launched(tfp4::launch_quantize(fmt, plane_mode, cs.sh, x, gin, gout, plane, scales, y,
+                                        need_work ? work : nullptr,
+                                        static_cast<hipStream_t>(stream)));
 }
 
-// Checks shared by decode_guidance and guided_fake_quant.
-int check_train_args(int fmt, int64_t n, const uint16_t* x, const uint8_t* guide, int64_t guide_bytes,
-                     uint32_t guide_align, bool guide_needed, const uint8_t* scales,
-                     const float* gscale) {
+// Checks shared by the training-side calls: scales, gscale, guide.
+int check_train(int fmt, int64_t n, const uint16_t* x, const uint8_t* guide, bool guide_needed,
+                uint32_t guide_align, const uint8_t* scales, const float* gscale) {
   if (fmt == TRACE_FMT_NVFP4) {
     if (gscale == nullptr) return TRACE_EINVAL;
   } else if (gscale != nullptr) {
@@ -124,9 +137,44 @@ int check_train_args(int fmt, int64_t n, const uint16_t* x, const uint8_t* guide
   if (!guide_needed && guide != nullptr) return TRACE_EINVAL;
   if (n > 0 && (x == nullptr || scales == nullptr || (guide_needed && guide == nullptr)))
     return TRACE_EINVAL;
-  if (!aligned(x, 16) || !aligned(guide, guide_align) || !aligned(gscale, 4)) return TRACE_EALIGN;
-  (void)guide_bytes;
   return TRACE_OK;
+}
+
+int run_guided(int fmt, int bits, int64_t rows, int64_t cols, int64_t group_rows,
+               const uint16_t* x, const uint16_t* xr, bool stats, const uint8_t* guide,
+               const uint8_t* scales, const float* gscale, uint16_t* y, uint8_t* codes,
+               double* acc3, int accumulate, void* work, int64_t work_bytes, void* stream) {
+  if (!valid_fmt(fmt) || (bits != 0 && bits != 1 && bits != 4)) return TRACE_EINVAL;
+  if (stats && accumulate != 0 && accumulate != 1) return TRACE_EINVAL;
+  CallShape cs;
+  int st = shape_of(fmt, rows, cols, group_rows, &cs);
+  if (st != TRACE_OK) return st;
+  const int64_t n = cs.n, G = cs.sh.groups;
+  st = check_train(fmt, n, x, guide, bits != 0, bits == 4 ? 4 : 1, scales, gscale);
+  if (st != TRACE_OK) return st;
+  if (n > 0 && y == nullptr) return TRACE_EINVAL;
+  int64_t wneed = 0;
+  if (stats) {
+    if (acc3 == nullptr || (n > 0 && xr == nullptr)) return TRACE_EINVAL;
+    wneed = n > 0 ? tfp4::guided_stats_work_bytes(cs.sh) : 0;
+    if (wneed > 0 && work == nullptr) return TRACE_EINVAL;
+    if (work_bytes < wneed) return TRACE_ESHAPE;
+  }
+  if (!aligned(x, 16) || !aligned(xr, 16) || !aligned(y, 16) || !aligned(codes, 4) ||
+      !aligned(guide, bits == 4 ? 4 : 1) || !aligned(gscale, 4) || !aligned(acc3, 8) ||
+      (wneed > 0 && !aligned(work, 8)))
+    return TRACE_EALIGN;
+  const int64_t gbytes = bits == 1 ? n / 8 : bits == 4 ? n / 2 : 0;
+  const Range ins[] = {{x, 2 * n}, {xr, stats ? 2 * n : 0}, {guide, gbytes},
+                       {scales, n / block_of(fmt)}, {gscale, 8 * G}};
+  const Range outs[] = {{y, 2 * n}, {codes, n / 2}, {acc3, stats ? 24 : 0},
+                        {wneed > 0 ? work : nullptr, wneed}};
+  if (any_alias(outs, ins)) return TRACE_EALIAS;
+  st = check_device();
+  if (st != TRACE_OK) return st;
+  return launched(tfp4::launch_guided(fmt, bits, false, cs.sh, x, guide, scales, gscale, y, codes,
+                                      stats ? xr : nullptr, stats ? acc3 : nullptr, accumulate,
+                                      wneed > 0 ? work : nullptr, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -148,84 +196,86 @@ const char* trace_status_str(int status) {
   }
 }
 
-int quantize_rtn(int fmt, int64_t rows, int64_t cols, const uint16_t* x, const float* gscale_in,
-                 uint8_t* codes, uint8_t* scales, float* gscale_out, uint16_t* y_opt, void* stream) {
-  if (!valid_fmt(fmt)) return TRACE_EINVAL;
-  int64_t n = 0;
-  int st = shape_n(fmt, rows, cols, &n);
-  if (st != TRACE_OK) return st;
-  st = check_rtn_args(fmt, n, x, gscale_in, codes, n / 2, 4, scales, gscale_out, y_opt);
-  if (st != TRACE_OK) return st;
-  return run_rtn(fmt, 0, n, x, gscale_in, codes, scales, gscale_out, y_opt, stream);
+int64_t trace_quant_workspace_bytes(int fmt, int64_t rows, int64_t cols, int64_t group_rows) {
+  if (!valid_fmt(fmt)) return -1;
+  CallShape cs;
+  if (shape_of(fmt, rows, cols, group_rows, &cs) != TRACE_OK) return -1;
+  return fmt == TRACE_FMT_NVFP4 ? tfp4::quant_work_bytes(cs.sh) : 0;
 }
 
-int encode_guidance(int fmt, int bits, int64_t rows, int64_t cols, const uint16_t* x_rollout,
-                    const float* gscale_in, uint8_t* guide, uint8_t* scales, float* gscale_out,
-                    uint16_t* y_rollout_opt, void* stream) {
-  if (!valid_fmt(fmt) || (bits != 1 && bits != 4)) return TRACE_EINVAL;
-  int64_t n = 0;
-  int st = shape_n(fmt, rows, cols, &n);
-  if (st != TRACE_OK) return st;
-  const int64_t gbytes = bits == 1 ? n / 8 : n / 2;
-  st = check_rtn_args(fmt, n, x_rollout, gscale_in, guide, gbytes, bits == 1 ? 1 : 4, scales,
-                      gscale_out, y_rollout_opt);
-  if (st != TRACE_OK) return st;
-  return run_rtn(fmt, bits == 1 ? 1 : 0, n, x_rollout, gscale_in, guide, scales, gscale_out,
-                 y_rollout_opt, stream);
-}
-
-int decode_guidance(int fmt, int64_t rows, int64_t cols, const uint16_t* x_train,
-                    const uint8_t* mbits, const uint8_t* scales, const float* gscale,
-                    uint8_t* ref_codes, void* stream) {
-  if (!valid_fmt(fmt)) return TRACE_EINVAL;
-  int64_t n = 0;
-  int st = shape_n(fmt, rows, cols, &n);
-  if (st != TRACE_OK) return st;
-  st = check_train_args(fmt, n, x_train, mbits, n / 8, 1, true, scales, gscale);
-  if (st != TRACE_OK) return st;
-  if (n > 0 && ref_codes == nullptr) return TRACE_EINVAL;
-  if (!aligned(ref_codes, 4)) return TRACE_EALIGN;
-  const Range ins[] = {{x_train, 2 * n}, {mbits, n / 8}, {scales, n / block_of(fmt)}, {gscale, 4}};
-  const Range outs[] = {{ref_codes, n / 2}};
-  if (any_alias(outs, 1, ins, 4)) return TRACE_EALIAS;
-  st = check_device();
-  if (st != TRACE_OK) return st;
-  return launched(tfp4::launch_guided(fmt, 1, true, x_train, n / tfp4::kUnitElems, mbits, scales,
-                                      gscale, nullptr, ref_codes, static_cast<hipStream_t>(stream)));
-}
-
-int guided_fake_quant(int fmt, int bits, int64_t rows, int64_t cols, const uint16_t* x_train,
-                      const uint8_t* guide, const uint8_t* scales, const float* gscale, uint16_t* y,
-                      uint8_t* codes_opt, void* stream) {
-  if (!valid_fmt(fmt) || (bits != 0 && bits != 1 && bits != 4)) return TRACE_EINVAL;
-  int64_t n = 0;
-  int st = shape_n(fmt, rows, cols, &n);
-  if (st != TRACE_OK) return st;
-  const int64_t gbytes = bits == 1 ? n / 8 : bits == 4 ? n / 2 : 0;
-  st = check_train_args(fmt, n, x_train, guide, gbytes, bits == 4 ? 4 : 1, bits != 0, scales, gscale);
-  if (st != TRACE_OK) return st;
-  if (n > 0 && y == nullptr) return TRACE_EINVAL;
-  if (!aligned(y, 16) || !aligned(codes_opt, 4)) return TRACE_EALIGN;
-  const Range ins[] = {{x_train, 2 * n}, {guide, gbytes}, {scales, n / block_of(fmt)}, {gscale, 4}};
-  const Range outs[] = {{y, 2 * n}, {codes_opt, n / 2}};
-  if (any_alias(outs, 2, ins, 4)) return TRACE_EALIAS;
-  st = check_device();
-  if (st != TRACE_OK) return st;
-  return launched(tfp4::launch_guided(fmt, bits, false, x_train, n / tfp4::kUnitElems, guide,
-                                      scales, gscale, y, codes_opt,
-                                      static_cast<hipStream_t>(stream)));
+int64_t trace_guided_stats_workspace_bytes(int fmt, int64_t rows, int64_t cols, int64_t group_rows) {
+  if (!valid_fmt(fmt)) return -1;
+  CallShape cs;
+  if (shape_of(fmt, rows, cols, group_rows, &cs) != TRACE_OK) return -1;
+  return tfp4::guided_stats_work_bytes(cs.sh);
 }
 
 int64_t trace_stats_workspace_bytes(int64_t n) {
   if (n < 0) return 0;
-  return 2 * (int64_t)sizeof(double) * tfp4::stats_groups(n);
+  return tfp4::stats_work_bytes(n);
+}
+
+int quantize_rtn(int fmt, int64_t rows, int64_t cols, int64_t group_rows, const uint16_t* x,
+                 const float* gscale_in, uint8_t* codes, uint8_t* scales, float* gscale_out,
+                 uint16_t* y_opt, void* work, int64_t work_bytes, void* stream) {
+  if (!valid_fmt(fmt)) return TRACE_EINVAL;
+  return run_rtn(fmt, 0, rows, cols, group_rows, x, gscale_in, codes, 2, 4, scales, gscale_out,
+                 y_opt, work, work_bytes, stream);
+}
+
+int encode_guidance(int fmt, int bits, int64_t rows, int64_t cols, int64_t group_rows,
+                    const uint16_t* x_rollout, const float* gscale_in, uint8_t* guide,
+                    uint8_t* scales, float* gscale_out, uint16_t* y_rollout_opt, void* work,
+                    int64_t work_bytes, void* stream) {
+  if (!valid_fmt(fmt) || (bits != 1 && bits != 4)) return TRACE_EINVAL;
+  return run_rtn(fmt, bits == 1 ? 1 : 0, rows, cols, group_rows, x_rollout, gscale_in, guide,
+                 bits == 1 ? 8 : 2, bits == 1 ? 1 : 4, scales, gscale_out, y_rollout_opt, work,
+                 work_bytes, stream);
+}
+
+int decode_guidance(int fmt, int64_t rows, int64_t cols, int64_t group_rows,
+                    const uint16_t* x_train, const uint8_t* mbits, const uint8_t* scales,
+                    const float* gscale, uint8_t* ref_codes, void* stream) {
+  if (!valid_fmt(fmt)) return TRACE_EINVAL;
+  CallShape cs;
+  int st = shape_of(fmt, rows, cols, group_rows, &cs);
+  if (st != TRACE_OK) return st;
+  const int64_t n = cs.n, G = cs.sh.groups;
+  st = check_train(fmt, n, x_train, mbits, true, 1, scales, gscale);
+  if (st != TRACE_OK) return st;
+  if (n > 0 && ref_codes == nullptr) return TRACE_EINVAL;
+  if (!aligned(x_train, 16) || !aligned(ref_codes, 4) || !aligned(gscale, 4)) return TRACE_EALIGN;
+  const Range ins[] = {{x_train, 2 * n}, {mbits, n / 8}, {scales, n / block_of(fmt)}, {gscale, 8 * G}};
+  const Range outs[] = {{ref_codes, n / 2}};
+  if (any_alias(outs, ins)) return TRACE_EALIAS;
+  st = check_device();
+  if (st != TRACE_OK) return st;
+  return launched(tfp4::launch_guided(fmt, 1, true, cs.sh, x_train, mbits, scales, gscale, nullptr,
+                                      ref_codes, nullptr, nullptr, 0, nullptr,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int guided_fake_quant(int fmt, int bits, int64_t rows, int64_t cols, int64_t group_rows,
+                      const uint16_t* x_train, const uint8_t* guide, const uint8_t* scales,
+                      const float* gscale, uint16_t* y, uint8_t* codes_opt, void* stream) {
+  return run_guided(fmt, bits, rows, cols, group_rows, x_train, nullptr, false, guide, scales,
+                    gscale, y, codes_opt, nullptr, 0, nullptr, 0, stream);
+}
+
+int guided_fake_quant_stats(int fmt, int bits, int64_t rows, int64_t cols, int64_t group_rows,
+                            const uint16_t* x_train, const uint16_t* x_rollout,
+                            const uint8_t* guide, const uint8_t* scales, const float* gscale,
+                            uint16_t* y, uint8_t* codes_opt, double* acc3, int accumulate,
+                            void* work, int64_t work_bytes, void* stream) {
+  return run_guided(fmt, bits, rows, cols, group_rows, x_train, x_rollout, true, guide, scales,
+                    gscale, y, codes_opt, acc3, accumulate, work, work_bytes, stream);
 }
 
 int discrepancy_stats(int64_t n, const uint16_t* x_t, const uint16_t* x_r, const uint16_t* y_t,
                       const uint16_t* y_r, double* acc3, int accumulate, void* work,
                       int64_t work_bytes, void* stream) {
   if (accumulate != 0 && accumulate != 1) return TRACE_EINVAL;
-  if (n < 0 || n > ((int64_t)1 << 50)) return TRACE_ESHAPE;
+  if (n < 0 || n > ((int64_t)1 << 44)) return TRACE_ESHAPE;
   if (acc3 == nullptr || work == nullptr) return TRACE_EINVAL;
   if (n > 0 && (x_t == nullptr || x_r == nullptr || y_t == nullptr || y_r == nullptr))
     return TRACE_EINVAL;
@@ -235,7 +285,7 @@ int discrepancy_stats(int64_t n, const uint16_t* x_t, const uint16_t* x_r, const
     return TRACE_EALIGN;
   const Range ins[] = {{x_t, 2 * n}, {x_r, 2 * n}, {y_t, 2 * n}, {y_r, 2 * n}};
   const Range outs[] = {{acc3, 24}, {work, work_bytes}};
-  if (any_alias(outs, 2, ins, 4)) return TRACE_EALIAS;
+  if (any_alias(outs, ins)) return TRACE_EALIAS;
   int st = check_device();
   if (st != TRACE_OK) return st;
   return launched(tfp4::launch_stats(n, x_t, x_r, y_t, y_r, acc3, accumulate,

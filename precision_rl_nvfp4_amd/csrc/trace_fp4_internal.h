@@ -7,38 +7,51 @@
 
 namespace tfp4 {
 
-// Element counts handled per thread step: one 16-byte load of 8 bf16.
+// One "unit" is a 16-byte load of 8 bf16 elements.
 constexpr int kUnitElems = 8;
 constexpr int kThreads = 256;
+// A workgroup tile: kThreads lanes x kUPT units.
+constexpr int kUPT = 8;
+constexpr int64_t kTileUnits = (int64_t)kThreads * kUPT;
 
-// Upper bound on the partial sums of discrepancy_stats (one per workgroup).
-constexpr int kStatsMaxGroups = 1024;
+// Amax partial maxima kept per global-scale group (one per workgroup of the
+// amax pass), and the workspace slots of the single-pass encoder.
+constexpr int kPartMax = 1024;
+constexpr int kSyncSlots = 64;
 
-int64_t stats_groups(int64_t n);
+// Shape of one call: G groups of `upg` units each (units = G * upg), every
+// group with its own FP32 global scale (NVFP4). Blocks never straddle groups.
+struct Shape {
+  int64_t groups;
+  int64_t upg;  // units per group
+};
 
-// Every launcher enqueues on `stream` and returns the first HIP error seen.
-// Sizes are already validated; `units` = N / 8.
+// Workspace of quantize_rtn / encode_guidance when S comes from the amax:
+// uint32 partial maxima [groups][kPartMax].
+int64_t quant_work_bytes(const Shape& sh);
+// Workspace of guided_fake_quant_stats: float64 partial sums, 2 per workgroup.
+int64_t guided_stats_work_bytes(const Shape& sh);
+// Workspace of discrepancy_stats.
+int64_t stats_work_bytes(int64_t n);
 
-// Global amax -> gscale_out = {S, A}. `x` may be NULL when units == 0.
-hipError_t launch_global_scale(const uint16_t* x, int64_t units, float* gscale_out,
-                               hipStream_t stream);
+// RTN quantization of a tensor (quantize_rtn / encode_guidance).
+//   fmt 0 NVFP4 / 1 MXFP4; plane_mode 0 = code plane u8[N/2], 1 = mantissa-bit
+//   plane u8[N/8]. NVFP4: exactly one of gin (S of group g at gin[2g]) and
+//   gout (receives {S, A} per group, computed from the amax) is non-NULL, and
+//   `work` holds quant_work_bytes when gout is used. MXFP4: both NULL.
+hipError_t launch_quantize(int fmt, int plane_mode, const Shape& sh, const uint16_t* x,
+                           const float* gin, float* gout, uint8_t* plane, uint8_t* scales,
+                           uint16_t* y, void* work, hipStream_t stream);
 
-// Quantize (RTN) one tensor: fmt 0 NVFP4 / 1 MXFP4; plane_mode 0 = code
-// plane (u8[N/2]), 1 = mantissa-bit plane (u8[N/8]). `gsrc` is the device
-// float holding S (NVFP4; NULL for MXFP4); when `s_from_amax` is set, gsrc
-// points at gscale_out, S is derived from gsrc[1] = A, and gsrc[0] gets S.
-hipError_t launch_quantize(int fmt, int plane_mode, bool s_from_amax, const uint16_t* x,
-                           int64_t units, float* gsrc, uint8_t* plane, uint8_t* scales,
-                           uint16_t* y, hipStream_t stream);
+// Guided rounding under the rollout scales (guided_fake_quant), Reconstruct
+// alone (decode_guidance: decode_only, bits 1, writes reference codes), and
+// the fused discrepancy sums (xr and acc3 non-NULL).
+hipError_t launch_guided(int fmt, int bits, bool decode_only, const Shape& sh,
+                         const uint16_t* x, const uint8_t* guide, const uint8_t* scales,
+                         const float* gscale, uint16_t* y, uint8_t* codes, const uint16_t* xr,
+                         double* acc3, int accumulate, void* work, hipStream_t stream);
 
-// Guided rounding / Reconstruct under the rollout scales. bits in {0, 1, 4};
-// decode_only writes reference codes (bits must be 1) into `codes` and no y.
-hipError_t launch_guided(int fmt, int bits, bool decode_only, const uint16_t* x,
-                         int64_t units, const uint8_t* guide, const uint8_t* scales,
-                         const float* gscale, uint16_t* y, uint8_t* codes,
-                         hipStream_t stream);
-
-// Deterministic float64 sums into acc3; `partials` holds 2 * stats_groups(n) doubles.
+// Deterministic float64 sums of discrepancy_stats into acc3.
 hipError_t launch_stats(int64_t n, const uint16_t* xt, const uint16_t* xr, const uint16_t* yt,
                         const uint16_t* yr, double* acc3, int accumulate, double* partials,
                         hipStream_t stream);

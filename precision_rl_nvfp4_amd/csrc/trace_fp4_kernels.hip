@@ -8,16 +8,29 @@
 //   Algorithm 1 prose: BracketFP4, Reconstruct, combined block/global scale.
 //   §4.3: the MXFP4 (E8M0, 32-element block) variant.
 //
-// Every kernel streams its tensor once: one 16-byte load of 8 bf16 per lane
-// ("unit"), consecutive lanes on consecutive units so each wave load is one
-// contiguous 1 KiB run. An NVFP4 block (16 elements) is two lanes and an
-// MXFP4 block (32) four; block maxima are exchanged with DPP quad
-// permutations, with every lane of the wave executing them. No MFMA: the
-// path is bound by HBM bandwidth, not by arithmetic.
+// Layout of the work. Every kernel streams its tensors once: a lane owns
+// "units" of 8 bf16 (one 16-byte load), consecutive lanes own consecutive
+// units, so a wave load is one contiguous 1 KiB run. An NVFP4 block (16
+// elements) spans two lanes and an MXFP4 block (32) four; block maxima are
+// exchanged with DPP quad permutations. A call may hold several global-scale
+// groups (e.g. the 8192-token chunks of a streamed layer); a workgroup tile
+// never straddles two groups. No MFMA: the path is bound by HBM bandwidth.
 //
-// Arithmetic is binary32 with every operation rounded (built with
-// -ffp-contract=off, denormals kept), so each step is exactly the one the
-// header documents.
+// Per-element arithmetic. The budget at the HBM roofline is ~20 VALU
+// operations per element, so the E2M1 work runs on gfx950's conversion
+// instructions and on the 8 codes of a unit at once, as nibbles of a dword:
+//   * t = x * r in binary32 (no FMA, denormals kept), exactly as specified;
+//   * RTN(t)  = v_cvt_scalef32_pk_fp4_f32 with scale 1.0 (round to nearest
+//     even index, saturating at 6, keeping the sign);
+//   * floor(t) (the lower end of BracketFP4) = the stochastic-rounding
+//     variant with zero random bits, which truncates the magnitude;
+//   * t is a codeword  <=>  floor(t) != floor(pred(t)), pred(t) the next
+//     binary32 value toward zero (a NaN pattern for t = +-0, which converts
+//     to magnitude 7, so zero also reads as a codeword);
+//   * bf16 results come from v_cvt_scalef32_pk_bf16_fp4 (exact decode; for
+//     MXFP4 it applies the E8M0 scale exactly) and v_cvt_pk_bf16_f32 (RNE).
+// These equivalences were checked against the CPU oracle on every boundary
+// of the grid (and are re-checked bit for bit by the parity tests).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -29,10 +42,10 @@
 namespace tfp4 {
 namespace {
 
-constexpr int kUnroll = 4;              // units per thread per workgroup slab
-constexpr float kFltMax = 3.40282346638528859812e+38f;
+typedef float f2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
 
-typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+constexpr float kFltMax = 3.40282346638528859812e+38f;
 
 // ------------------------------------------------------------ lane exchange
 
@@ -44,73 +57,143 @@ __device__ __forceinline__ uint32_t xor2(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
 }
 
+// ------------------------------------------------------------ unit helpers
+
 // Largest bf16 magnitude (bits & 0x7FFF) among the 8 elements of a unit.
 __device__ __forceinline__ uint32_t unit_amax_bits(const uint4& v) {
+  typedef unsigned short us2 __attribute__((ext_vector_type(2)));
   us2 a = __builtin_bit_cast(us2, v.x & 0x7FFF7FFFu);
   us2 b = __builtin_bit_cast(us2, v.y & 0x7FFF7FFFu);
   us2 c = __builtin_bit_cast(us2, v.z & 0x7FFF7FFFu);
   us2 d = __builtin_bit_cast(us2, v.w & 0x7FFF7FFFu);
-  us2 m = __builtin_elementwise_max(__builtin_elementwise_max(a, b),
-                                    __builtin_elementwise_max(c, d));
+  us2 m = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
   uint32_t mm = __builtin_bit_cast(uint32_t, m);
   return max(mm & 0xFFFFu, mm >> 16);
 }
 
-__device__ __forceinline__ uint32_t elem_bits(const uint4& v, int e) {
-  uint32_t w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
-  return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
+// The 8 bf16 of a unit as binary32 (exact). Element 2i is the low half of word i.
+__device__ __forceinline__ void unit_f32(const uint4& v, float (&f)[8]) {
+  f[0] = __uint_as_float(v.x << 16);
+  f[1] = __uint_as_float(v.x & 0xFFFF0000u);
+  f[2] = __uint_as_float(v.y << 16);
+  f[3] = __uint_as_float(v.y & 0xFFFF0000u);
+  f[4] = __uint_as_float(v.z << 16);
+  f[5] = __uint_as_float(v.z & 0xFFFF0000u);
+  f[6] = __uint_as_float(v.w << 16);
+  f[7] = __uint_as_float(v.w & 0xFFFF0000u);
 }
 
-// ------------------------------------------------------------ number formats
+// ------------------------------------------------------------ E2M1 codes
 
-// bf16 magnitude bits -> binary32 value (exact).
-__device__ __forceinline__ float mag_f32(uint32_t xb) { return __uint_as_float((xb & 0x7FFFu) << 16); }
-
-// binary32 -> bf16 bits, round to nearest even (finite or +Inf input).
-__device__ __forceinline__ uint32_t bf16_rne(float v) {
-  uint32_t b = __float_as_uint(v);
-  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+// RTN codes of 8 signed values; element i in nibble i (bits 4i..4i+3).
+__device__ __forceinline__ uint32_t rtn_codes(const float (&t)[8]) {
+  uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, t[0], t[1], 1.0f, 0);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, t[2], t[3], 1.0f, 1);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, t[4], t[5], 1.0f, 2);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, t[6], t[7], 1.0f, 3);
+  return c;
 }
 
-// E2M1 magnitude of index k: 0, .5, 1, 1.5, 2, 3, 4, 6.
-__device__ __forceinline__ float e2m1_val(uint32_t k) {
-  uint32_t b = (k + 252u) << 22;          // k >= 2: exponent/mantissa fields line up
-  b = (k == 1u) ? 0x3F000000u : b;
-  b = (k == 0u) ? 0u : b;
-  return __uint_as_float(b);
+// Codes of floor(|t|) onto the E2M1 magnitudes (sign kept). Only byte 0 of
+// each conversion is defined, so the four bytes are gathered with v_perm.
+__device__ __forceinline__ uint32_t floor_pair(float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, (f2_t){a, b}, 0u, 1.0f, 0);
+}
+__device__ __forceinline__ uint32_t floor_codes(const float (&t)[8]) {
+  const uint32_t s0 = floor_pair(t[0], t[1]), s1 = floor_pair(t[2], t[3]);
+  const uint32_t s2 = floor_pair(t[4], t[5]), s3 = floor_pair(t[6], t[7]);
+  const uint32_t lo = __builtin_amdgcn_perm(s1, s0, 0x0C0C0400u);  // [s0.b0, s1.b0, 0, 0]
+  const uint32_t hi = __builtin_amdgcn_perm(s3, s2, 0x0C0C0400u);  // [s2.b0, s3.b0, 0, 0]
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);               // [lo.b0, lo.b1, hi.b0, hi.b1]
 }
 
-// Round-to-nearest onto E2M1, ties to the even index, saturating at 6.
-__device__ __forceinline__ uint32_t rtn_index(float t) {
-  return (uint32_t)(t > 0.25f) + (uint32_t)(t >= 0.75f) + (uint32_t)(t > 1.25f) +
-         (uint32_t)(t >= 1.75f) + (uint32_t)(t > 2.5f) + (uint32_t)(t >= 3.5f) +
-         (uint32_t)(t > 5.0f);
+// Mantissa bits (bit 0 of each nibble) of a code dword -> one byte, element i at bit i.
+__device__ __forceinline__ uint32_t gather_mbits(uint32_t k) {
+  uint32_t m = k & 0x11111111u;
+  m = (m | (m >> 3)) & 0x03030303u;
+  m = (m | (m >> 6)) & 0x000F000Fu;
+  return (m | (m >> 12)) & 0xFFu;
+}
+// Inverse: bit i of a byte -> bit 0 of nibble i.
+__device__ __forceinline__ uint32_t spread_bits(uint32_t c) {
+  c = (c | (c << 12)) & 0x000F000Fu;
+  c = (c | (c << 6)) & 0x03030303u;
+  return (c | (c << 3)) & 0x11111111u;
 }
 
-// Largest k with v(k) <= t (7 for t >= 6): the lower end of BracketFP4.
-__device__ __forceinline__ uint32_t floor_index(float t) {
-  return (uint32_t)(t >= 0.5f) + (uint32_t)(t >= 1.0f) + (uint32_t)(t >= 1.5f) +
-         (uint32_t)(t >= 2.0f) + (uint32_t)(t >= 3.0f) + (uint32_t)(t >= 4.0f) +
-         (uint32_t)(t >= 6.0f);
+// Training-side selection under the rollout scale for the 8 elements of a
+// unit (t signed, carrying the training sign). Returns the chosen codes.
+//   BITS 0: RTN.
+//   BITS 1: compact record g = the rollout mantissa bits (byte). Of the
+//           bracket {lo, hi} take hi when t lies strictly inside it, lo < 7,
+//           hi's mantissa bit is the rollout's, and t is not in a dead zone
+//           (2, 2.25) or (4, 4.5), where the Reconstruct reference is lo - 1.
+//   BITS 4: full record g = rollout codes (dword). Take hi when t is inside,
+//           lo < 7, the signs agree and the rollout magnitude exceeds lo.
+//   DECODE (BITS 1): the Reconstruct reference itself instead of the choice.
+template <int BITS, bool DECODE>
+__device__ __forceinline__ uint32_t select_codes(const float (&t)[8], uint32_t g) {
+  if constexpr (BITS == 0) {
+    return rtn_codes(t);
+  } else {
+    const uint32_t L = floor_codes(t);
+    float tp[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tp[i] = __uint_as_float(__float_as_uint(t[i]) - 1u);
+    const uint32_t Lp = floor_codes(tp);
+    const uint32_t z = (L ^ Lp) & 0x77777777u;
+    const uint32_t X = (z | (z >> 1) | (z >> 2)) & 0x11111111u;  // t is a codeword
+    const uint32_t M = L & 0x77777777u;
+    const uint32_t S7 = M & (M >> 1) & (M >> 2) & 0x11111111u;   // lo == 7 (|t| >= 6)
+    if constexpr (BITS == 4) {
+      const uint32_t same_sign = ~(L ^ g) & 0x88888888u;
+      const uint32_t r_gt = ~((M | 0x88888888u) - (g & 0x77777777u)) & 0x88888888u;
+      return L + (((same_sign & r_gt) >> 3) & ~(X | S7));
+    } else {
+      const uint32_t P = (M ^ spread_bits(g)) & 0x11111111u;     // mantissa(lo) != c
+      uint32_t D = 0;                                            // |t| in [2,2.25) or [4,4.5)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        D |= ((((__float_as_uint(t[i]) & 0x7F700000u) ^ 0x40000000u) - 1u) >> 31) << (4 * i);
+      if constexpr (!DECODE) {
+        return L + (P & ~(X | S7 | D));
+      } else {
+        // Reference = nearest magnitude with mantissa c, ties up: lo when c
+        // matches; else hi, or lo - 1 in a dead zone or above 6; for a
+        // codeword t the nearer neighbour, lo - 1 exactly for lo in {4, 6, 7}.
+        const uint32_t Q = (M >> 2) & ((M >> 1) | ~M) & 0x11111111u;
+        const uint32_t up = P & ((~X & ~(S7 | D)) | (X & ~Q));
+        const uint32_t dn = P & ((~X & (S7 | D)) | (X & Q));
+        return L + up - dn;
+      }
+    }
+  }
 }
 
-// E4M3 (bias 7) byte of u in [0, 448], round to nearest even, subnormals kept.
-__device__ __forceinline__ uint32_t e4m3_rne(float u) {
-  uint32_t ub = __float_as_uint(u);
-  // Normal range (u >= 2^-6): keep 3 mantissa bits, rebias the exponent 127 -> 7.
-  uint32_t rn = ub + 0x7FFFFu + ((ub >> 20) & 1u);
-  uint32_t nb = (rn >> 20) - (120u << 3);
-  // Subnormal range: u * 2^9 rounded to an integer in [0, 8] (8 = 2^-6).
-  float s = u * 512.0f + 8388608.0f;      // the add to 2^23 rounds to nearest even
-  uint32_t sb = __float_as_uint(s) - 0x4B000000u;
-  return (u < 0.015625f) ? sb : nb;
+// ------------------------------------------------------------ dequantization
+
+template <int SEL>
+__device__ __forceinline__ uint32_t dec_bf16(uint32_t codes, float scale) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, SEL));
+}
+template <int SEL>
+__device__ __forceinline__ uint32_t dequant_nv_pair(uint32_t codes, float d) {
+  const uint32_t v = dec_bf16<SEL>(codes, 1.0f);
+  const f2_t p = {__uint_as_float(v << 16) * d, __uint_as_float(v & 0xFFFF0000u) * d};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf2_t));
+}
+// y = sign * bf16(v(k) * d) for the 8 codes (NVFP4: d any binary32).
+__device__ __forceinline__ uint4 dequant_nv(uint32_t codes, float d) {
+  return make_uint4(dequant_nv_pair<0>(codes, d), dequant_nv_pair<1>(codes, d),
+                    dequant_nv_pair<2>(codes, d), dequant_nv_pair<3>(codes, d));
+}
+// MXFP4: d = 2^E applied exactly by the conversion (scale = E8M0 byte << 23).
+__device__ __forceinline__ uint4 dequant_mx(uint32_t codes, float dscale) {
+  return make_uint4(dec_bf16<0>(codes, dscale), dec_bf16<1>(codes, dscale),
+                    dec_bf16<2>(codes, dscale), dec_bf16<3>(codes, dscale));
 }
 
-// E4M3 byte (sign ignored) -> value.
-__device__ __forceinline__ float e4m3_value(uint32_t byte) {
-  uint32_t ex = (byte >> 3) & 0xFu, m = byte & 7u;
-  return ex == 0u ? (float)m * 0x1p-9f : ldexpf(1.0f + (float)m * 0.125f, (int)ex - 7);
-}
+// ------------------------------------------------------------ scales
 
 // NVFP4 global scale from the tensor amax: 2688 / A, 1 for A == 0, <= FLT_MAX.
 __device__ __forceinline__ float global_scale(float amax) {
@@ -118,13 +201,28 @@ __device__ __forceinline__ float global_scale(float amax) {
   return fminf(2688.0f / amax, kFltMax);
 }
 
-// Per-workgroup table of the NVFP4 encode and decode factors of every E4M3
-// scale byte under the call's S: lut[e] = {r = min(S/e, FLT_MAX), d = e/S},
-// {0, 0} for e == 0. Replaces two divisions per block with one LDS read.
+// E4M3 scale byte of a block with max magnitude bits `bm` (bf16):
+// e = E4M3_RNE(min(fp32(fp32(a / 6) * S), 448)). fp32(a / 6) equals the
+// binary64 product a * fl64(1/6) rounded once to binary32 for every bf16 a.
+__device__ __forceinline__ uint32_t nv_scale_byte(uint32_t bm, float S) {
+  const float a = __uint_as_float(bm << 16);
+  const float q = (float)((double)a * (1.0 / 6.0));
+  const float u = fminf(q * S, 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(u, 0.0f, 0, false) & 0xFFu;
+}
+
+// E4M3 byte (0..127) -> value.
+__device__ __forceinline__ float e4m3_value(uint32_t b) {
+  const uint32_t ex = b >> 3, m = b & 7u;
+  return ex == 0u ? (float)m * 0x1p-9f : __uint_as_float(((ex + 120u) << 23) | (m << 20));
+}
+
+// Workgroup table of the NVFP4 factors of every E4M3 byte under S:
+// lut[e] = {r = min(S / e, FLT_MAX), d = e / S}, {0, 0} for e == 0.
 __device__ __forceinline__ void build_factor_lut(float2* lut, float S) {
-  int i = threadIdx.x;
+  const int i = threadIdx.x;
   if (i < 128) {
-    float e = e4m3_value((uint32_t)i);
+    const float e = e4m3_value((uint32_t)i);
     float r = 0.0f, d = 0.0f;
     if (e != 0.0f) {
       d = e / S;
@@ -134,222 +232,30 @@ __device__ __forceinline__ void build_factor_lut(float2* lut, float S) {
   }
 }
 
-// MXFP4 factors of an E8M0 byte: r = 2^-E, d = 2^E (exact).
-__device__ __forceinline__ void mx_factors(uint32_t byte, float& r, float& d) {
-  int E = (int)byte - 127;
-  r = ldexpf(1.0f, -E);
-  d = ldexpf(1.0f, E);
+// MXFP4: E8M0 byte of a block with max magnitude bits bm:
+// E = clamp(floor(log2 a) - 2, -127, 127), byte = E + 127.
+__device__ __forceinline__ uint32_t mx_scale_byte(uint32_t bm) {
+  return (uint32_t)max((int)((bm >> 7) & 0xFFu) - 2, 0);
 }
-
-__device__ __forceinline__ uint32_t dequant_bits(uint32_t k, float d, uint32_t sign) {
-  return bf16_rne(e2m1_val(k) * d) | (sign << 15);
+// r = 2^-E (exact; 2^-127 is subnormal).
+__device__ __forceinline__ float mx_r(uint32_t sb) {
+  return __uint_as_float(sb >= 254u ? 0x00400000u : (254u - sb) << 23);
 }
+// Scale operand that makes the bf16 decode multiply by 2^E.
+__device__ __forceinline__ float mx_dscale(uint32_t sb) { return __uint_as_float(sb << 23); }
 
-// ------------------------------------------------------------ kernels
+// ------------------------------------------------------------ reductions
 
-__global__ __launch_bounds__(64) void init_gscale_kernel(float* g) {
-  if (threadIdx.x == 0) {
-    g[0] = 1.0f;
-    g[1] = 0.0f;
-  }
-}
-
-// Tensor amax: max over bf16 magnitude bits; one atomic max per workgroup
-// on the binary32 bits of A (monotonic for non-negative values).
-__global__ __launch_bounds__(kThreads) void amax_kernel(const uint4* __restrict__ x, int64_t units,
-                                                        uint32_t* __restrict__ slot) {
-  uint32_t m = 0;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  for (; u + 3 * stride < units; u += 4 * stride) {
-    uint4 a = x[u], b = x[u + stride], c = x[u + 2 * stride], d = x[u + 3 * stride];
-    m = max(m, max(max(unit_amax_bits(a), unit_amax_bits(b)),
-                   max(unit_amax_bits(c), unit_amax_bits(d))));
-  }
-  for (; u < units; u += stride) m = max(m, unit_amax_bits(x[u]));
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t m) {
   for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-  __shared__ uint32_t wmax[kThreads / 64];
-  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t b = wmax[0];
-    for (int w = 1; w < kThreads / 64; ++w) b = max(b, wmax[w]);
-    atomicMax(slot, b << 16);
-  }
+  return m;
 }
-
-// RTN quantization of one tensor (quantize_rtn / encode_guidance).
-// FMT 0 NVFP4 / 1 MXFP4; PLANE 0 writes codes (u32 per unit), 1 writes the
-// mantissa-bit plane (one byte per unit); WY writes y; SFA derives S from the
-// amax in gsrc[1] and stores it to gsrc[0] (else S = gsrc[0]).
-template <int FMT, int PLANE, bool WY, bool SFA>
-__global__ __launch_bounds__(kThreads) void quantize_kernel(const uint4* __restrict__ x, int64_t units,
-                                                            float* gsrc, uint8_t* __restrict__ plane,
-                                                            uint8_t* __restrict__ scales,
-                                                            uint4* __restrict__ y) {
-  __shared__ float2 lut[128];
-  float S = 1.0f;
-  if constexpr (FMT == 0) {
-    if constexpr (SFA) {
-      S = global_scale(gsrc[1]);
-      if (blockIdx.x == 0 && threadIdx.x == 0) gsrc[0] = S;
-    } else {
-      S = gsrc[0];
-    }
-    build_factor_lut(lut, S);
-    __syncthreads();
-  }
-  const int64_t base = (int64_t)blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
-  uint4 v[kUnroll];
-#pragma unroll
-  for (int j = 0; j < kUnroll; ++j) {
-    int64_t u = base + j * kThreads;
-    v[j] = u < units ? x[u] : make_uint4(0u, 0u, 0u, 0u);
-  }
-#pragma unroll
-  for (int j = 0; j < kUnroll; ++j) {
-    const int64_t u = base + j * kThreads;
-    uint32_t bm = unit_amax_bits(v[j]);
-    bm = max(bm, xor1(bm));
-    if constexpr (FMT == 1) bm = max(bm, xor2(bm));
-    float r, d;
-    uint32_t sbyte;
-    if constexpr (FMT == 0) {
-      float a = __uint_as_float(bm << 16);
-      float su = fminf((a / 6.0f) * S, 448.0f);
-      sbyte = e4m3_rne(su);
-      float2 rd = lut[sbyte & 0x7Fu];
-      r = rd.x;
-      d = rd.y;
-    } else {
-      int ef = (int)((bm >> 7) & 0xFFu);
-      sbyte = (uint32_t)max(ef - 2, 0);
-      mx_factors(sbyte, r, d);
-    }
-    uint32_t codes = 0, mbits = 0;
-    uint32_t yw[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint32_t xb = elem_bits(v[j], e);
-      uint32_t s = xb >> 15;
-      float t = mag_f32(xb) * r;
-      uint32_t k = rtn_index(t);
-      codes |= ((s << 3) | k) << (4 * e);
-      mbits |= (k & 1u) << e;
-      if constexpr (WY) yw[e >> 1] |= dequant_bits(k, d, s) << (16 * (e & 1));
-    }
-    if (u < units) {
-      if constexpr (PLANE == 0) reinterpret_cast<uint32_t*>(plane)[u] = codes;
-      else plane[u] = (uint8_t)mbits;
-      if constexpr (FMT == 0) {
-        if ((u & 1) == 0) scales[u >> 1] = (uint8_t)sbyte;
-      } else {
-        if ((u & 3) == 0) scales[u >> 2] = (uint8_t)sbyte;
-      }
-      if constexpr (WY) y[u] = make_uint4(yw[0], yw[1], yw[2], yw[3]);
-    }
-  }
-}
-
-// Guided rounding under the rollout scales (guided_fake_quant) and the
-// Reconstruct step alone (decode_guidance, DECODE = true).
-// BITS 0: RTN; 1: compact (mantissa bit); 4: full rollout code.
-template <int FMT, int BITS, bool DECODE, bool WCODES>
-__global__ __launch_bounds__(kThreads) void guided_kernel(const uint4* __restrict__ x, int64_t units,
-                                                          const uint8_t* __restrict__ guide,
-                                                          const uint8_t* __restrict__ scales,
-                                                          const float* __restrict__ gscale,
-                                                          uint4* __restrict__ y,
-                                                          uint32_t* __restrict__ codes_out) {
-  __shared__ float2 lut[128];
-  if constexpr (FMT == 0) {
-    build_factor_lut(lut, gscale[0]);
-    __syncthreads();
-  }
-  const int64_t base = (int64_t)blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
-  uint4 v[kUnroll];
-  uint32_t sb[kUnroll], g[kUnroll];
-#pragma unroll
-  for (int j = 0; j < kUnroll; ++j) {
-    int64_t u = base + j * kThreads;
-    bool ok = u < units;
-    v[j] = ok ? x[u] : make_uint4(0u, 0u, 0u, 0u);
-    sb[j] = ok ? (uint32_t)scales[FMT == 0 ? (u >> 1) : (u >> 2)] : 0u;
-    if constexpr (BITS == 1) g[j] = ok ? (uint32_t)guide[u] : 0u;
-    else if constexpr (BITS == 4) g[j] = ok ? reinterpret_cast<const uint32_t*>(guide)[u] : 0u;
-    else g[j] = 0u;
-  }
-#pragma unroll
-  for (int j = 0; j < kUnroll; ++j) {
-    const int64_t u = base + j * kThreads;
-    float r, d;
-    if constexpr (FMT == 0) {
-      float2 rd = lut[sb[j] & 0x7Fu];
-      r = rd.x;
-      d = rd.y;
-    } else {
-      mx_factors(sb[j], r, d);
-    }
-    uint32_t codes = 0;
-    uint32_t yw[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint32_t xb = elem_bits(v[j], e);
-      uint32_t s = xb >> 15;
-      float t = mag_f32(xb) * r;
-      uint32_t k;
-      if constexpr (BITS == 0) {
-        k = rtn_index(t);
-      } else {
-        uint32_t f = floor_index(t);
-        bool inside = (t != e2m1_val(f)) && (f < 7u);
-        if constexpr (BITS == 1) {
-          uint32_t c = (g[j] >> e) & 1u;
-          // The nearest magnitude of the other parity lies above t unless t is
-          // in a dead zone, (2, 2.25) below 3 or (4, 4.5) below 6, where the
-          // one below is nearer (ties go up).
-          bool dead = (f == 4u && t < 2.25f) || (f == 6u && t < 4.5f);
-          if constexpr (DECODE) {
-            k = (c == (f & 1u)) ? f : ((f < 7u && !dead) ? f + 1u : f - 1u);
-          } else {
-            k = f + (uint32_t)(inside && c != (f & 1u) && !dead);
-          }
-        } else {
-          uint32_t cr = (g[j] >> (4 * e)) & 0xFu;
-          k = f + (uint32_t)(inside && (cr >> 3) == s && (cr & 7u) > f);
-        }
-      }
-      codes |= ((s << 3) | k) << (4 * e);
-      if constexpr (!DECODE) yw[e >> 1] |= dequant_bits(k, d, s) << (16 * (e & 1));
-    }
-    if (u < units) {
-      if constexpr (DECODE || WCODES) codes_out[u] = codes;
-      if constexpr (!DECODE) y[u] = make_uint4(yw[0], yw[1], yw[2], yw[3]);
-    }
-  }
-}
-
-// ------------------------------------------------------------ discrepancy sums
-
-__device__ __forceinline__ double bf16_f64(uint32_t b) { return (double)__uint_as_float(b << 16); }
-
-__device__ __forceinline__ void accum_unit(const uint4& a, const uint4& b, double& acc) {
-  const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    double d0 = bf16_f64(wa[i] & 0xFFFFu) - bf16_f64(wb[i] & 0xFFFFu);
-    double d1 = bf16_f64(wa[i] >> 16) - bf16_f64(wb[i] >> 16);
-    acc += d0 * d0;
-    acc += d1 * d1;
-  }
-}
-
 __device__ __forceinline__ double wave_sum(double v) {
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
   return v;
 }
 
-// Fixed-order sum of a workgroup's per-thread values; result valid in thread 0.
+// Fixed-order sum of the workgroup's per-thread values; result valid in thread 0.
 __device__ __forceinline__ void group_sum2(double& a, double& b) {
   __shared__ double sa[kThreads / 64], sbuf[kThreads / 64];
   a = wave_sum(a);
@@ -369,6 +275,301 @@ __device__ __forceinline__ void group_sum2(double& a, double& b) {
   }
 }
 
+// Sum of 8 non-negative binary32 terms, pairwise.
+__device__ __forceinline__ float sum8(const float (&s)[8]) {
+  return ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
+}
+
+// sum_i (a_i - b_i)^2 over 8 pairs of binary32 values, returned as binary64.
+// Fast path in binary32: each term passes through at most 5 roundings, so the
+// relative error of the (non-negative) sum is below 5 * 2^-24. When the
+// binary32 sum leaves [2^-100, FLT_MAX] (a square overflowed, or every term is
+// tiny enough for underflow to matter) the unit is summed in binary64.
+__device__ __forceinline__ double sq_diff_sum(const float (&a)[8], const float (&b)[8]) {
+  float sq[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float d = a[i] - b[i];
+    sq[i] = d * d;
+  }
+  const float s = sum8(sq);
+  if (s >= 0x1p-100f && s <= kFltMax) return (double)s;
+  double acc = 0.0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const double d = (double)a[i] - (double)b[i];
+    acc += d * d;
+  }
+  return acc;
+}
+
+// ------------------------------------------------------------ kernel arguments
+
+struct TileMap {
+  int64_t upg;        // units per group
+  int64_t tiles;      // tiles per group
+};
+
+__device__ __forceinline__ void tile_of(const TileMap& m, int64_t& g, int64_t& tbase) {
+  const int64_t b = blockIdx.x;
+  g = b / m.tiles;
+  tbase = (b - g * m.tiles) * kTileUnits;
+}
+
+struct QuantArgs {
+  TileMap map;
+  const uint4* x;
+  const float* gin;          // S of group g at gin[2g]
+  float* gout;               // {S, A} per group
+  const uint32_t* part;      // amax partials [groups][kPartMax]
+  int nparts;                // partials per group
+  uint8_t* plane;
+  uint8_t* scales;
+  uint4* y;
+};
+
+struct GuidedArgs {
+  TileMap map;
+  const uint4* x;
+  const uint8_t* guide;
+  const uint8_t* scales;
+  const float* gscale;       // S of group g at gscale[2g]
+  uint4* y;
+  uint32_t* codes;
+  const uint4* xr;           // rollout input (stats)
+  double* partials;          // 2 per workgroup (stats)
+};
+
+struct AmaxArgs {
+  const uint4* x;
+  int64_t upg;
+  int nparts;
+  uint32_t* part;
+};
+
+// ------------------------------------------------------------ kernels
+
+__global__ __launch_bounds__(64) void fill_gscale_kernel(float* g, int64_t groups) {
+  const int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  if (i < groups) {
+    g[2 * i] = 1.0f;
+    g[2 * i + 1] = 0.0f;
+  }
+}
+
+// Partial tensor amax: workgroup w of group g writes the max bf16 magnitude
+// (as binary32 bits) of its strided share of the group to part[g][w].
+__global__ __launch_bounds__(kThreads) void amax_kernel(AmaxArgs a) {
+  const int64_t g = blockIdx.x / a.nparts;
+  const int w = (int)(blockIdx.x - g * a.nparts);
+  const uint4* x = a.x + g * a.upg;
+  const int64_t stride = (int64_t)a.nparts * kThreads;
+  uint32_t m = 0;
+  int64_t u = (int64_t)w * kThreads + threadIdx.x;
+  for (; u + 3 * stride < a.upg; u += 4 * stride) {
+    const uint4 p = x[u], q = x[u + stride], r = x[u + 2 * stride], s = x[u + 3 * stride];
+    m = max(m, max(max(unit_amax_bits(p), unit_amax_bits(q)), max(unit_amax_bits(r), unit_amax_bits(s))));
+  }
+  for (; u < a.upg; u += stride) m = max(m, unit_amax_bits(x[u]));
+  m = wave_max_u32(m);
+  __shared__ uint32_t wm[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t b = wm[0];
+    for (int i = 1; i < kThreads / 64; ++i) b = max(b, wm[i]);
+    a.part[g * kPartMax + w] = b << 16;
+  }
+}
+
+// RTN quantization (quantize_rtn / encode_guidance).
+// FMT 0 NVFP4 / 1 MXFP4; PLANE 0 codes (u32 per unit) / 1 mantissa bits (u8
+// per unit); WY writes y; SSRC (NVFP4) 0: S = gin[2g]; 1: S from the amax
+// partials, {S, A} stored to gout by the group's first tile.
+template <int FMT, int PLANE, bool WY, int SSRC>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
+  __shared__ float2 lut[128];
+  __shared__ uint32_t red[kThreads / 64];
+  int64_t g, tbase;
+  tile_of(a.map, g, tbase);
+  float S = 1.0f;
+  if constexpr (FMT == 0) {
+    if constexpr (SSRC == 1) {
+      uint32_t m = 0;
+      for (int i = threadIdx.x; i < a.nparts; i += kThreads) m = max(m, a.part[g * kPartMax + i]);
+      m = wave_max_u32(m);
+      if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+      __syncthreads();
+      m = max(max(red[0], red[1]), max(red[2], red[3]));
+      const float A = __uint_as_float(m);
+      S = global_scale(A);
+      if (tbase == 0 && threadIdx.x == 0) {
+        a.gout[2 * g] = S;
+        a.gout[2 * g + 1] = A;
+      }
+    } else {
+      S = a.gin[2 * g];
+    }
+    build_factor_lut(lut, S);
+    __syncthreads();
+  }
+  const int64_t gbase = g * a.map.upg;
+  uint4 v[kUPT];
+#pragma unroll
+  for (int j = 0; j < kUPT; ++j) {
+    const int64_t u = tbase + j * kThreads + threadIdx.x;
+    v[j] = u < a.map.upg ? a.x[gbase + u] : make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int j = 0; j < kUPT; ++j) {
+    const int64_t u = tbase + j * kThreads + threadIdx.x;
+    uint32_t bm = unit_amax_bits(v[j]);
+    bm = max(bm, xor1(bm));
+    if constexpr (FMT == 1) bm = max(bm, xor2(bm));
+    float r, d = 0.0f, dsc = 0.0f;
+    uint32_t sb;
+    if constexpr (FMT == 0) {
+      sb = nv_scale_byte(bm, S);
+      const float2 rd = lut[sb & 0x7Fu];
+      r = rd.x;
+      d = rd.y;
+    } else {
+      sb = mx_scale_byte(bm);
+      r = mx_r(sb);
+      dsc = mx_dscale(sb);
+    }
+    float f[8];
+    unit_f32(v[j], f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] *= r;
+    const uint32_t K = rtn_codes(f);
+    if (u < a.map.upg) {
+      const int64_t gu = gbase + u;
+      if constexpr (PLANE == 0) reinterpret_cast<uint32_t*>(a.plane)[gu] = K;
+      else a.plane[gu] = (uint8_t)gather_mbits(K);
+      if constexpr (FMT == 0) {
+        if ((gu & 1) == 0) a.scales[gu >> 1] = (uint8_t)sb;
+      } else {
+        if ((gu & 3) == 0) a.scales[gu >> 2] = (uint8_t)sb;
+      }
+      if constexpr (WY) a.y[gu] = FMT == 0 ? dequant_nv(K, d) : dequant_mx(K, dsc);
+    }
+  }
+}
+
+// Guided rounding under the rollout scales (guided_fake_quant), Reconstruct
+// alone (DECODE: reference codes, no y), and the fused discrepancy sums
+// (STATS: SB = sum (x_t - x_r)^2 over the inputs; SF = sum (y_t - y_r)^2 with
+// y_r the rollout's RTN output under the same scales, recomputed from x_r).
+template <int FMT, int BITS, bool DECODE, bool WCODES, bool STATS>
+__global__ __launch_bounds__(kThreads) void guided_kernel(GuidedArgs a) {
+  __shared__ float2 lut[128];
+  int64_t g, tbase;
+  tile_of(a.map, g, tbase);
+  if constexpr (FMT == 0) {
+    build_factor_lut(lut, a.gscale[2 * g]);
+    __syncthreads();
+  }
+  const int64_t gbase = g * a.map.upg;
+  uint4 v[kUPT];
+  uint4 vr[STATS ? kUPT : 1];
+  uint32_t sbv[kUPT], gv[kUPT];
+#pragma unroll
+  for (int j = 0; j < kUPT; ++j) {
+    const int64_t u = tbase + j * kThreads + threadIdx.x;
+    const bool ok = u < a.map.upg;
+    const int64_t gu = gbase + u;
+    v[j] = ok ? a.x[gu] : make_uint4(0u, 0u, 0u, 0u);
+    if constexpr (STATS) vr[j] = ok ? a.xr[gu] : make_uint4(0u, 0u, 0u, 0u);
+    sbv[j] = ok ? (uint32_t)a.scales[FMT == 0 ? (gu >> 1) : (gu >> 2)] : 0u;
+    if constexpr (BITS == 1) gv[j] = ok ? (uint32_t)a.guide[gu] : 0u;
+    else if constexpr (BITS == 4) gv[j] = ok ? reinterpret_cast<const uint32_t*>(a.guide)[gu] : 0u;
+    else gv[j] = 0u;
+  }
+  double acc_b = 0.0, acc_f = 0.0;
+#pragma unroll
+  for (int j = 0; j < kUPT; ++j) {
+    const int64_t u = tbase + j * kThreads + threadIdx.x;
+    float r, d = 0.0f, dsc = 0.0f;
+    if constexpr (FMT == 0) {
+      const float2 rd = lut[sbv[j] & 0x7Fu];
+      r = rd.x;
+      d = rd.y;
+    } else {
+      r = mx_r(sbv[j]);
+      dsc = mx_dscale(sbv[j]);
+    }
+    float f[8], t[8];
+    unit_f32(v[j], f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = f[i] * r;
+    const uint32_t K = select_codes<BITS, DECODE>(t, gv[j]);
+    uint4 yv = make_uint4(0u, 0u, 0u, 0u);
+    if constexpr (!DECODE) yv = FMT == 0 ? dequant_nv(K, d) : dequant_mx(K, dsc);
+    if constexpr (STATS) {
+      float fr[8];
+      unit_f32(vr[j], fr);
+      acc_b += sq_diff_sum(f, fr);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) fr[i] *= r;
+      const uint32_t KR = rtn_codes(fr);
+      if (K != KR) {  // equal codes under one scale give equal outputs
+        const uint4 yr = FMT == 0 ? dequant_nv(KR, d) : dequant_mx(KR, dsc);
+        float ft[8], fq[8];
+        unit_f32(yv, ft);
+        unit_f32(yr, fq);
+        acc_f += sq_diff_sum(ft, fq);
+      }
+    }
+    if (u < a.map.upg) {
+      const int64_t gu = gbase + u;
+      if constexpr (DECODE || WCODES) a.codes[gu] = K;
+      if constexpr (!DECODE) a.y[gu] = yv;
+    }
+  }
+  if constexpr (STATS) {
+    group_sum2(acc_b, acc_f);
+    if (threadIdx.x == 0) {
+      a.partials[2 * blockIdx.x] = acc_b;
+      a.partials[2 * blockIdx.x + 1] = acc_f;
+    }
+  }
+}
+
+// Fixed-order reduction of `groups` partial pairs into acc3 = {SB, SF, n}.
+__global__ __launch_bounds__(kThreads) void sums_final_kernel(const double* __restrict__ partials,
+                                                              int64_t groups, int64_t n, double* acc3,
+                                                              int accumulate) {
+  double sb = 0.0, sf = 0.0;
+  for (int64_t i = threadIdx.x; i < groups; i += kThreads) {
+    sb += partials[2 * i];
+    sf += partials[2 * i + 1];
+  }
+  group_sum2(sb, sf);
+  if (threadIdx.x == 0) {
+    if (accumulate) {
+      acc3[0] += sb;
+      acc3[1] += sf;
+      acc3[2] += (double)n;
+    } else {
+      acc3[0] = sb;
+      acc3[1] = sf;
+      acc3[2] = (double)n;
+    }
+  }
+}
+
+// ------------------------------------------------------------ discrepancy_stats
+
+__device__ __forceinline__ void accum_unit(const uint4& a, const uint4& b, double& acc) {
+  float fa[8], fb[8];
+  unit_f32(a, fa);
+  unit_f32(b, fb);
+  acc += sq_diff_sum(fa, fb);
+}
+
+__device__ __forceinline__ double bf16_f64(uint32_t b) { return (double)__uint_as_float(b << 16); }
+
 __global__ __launch_bounds__(kThreads) void stats_partial_kernel(const uint16_t* __restrict__ xt,
                                                                  const uint16_t* __restrict__ xr,
                                                                  const uint16_t* __restrict__ yt,
@@ -387,8 +588,8 @@ __global__ __launch_bounds__(kThreads) void stats_partial_kernel(const uint16_t*
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     for (int64_t i = units * kUnitElems; i < n; ++i) {
-      double dx = bf16_f64(xt[i]) - bf16_f64(xr[i]);
-      double dy = bf16_f64(yt[i]) - bf16_f64(yr[i]);
+      const double dx = bf16_f64(xt[i]) - bf16_f64(xr[i]);
+      const double dy = bf16_f64(yt[i]) - bf16_f64(yr[i]);
       sb += dx * dx;
       sf += dy * dy;
     }
@@ -397,28 +598,6 @@ __global__ __launch_bounds__(kThreads) void stats_partial_kernel(const uint16_t*
   if (threadIdx.x == 0) {
     partials[2 * blockIdx.x] = sb;
     partials[2 * blockIdx.x + 1] = sf;
-  }
-}
-
-__global__ __launch_bounds__(kThreads) void stats_final_kernel(const double* __restrict__ partials,
-                                                               int groups, int64_t n, double* acc3,
-                                                               int accumulate) {
-  double sb = 0.0, sf = 0.0;
-  for (int i = threadIdx.x; i < groups; i += kThreads) {
-    sb += partials[2 * i];
-    sf += partials[2 * i + 1];
-  }
-  group_sum2(sb, sf);
-  if (threadIdx.x == 0) {
-    if (accumulate) {
-      acc3[0] += sb;
-      acc3[1] += sf;
-      acc3[2] += (double)n;
-    } else {
-      acc3[0] = sb;
-      acc3[1] = sf;
-      acc3[2] = (double)n;
-    }
   }
 }
 
@@ -439,98 +618,139 @@ hipError_t launch(void (*k)(P...), dim3 grid, dim3 block, hipStream_t s, A... ar
   return hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, argv, 0, s);
 }
 
-inline unsigned grid_for(int64_t units) {
-  return (unsigned)((units + (int64_t)kThreads * kUnroll - 1) / ((int64_t)kThreads * kUnroll));
+TileMap tile_map(const Shape& sh) {
+  TileMap m;
+  m.upg = sh.upg;
+  m.tiles = (sh.upg + kTileUnits - 1) / kTileUnits;
+  return m;
 }
 
-template <int FMT, int PLANE, bool WY, bool SFA>
-hipError_t quant_dispatch(const uint16_t* x, int64_t units, float* gsrc, uint8_t* plane,
-                          uint8_t* scales, uint16_t* y, hipStream_t s) {
-  return launch(quantize_kernel<FMT, PLANE, WY, SFA>, dim3(grid_for(units)), dim3(kThreads), s,
-                reinterpret_cast<const uint4*>(x), units, gsrc, plane, scales,
-                reinterpret_cast<uint4*>(y));
+unsigned tile_grid(const Shape& sh) { return (unsigned)(sh.groups * tile_map(sh).tiles); }
+
+int amax_parts(int64_t upg) {
+  int64_t p = (upg + (int64_t)kThreads * 8 - 1) / ((int64_t)kThreads * 8);
+  if (p < 1) p = 1;
+  if (p > kPartMax) p = kPartMax;
+  return (int)p;
+}
+
+template <int FMT, int PLANE, bool WY, int SSRC>
+hipError_t quant_go(const QuantArgs& a, const Shape& sh, hipStream_t s) {
+  return launch(quantize_kernel<FMT, PLANE, WY, SSRC>, dim3(tile_grid(sh)), dim3(kThreads), s, a);
 }
 
 template <int FMT, int PLANE>
-hipError_t quant_dispatch_y(bool wy, bool sfa, const uint16_t* x, int64_t units, float* gsrc,
-                            uint8_t* plane, uint8_t* scales, uint16_t* y, hipStream_t s) {
-  if (wy) {
-    return sfa ? quant_dispatch<FMT, PLANE, true, true>(x, units, gsrc, plane, scales, y, s)
-               : quant_dispatch<FMT, PLANE, true, false>(x, units, gsrc, plane, scales, y, s);
-  }
-  return sfa ? quant_dispatch<FMT, PLANE, false, true>(x, units, gsrc, plane, scales, y, s)
-             : quant_dispatch<FMT, PLANE, false, false>(x, units, gsrc, plane, scales, y, s);
+hipError_t quant_wy(bool wy, int ssrc, const QuantArgs& a, const Shape& sh, hipStream_t s) {
+  if (wy) return ssrc ? quant_go<FMT, PLANE, true, 1>(a, sh, s) : quant_go<FMT, PLANE, true, 0>(a, sh, s);
+  return ssrc ? quant_go<FMT, PLANE, false, 1>(a, sh, s) : quant_go<FMT, PLANE, false, 0>(a, sh, s);
 }
 
-template <int FMT, int BITS, bool DECODE, bool WCODES>
-hipError_t guided_dispatch(const uint16_t* x, int64_t units, const uint8_t* guide,
-                           const uint8_t* scales, const float* gscale, uint16_t* y, uint8_t* codes,
-                           hipStream_t s) {
-  return launch(guided_kernel<FMT, BITS, DECODE, WCODES>, dim3(grid_for(units)), dim3(kThreads), s,
-                reinterpret_cast<const uint4*>(x), units, guide, scales, gscale,
-                reinterpret_cast<uint4*>(y), reinterpret_cast<uint32_t*>(codes));
+template <int FMT, int BITS, bool DECODE, bool WCODES, bool STATS>
+hipError_t guided_go(const GuidedArgs& a, const Shape& sh, hipStream_t s) {
+  return launch(guided_kernel<FMT, BITS, DECODE, WCODES, STATS>, dim3(tile_grid(sh)), dim3(kThreads), s, a);
+}
+
+template <int FMT, int BITS>
+hipError_t guided_bits(bool wc, bool stats, const GuidedArgs& a, const Shape& sh, hipStream_t s) {
+  if (stats) return wc ? guided_go<FMT, BITS, false, true, true>(a, sh, s)
+                       : guided_go<FMT, BITS, false, false, true>(a, sh, s);
+  return wc ? guided_go<FMT, BITS, false, true, false>(a, sh, s)
+            : guided_go<FMT, BITS, false, false, false>(a, sh, s);
 }
 
 template <int FMT>
-hipError_t guided_fmt(int bits, bool decode, const uint16_t* x, int64_t units, const uint8_t* guide,
-                      const uint8_t* scales, const float* gscale, uint16_t* y, uint8_t* codes,
-                      hipStream_t s) {
-  if (decode) return guided_dispatch<FMT, 1, true, true>(x, units, guide, scales, gscale, y, codes, s);
-  const bool wc = codes != nullptr;
+hipError_t guided_fmt(int bits, bool decode, bool wc, bool stats, const GuidedArgs& a,
+                      const Shape& sh, hipStream_t s) {
+  if (decode) return guided_go<FMT, 1, true, true, false>(a, sh, s);
   switch (bits) {
-    case 0:
-      return wc ? guided_dispatch<FMT, 0, false, true>(x, units, guide, scales, gscale, y, codes, s)
-                : guided_dispatch<FMT, 0, false, false>(x, units, guide, scales, gscale, y, codes, s);
-    case 1:
-      return wc ? guided_dispatch<FMT, 1, false, true>(x, units, guide, scales, gscale, y, codes, s)
-                : guided_dispatch<FMT, 1, false, false>(x, units, guide, scales, gscale, y, codes, s);
-    default:
-      return wc ? guided_dispatch<FMT, 4, false, true>(x, units, guide, scales, gscale, y, codes, s)
-                : guided_dispatch<FMT, 4, false, false>(x, units, guide, scales, gscale, y, codes, s);
+    case 0: return guided_bits<FMT, 0>(wc, stats, a, sh, s);
+    case 1: return guided_bits<FMT, 1>(wc, stats, a, sh, s);
+    default: return guided_bits<FMT, 4>(wc, stats, a, sh, s);
   }
 }
 
 }  // namespace
 
+int64_t quant_work_bytes(const Shape& sh) {
+  return sh.groups * (int64_t)kPartMax * (int64_t)sizeof(uint32_t);
+}
+
+int64_t guided_stats_work_bytes(const Shape& sh) {
+  return 2 * (int64_t)sizeof(double) * (int64_t)tile_grid(sh);
+}
+
 int64_t stats_groups(int64_t n) {
   int64_t units = n / kUnitElems;
   int64_t g = (units + (int64_t)kThreads * 4 - 1) / ((int64_t)kThreads * 4);
   if (g < 1) g = 1;
-  if (g > kStatsMaxGroups) g = kStatsMaxGroups;
+  if (g > 1024) g = 1024;
   return g;
 }
 
-hipError_t launch_global_scale(const uint16_t* x, int64_t units, float* gscale_out,
-                               hipStream_t stream) {
-  hipError_t e = launch(init_gscale_kernel, dim3(1), dim3(64), stream, gscale_out);
-  if (e != hipSuccess || units == 0) return e;
-  int64_t g = (units + (int64_t)kThreads * 8 - 1) / ((int64_t)kThreads * 8);
-  if (g > 2048) g = 2048;
-  return launch(amax_kernel, dim3((unsigned)g), dim3(kThreads), stream,
-                reinterpret_cast<const uint4*>(x), units, reinterpret_cast<uint32_t*>(gscale_out + 1));
-}
+int64_t stats_work_bytes(int64_t n) { return 2 * (int64_t)sizeof(double) * stats_groups(n); }
 
-hipError_t launch_quantize(int fmt, int plane_mode, bool s_from_amax, const uint16_t* x,
-                           int64_t units, float* gsrc, uint8_t* plane, uint8_t* scales,
-                           uint16_t* y, hipStream_t stream) {
-  if (units == 0) return hipSuccess;
-  const bool wy = y != nullptr;
-  if (fmt == 0) {
-    return plane_mode == 0
-               ? quant_dispatch_y<0, 0>(wy, s_from_amax, x, units, gsrc, plane, scales, y, stream)
-               : quant_dispatch_y<0, 1>(wy, s_from_amax, x, units, gsrc, plane, scales, y, stream);
+hipError_t launch_quantize(int fmt, int plane_mode, const Shape& sh, const uint16_t* x,
+                           const float* gin, float* gout, uint8_t* plane, uint8_t* scales,
+                           uint16_t* y, void* work, hipStream_t stream) {
+  const int64_t units = sh.groups * sh.upg;
+  if (units == 0) {
+    if (gout == nullptr || sh.groups == 0) return hipSuccess;
+    return launch(fill_gscale_kernel, dim3((unsigned)((sh.groups + 63) / 64)), dim3(64), stream, gout,
+                  sh.groups);
   }
-  return plane_mode == 0
-             ? quant_dispatch_y<1, 0>(wy, false, x, units, gsrc, plane, scales, y, stream)
-             : quant_dispatch_y<1, 1>(wy, false, x, units, gsrc, plane, scales, y, stream);
+  QuantArgs a{};
+  a.map = tile_map(sh);
+  a.x = reinterpret_cast<const uint4*>(x);
+  a.gin = gin;
+  a.gout = gout;
+  a.plane = plane;
+  a.scales = scales;
+  a.y = reinterpret_cast<uint4*>(y);
+  int ssrc = 0;
+  if (fmt == 0 && gout != nullptr) {
+    ssrc = 1;
+    AmaxArgs m;
+    m.x = a.x;
+    m.upg = sh.upg;
+    m.nparts = amax_parts(sh.upg);
+    m.part = static_cast<uint32_t*>(work);
+    hipError_t e = launch(amax_kernel, dim3((unsigned)(sh.groups * m.nparts)), dim3(kThreads), stream, m);
+    if (e != hipSuccess) return e;
+    a.part = m.part;
+    a.nparts = m.nparts;
+  }
+  const bool wy = y != nullptr;
+  if (fmt == 0) return plane_mode == 0 ? quant_wy<0, 0>(wy, ssrc, a, sh, stream) : quant_wy<0, 1>(wy, ssrc, a, sh, stream);
+  return plane_mode == 0 ? quant_wy<1, 0>(wy, 0, a, sh, stream) : quant_wy<1, 1>(wy, 0, a, sh, stream);
 }
 
-hipError_t launch_guided(int fmt, int bits, bool decode_only, const uint16_t* x, int64_t units,
+hipError_t launch_guided(int fmt, int bits, bool decode_only, const Shape& sh, const uint16_t* x,
                          const uint8_t* guide, const uint8_t* scales, const float* gscale,
-                         uint16_t* y, uint8_t* codes, hipStream_t stream) {
-  if (units == 0) return hipSuccess;
-  return fmt == 0 ? guided_fmt<0>(bits, decode_only, x, units, guide, scales, gscale, y, codes, stream)
-                  : guided_fmt<1>(bits, decode_only, x, units, guide, scales, gscale, y, codes, stream);
+                         uint16_t* y, uint8_t* codes, const uint16_t* xr, double* acc3,
+                         int accumulate, void* work, hipStream_t stream) {
+  const int64_t units = sh.groups * sh.upg;
+  const bool stats = acc3 != nullptr;
+  if (units == 0) {
+    if (!stats) return hipSuccess;
+    return launch(sums_final_kernel, dim3(1), dim3(kThreads), stream, (const double*)nullptr,
+                  (int64_t)0, (int64_t)0, acc3, accumulate);
+  }
+  GuidedArgs a{};
+  a.map = tile_map(sh);
+  a.x = reinterpret_cast<const uint4*>(x);
+  a.guide = guide;
+  a.scales = scales;
+  a.gscale = gscale;
+  a.y = reinterpret_cast<uint4*>(y);
+  a.codes = reinterpret_cast<uint32_t*>(codes);
+  a.xr = reinterpret_cast<const uint4*>(xr);
+  a.partials = static_cast<double*>(work);
+  const bool wc = codes != nullptr;
+  hipError_t e = fmt == 0 ? guided_fmt<0>(bits, decode_only, wc, stats, a, sh, stream)
+                          : guided_fmt<1>(bits, decode_only, wc, stats, a, sh, stream);
+  if (e != hipSuccess || !stats) return e;
+  return launch(sums_final_kernel, dim3(1), dim3(kThreads), stream, (const double*)a.partials,
+                (int64_t)tile_grid(sh), units * kUnitElems, acc3, accumulate);
 }
 
 hipError_t launch_stats(int64_t n, const uint16_t* xt, const uint16_t* xr, const uint16_t* yt,
@@ -540,8 +760,8 @@ hipError_t launch_stats(int64_t n, const uint16_t* xt, const uint16_t* xr, const
   hipError_t e = launch(stats_partial_kernel, dim3(groups), dim3(kThreads), stream, xt, xr, yt, yr,
                         n, partials);
   if (e != hipSuccess) return e;
-  return launch(stats_final_kernel, dim3(1), dim3(kThreads), stream, (const double*)partials, groups,
-                n, acc3, accumulate);
+  return launch(sums_final_kernel, dim3(1), dim3(kThreads), stream, (const double*)partials,
+                (int64_t)groups, n, acc3, accumulate);
 }
 
 }  // namespace tfp4

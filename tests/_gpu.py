@@ -1,6 +1,7 @@
 """Helpers shared by the GPU parity tests: move bit patterns between numpy
-(oracle side) and torch device tensors (library side), and compare the
-library's outputs with the oracle's element by element."""
+(oracle side) and torch device tensors (library side), run the oracle group
+by group (a grouped call quantizes each group of rows as its own tensor), and
+compare the library's outputs with the oracle's element by element."""
 
 from __future__ import annotations
 
@@ -54,50 +55,118 @@ def assert_same(got, want, what):
     assert d is None, f"{what}: {d}"
 
 
-def fmt_of(name):
-    return tq.NVFP4 if name == "nvfp4" else tq.MXFP4
+def rel_close(got, want, tol=1e-6):
+    return abs(got - want) <= tol * abs(want) or got == want
 
 
-def check_quantize(xb: np.ndarray, rows: int, cols: int, fmt: int, gscale=None, with_y=True):
+# ---------------------------------------------------------------- grouped oracle
+
+def n_groups(rows, group_rows):
+    return rows // group_rows if group_rows else 1
+
+
+def group_slices(n, G, fmt, plane_div):
+    """Element, plane-byte and scale-byte slices of each of G equal groups."""
+    ng = n // G
+    B = ofp4.BLOCK[fmt]
+    return [(slice(g * ng, (g + 1) * ng), slice(g * ng // plane_div, (g + 1) * ng // plane_div),
+             slice(g * ng // B, (g + 1) * ng // B)) for g in range(G)]
+
+
+def oracle_quantize(fmt, xb, rows, group_rows=0, gscale=None):
+    """quantize_rtn of the oracle, applied per group. gscale: one S for every
+    group or an array of per-group S."""
+    G = n_groups(rows, group_rows)
+    parts = []
+    for g, (es, _, _) in enumerate(group_slices(xb.size, G, fmt, 2)):
+        s = None if gscale is None else np.asarray(gscale, np.float32).reshape(-1)[g % np.size(gscale)]
+        parts.append(ofp4.quantize_rtn(fmt, xb[es], s))
+    cat = lambda k: np.concatenate([p[k] for p in parts]) if parts else np.zeros(0)
+    out = {k: cat(k) for k in ("codes", "scales", "y", "k", "sign")}
+    out["gscale"] = np.array([p["gscale"] for p in parts], np.float32) if fmt == ofp4.NVFP4 else None
+    out["amax"] = np.array([p["amax"] for p in parts], np.float32) if fmt == ofp4.NVFP4 else None
+    return out
+
+
+def oracle_encode(fmt, bits, xb, rows, group_rows=0):
+    G = n_groups(rows, group_rows)
+    parts = [ofp4.encode_guidance(fmt, bits, xb[es])
+             for es, _, _ in group_slices(xb.size, G, fmt, 8 if bits == 1 else 2)]
+    out = {k: np.concatenate([p[k] for p in parts]) for k in ("guide", "scales", "y")}
+    out["gscale"] = np.array([p["gscale"] for p in parts], np.float32) if fmt == ofp4.NVFP4 else None
+    return out
+
+
+def oracle_guided(fmt, bits, xt, enc, rows, group_rows=0):
+    """guided_fake_quant of the oracle per group against an oracle record."""
+    G = n_groups(rows, group_rows)
+    div = 8 if bits == 1 else 2
+    ys, cs = [], []
+    for g, (es, ps, ss) in enumerate(group_slices(xt.size, G, fmt, div)):
+        guide = None if bits == 0 else enc["guide"][ps]
+        S = None if enc["gscale"] is None else enc["gscale"][g]
+        o = ofp4.guided_fake_quant(fmt, bits, xt[es], guide, enc["scales"][ss], S)
+        ys.append(o["y"])
+        cs.append(o["codes"])
+    return {"y": np.concatenate(ys), "codes": np.concatenate(cs)}
+
+
+def oracle_decode(fmt, xt, enc, rows, group_rows=0):
+    G = n_groups(rows, group_rows)
+    out = []
+    for g, (es, ps, ss) in enumerate(group_slices(xt.size, G, fmt, 8)):
+        S = None if enc["gscale"] is None else enc["gscale"][g]
+        out.append(ofp4.decode_guidance(fmt, xt[es], enc["guide"][ps], enc["scales"][ss], S))
+    return np.concatenate(out)
+
+
+# ---------------------------------------------------------------- checks
+
+def check_quantize(xb: np.ndarray, rows: int, cols: int, fmt: int, gscale=None, with_y=True,
+                   group_rows=0):
     """quantize_rtn on the GPU vs the oracle; returns the oracle result."""
     x = to_dev(xb, rows, cols)
-    g_in = None if gscale is None else torch.tensor([gscale, 0.0], dtype=torch.float32, device=DEV)
-    q = tq.quantize_rtn(x, fmt, gscale=g_in, with_y=with_y)
-    o = ofp4.quantize_rtn(fmt, xb, gscale)
+    G = n_groups(rows, group_rows)
+    g_in = None
+    if gscale is not None:
+        s = np.broadcast_to(np.asarray(gscale, np.float32).reshape(-1), (G,))
+        g_in = torch.from_numpy(np.stack([s, np.zeros(G, np.float32)], 1).copy()).to(DEV)
+    q = tq.quantize_rtn(x, fmt, gscale=g_in, with_y=with_y, group_rows=group_rows)
+    o = oracle_quantize(fmt, xb, rows, group_rows, gscale)
     assert_same(u8(q.codes), o["codes"], "codes")
     assert_same(u8(q.scales), o["scales"], "scales")
     if with_y:
         assert_same(bits_of(q.y), o["y"], "y")
     if fmt == tq.NVFP4 and gscale is None:
-        g = f32(q.gscale)
-        assert g[0] == o["gscale"], (g, o["gscale"])
-        assert g[1] == o["amax"], (g, o["amax"])
+        g = f32(q.gscale).reshape(G, 2)
+        assert_same(g[:, 0], o["gscale"], "S")
+        assert_same(g[:, 1], o["amax"], "A")
     return o
 
 
-def check_encode(xb, rows, cols, fmt, bits, with_y=True):
+def check_encode(xb, rows, cols, fmt, bits, with_y=True, group_rows=0):
     x = to_dev(xb, rows, cols)
-    g = tq.encode_guidance(x, fmt, bits, with_y=with_y)
-    o = ofp4.encode_guidance(fmt, bits, xb)
+    g = tq.encode_guidance(x, fmt, bits, with_y=with_y, group_rows=group_rows)
+    o = oracle_encode(fmt, bits, xb, rows, group_rows)
     assert_same(u8(g.guide), o["guide"], f"guide bits={bits}")
     assert_same(u8(g.scales), o["scales"], "scales")
     if with_y:
         assert_same(bits_of(g.y), o["y"], "rollout y")
     if fmt == tq.NVFP4:
-        assert f32(g.gscale)[0] == o["gscale"]
+        assert_same(f32(g.gscale).reshape(-1, 2)[:, 0], o["gscale"], "S")
     return g, o
 
 
-def check_guided(xt_bits, xr_bits, rows, cols, fmt, bits, with_codes=True):
+def check_guided(xt_bits, xr_bits, rows, cols, fmt, bits, with_codes=True, group_rows=0):
     """Encode the rollout (bits 1 or 4; bits 0 uses a bits=4 record's scales),
     then guided rounding of the training tensor, GPU vs oracle."""
     rec_bits = 4 if bits == 0 else bits
     xr = to_dev(xr_bits, rows, cols)
     xt = to_dev(xt_bits, rows, cols)
-    g = tq.encode_guidance(xr, fmt, rec_bits, with_y=True)
+    g = tq.encode_guidance(xr, fmt, rec_bits, with_y=True, group_rows=group_rows)
     y, codes = tq.guided_fake_quant(xt, g, bits=bits, with_codes=with_codes)
-    o_enc = ofp4.encode_guidance(fmt, rec_bits, xr_bits)
-    o = ofp4.guided_fake_quant(fmt, bits, xt_bits, o_enc["guide"], o_enc["scales"], o_enc["gscale"])
+    o_enc = oracle_encode(fmt, rec_bits, xr_bits, rows, group_rows)
+    o = oracle_guided(fmt, bits, xt_bits, o_enc, rows, group_rows)
     assert_same(u8(g.guide), o_enc["guide"], "guide")
     assert_same(bits_of(y), o["y"], f"guided y bits={bits}")
     if with_codes:
@@ -105,11 +174,31 @@ def check_guided(xt_bits, xr_bits, rows, cols, fmt, bits, with_codes=True):
     return g, y, o_enc, o
 
 
-def check_decode(xt_bits, xr_bits, rows, cols, fmt):
+def check_guided_stats(xt_bits, xr_bits, rows, cols, fmt, bits, group_rows=0, tol=1e-6):
+    """guided_fake_quant_stats: y and codes bit-exact; {SB, SF, n} within tol
+    of the oracle's sums over (x_t, x_r, guided y, rollout y)."""
+    rec_bits = 4 if bits == 0 else bits
     xr = to_dev(xr_bits, rows, cols)
     xt = to_dev(xt_bits, rows, cols)
-    g = tq.encode_guidance(xr, fmt, 1)
+    g = tq.encode_guidance(xr, fmt, rec_bits, with_y=False, group_rows=group_rows)
+    y, codes, acc = tq.guided_fake_quant_stats(xt, xr, g, bits=bits, with_codes=True)
+    o_enc = oracle_encode(fmt, rec_bits, xr_bits, rows, group_rows)
+    o = oracle_guided(fmt, bits, xt_bits, o_enc, rows, group_rows)
+    assert_same(bits_of(y), o["y"], f"guided y (stats) bits={bits}")
+    assert_same(u8(codes), o["codes"], f"guided codes (stats) bits={bits}")
+    sb, sf, n = ofp4.discrepancy_stats(xt_bits, xr_bits, o["y"], o_enc["y"])
+    a = acc.cpu().numpy()
+    assert a[2] == n, (a, n)
+    assert rel_close(a[0], sb, tol), ("SB", a[0], sb)
+    assert rel_close(a[1], sf, tol), ("SF", a[1], sf)
+    return a, (sb, sf, n)
+
+
+def check_decode(xt_bits, xr_bits, rows, cols, fmt, group_rows=0):
+    xr = to_dev(xr_bits, rows, cols)
+    xt = to_dev(xt_bits, rows, cols)
+    g = tq.encode_guidance(xr, fmt, 1, group_rows=group_rows)
     ref = tq.decode_guidance(xt, g)
-    o_enc = ofp4.encode_guidance(fmt, 1, xr_bits)
-    o = ofp4.decode_guidance(fmt, xt_bits, o_enc["guide"], o_enc["scales"], o_enc["gscale"])
+    o_enc = oracle_encode(fmt, 1, xr_bits, rows, group_rows)
+    o = oracle_decode(fmt, xt_bits, o_enc, rows, group_rows)
     assert_same(u8(ref), o, "reference codes")

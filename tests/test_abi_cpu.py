@@ -51,80 +51,123 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.trace_abi_version() == 1
+    assert lib.trace_abi_version() == 2
     for code, name in [(0, "TRACE_OK"), (-1, "TRACE_EINVAL"), (-2, "TRACE_ESHAPE"),
                        (-3, "TRACE_EALIGN"), (-4, "TRACE_EALIAS"), (-5, "TRACE_EDEVICE"),
                        (-6, "TRACE_ELAUNCH"), (7, "unknown status")]:
         assert _abi.status_str(code) == name
 
 
-def test_workspace_size(lib):
+def test_workspace_sizes(lib):
     assert lib.trace_stats_workspace_bytes(0) == 16
     assert lib.trace_stats_workspace_bytes(8192 * 2048) == 16 * 1024
     assert lib.trace_stats_workspace_bytes(-1) == 0
+    # one kPartMax (1024) array of uint32 partial maxima per global-scale group
+    assert lib.trace_quant_workspace_bytes(0, 4, 32, 0) == 4096
+    assert lib.trace_quant_workspace_bytes(0, 17 * 8192, 2048, 8192) == 17 * 4096
+    assert lib.trace_quant_workspace_bytes(1, 4, 32, 0) == 0            # MXFP4: no amax pass
+    assert lib.trace_quant_workspace_bytes(0, 5, 32, 2) == -1           # 2 does not divide 5
+    assert lib.trace_quant_workspace_bytes(3, 4, 32, 0) == -1           # bad format
+    # two float64 partial sums per workgroup tile of 2048 units (16384 elements)
+    assert lib.trace_guided_stats_workspace_bytes(0, 4, 32, 0) == 16
+    assert lib.trace_guided_stats_workspace_bytes(0, 17 * 8192, 2048, 8192) == 16 * 17 * 1024
+    assert lib.trace_guided_stats_workspace_bytes(0, 4, 24, 0) == -1    # cols % 16
 
 
-# quantize_rtn(fmt, rows, cols, x, gin, codes, scales, gout, y, stream)
+W = 0x600000            # a fake workspace address
+WB = 4096               # quantize workspace bytes for one group
+
+
+# quantize_rtn(fmt, rows, cols, group_rows, x, gin, codes, scales, gout, y, work, work_bytes, stream)
 @pytest.mark.parametrize("args,status", [
-    ((2, 4, 32, A, None, B, C, D, None, None), _abi.EINVAL),          # bad fmt
-    ((0, 4, 24, A, None, B, C, D, None, None), _abi.ESHAPE),          # cols % 16
-    ((1, 4, 48, A, None, B, C, None, None, None), _abi.ESHAPE),       # cols % 32
-    ((0, -1, 32, A, None, B, C, D, None, None), _abi.ESHAPE),         # negative rows
-    ((0, 2 ** 40, 2 ** 20, A, None, B, C, D, None, None), _abi.ESHAPE),  # N overflow guard
-    ((0, 4, 32, A, None, B, C, None, None, None), _abi.EINVAL),       # NVFP4 needs a gscale
-    ((0, 4, 32, A, E, B, C, D, None, None), _abi.EINVAL),             # both gscale_in and out
-    ((1, 4, 32, A, E, B, C, None, None, None), _abi.EINVAL),          # MXFP4 takes no gscale
-    ((0, 4, 32, None, None, B, C, D, None, None), _abi.EINVAL),       # NULL x
-    ((0, 4, 32, A, None, None, C, D, None, None), _abi.EINVAL),       # NULL codes
-    ((0, 4, 32, A + 8, None, B, C, D, None, None), _abi.EALIGN),      # x not 16-B aligned
-    ((0, 4, 32, A, None, B + 2, C, D, None, None), _abi.EALIGN),      # codes not 4-B aligned
-    ((0, 4, 32, A, None, B, C, D, A + 16, None), _abi.EALIAS),        # y overlaps x
-    ((0, 4, 32, A, None, B, B + 8, D, None, None), _abi.EALIAS),      # scales overlap codes
-    ((0, 4, 32, A, None, B, C, A + 4, None, None), _abi.EALIAS),      # gscale_out inside x
+    ((2, 4, 32, 0, A, None, B, C, D, None, W, WB, None), _abi.EINVAL),          # bad fmt
+    ((0, 4, 24, 0, A, None, B, C, D, None, W, WB, None), _abi.ESHAPE),          # cols % 16
+    ((1, 4, 48, 0, A, None, B, C, None, None, None, 0, None), _abi.ESHAPE),     # cols % 32
+    ((0, -1, 32, 0, A, None, B, C, D, None, W, WB, None), _abi.ESHAPE),         # negative rows
+    ((0, 4, 32, -2, A, None, B, C, D, None, W, WB, None), _abi.ESHAPE),         # negative group_rows
+    ((0, 4, 32, 3, A, None, B, C, D, None, W, WB, None), _abi.ESHAPE),          # 3 does not divide 4
+    ((0, 2 ** 40, 2 ** 20, 0, A, None, B, C, D, None, W, WB, None), _abi.ESHAPE),  # N limit
+    ((0, 4, 32, 0, A, None, B, C, None, None, W, WB, None), _abi.EINVAL),       # NVFP4 needs a gscale
+    ((0, 4, 32, 0, A, E, B, C, D, None, W, WB, None), _abi.EINVAL),             # both gscale_in and out
+    ((1, 4, 32, 0, A, E, B, C, None, None, None, 0, None), _abi.EINVAL),        # MXFP4 takes no gscale
+    ((0, 4, 32, 0, None, None, B, C, D, None, W, WB, None), _abi.EINVAL),       # NULL x
+    ((0, 4, 32, 0, A, None, None, C, D, None, W, WB, None), _abi.EINVAL),       # NULL codes
+    ((0, 4, 32, 0, A, None, B, C, D, None, None, WB, None), _abi.EINVAL),       # amax needs work
+    ((0, 4, 32, 0, A, None, B, C, D, None, W, WB - 4, None), _abi.ESHAPE),      # work too small
+    ((0, 8, 32, 4, A, None, B, C, D, None, W, WB, None), _abi.ESHAPE),          # 2 groups need 2*WB
+    ((0, 4, 32, 0, A + 8, None, B, C, D, None, W, WB, None), _abi.EALIGN),      # x not 16-B aligned
+    ((0, 4, 32, 0, A, None, B + 2, C, D, None, W, WB, None), _abi.EALIGN),      # codes not 4-B aligned
+    ((0, 4, 32, 0, A, None, B, C, D, None, W + 4, WB, None), _abi.EALIGN),      # work not 8-B aligned
+    ((0, 4, 32, 0, A, None, B, C, D, A + 16, W, WB, None), _abi.EALIAS),        # y overlaps x
+    ((0, 4, 32, 0, A, None, B, B + 8, D, None, W, WB, None), _abi.EALIAS),      # scales overlap codes
+    ((0, 4, 32, 0, A, None, B, C, A + 4, None, W, WB, None), _abi.EALIAS),      # gscale_out inside x
+    ((0, 4, 32, 0, A, None, B, C, D, None, A, WB, None), _abi.EALIAS),          # work over x
+    ((0, 4, 32, 0, A, None, B, C, D, None, D - 8, WB, None), _abi.EALIAS),      # work over gscale_out
 ])
 def test_quantize_rtn_rejects(lib, args, status):
     assert lib.quantize_rtn(*args) == status
 
 
-# encode_guidance(fmt, bits, rows, cols, x, gin, guide, scales, gout, y, stream)
+# encode_guidance(fmt, bits, rows, cols, group_rows, x, gin, guide, scales, gout, y, work, wb, stream)
 @pytest.mark.parametrize("args,status", [
-    ((0, 2, 4, 32, A, None, B, C, D, None, None), _abi.EINVAL),       # bits 2
-    ((0, 0, 4, 32, A, None, B, C, D, None, None), _abi.EINVAL),       # bits 0
-    ((0, 4, 4, 32, A, None, B + 1, C, D, None, None), _abi.EALIGN),   # code plane alignment
-    ((0, 1, 4, 32, A, None, B, B + 8, D, None, None), _abi.EALIAS),   # bit plane is 16 B here
-    ((0, 1, 4, 32, A, None, A + 100, C, D, None, None), _abi.EALIAS),
+    ((0, 2, 4, 32, 0, A, None, B, C, D, None, W, WB, None), _abi.EINVAL),       # bits 2
+    ((0, 0, 4, 32, 0, A, None, B, C, D, None, W, WB, None), _abi.EINVAL),       # bits 0
+    ((0, 4, 4, 32, 0, A, None, B + 1, C, D, None, W, WB, None), _abi.EALIGN),   # code plane alignment
+    ((0, 1, 4, 32, 0, A, None, B, B + 8, D, None, W, WB, None), _abi.EALIAS),   # bit plane is 16 B here
+    ((0, 1, 4, 32, 0, A, None, A + 100, C, D, None, W, WB, None), _abi.EALIAS),
 ])
 def test_encode_guidance_rejects(lib, args, status):
     assert lib.encode_guidance(*args) == status
 
 
-# decode_guidance(fmt, rows, cols, x, mbits, scales, gscale, ref, stream)
+# decode_guidance(fmt, rows, cols, group_rows, x, mbits, scales, gscale, ref, stream)
 @pytest.mark.parametrize("args,status", [
-    ((0, 4, 32, A, B, C, None, D, None), _abi.EINVAL),               # NVFP4 needs rollout S
-    ((1, 4, 32, A, B, C, E, D, None), _abi.EINVAL),                  # MXFP4 takes none
-    ((0, 4, 32, A, None, C, E, D, None), _abi.EINVAL),               # NULL mbits
-    ((0, 4, 32, A, B, C, E, None, None), _abi.EINVAL),               # NULL output
-    ((0, 4, 32, A, B, C, E, D + 1, None), _abi.EALIGN),
-    ((0, 4, 32, A, B, C, E, B, None), _abi.EALIAS),                  # output on the bits
+    ((0, 4, 32, 0, A, B, C, None, D, None), _abi.EINVAL),               # NVFP4 needs rollout S
+    ((1, 4, 32, 0, A, B, C, E, D, None), _abi.EINVAL),                  # MXFP4 takes none
+    ((0, 4, 32, 0, A, None, C, E, D, None), _abi.EINVAL),               # NULL mbits
+    ((0, 4, 32, 0, A, B, C, E, None, None), _abi.EINVAL),               # NULL output
+    ((0, 4, 32, 3, A, B, C, E, D, None), _abi.ESHAPE),                  # grouping
+    ((0, 4, 32, 0, A, B, C, E, D + 1, None), _abi.EALIGN),
+    ((0, 4, 32, 0, A, B, C, E, B, None), _abi.EALIAS),                  # output on the bits
 ])
 def test_decode_guidance_rejects(lib, args, status):
     assert lib.decode_guidance(*args) == status
 
 
-# guided_fake_quant(fmt, bits, rows, cols, x, guide, scales, gscale, y, codes, stream)
+# guided_fake_quant(fmt, bits, rows, cols, group_rows, x, guide, scales, gscale, y, codes, stream)
 @pytest.mark.parametrize("args,status", [
-    ((0, 3, 4, 32, A, B, C, E, D, None, None), _abi.EINVAL),          # bits 3
-    ((0, 0, 4, 32, A, B, C, E, D, None, None), _abi.EINVAL),          # bits 0 takes no guide
-    ((0, 1, 4, 32, A, None, C, E, D, None, None), _abi.EINVAL),       # bits 1 needs a guide
-    ((0, 1, 4, 32, A, B, C, E, None, None, None), _abi.EINVAL),       # NULL y
-    ((0, 4, 4, 32, A, B + 2, C, E, D, None, None), _abi.EALIGN),      # code guide alignment
-    ((0, 1, 4, 32, A, B, C, E, D + 8, None, None), _abi.EALIGN),      # y alignment
-    ((0, 1, 4, 32, A, B, C, E, A, None, None), _abi.EALIAS),          # in-place y over x
-    ((0, 1, 4, 32, A, B, C, E, D, D + 64, None), _abi.EALIAS),        # codes inside y
-    ((0, 1, 4, 32, A, B, C, E, D, C, None), _abi.EALIAS),             # codes over scales
+    ((0, 3, 4, 32, 0, A, B, C, E, D, None, None), _abi.EINVAL),          # bits 3
+    ((0, 0, 4, 32, 0, A, B, C, E, D, None, None), _abi.EINVAL),          # bits 0 takes no guide
+    ((0, 1, 4, 32, 0, A, None, C, E, D, None, None), _abi.EINVAL),       # bits 1 needs a guide
+    ((0, 1, 4, 32, 0, A, B, C, E, None, None, None), _abi.EINVAL),       # NULL y
+    ((0, 1, 4, 32, 8, A, B, C, E, D, None, None), _abi.ESHAPE),          # 8 does not divide 4
+    ((0, 4, 4, 32, 0, A, B + 2, C, E, D, None, None), _abi.EALIGN),      # code guide alignment
+    ((0, 1, 4, 32, 0, A, B, C, E, D + 8, None, None), _abi.EALIGN),      # y alignment
+    ((0, 1, 4, 32, 0, A, B, C, E, A, None, None), _abi.EALIAS),          # in-place y over x
+    ((0, 1, 4, 32, 0, A, B, C, E, D, D + 64, None), _abi.EALIAS),        # codes inside y
+    ((0, 1, 4, 32, 0, A, B, C, E, D, C, None), _abi.EALIAS),             # codes over scales
+    ((0, 1, 8, 32, 4, A, B, C, E, D, E + 8, None), _abi.EALIAS),         # codes over group 1's S
 ])
 def test_guided_fake_quant_rejects(lib, args, status):
     assert lib.guided_fake_quant(*args) == status
+
+
+F = 0x700000            # a fake x_rollout address
+# guided_fake_quant_stats(fmt, bits, rows, cols, group_rows, x, xr, guide, scales, gscale, y, codes,
+#                         acc3, accumulate, work, work_bytes, stream)
+@pytest.mark.parametrize("args,status", [
+    ((0, 1, 4, 32, 0, A, F, B, C, E, D, None, W, 2, W + 64, 16, None), _abi.EINVAL),     # flag
+    ((0, 1, 4, 32, 0, A, None, B, C, E, D, None, W, 0, W + 64, 16, None), _abi.EINVAL),  # NULL x_r
+    ((0, 1, 4, 32, 0, A, F, B, C, E, D, None, None, 0, W + 64, 16, None), _abi.EINVAL),  # NULL acc
+    ((0, 1, 4, 32, 0, A, F, B, C, E, D, None, W, 0, None, 16, None), _abi.EINVAL),       # NULL work
+    ((0, 1, 4, 32, 0, A, F, B, C, E, D, None, W, 0, W + 64, 8, None), _abi.ESHAPE),      # work small
+    ((0, 1, 4, 32, 0, A, F + 8, B, C, E, D, None, W, 0, W + 64, 16, None), _abi.EALIGN),  # x_r align
+    ((0, 1, 4, 32, 0, A, F, B, C, E, D, None, W + 4, 0, W + 64, 16, None), _abi.EALIGN),  # acc align
+    ((0, 1, 4, 32, 0, A, F, B, C, E, F, None, W, 0, W + 64, 16, None), _abi.EALIAS),     # y over x_r
+    ((0, 1, 4, 32, 0, A, F, B, C, E, D, None, W, 0, W + 8, 16, None), _abi.EALIAS),      # work over acc
+])
+def test_guided_fake_quant_stats_rejects(lib, args, status):
+    assert lib.guided_fake_quant_stats(*args) == status
 
 
 # discrepancy_stats(n, xt, xr, yt, yr, acc, accumulate, work, work_bytes, stream)
@@ -145,8 +188,12 @@ def test_discrepancy_stats_rejects(lib, args, status):
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is visible: valid calls would launch")
 def test_valid_call_without_gpu_is_edevice(lib):
-    assert lib.quantize_rtn(0, 4, 32, A, None, B, C, D, None, None) == _abi.EDEVICE
-    assert lib.guided_fake_quant(1, 1, 4, 32, A, B, C, None, D, None, None) == _abi.EDEVICE
+    assert lib.quantize_rtn(0, 4, 32, 0, A, None, B, C, D, None, W, WB, None) == _abi.EDEVICE
+    assert lib.encode_guidance(0, 1, 4, 32, 0, A, E, B, C, None, None, None, 0, None) == _abi.EDEVICE
+    assert lib.guided_fake_quant(1, 1, 4, 32, 0, A, B, C, None, D, None, None) == _abi.EDEVICE
+    assert lib.guided_fake_quant_stats(0, 1, 4, 32, 0, A, F, B, C, E, D, None, W, 0, W + 64, 16,
+                                       None) == _abi.EDEVICE
+    assert lib.decode_guidance(0, 8, 32, 4, A, B, C, E, D, None) == _abi.EDEVICE
     assert lib.discrepancy_stats(64, A, B, C, D, E, 0, E + 64, 16, None) == _abi.EDEVICE
 
 

@@ -1,0 +1,210 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times (one call per tensor or per streamed layer).
+
+The oracle is too slow for whole tensors, so every block-level output is
+checked on sampled row ranges: the oracle quantizes those rows with the
+group's global scale (computed by the oracle from the whole group's amax),
+which fixes every block exactly. Properties that hold at any size are checked
+on everything: the group scales against the oracle's amax, duplicate routed
+rows giving identical outputs, the fused statistics against the oracle's SB
+and against sums over the library's own (sample-verified) outputs.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import precision_rl_nvfp4_amd as tq
+import synthetic as syn
+from oracle import fp4 as ofp4
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+
+NV, MX = tq.NVFP4, tq.MXFP4
+
+
+def _bits(t):
+    return G.bits_of(t)
+
+
+def _samples(rows, k=3, span=48):
+    """k row ranges spread over the tensor (first, middle, last), `span` rows each."""
+    starts = sorted({0, max(0, rows // 2 - span // 2), max(0, rows - span)})[:k]
+    return [(s, min(rows, s + span)) for s in starts]
+
+
+def _group_S(fmt, xb_group):
+    if fmt != NV:
+        return None
+    return ofp4.nvfp4_global_scale(ofp4.tensor_amax(xb_group))
+
+
+def _check_rows(fmt, bits, xt_b, xr_b, cols, r0, r1, S, enc, y_g=None, codes_g=None, y_r=None,
+                gbits=None):
+    """Oracle on rows [r0, r1) of one group against the library's planes: the
+    oracle encodes the rollout rows with the group scale S (the oracle's own)
+    and guides the training rows with its own record (gbits: guided bits,
+    default the record's)."""
+    B = ofp4.BLOCK[fmt]
+    es = slice(r0 * cols, r1 * cols)
+    o = ofp4.encode_guidance(fmt, bits, xr_b[es], S)
+    div = 8 if bits == 1 else 2
+    G.assert_same(G.u8(enc.guide).reshape(-1)[r0 * cols // div:r1 * cols // div], o["guide"],
+                  f"guide rows {r0}:{r1}")
+    G.assert_same(G.u8(enc.scales).reshape(-1)[r0 * cols // B:r1 * cols // B], o["scales"],
+                  f"scales rows {r0}:{r1}")
+    if y_r is not None:
+        G.assert_same(_bits(y_r)[es], o["y"], f"rollout y rows {r0}:{r1}")
+    if y_g is not None:
+        gb = bits if gbits is None else gbits
+        og = ofp4.guided_fake_quant(fmt, gb, xt_b[es], None if gb == 0 else o["guide"], o["scales"], S)
+        G.assert_same(_bits(y_g)[es], og["y"], f"guided y rows {r0}:{r1}")
+        if codes_g is not None:
+            G.assert_same(G.u8(codes_g).reshape(-1)[r0 * cols // 2:r1 * cols // 2], og["codes"],
+                          f"guided codes rows {r0}:{r1}")
+    return o
+
+
+def test_stream_layer_bench_configuration():
+    """One streamed layer exactly as the benchmark calls it: 17 chunks of
+    [8192, 2048] in one call, one global scale per chunk; encode (bits=1),
+    then guided_fake_quant_stats (bits=1)."""
+    G.say("full size: streamed layer, 17 x [8192, 2048], group_rows=8192")
+    layer, chunks, CH = 20, 17, syn.STREAM_CHUNK
+    dev = G.DEV
+    sigma = syn.stream_sigma(layer, dev)
+    xt = torch.empty((chunks * CH, syn.HIDDEN), dtype=torch.bfloat16, device=dev)
+    xr = torch.empty_like(xt)
+    for c in range(chunks):
+        a, b = syn.stream_pair(layer, c, dev, sigma=sigma)
+        xt[c * CH:(c + 1) * CH].copy_(a)
+        xr[c * CH:(c + 1) * CH].copy_(b)
+    g = tq.encode_guidance(xr, NV, 1, with_y=True, group_rows=CH)
+    y, codes, acc = tq.guided_fake_quant_stats(xt, xr, g, with_codes=True)
+    y_plain, _ = tq.guided_fake_quant(xt, g)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y_plain.view(torch.int16))
+    xt_b, xr_b = _bits(xt), _bits(xr)
+    gs = G.f32(g.gscale).reshape(chunks, 2)
+    n_chunk = CH * syn.HIDDEN
+    sb_total = 0.0
+    S_oracle = []
+    for c in range(chunks):
+        es = slice(c * n_chunk, (c + 1) * n_chunk)
+        A = ofp4.tensor_amax(xr_b[es])
+        S_oracle.append(ofp4.nvfp4_global_scale(A))
+        assert gs[c, 1] == A and gs[c, 0] == S_oracle[c], (c, gs[c])
+        d = (ofp4.bf16_to_f32(xt_b[es]).astype(np.float64) - ofp4.bf16_to_f32(xr_b[es]).astype(np.float64))
+        sb_total += float(np.sum(d * d))
+    for c in (0, 8, 16):
+        for r0, r1 in _samples(CH):
+            rr0, rr1 = c * CH + r0, c * CH + r1
+            _check_rows(NV, 1, xt_b, xr_b, syn.HIDDEN, rr0, rr1, S_oracle[c], g, y_g=y, codes_g=codes,
+                        y_r=g.y)
+    a = acc.cpu().numpy()
+    assert a[2] == xt.numel()
+    assert G.rel_close(a[0], sb_total), (a[0], sb_total)
+    # SF against the sum over the library's own outputs (sample-verified above)
+    ref = tq.discrepancy_stats(xt.view(-1), xr.view(-1), y.view(-1), g.y.view(-1)).cpu().numpy()
+    assert G.rel_close(a[1], ref[1]) and G.rel_close(a[0], ref[0])
+
+
+@pytest.mark.parametrize("bits", [0, 1, 4])
+def test_moe_layer_full_size(bits):
+    """Routed-expert inputs of one MoE layer: 65,536 permuted rows x 2048,
+    NVFP4, one global scale for the tensor."""
+    G.say(f"full size: MoE layer [65536, 2048] bits={bits}")
+    xt, xr, rows_token, _ = syn.moe_pair(20, device=G.DEV)
+    rows, cols = xt.shape
+    rec = 4 if bits == 0 else bits
+    g = tq.encode_guidance(xr, NV, rec, with_y=True)
+    y, codes = tq.guided_fake_quant(xt, g, bits=bits, with_codes=True)
+    q = tq.quantize_rtn(xt, NV)
+    torch.cuda.synchronize()
+    xt_b, xr_b = _bits(xt), _bits(xr)
+    S = _group_S(NV, xr_b)
+    S_t = _group_S(NV, xt_b)
+    assert G.f32(g.gscale)[0] == S
+    assert G.f32(q.gscale)[0] == S_t
+    for r0, r1 in _samples(rows):
+        _check_rows(NV, rec, xt_b, xr_b, cols, r0, r1, S, g, y_g=y, codes_g=codes, y_r=g.y, gbits=bits)
+        es = slice(r0 * cols, r1 * cols)
+        oq = ofp4.quantize_rtn(NV, xt_b[es], S_t)
+        G.assert_same(G.u8(q.codes).reshape(rows, -1)[r0:r1].reshape(-1), oq["codes"], "rtn codes")
+        G.assert_same(_bits(q.y)[es], oq["y"], "rtn y")
+    # duplicate routed rows (one token in 8 experts) give identical outputs
+    order = torch.argsort(rows_token, stable=True)
+    tok_sorted = rows_token[order]
+    first = order[0::8]
+    assert torch.equal(tok_sorted[0::8], tok_sorted[7::8])
+    for k in range(1, 8):
+        other = order[k::8]
+        assert torch.equal(y[first].view(torch.int16), y[other].view(torch.int16))
+        assert torch.equal(g.guide[first], g.guide[other])
+        assert torch.equal(g.scales[first], g.scales[other])
+
+
+@pytest.mark.parametrize("which", [0, 1])
+def test_kv_full_size(which):
+    """FP4 KV cache guidance: K or V of one layer as [65536, 256], NVFP4 block
+    16 along head_dim, full codes (bits=4) and the 1-bit record."""
+    G.say(f"full size: KV [65536, 256] which={which}")
+    xt, xr = syn.kv_pair(20, which, device=G.DEV)
+    rows, cols = xt.shape
+    xt_b, xr_b = _bits(xt), _bits(xr)
+    S = _group_S(NV, xr_b)
+    for bits in (4, 1):
+        g = tq.encode_guidance(xr, NV, bits, with_y=True)
+        y, codes, acc = tq.guided_fake_quant_stats(xt, xr, g, with_codes=True)
+        torch.cuda.synchronize()
+        assert G.f32(g.gscale)[0] == S
+        for r0, r1 in _samples(rows, span=256):
+            _check_rows(NV, bits, xt_b, xr_b, cols, r0, r1, S, g, y_g=y, codes_g=codes, y_r=g.y)
+        ref = tq.discrepancy_stats(xt, xr, y, g.y).cpu().numpy()
+        a = acc.cpu().numpy()
+        assert a[2] == ref[2] and G.rel_close(a[0], ref[0]) and G.rel_close(a[1], ref[1])
+
+
+def test_mxfp4_full_size_with_ties():
+    """MXFP4 W4A4: [65536, 2048] pairs with 0.1% of the elements exactly on
+    E2M1 rounding midpoints."""
+    G.say("full size: MXFP4 [65536, 2048] with midpoint ties")
+    xt, xr = syn.mxfp4_pair(device=G.DEV)
+    rows, cols = xt.shape
+    xt_b, xr_b = _bits(xt), _bits(xr)
+    q = tq.quantize_rtn(xt, MX)
+    torch.cuda.synchronize()
+    for bits in (1, 4):
+        g = tq.encode_guidance(xr, MX, bits, with_y=True)
+        y, codes = tq.guided_fake_quant(xt, g, with_codes=True)
+        torch.cuda.synchronize()
+        for r0, r1 in _samples(rows):
+            _check_rows(MX, bits, xt_b, xr_b, cols, r0, r1, None, g, y_g=y, codes_g=codes, y_r=g.y)
+    for r0, r1 in _samples(rows):
+        es = slice(r0 * cols, r1 * cols)
+        oq = ofp4.quantize_rtn(MX, xt_b[es])
+        G.assert_same(G.u8(q.codes).reshape(rows, -1)[r0:r1].reshape(-1), oq["codes"], "mx rtn codes")
+        G.assert_same(_bits(q.y)[es], oq["y"], "mx rtn y")
+    # the sampled rows hold injected ties (t exactly on an E2M1 midpoint)
+    n_ties = 0
+    for r0, r1 in _samples(rows):
+        es = slice(r0 * cols, r1 * cols)
+        sc = ofp4.mxfp4_block_scales(xt_b[es])
+        _, r = ofp4.mxfp4_block_factors(sc)
+        t = ofp4.normalize(xt_b[es], r, 32)
+        n_ties += int(np.isin(t, np.array(syn.MIDPOINT_MULTIPLES, np.float32)).sum())
+    assert n_ties > 100, n_ties
+
+
+def test_tiny_pair_whole_tensor():
+    """The tiny NVFP4 pair (256 x 2048, seed 0): every call, whole tensor."""
+    G.say("tiny pair, whole tensor")
+    xt, xr = syn.tiny_pair()
+    xt_b, xr_b = syn.bits_u16(xt).reshape(-1), syn.bits_u16(xr).reshape(-1)
+    G.check_quantize(xt_b, 256, 2048, NV)
+    for bits in (1, 4):
+        G.check_encode(xr_b, 256, 2048, NV, bits)
+        G.check_guided_stats(xt_b, xr_b, 256, 2048, NV, bits)
+    G.check_guided(xt_b, xr_b, 256, 2048, NV, 0)
+    G.check_decode(xt_b, xr_b, 256, 2048, NV)

@@ -85,6 +85,13 @@ def test_empty_tensors():
     assert y.numel() == 0 and c.numel() == 0
     acc = tq.discrepancy_stats(x, x, x, x)
     assert acc.cpu().tolist() == [0.0, 0.0, 0.0]
+    gn = tq.encode_guidance(x, NV, 1)
+    y, _, acc = tq.guided_fake_quant_stats(x, x, gn)
+    assert y.numel() == 0 and acc.cpu().tolist() == [0.0, 0.0, 0.0]
+    # zero-width rows in groups: every group gets S = 1, A = 0
+    z = torch.empty(6, 0, dtype=torch.bfloat16, device=G.DEV)
+    q = tq.quantize_rtn(z, NV, group_rows=2)
+    assert G.f32(q.gscale).tolist() == [1.0, 0.0] * 3
 
 
 def _edge_tensor():
@@ -276,7 +283,7 @@ def test_writes_stay_in_bounds():
         ry, yb = guarded(2 * n)
         rg, gs = guarded(8)
         tq.quantize_rtn(t, fmt, codes=codes.view(rows, cols // 2), scales=scales.view(rows, cols // B),
-                        gscale_out=gs.view(torch.float32) if fmt == NV else None,
+                        gscale_out=gs.view(torch.float32).view(1, 2) if fmt == NV else None,
                         y=yb.view(torch.bfloat16).view(rows, cols))
         torch.cuda.synchronize()
         assert intact(rc, n // 2) and intact(rs, n // B) and intact(ry, 2 * n) and intact(rg, 8)
@@ -290,3 +297,100 @@ def test_writes_stay_in_bounds():
         tq.decode_guidance(t, g, ref_codes=refc.view(rows, cols // 2))
         torch.cuda.synchronize()
         assert intact(rb, n // 8) and intact(ry2, 2 * n) and intact(rc2, n // 2) and intact(rr, n // 2)
+
+
+# ---------------------------------------------------------------- grouped calls
+
+def _grouped_pair(G_, group_rows, cols, seed, mx=False):
+    """G_ groups with different magnitudes, so every group has its own S."""
+    xs, rs = [], []
+    for g in range(G_):
+        if mx:
+            xt, xr = syn.mxfp4_pair(rows=group_rows, cols=cols, frac=0.01)
+        else:
+            xt, xr = syn.activation_pair(group_rows, cols, (91, seed, g))
+        k = float(2.0 ** (3 * g - 4)) * (1.0 + 0.37 * g)
+        xs.append((xt.float() * k).to(torch.bfloat16))
+        rs.append((xr.float() * k).to(torch.bfloat16))
+    return syn.bits_u16(torch.cat(xs)).reshape(-1), syn.bits_u16(torch.cat(rs)).reshape(-1)
+
+
+GROUPED = [(3, 37, 2048), (5, 2, 64), (4, 64, 256), (2, 8192 // 32, 2048)]
+
+
+@pytest.mark.parametrize("fmt", [NV, MX])
+@pytest.mark.parametrize("G_,gr,cols", GROUPED)
+def test_grouped_quantize_and_encode(fmt, G_, gr, cols):
+    G.say(f"grouped quantize/encode fmt={fmt} groups={G_} x ({gr},{cols})")
+    xt, xr = _grouped_pair(G_, gr, cols, 1, mx=(fmt == MX))
+    rows = G_ * gr
+    G.check_quantize(xt, rows, cols, fmt, group_rows=gr)
+    for bits in (1, 4):
+        G.check_encode(xr, rows, cols, fmt, bits, group_rows=gr)
+    if fmt == NV:
+        G.check_quantize(xt, rows, cols, fmt, gscale=np.float32(0.75), group_rows=gr)
+
+
+@pytest.mark.parametrize("fmt", [NV, MX])
+@pytest.mark.parametrize("G_,gr,cols", GROUPED)
+def test_grouped_guided_and_decode(fmt, G_, gr, cols):
+    G.say(f"grouped guided/decode fmt={fmt} groups={G_} x ({gr},{cols})")
+    xt, xr = _grouped_pair(G_, gr, cols, 2, mx=(fmt == MX))
+    rows = G_ * gr
+    for bits in (0, 1, 4):
+        G.check_guided(xt, xr, rows, cols, fmt, bits, group_rows=gr)
+    G.check_decode(xt, xr, rows, cols, fmt, group_rows=gr)
+
+
+# ---------------------------------------------------------------- fused statistics
+
+@pytest.mark.parametrize("fmt", [NV, MX])
+@pytest.mark.parametrize("bits", [0, 1, 4])
+@pytest.mark.parametrize("rows,cols", [(1, 32), (37, 2048), (256, 2048), (333, 256)])
+def test_guided_fake_quant_stats(fmt, bits, rows, cols):
+    G.say(f"guided_fake_quant_stats fmt={fmt} bits={bits} shape=({rows},{cols})")
+    xt, xr = _pair(rows, cols, rows + 4, mx=(fmt == MX))
+    G.check_guided_stats(xt, xr, rows, cols, fmt, bits)
+
+
+@pytest.mark.parametrize("fmt", [NV, MX])
+def test_guided_fake_quant_stats_grouped_and_accumulated(fmt):
+    G.say(f"guided_fake_quant_stats grouped fmt={fmt}")
+    xt, xr = _grouped_pair(3, 37, 2048, 3, mx=(fmt == MX))
+    a, _ = G.check_guided_stats(xt, xr, 111, 2048, fmt, 1, group_rows=37)
+    # accumulate=True over two calls equals the sums of the two halves
+    t, r = G.to_dev(xt, 111, 2048), G.to_dev(xr, 111, 2048)
+    g = tq.encode_guidance(r, fmt, 1, group_rows=37)
+    _, _, acc = tq.guided_fake_quant_stats(t, r, g)
+    tq.guided_fake_quant_stats(t, r, g, acc=acc, accumulate=True)
+    b = acc.cpu().numpy()
+    assert b[2] == 2 * a[2] and G.rel_close(b[0], 2 * a[0], 1e-12) and G.rel_close(b[1], 2 * a[1], 1e-12)
+
+
+@pytest.mark.parametrize("fmt", [NV, MX])
+def test_guided_fake_quant_stats_extreme_values(fmt):
+    """Squares that overflow binary32 and differences that underflow it take
+    the exact binary64 path; corner-case scales as in the quantization test."""
+    G.say(f"guided_fake_quant_stats extreme values fmt={fmt}")
+    b = _edge_tensor()
+    b2 = b.copy()
+    b2[::3] ^= 0x0001
+    b2[1::7] ^= 0x8000                       # sign flips: (x_t - x_r)^2 ~ (2x)^2 overflows binary32
+    for bits in (0, 1, 4):
+        G.check_guided_stats(b2, b, 16, 64, fmt, bits)
+    tiny = np.zeros(64, np.uint16)
+    tiny[:32] = np.arange(1, 33)             # bf16 subnormals: squares underflow binary32
+    tiny2 = tiny.copy()
+    tiny2[:32] += 1
+    G.check_guided_stats(tiny2, tiny, 2, 32, fmt, 1)
+
+
+def test_discrepancy_stats_extreme_values():
+    G.say("discrepancy_stats extreme values")
+    big = formats.f32_to_bf16(np.array([3e38, -3e38, 1e20, -1e-30, 0, 5] * 8, np.float32))
+    tiny = np.arange(1, 49, dtype=np.uint16)
+    for a, b in ((big, big[::-1].copy()), (tiny, tiny[::-1].copy())):
+        devs = [torch.from_numpy(v.view(np.int16).copy()).view(torch.bfloat16).to(G.DEV) for v in (a, b, b, a)]
+        acc = tq.discrepancy_stats(*devs).cpu().numpy()
+        sb, sf, n = ofp4.discrepancy_stats(a, b, b, a)
+        assert acc[2] == n and G.rel_close(acc[0], sb) and G.rel_close(acc[1], sf), (acc, sb, sf)
