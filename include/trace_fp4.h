@@ -103,6 +103,17 @@ int trace_abi_version(void);
 /* Static name of a status code ("TRACE_OK", ...); "unknown status" otherwise. */
 const char* trace_status_str(int status);
 
+/* How NVFP4 calls that derive S from the amax schedule their two passes over
+ * the input (amax, then quantize): the groups go in batches, and each launch
+ * quantizes one batch while it reads the next batch for its amax, so a batch
+ * is re-read while it is still in the Infinity Cache. groups_per_batch = 0
+ * (the default) sizes batches to about 96 MiB of input; n > 0 uses n groups
+ * per batch (n >= G: one amax pass over every group, then one quantize pass).
+ * Results are bit-identical for every setting; the knob exists to exercise
+ * and compare schedules. Process-wide. Returns the previous setting, or
+ * TRACE_EINVAL for a negative value. */
+int64_t trace_set_encode_batch(int64_t groups_per_batch);
+
 /* Workspace bytes quantize_rtn / encode_guidance need to derive the global
  * scales from the amax (NVFP4 with gscale_out); 0 for MXFP4. -1 for an
  * invalid shape. */

@@ -22,6 +22,7 @@ _vp = ctypes.c_void_p
 SIGNATURES = {
     "trace_abi_version": (_int, []),
     "trace_status_str": (ctypes.c_char_p, [_int]),
+    "trace_set_encode_batch": (_i64, [_i64]),
     "trace_quant_workspace_bytes": (_i64, [_int, _i64, _i64, _i64]),
     "trace_guided_stats_workspace_bytes": (_i64, [_int, _i64, _i64, _i64]),
     "trace_stats_workspace_bytes": (_i64, [_i64]),

@@ -66,9 +66,9 @@ int shape_of(int fmt, int64_t rows, int64_t cols, int64_t group_rows, CallShape*
   out->n = rows * cols;
   out->sh.groups = group_rows > 0 ? rows / group_rows : 1;
   out->sh.upg = grows * cols / tfp4::kUnitElems;
+  // A launch holds up to G tiles per group plus G amax workgroups per group.
   const int64_t tiles = (out->sh.upg + tfp4::kTileUnits - 1) / tfp4::kTileUnits;
-  if (out->sh.groups > 0 && (tiles > INT32_MAX / out->sh.groups || out->sh.groups > INT32_MAX / tfp4::kPartMax))
-    return TRACE_ESHAPE;
+  if (out->sh.groups > 0 && tiles + tfp4::kPartMax > INT32_MAX / out->sh.groups) return TRACE_ESHAPE;
   return TRACE_OK;
 }
 
@@ -194,6 +194,11 @@ const char* trace_status_str(int status) {
     case TRACE_ELAUNCH: return "TRACE_ELAUNCH";
     default: return "unknown status";
   }
+}
+
+int64_t trace_set_encode_batch(int64_t groups_per_batch) {
+  if (groups_per_batch < 0) return TRACE_EINVAL;
+  return tfp4::set_encode_batch(groups_per_batch);
 }
 
 int64_t trace_quant_workspace_bytes(int fmt, int64_t rows, int64_t cols, int64_t group_rows) {

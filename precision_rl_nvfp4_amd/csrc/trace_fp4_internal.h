@@ -15,9 +15,8 @@ constexpr int kUPT = 8;
 constexpr int64_t kTileUnits = (int64_t)kThreads * kUPT;
 
 // Amax partial maxima kept per global-scale group (one per workgroup of the
-// amax pass), and the workspace slots of the single-pass encoder.
+// amax pass).
 constexpr int kPartMax = 1024;
-constexpr int kSyncSlots = 64;
 
 // Shape of one call: G groups of `upg` units each (units = G * upg), every
 // group with its own FP32 global scale (NVFP4). Blocks never straddle groups.
@@ -50,6 +49,11 @@ hipError_t launch_guided(int fmt, int bits, bool decode_only, const Shape& sh,
                          const uint16_t* x, const uint8_t* guide, const uint8_t* scales,
                          const float* gscale, uint16_t* y, uint8_t* codes, const uint16_t* xr,
                          double* acc3, int accumulate, void* work, hipStream_t stream);
+
+// Groups per batch of NVFP4 encoding with scales from the amax (each launch
+// quantizes one batch and reads the next for its amax); 0 = sized for the
+// Infinity Cache. Returns the previous value.
+int64_t set_encode_batch(int64_t groups);
 
 // Deterministic float64 sums of discrepancy_stats into acc3.
 hipError_t launch_stats(int64_t n, const uint16_t* xt, const uint16_t* xr, const uint16_t* yt,

@@ -35,6 +35,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <tuple>
 
 #include "trace_fp4_internal.h"
@@ -46,6 +47,7 @@ typedef float f2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kFltMax = 3.40282346638528859812e+38f;
+constexpr int kMidGroups = 64;          // first level of the partial-sum reduction
 
 // ------------------------------------------------------------ lane exchange
 
@@ -316,8 +318,19 @@ __device__ __forceinline__ void tile_of(const TileMap& m, int64_t& g, int64_t& t
   tbase = (b - g * m.tiles) * kTileUnits;
 }
 
+struct AmaxArgs {
+  const uint4* x;
+  int64_t upg;
+  int64_t g0;                // first group of this pass
+  int nparts;                // workgroups (partials) per group
+  uint32_t* part;            // [groups][kPartMax]
+};
+
 struct QuantArgs {
   TileMap map;
+  int64_t g0;                // first group quantized by this launch
+  int64_t qblocks;           // workgroups quantizing; the rest run `side`
+  AmaxArgs side;             // amax pass of the next batch of groups
   const uint4* x;
   const float* gin;          // S of group g at gin[2g]
   float* gout;               // {S, A} per group
@@ -340,12 +353,6 @@ struct GuidedArgs {
   double* partials;          // 2 per workgroup (stats)
 };
 
-struct AmaxArgs {
-  const uint4* x;
-  int64_t upg;
-  int nparts;
-  uint32_t* part;
-};
 
 // ------------------------------------------------------------ kernels
 
@@ -357,11 +364,13 @@ __global__ __launch_bounds__(64) void fill_gscale_kernel(float* g, int64_t group
   }
 }
 
-// Partial tensor amax: workgroup w of group g writes the max bf16 magnitude
+// Partial group amax: workgroup w of group g writes the max bf16 magnitude
 // (as binary32 bits) of its strided share of the group to part[g][w].
-__global__ __launch_bounds__(kThreads) void amax_kernel(AmaxArgs a) {
-  const int64_t g = blockIdx.x / a.nparts;
-  const int w = (int)(blockIdx.x - g * a.nparts);
+// `blk` is the workgroup's index within the amax pass.
+__device__ __forceinline__ void amax_body(const AmaxArgs& a, int64_t blk, uint32_t* red) {
+  const int64_t gi = blk / a.nparts;
+  const int w = (int)(blk - gi * a.nparts);
+  const int64_t g = a.g0 + gi;
   const uint4* x = a.x + g * a.upg;
   const int64_t stride = (int64_t)a.nparts * kThreads;
   uint32_t m = 0;
@@ -372,26 +381,43 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(AmaxArgs a) {
   }
   for (; u < a.upg; u += stride) m = max(m, unit_amax_bits(x[u]));
   m = wave_max_u32(m);
-  __shared__ uint32_t wm[kThreads / 64];
-  if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = m;
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t b = wm[0];
-    for (int i = 1; i < kThreads / 64; ++i) b = max(b, wm[i]);
-    a.part[g * kPartMax + w] = b << 16;
-  }
+  if (threadIdx.x == 0) a.part[g * kPartMax + w] = max(max(red[0], red[1]), max(red[2], red[3])) << 16;
+}
+
+__global__ __launch_bounds__(kThreads) void amax_kernel(AmaxArgs a) {
+  __shared__ uint32_t red[kThreads / 64];
+  amax_body(a, blockIdx.x, red);
 }
 
 // RTN quantization (quantize_rtn / encode_guidance).
 // FMT 0 NVFP4 / 1 MXFP4; PLANE 0 codes (u32 per unit) / 1 mantissa bits (u8
 // per unit); WY writes y; SSRC (NVFP4) 0: S = gin[2g]; 1: S from the amax
-// partials, {S, A} stored to gout by the group's first tile.
+// partials, {S, A} stored to gout by the group's first tile. With SSRC 1 the
+// workgroups past `qblocks` run the amax pass of the next batch of groups, so
+// one launch quantizes batch b while reading batch b + 1 for its amax.
 template <int FMT, int PLANE, bool WY, int SSRC>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
   __shared__ float2 lut[128];
   __shared__ uint32_t red[kThreads / 64];
+  if constexpr (SSRC == 1) {
+    if ((int64_t)blockIdx.x >= a.qblocks) {
+      amax_body(a.side, (int64_t)blockIdx.x - a.qblocks, red);
+      return;
+    }
+  }
   int64_t g, tbase;
   tile_of(a.map, g, tbase);
+  g += a.g0;
+  const int64_t gbase = g * a.map.upg;
+  // Issue the tile's loads first; the scale and its factor table follow.
+  uint4 v[kUPT];
+#pragma unroll
+  for (int j = 0; j < kUPT; ++j) {
+    const int64_t u = tbase + j * kThreads + threadIdx.x;
+    v[j] = u < a.map.upg ? a.x[gbase + u] : make_uint4(0u, 0u, 0u, 0u);
+  }
   float S = 1.0f;
   if constexpr (FMT == 0) {
     if constexpr (SSRC == 1) {
@@ -412,13 +438,6 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
     }
     build_factor_lut(lut, S);
     __syncthreads();
-  }
-  const int64_t gbase = g * a.map.upg;
-  uint4 v[kUPT];
-#pragma unroll
-  for (int j = 0; j < kUPT; ++j) {
-    const int64_t u = tbase + j * kThreads + threadIdx.x;
-    v[j] = u < a.map.upg ? a.x[gbase + u] : make_uint4(0u, 0u, 0u, 0u);
   }
 #pragma unroll
   for (int j = 0; j < kUPT; ++j) {
@@ -466,11 +485,8 @@ __global__ __launch_bounds__(kThreads) void guided_kernel(GuidedArgs a) {
   __shared__ float2 lut[128];
   int64_t g, tbase;
   tile_of(a.map, g, tbase);
-  if constexpr (FMT == 0) {
-    build_factor_lut(lut, a.gscale[2 * g]);
-    __syncthreads();
-  }
   const int64_t gbase = g * a.map.upg;
+  // Issue the tile's loads first; the factor table is built while they fly.
   uint4 v[kUPT];
   uint4 vr[STATS ? kUPT : 1];
   uint32_t sbv[kUPT], gv[kUPT];
@@ -485,6 +501,10 @@ __global__ __launch_bounds__(kThreads) void guided_kernel(GuidedArgs a) {
     if constexpr (BITS == 1) gv[j] = ok ? (uint32_t)a.guide[gu] : 0u;
     else if constexpr (BITS == 4) gv[j] = ok ? reinterpret_cast<const uint32_t*>(a.guide)[gu] : 0u;
     else gv[j] = 0u;
+  }
+  if constexpr (FMT == 0) {
+    build_factor_lut(lut, a.gscale[2 * g]);
+    __syncthreads();
   }
   double acc_b = 0.0, acc_f = 0.0;
 #pragma unroll
@@ -533,6 +553,25 @@ __global__ __launch_bounds__(kThreads) void guided_kernel(GuidedArgs a) {
       a.partials[2 * blockIdx.x] = acc_b;
       a.partials[2 * blockIdx.x + 1] = acc_f;
     }
+  }
+}
+
+// First level of the partial-sum reduction: workgroup w sums pairs
+// [w*per, min((w+1)*per, count)) of `in` into out[w] (fixed order).
+__global__ __launch_bounds__(kThreads) void sums_mid_kernel(const double* __restrict__ in,
+                                                            int64_t count, int64_t per,
+                                                            double* __restrict__ out) {
+  const int64_t lo = (int64_t)blockIdx.x * per;
+  const int64_t hi = min(lo + per, count);
+  double sb = 0.0, sf = 0.0;
+  for (int64_t i = lo + threadIdx.x; i < hi; i += kThreads) {
+    sb += in[2 * i];
+    sf += in[2 * i + 1];
+  }
+  group_sum2(sb, sf);
+  if (threadIdx.x == 0) {
+    out[2 * blockIdx.x] = sb;
+    out[2 * blockIdx.x + 1] = sf;
   }
 }
 
@@ -627,6 +666,9 @@ TileMap tile_map(const Shape& sh) {
 
 unsigned tile_grid(const Shape& sh) { return (unsigned)(sh.groups * tile_map(sh).tiles); }
 
+std::atomic<int64_t> g_encode_batch{0};   // groups per batch; 0 = sized for the Infinity Cache
+constexpr int64_t kCacheBatchBytes = (int64_t)96 << 20;
+
 int amax_parts(int64_t upg) {
   int64_t p = (upg + (int64_t)kThreads * 8 - 1) / ((int64_t)kThreads * 8);
   if (p < 1) p = 1;
@@ -635,14 +677,19 @@ int amax_parts(int64_t upg) {
 }
 
 template <int FMT, int PLANE, bool WY, int SSRC>
-hipError_t quant_go(const QuantArgs& a, const Shape& sh, hipStream_t s) {
-  return launch(quantize_kernel<FMT, PLANE, WY, SSRC>, dim3(tile_grid(sh)), dim3(kThreads), s, a);
+hipError_t quant_go(const QuantArgs& a, int64_t blocks, hipStream_t s) {
+  return launch(quantize_kernel<FMT, PLANE, WY, SSRC>, dim3((unsigned)blocks), dim3(kThreads), s, a);
 }
 
+// `blocks`: the launch's workgroups (quantize tiles, then side amax work).
 template <int FMT, int PLANE>
-hipError_t quant_wy(bool wy, int ssrc, const QuantArgs& a, const Shape& sh, hipStream_t s) {
-  if (wy) return ssrc ? quant_go<FMT, PLANE, true, 1>(a, sh, s) : quant_go<FMT, PLANE, true, 0>(a, sh, s);
-  return ssrc ? quant_go<FMT, PLANE, false, 1>(a, sh, s) : quant_go<FMT, PLANE, false, 0>(a, sh, s);
+hipError_t quant_wy(bool wy, int ssrc, const QuantArgs& a, int64_t blocks, hipStream_t s) {
+  if constexpr (FMT == 1) {
+    return wy ? quant_go<1, PLANE, true, 0>(a, blocks, s) : quant_go<1, PLANE, false, 0>(a, blocks, s);
+  } else {
+    if (wy) return ssrc ? quant_go<0, PLANE, true, 1>(a, blocks, s) : quant_go<0, PLANE, true, 0>(a, blocks, s);
+    return ssrc ? quant_go<0, PLANE, false, 1>(a, blocks, s) : quant_go<0, PLANE, false, 0>(a, blocks, s);
+  }
 }
 
 template <int FMT, int BITS, bool DECODE, bool WCODES, bool STATS>
@@ -676,7 +723,7 @@ int64_t quant_work_bytes(const Shape& sh) {
 }
 
 int64_t guided_stats_work_bytes(const Shape& sh) {
-  return 2 * (int64_t)sizeof(double) * (int64_t)tile_grid(sh);
+  return 2 * (int64_t)sizeof(double) * ((int64_t)tile_grid(sh) + kMidGroups);
 }
 
 int64_t stats_groups(int64_t n) {
@@ -706,22 +753,47 @@ hipError_t launch_quantize(int fmt, int plane_mode, const Shape& sh, const uint1
   a.plane = plane;
   a.scales = scales;
   a.y = reinterpret_cast<uint4*>(y);
-  int ssrc = 0;
-  if (fmt == 0 && gout != nullptr) {
-    ssrc = 1;
-    AmaxArgs m;
-    m.x = a.x;
-    m.upg = sh.upg;
-    m.nparts = amax_parts(sh.upg);
-    m.part = static_cast<uint32_t*>(work);
-    hipError_t e = launch(amax_kernel, dim3((unsigned)(sh.groups * m.nparts)), dim3(kThreads), stream, m);
-    if (e != hipSuccess) return e;
-    a.part = m.part;
-    a.nparts = m.nparts;
-  }
   const bool wy = y != nullptr;
-  if (fmt == 0) return plane_mode == 0 ? quant_wy<0, 0>(wy, ssrc, a, sh, stream) : quant_wy<0, 1>(wy, ssrc, a, sh, stream);
-  return plane_mode == 0 ? quant_wy<1, 0>(wy, 0, a, sh, stream) : quant_wy<1, 1>(wy, 0, a, sh, stream);
+  if (fmt == 1 || gout == nullptr) {
+    a.qblocks = (int64_t)tile_grid(sh);
+    if (fmt == 0) return plane_mode == 0 ? quant_wy<0, 0>(wy, 0, a, a.qblocks, stream)
+                                         : quant_wy<0, 1>(wy, 0, a, a.qblocks, stream);
+    return plane_mode == 0 ? quant_wy<1, 0>(wy, 0, a, a.qblocks, stream)
+                           : quant_wy<1, 1>(wy, 0, a, a.qblocks, stream);
+  }
+  // NVFP4 with S from the amax: the input is read twice (amax, then
+  // quantize). Groups go in batches of about kCacheBatchBytes of input, and
+  // the launch that quantizes batch b also runs the amax pass of batch b + 1,
+  // so each batch is re-read one launch after its first read, while it still
+  // sits in the 256 MB Infinity Cache. A caller-set batch size overrides the
+  // automatic one (trace_set_encode_batch).
+  AmaxArgs m{};
+  m.x = a.x;
+  m.upg = sh.upg;
+  m.nparts = amax_parts(sh.upg);
+  m.part = static_cast<uint32_t*>(work);
+  a.part = m.part;
+  a.nparts = m.nparts;
+  const int64_t gbytes = sh.upg * (int64_t)sizeof(uint4);
+  int64_t bg = g_encode_batch.load(std::memory_order_relaxed);
+  if (bg == 0) bg = kCacheBatchBytes / (gbytes > 0 ? gbytes : 1);
+  if (bg < 1) bg = 1;
+  if (bg > sh.groups) bg = sh.groups;
+  m.g0 = 0;
+  hipError_t e = launch(amax_kernel, dim3((unsigned)(bg * m.nparts)), dim3(kThreads), stream, m);
+  for (int64_t g0 = 0; e == hipSuccess && g0 < sh.groups; g0 += bg) {
+    const int64_t nq = min(bg, sh.groups - g0);
+    const int64_t rest = sh.groups - g0 - nq;
+    const int64_t na = rest < bg ? rest : bg;
+    a.g0 = g0;
+    a.qblocks = nq * a.map.tiles;
+    a.side = m;
+    a.side.g0 = g0 + nq;
+    const int64_t blocks = a.qblocks + na * m.nparts;
+    e = plane_mode == 0 ? quant_wy<0, 0>(wy, 1, a, blocks, stream)
+                        : quant_wy<0, 1>(wy, 1, a, blocks, stream);
+  }
+  return e;
 }
 
 hipError_t launch_guided(int fmt, int bits, bool decode_only, const Shape& sh, const uint16_t* x,
@@ -749,8 +821,15 @@ hipError_t launch_guided(int fmt, int bits, bool decode_only, const Shape& sh, c
   hipError_t e = fmt == 0 ? guided_fmt<0>(bits, decode_only, wc, stats, a, sh, stream)
                           : guided_fmt<1>(bits, decode_only, wc, stats, a, sh, stream);
   if (e != hipSuccess || !stats) return e;
-  return launch(sums_final_kernel, dim3(1), dim3(kThreads), stream, (const double*)a.partials,
-                (int64_t)tile_grid(sh), units * kUnitElems, acc3, accumulate);
+  // Per-tile pairs -> kMidGroups pairs -> acc3, each level in a fixed order.
+  const int64_t tiles = tile_grid(sh);
+  const int64_t per = (tiles + kMidGroups - 1) / kMidGroups;
+  double* mid = a.partials + 2 * tiles;
+  e = launch(sums_mid_kernel, dim3(kMidGroups), dim3(kThreads), stream, (const double*)a.partials,
+             tiles, per, mid);
+  if (e != hipSuccess) return e;
+  return launch(sums_final_kernel, dim3(1), dim3(kThreads), stream, (const double*)mid,
+                (int64_t)kMidGroups, units * kUnitElems, acc3, accumulate);
 }
 
 hipError_t launch_stats(int64_t n, const uint16_t* xt, const uint16_t* xr, const uint16_t* yt,
@@ -764,4 +843,8 @@ hipError_t launch_stats(int64_t n, const uint16_t* xt, const uint16_t* xr, const
                 (int64_t)groups, n, acc3, accumulate);
 }
 
+}  // namespace tfp4
+
+namespace tfp4 {
+int64_t set_encode_batch(int64_t groups) { return g_encode_batch.exchange(groups); }
 }  // namespace tfp4

@@ -58,6 +58,13 @@ def test_version_and_status_strings(lib):
         assert _abi.status_str(code) == name
 
 
+def test_encode_batch_setting(lib):
+    assert lib.trace_set_encode_batch(3) == 0
+    assert lib.trace_set_encode_batch(0) == 3
+    assert lib.trace_set_encode_batch(-1) == _abi.EINVAL
+    assert lib.trace_set_encode_batch(0) == 0
+
+
 def test_workspace_sizes(lib):
     assert lib.trace_stats_workspace_bytes(0) == 16
     assert lib.trace_stats_workspace_bytes(8192 * 2048) == 16 * 1024
@@ -68,9 +75,10 @@ def test_workspace_sizes(lib):
     assert lib.trace_quant_workspace_bytes(1, 4, 32, 0) == 0            # MXFP4: no amax pass
     assert lib.trace_quant_workspace_bytes(0, 5, 32, 2) == -1           # 2 does not divide 5
     assert lib.trace_quant_workspace_bytes(3, 4, 32, 0) == -1           # bad format
-    # two float64 partial sums per workgroup tile of 2048 units (16384 elements)
-    assert lib.trace_guided_stats_workspace_bytes(0, 4, 32, 0) == 16
-    assert lib.trace_guided_stats_workspace_bytes(0, 17 * 8192, 2048, 8192) == 16 * 17 * 1024
+    # two float64 partial sums per workgroup tile of 2048 units (16384 elements),
+    # plus 64 pairs for the first level of the reduction
+    assert lib.trace_guided_stats_workspace_bytes(0, 4, 32, 0) == 16 * (1 + 64)
+    assert lib.trace_guided_stats_workspace_bytes(0, 17 * 8192, 2048, 8192) == 16 * (17 * 1024 + 64)
     assert lib.trace_guided_stats_workspace_bytes(0, 4, 24, 0) == -1    # cols % 16
 
 
@@ -153,18 +161,19 @@ def test_guided_fake_quant_rejects(lib, args, status):
 
 
 F = 0x700000            # a fake x_rollout address
+SW, SB = W + 4096, 16 * 65   # stats workspace address and bytes for [4, 32]
 # guided_fake_quant_stats(fmt, bits, rows, cols, group_rows, x, xr, guide, scales, gscale, y, codes,
 #                         acc3, accumulate, work, work_bytes, stream)
 @pytest.mark.parametrize("args,status", [
-    ((0, 1, 4, 32, 0, A, F, B, C, E, D, None, W, 2, W + 64, 16, None), _abi.EINVAL),     # flag
-    ((0, 1, 4, 32, 0, A, None, B, C, E, D, None, W, 0, W + 64, 16, None), _abi.EINVAL),  # NULL x_r
-    ((0, 1, 4, 32, 0, A, F, B, C, E, D, None, None, 0, W + 64, 16, None), _abi.EINVAL),  # NULL acc
-    ((0, 1, 4, 32, 0, A, F, B, C, E, D, None, W, 0, None, 16, None), _abi.EINVAL),       # NULL work
-    ((0, 1, 4, 32, 0, A, F, B, C, E, D, None, W, 0, W + 64, 8, None), _abi.ESHAPE),      # work small
-    ((0, 1, 4, 32, 0, A, F + 8, B, C, E, D, None, W, 0, W + 64, 16, None), _abi.EALIGN),  # x_r align
-    ((0, 1, 4, 32, 0, A, F, B, C, E, D, None, W + 4, 0, W + 64, 16, None), _abi.EALIGN),  # acc align
-    ((0, 1, 4, 32, 0, A, F, B, C, E, F, None, W, 0, W + 64, 16, None), _abi.EALIAS),     # y over x_r
-    ((0, 1, 4, 32, 0, A, F, B, C, E, D, None, W, 0, W + 8, 16, None), _abi.EALIAS),      # work over acc
+    ((0, 1, 4, 32, 0, A, F, B, C, E, D, None, W, 2, SW, SB, None), _abi.EINVAL),        # flag
+    ((0, 1, 4, 32, 0, A, None, B, C, E, D, None, W, 0, SW, SB, None), _abi.EINVAL),     # NULL x_r
+    ((0, 1, 4, 32, 0, A, F, B, C, E, D, None, None, 0, SW, SB, None), _abi.EINVAL),     # NULL acc
+    ((0, 1, 4, 32, 0, A, F, B, C, E, D, None, W, 0, None, SB, None), _abi.EINVAL),      # NULL work
+    ((0, 1, 4, 32, 0, A, F, B, C, E, D, None, W, 0, SW, SB - 8, None), _abi.ESHAPE),    # work small
+    ((0, 1, 4, 32, 0, A, F + 8, B, C, E, D, None, W, 0, SW, SB, None), _abi.EALIGN),    # x_r align
+    ((0, 1, 4, 32, 0, A, F, B, C, E, D, None, W + 4, 0, SW, SB, None), _abi.EALIGN),    # acc align
+    ((0, 1, 4, 32, 0, A, F, B, C, E, F, None, W, 0, SW, SB, None), _abi.EALIAS),        # y over x_r
+    ((0, 1, 4, 32, 0, A, F, B, C, E, D, None, W, 0, W + 8, SB, None), _abi.EALIAS),     # work over acc
 ])
 def test_guided_fake_quant_stats_rejects(lib, args, status):
     assert lib.guided_fake_quant_stats(*args) == status
@@ -191,7 +200,7 @@ def test_valid_call_without_gpu_is_edevice(lib):
     assert lib.quantize_rtn(0, 4, 32, 0, A, None, B, C, D, None, W, WB, None) == _abi.EDEVICE
     assert lib.encode_guidance(0, 1, 4, 32, 0, A, E, B, C, None, None, None, 0, None) == _abi.EDEVICE
     assert lib.guided_fake_quant(1, 1, 4, 32, 0, A, B, C, None, D, None, None) == _abi.EDEVICE
-    assert lib.guided_fake_quant_stats(0, 1, 4, 32, 0, A, F, B, C, E, D, None, W, 0, W + 64, 16,
+    assert lib.guided_fake_quant_stats(0, 1, 4, 32, 0, A, F, B, C, E, D, None, W, 0, SW, SB,
                                        None) == _abi.EDEVICE
     assert lib.decode_guidance(0, 8, 32, 4, A, B, C, E, D, None) == _abi.EDEVICE
     assert lib.discrepancy_stats(64, A, B, C, D, E, 0, E + 64, 16, None) == _abi.EDEVICE

@@ -394,3 +394,60 @@ def test_discrepancy_stats_extreme_values():
         acc = tq.discrepancy_stats(*devs).cpu().numpy()
         sb, sf, n = ofp4.discrepancy_stats(a, b, b, a)
         assert acc[2] == n and G.rel_close(acc[0], sb) and G.rel_close(acc[1], sf), (acc, sb, sf)
+
+
+# ---------------------------------------------------------------- encode schedules
+
+@pytest.fixture
+def one_batch():
+    """One amax pass over every group, then one quantize pass."""
+    lib = tq.load()
+    prev = lib.trace_set_encode_batch(1 << 40)
+    yield
+    lib.trace_set_encode_batch(prev)
+
+
+@pytest.mark.parametrize("per_batch", [1, 2, 3, 1 << 40])
+def test_encode_batches_grouped(per_batch):
+    """Batches of 1, 2, 3 and all of 5 groups: every launch quantizes one
+    batch and runs the amax pass of the next."""
+    G.say(f"encode batches of {per_batch} groups, 5 groups x (37, 2048)")
+    lib = tq.load()
+    prev = lib.trace_set_encode_batch(per_batch)
+    try:
+        xt, xr = _grouped_pair(5, 37, 2048, 6)
+        G.check_quantize(xt, 185, 2048, NV, group_rows=37)
+        for bits in (1, 4):
+            G.check_encode(xr, 185, 2048, NV, bits, group_rows=37)
+        G.check_guided_stats(xt, xr, 185, 2048, NV, 1, group_rows=37)
+    finally:
+        lib.trace_set_encode_batch(prev)
+
+
+def test_one_batch_corner_cases(one_batch):
+    G.say("one-batch encode: scale corner cases and enumeration anchors")
+    b = _edge_tensor()
+    G.check_quantize(b, 16, 64, NV)
+    G.check_encode(b, 16, 64, NV, 1)
+    test_enumerate_bf16_block_max()
+
+
+def test_schedules_agree_on_streamed_chunks():
+    """The cache-sized batches and the single batch give identical encodings
+    of 17 streamed chunks."""
+    G.say("cache-sized batches vs one batch on [17 x 8192, 2048]")
+    CH = syn.STREAM_CHUNK
+    xr = torch.cat([syn.stream_pair(21, c, G.DEV)[1] for c in range(17)])
+    lib = tq.load()
+    outs = []
+    for per_batch in (0, 1 << 40):
+        prev = lib.trace_set_encode_batch(per_batch)
+        try:
+            g = tq.encode_guidance(xr, NV, 1, with_y=True, group_rows=CH)
+            q = tq.quantize_rtn(xr, NV, group_rows=CH, with_y=False)
+            torch.cuda.synchronize()
+        finally:
+            lib.trace_set_encode_batch(prev)
+        outs.append([G.u8(g.guide), G.u8(g.scales), G.f32(g.gscale), G.bits_of(g.y), G.u8(q.codes)])
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
