@@ -77,6 +77,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle wall time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the plain guided_fake_quant timing")
+    ap.add_argument("--encode-batch", type=int, default=-1,
+                    help="groups per batch of the two-pass NVFP4 encode (library default if < 0)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -259,6 +261,8 @@ def main():
     from precision_rl_nvfp4_amd import _abi
 
     lib = _abi.load()
+    if args.encode_batch >= 0:
+        lib.trace_set_encode_batch(args.encode_batch)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"bench: generating {args.layers} layers x {args.chunks} chunks of [{CHUNK}, {HIDDEN}] pairs")
@@ -334,6 +338,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "stream_nvfp4_136k_tokens", "layers": w.layers, "chunks": w.chunks,
+                   "encode_batch": args.encode_batch,
                    "chunk_tokens": CHUNK, "hidden": HIDDEN, "format": "nvfp4", "guide_bits": 1,
                    "elements_per_side_per_step": elems_step},
         "roofline": roofline,
