@@ -20,9 +20,11 @@ through the C ABI of libtrace_fp4.so; the binding only passes pointers.
 
 Prints one JSON line. ``roofline`` covers the call with the largest share of
 step time, from HIP events recorded on the launch stream around each phase;
-``kernels`` also reports plain guided_fake_quant (no statistics) timed the same
-way outside the step; ``cpu_baseline`` times the CPU oracle on a bounded
-sample of the same workload in a process pool.
+``kernels`` also reports plain guided_fake_quant (no statistics) and the
+statistics pass with mismatch counts, each timed the same way outside the
+step; ``mismatch`` summarizes those counts (code distances between the
+training and rollout sides, per layer); ``cpu_baseline`` times the CPU oracle
+on a bounded sample of the same workload in a process pool.
 """
 
 from __future__ import annotations
@@ -51,12 +53,14 @@ BPE = {
     "encode_guidance": 2 + 1 / 8 + 1 / 16,                 # x_r in; mantissa bits, scales out
     "guided_fake_quant_stats": 2 + 2 + 1 / 8 + 1 / 16 + 2,  # x_t, x_r, bits, scales in; y_t out
     "guided_fake_quant": 2 + 1 / 8 + 1 / 16 + 2,           # x_t, bits, scales in; y_t out
+    "guided_fake_quant_stats+mismatch": 2 + 2 + 1 / 8 + 1 / 16 + 2,
 }
 # rocprofv3 kernel names of each call's main kernel.
 KERNEL_NAME = {
     "encode_guidance": "quantize_kernel",
     "guided_fake_quant_stats": "guided_kernel",
     "guided_fake_quant": "guided_kernel",
+    "guided_fake_quant_stats+mismatch": "guided_kernel",
 }
 KERNEL_SRC = os.path.join(ROOT, "precision_rl_nvfp4_amd", "csrc", "trace_fp4_kernels.hip")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -77,6 +81,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle wall time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the plain guided_fake_quant timing")
+    ap.add_argument("--no-diag", action="store_true", help="skip the mismatch-diagnostics pass")
     ap.add_argument("--encode-batch", type=int, default=-1,
                     help="groups per batch of the two-pass NVFP4 encode (library default if < 0)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -108,6 +113,7 @@ class Workload:
         self.gscale = torch.empty((layers, chunks, 2), dtype=torch.float32, device=dev)
         self.yt = torch.empty_like(self.xt)
         self.acc = torch.zeros((layers, 3), dtype=torch.float64, device=dev)
+        self.counts = torch.zeros((layers, 32), dtype=torch.int64, device=dev)
 
     def bytes_resident(self):
         ts = [self.xt, self.xr, self.guide, self.scales, self.gscale, self.yt, self.acc]
@@ -117,19 +123,42 @@ class Workload:
 def build_phases(lib, w, stream, qwork, swork):
     """Argument tuples of every ABI call, grouped by phase."""
     qb, sb = qwork.numel() * qwork.element_size(), swork.numel() * swork.element_size()
-    enc, gst, gfq = [], [], []
+    enc, gst, gfq, dia = [], [], [], []
     for i in range(w.layers):
         p = lambda t: t[i].data_ptr()  # noqa: E731
         enc.append((NV, 1, w.rows, HIDDEN, CHUNK, p(w.xr), None, p(w.guide), p(w.scales),
                     p(w.gscale), None, qwork.data_ptr(), qb, stream))
         gst.append((NV, 1, w.rows, HIDDEN, CHUNK, p(w.xt), p(w.xr), p(w.guide), p(w.scales),
-                    p(w.gscale), p(w.yt), None, p(w.acc), 0, swork.data_ptr(), sb, stream))
+                    p(w.gscale), p(w.yt), None, p(w.acc), None, 0, swork.data_ptr(), sb, stream))
         gfq.append((NV, 1, w.rows, HIDDEN, CHUNK, p(w.xt), p(w.guide), p(w.scales), p(w.gscale),
                     p(w.yt), None, stream))
+        dia.append((NV, 1, w.rows, HIDDEN, CHUNK, p(w.xt), p(w.xr), p(w.guide), p(w.scales),
+                    p(w.gscale), p(w.yt), None, p(w.acc), p(w.counts), 0, swork.data_ptr(), sb, stream))
     step = [("encode_guidance", lib.encode_guidance, enc),
             ("guided_fake_quant_stats", lib.guided_fake_quant_stats, gst)]
     extra = [("guided_fake_quant", lib.guided_fake_quant, gfq)]
-    return step, extra
+    diag = [("guided_fake_quant_stats+mismatch", lib.guided_fake_quant_stats, dia)]
+    return step, extra, diag
+
+
+def mismatch_report(counts):
+    """Fig. 6-style summary of the per-layer mismatch counts: how often RTN
+    under the rollout scales misses the rollout code, how many of those misses
+    are one codeword away, how often the guided code still misses, and how
+    often guidance moves the magnitude up or down."""
+    def frac(a, b):
+        return round(a / b, 6) if b else None
+    tot = [sum(c[k] for c in counts) for k in range(32)]
+    n = sum(tot[:15])
+    rtn_mis, g_mis = n - tot[15], n - tot[0]
+    return {"elements": n,
+            "rtn_mismatch_rate": frac(rtn_mis, n),
+            "rtn_adjacent_fraction": frac(tot[16], rtn_mis),
+            "guided_mismatch_rate": frac(g_mis, n),
+            "guided_adjacent_fraction": frac(tot[1], g_mis),
+            "moved_up_per_layer": [c[30] for c in counts],
+            "moved_down_per_layer": [c[31] for c in counts],
+            "rtn_mismatch_rate_per_layer": [frac(sum(c[15:30]) - c[15], sum(c[15:30])) for c in counts]}
 
 
 def run_phases(phases, events=None):
@@ -277,7 +306,7 @@ def main():
         f"{w.bytes_resident() / 2**30:.1f} GiB resident")
 
     stream = torch.cuda.current_stream(dev)
-    step, extra = build_phases(lib, w, stream.cuda_stream, qwork, swork)
+    step, extra, diag = build_phases(lib, w, stream.cuda_stream, qwork, swork)
 
     for i in range(args.warmup):
         run_phases(step)
@@ -295,6 +324,17 @@ def main():
         kernels["guided_fake_quant"] = kernel_entry("guided_fake_quant", per_x[0], len(extra[0][2]), w.n)
         kernels["guided_fake_quant"]["note"] = "timed outside the step (no statistics)"
         log("bench: plain guided_fake_quant timed")
+
+    mismatch = None
+    if not args.no_diag:
+        # Mismatch diagnostics (outside the timed step): the same fused pass
+        # with the per-layer code-distance histograms.
+        run_phases(diag)
+        _, per_d = timed(torch, diag, max(3, args.steps // 4))
+        kernels[diag[0][0]] = kernel_entry(diag[0][0], per_d[0], len(diag[0][2]), w.n)
+        kernels[diag[0][0]]["note"] = "timed outside the step (statistics + mismatch counts)"
+        mismatch = mismatch_report(w.counts.cpu().tolist())
+        log("bench: mismatch diagnostics done")
 
     elems_step = w.layers * w.n
     ms_step = wall * 1e3 / args.steps
@@ -346,6 +386,7 @@ def main():
         "kernels": kernels,
         "step_GB_s": round(sum(BPE[k] for k, _, _ in step) * elems_step / (ms_step * 1e-3) / 1e9, 1),
         "rel_excess_mse_guided_per_layer": [round(r, 6) for r in rel],
+        "mismatch": mismatch,
     }
     print(json.dumps(out), flush=True)
 

@@ -82,7 +82,10 @@
 extern "C" {
 #endif
 
-#define TRACE_ABI_VERSION 2
+#define TRACE_ABI_VERSION 3
+
+/* Entries of the mismatch diagnostics of guided_fake_quant_stats. */
+#define TRACE_MISMATCH_COUNTS 32
 
 enum trace_fmt { TRACE_FMT_NVFP4 = 0, TRACE_FMT_MXFP4 = 1 };
 
@@ -214,6 +217,19 @@ int guided_fake_quant(int fmt, int bits, int64_t rows, int64_t cols, int64_t gro
  *
  *   x_rollout  in   bf16[N], the rollout input the record was encoded from
  *   acc3, accumulate           as in discrepancy_stats
+ *   counts_opt out  int64[TRACE_MISMATCH_COUNTS] or NULL: mismatch
+ *              diagnostics (paper §3.2 "Key Design", Fig. 6: how far the
+ *              training codes land from the rollout codes, and in which
+ *              direction guidance moves them). With p(c) = the signed grid
+ *              position of code c (magnitude index k with the code's sign,
+ *              -7..7, +-0 both 0), guided codes c_t, rollout RTN codes c_r
+ *              and training RTN codes c_b (both under the rollout scales):
+ *                [0..14]  number of elements with |p(c_t) - p(c_r)| = 0..14
+ *                [15..29] number of elements with |p(c_b) - p(c_r)| = 0..14
+ *                [30]     elements whose guided magnitude index exceeds c_b's
+ *                [31]     elements whose guided magnitude index is below c_b's
+ *              Overwritten or, with accumulate = 1, added to (as acc3).
+ *              Exact integer counts. Computing them costs extra time.
  *   work, work_bytes           trace_guided_stats_workspace_bytes(...) bytes
  *   other arguments            as in guided_fake_quant
  *
@@ -224,8 +240,8 @@ int guided_fake_quant(int fmt, int bits, int64_t rows, int64_t cols, int64_t gro
 int guided_fake_quant_stats(int fmt, int bits, int64_t rows, int64_t cols, int64_t group_rows,
                             const uint16_t* x_train, const uint16_t* x_rollout,
                             const uint8_t* guide, const uint8_t* scales, const float* gscale,
-                            uint16_t* y, uint8_t* codes_opt, double* acc3, int accumulate,
-                            void* work, int64_t work_bytes, void* stream);
+                            uint16_t* y, uint8_t* codes_opt, double* acc3, int64_t* counts_opt,
+                            int accumulate, void* work, int64_t work_bytes, void* stream);
 
 /*
  * discrepancy_stats — the sums behind the train–rollout discrepancy

@@ -392,6 +392,40 @@ def discrepancy_stats(x_t_bits, x_r_bits, y_t_bits, y_r_bits):
     return sb, sf, float(xt.size)
 
 
+def code_position(codes) -> np.ndarray:
+    """Position of an (unpacked) E2M1 code on the signed grid
+    -6 < -4 < ... < -0.5 < 0 < 0.5 < ... < 6: the magnitude index with the
+    code's sign (+0 and -0 are both 0), so adjacent codewords are one apart."""
+    c = np.asarray(codes, dtype=np.int64)
+    k = c & 7
+    return np.where((c & 8) != 0, -k, k)
+
+
+MISMATCH_BINS = 15          # distances 0..14 on the signed grid
+MISMATCH_COUNTS = 2 * MISMATCH_BINS + 2
+
+
+def mismatch_counts(codes_t, codes_r, codes_b):
+    """Diagnostics of the mismatch between training and rollout codes
+    (§3.2 "Key Design", Fig. 6: over 99% of mismatched values differ by one
+    adjacent codebook entry; corrections toward lower codewords concentrate
+    in deeper layers). Inputs are unpacked codes: the guided training codes,
+    the rollout codes, and the training codes under RTN with the rollout
+    scale (the vanilla baseline under the same candidate set). Returns
+    int64[32]: [0..14] histogram of |p(t) - p(r)|; [15..29] histogram of
+    |p(b) - p(r)|; [30] elements where the guided magnitude exceeds the RTN
+    one; [31] elements where it is lower."""
+    pt, pr, pb = code_position(codes_t), code_position(codes_r), code_position(codes_b)
+    out = np.zeros(MISMATCH_COUNTS, dtype=np.int64)
+    out[:MISMATCH_BINS] = np.bincount(np.abs(pt - pr), minlength=MISMATCH_BINS)[:MISMATCH_BINS]
+    out[MISMATCH_BINS:2 * MISMATCH_BINS] = np.bincount(np.abs(pb - pr), minlength=MISMATCH_BINS)[:MISMATCH_BINS]
+    kt = np.asarray(codes_t, dtype=np.int64) & 7
+    kb = np.asarray(codes_b, dtype=np.int64) & 7
+    out[2 * MISMATCH_BINS] = int(np.count_nonzero(kt > kb))
+    out[2 * MISMATCH_BINS + 1] = int(np.count_nonzero(kt < kb))
+    return out
+
+
 def derived_metrics(sb, sf, n):
     """D_BF16, D_FP4, relative excess and D_act = ||Q_t(X_t) - Q_r(X_r)||_F.
     The relative excess is +inf for SB == 0 < SF and NaN for 0 / 0."""

@@ -27,12 +27,14 @@ from typing import NamedTuple, Optional
 import torch
 
 from . import _abi
-from ._abi import MXFP4, NVFP4, TraceError, load, status_str  # noqa: F401
+from ._abi import MISMATCH_COUNTS, MXFP4, NVFP4, TraceError, load, status_str  # noqa: F401
+
+MISMATCH_BINS = MISMATCH_COUNTS // 2 - 1   # distances 0..14 per histogram
 
 __all__ = ["NVFP4", "MXFP4", "TraceError", "Quantized", "Guidance", "quantize_rtn",
            "encode_guidance", "decode_guidance", "guided_fake_quant", "guided_fake_quant_stats",
            "discrepancy_stats", "stats_workspace", "quant_workspace", "guided_stats_workspace",
-           "derived_metrics", "fmt_id", "BLOCK"]
+           "derived_metrics", "mismatch_summary", "fmt_id", "BLOCK", "MISMATCH_COUNTS"]
 
 BLOCK = {NVFP4: 16, MXFP4: 32}
 
@@ -209,10 +211,13 @@ def guided_fake_quant(x_train: torch.Tensor, g: Guidance, bits: Optional[int] = 
 def guided_fake_quant_stats(x_train: torch.Tensor, x_rollout: torch.Tensor, g: Guidance,
                             bits: Optional[int] = None, with_codes: bool = False,
                             acc: Optional[torch.Tensor] = None, accumulate: bool = False,
-                            y=None, codes=None, work=None):
+                            y=None, codes=None, work=None, mismatch: bool = False,
+                            counts: Optional[torch.Tensor] = None):
     """guided_fake_quant plus {SB, SF, n} against the rollout (whose RTN output
     under the record's scales is recomputed from x_rollout). Returns
-    (y, codes or None, acc float64[3])."""
+    (y, codes or None, acc float64[3]); with mismatch=True (or a counts
+    tensor) also the int64[32] mismatch diagnostics, as a fourth element
+    (layout in mismatch_summary)."""
     b, rows, cols, y, codes, guide = _guided_common(x_train, g, bits, with_codes, y, codes)
     _check_x(x_rollout, "x_rollout")
     if tuple(x_rollout.shape) != (rows, cols):
@@ -221,11 +226,23 @@ def guided_fake_quant_stats(x_train: torch.Tensor, x_rollout: torch.Tensor, g: G
         if accumulate:
             raise ValueError("accumulate=True needs an acc tensor")
         acc = torch.empty(3, dtype=torch.float64, device=x_train.device)
+    want_counts = mismatch or counts is not None
+    if want_counts:
+        if counts is None:
+            if accumulate:
+                raise ValueError("accumulate=True needs a counts tensor")
+            counts = torch.empty(MISMATCH_COUNTS, dtype=torch.int64, device=x_train.device)
+        elif (counts.dtype != torch.int64 or counts.numel() != MISMATCH_COUNTS
+              or not counts.is_contiguous() or counts.device != x_train.device):
+            raise ValueError(f"counts must be a contiguous int64[{MISMATCH_COUNTS}] on x_train's device")
     need = int(load().trace_guided_stats_workspace_bytes(g.fmt, rows, cols, g.group_rows))
     work = _workspace(need, x_train.device, work)
     _abi.call("guided_fake_quant_stats", g.fmt, b, rows, cols, g.group_rows, _ptr(x_train),
               _ptr(x_rollout), _ptr(guide), _ptr(g.scales), _ptr(g.gscale), _ptr(y), _ptr(codes),
-              _ptr(acc), 1 if accumulate else 0, _ptr(work), _nbytes(work), _stream(x_train))
+              _ptr(acc), _ptr(counts) if want_counts else None, 1 if accumulate else 0, _ptr(work),
+              _nbytes(work), _stream(x_train))
+    if want_counts:
+        return y, codes, acc, counts
     return y, codes, acc
 
 
@@ -245,6 +262,27 @@ def discrepancy_stats(x_t, x_r, y_t, y_r, acc: Optional[torch.Tensor] = None,
     _abi.call("discrepancy_stats", n, _ptr(x_t), _ptr(x_r), _ptr(y_t), _ptr(y_r), _ptr(acc),
               1 if accumulate else 0, _ptr(work), _nbytes(work), _stream(x_t))
     return acc
+
+
+def mismatch_summary(counts) -> dict:
+    """Host-side view of guided_fake_quant_stats' mismatch counts (§3.2
+    "Key Design", Fig. 6). counts[0..14]: elements whose guided code is
+    0..14 grid positions from the rollout code; counts[15..29]: the same for
+    RTN under the rollout scales; counts[30] / [31]: guidance moved the
+    magnitude up / down relative to RTN."""
+    c = [int(v) for v in (counts.tolist() if hasattr(counts, "tolist") else counts)]
+    nb = MISMATCH_BINS
+    guided, rtn = c[:nb], c[nb:2 * nb]
+    n = sum(guided)
+    rtn_mis = n - rtn[0]
+    guided_mis = n - guided[0]
+    return {"n": n,
+            "rtn_mismatch": rtn_mis, "rtn_mismatch_rate": rtn_mis / n if n else math.nan,
+            "rtn_adjacent_fraction": rtn[1] / rtn_mis if rtn_mis else math.nan,
+            "guided_mismatch": guided_mis, "guided_mismatch_rate": guided_mis / n if n else math.nan,
+            "guided_adjacent_fraction": guided[1] / guided_mis if guided_mis else math.nan,
+            "moved_up": c[2 * nb], "moved_down": c[2 * nb + 1],
+            "guided_hist": guided, "rtn_hist": rtn}
 
 
 def derived_metrics(acc3) -> dict:

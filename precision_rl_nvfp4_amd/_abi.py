@@ -13,6 +13,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtrace_fp
 
 OK, EINVAL, ESHAPE, EALIGN, EALIAS, EDEVICE, ELAUNCH = 0, -1, -2, -3, -4, -5, -6
 NVFP4, MXFP4 = 0, 1
+ABI_VERSION = 3
+MISMATCH_COUNTS = 32
 
 _i64 = ctypes.c_int64
 _int = ctypes.c_int
@@ -34,10 +36,10 @@ SIGNATURES = {
     "decode_guidance": (_int, [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
     # fmt, bits, rows, cols, group_rows, x_t, guide, scales, gscale, y, codes, stream
     "guided_fake_quant": (_int, [_int, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
-    # fmt, bits, rows, cols, group_rows, x_t, x_r, guide, scales, gscale, y, codes, acc3, accumulate,
-    # work, work_bytes, stream
+    # fmt, bits, rows, cols, group_rows, x_t, x_r, guide, scales, gscale, y, codes, acc3, counts,
+    # accumulate, work, work_bytes, stream
     "guided_fake_quant_stats": (_int, [_int, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                       _vp, _int, _vp, _i64, _vp]),
+                                       _vp, _vp, _int, _vp, _i64, _vp]),
     # n, x_t, x_r, y_t, y_r, acc3, accumulate, work, work_bytes, stream
     "discrepancy_stats": (_int, [_i64, _vp, _vp, _vp, _vp, _vp, _int, _vp, _i64, _vp]),
 }
@@ -64,6 +66,9 @@ def load() -> ctypes.CDLL:
             fn = getattr(lib, name)
             fn.restype = res
             fn.argtypes = args
+        if lib.trace_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {lib.trace_abi_version()}, the binding "
+                               f"expects {ABI_VERSION}: rebuild the library")
         _lib = lib
     return _lib
 

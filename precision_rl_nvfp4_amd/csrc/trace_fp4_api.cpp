@@ -17,6 +17,8 @@
 #include "../../include/trace_fp4.h"
 #include "trace_fp4_internal.h"
 
+static_assert(TRACE_MISMATCH_COUNTS == tfp4::kMismatchCounts, "mismatch count layout");
+
 namespace {
 
 struct Range {
@@ -143,7 +145,8 @@ int check_train(int fmt, int64_t n, const uint16_t* x, const uint8_t* guide, boo
 int run_guided(int fmt, int bits, int64_t rows, int64_t cols, int64_t group_rows,
                const uint16_t* x, const uint16_t* xr, bool stats, const uint8_t* guide,
                const uint8_t* scales, const float* gscale, uint16_t* y, uint8_t* codes,
-               double* acc3, int accumulate, void* work, int64_t work_bytes, void* stream) {
+               double* acc3, int64_t* counts, int accumulate, void* work, int64_t work_bytes,
+               void* stream) {
   if (!valid_fmt(fmt) || (bits != 0 && bits != 1 && bits != 4)) return TRACE_EINVAL;
   if (stats && accumulate != 0 && accumulate != 1) return TRACE_EINVAL;
   CallShape cs;
@@ -162,18 +165,20 @@ int run_guided(int fmt, int bits, int64_t rows, int64_t cols, int64_t group_rows
   }
   if (!aligned(x, 16) || !aligned(xr, 16) || !aligned(y, 16) || !aligned(codes, 4) ||
       !aligned(guide, bits == 4 ? 4 : 1) || !aligned(gscale, 4) || !aligned(acc3, 8) ||
-      (wneed > 0 && !aligned(work, 8)))
+      !aligned(counts, 8) || (wneed > 0 && !aligned(work, 8)))
     return TRACE_EALIGN;
   const int64_t gbytes = bits == 1 ? n / 8 : bits == 4 ? n / 2 : 0;
   const Range ins[] = {{x, 2 * n}, {xr, stats ? 2 * n : 0}, {guide, gbytes},
                        {scales, n / block_of(fmt)}, {gscale, 8 * G}};
   const Range outs[] = {{y, 2 * n}, {codes, n / 2}, {acc3, stats ? 24 : 0},
+                        {counts, stats ? 8 * (int64_t)TRACE_MISMATCH_COUNTS : 0},
                         {wneed > 0 ? work : nullptr, wneed}};
   if (any_alias(outs, ins)) return TRACE_EALIAS;
   st = check_device();
   if (st != TRACE_OK) return st;
   return launched(tfp4::launch_guided(fmt, bits, false, cs.sh, x, guide, scales, gscale, y, codes,
-                                      stats ? xr : nullptr, stats ? acc3 : nullptr, accumulate,
+                                      stats ? xr : nullptr, stats ? acc3 : nullptr,
+                                      stats ? counts : nullptr, accumulate,
                                       wneed > 0 ? work : nullptr, static_cast<hipStream_t>(stream)));
 }
 
@@ -256,7 +261,7 @@ int decode_guidance(int fmt, int64_t rows, int64_t cols, int64_t group_rows,
   st = check_device();
   if (st != TRACE_OK) return st;
   return launched(tfp4::launch_guided(fmt, 1, true, cs.sh, x_train, mbits, scales, gscale, nullptr,
-                                      ref_codes, nullptr, nullptr, 0, nullptr,
+                                      ref_codes, nullptr, nullptr, nullptr, 0, nullptr,
                                       static_cast<hipStream_t>(stream)));
 }
 
@@ -264,16 +269,16 @@ int guided_fake_quant(int fmt, int bits, int64_t rows, int64_t cols, int64_t gro
                       const uint16_t* x_train, const uint8_t* guide, const uint8_t* scales,
                       const float* gscale, uint16_t* y, uint8_t* codes_opt, void* stream) {
   return run_guided(fmt, bits, rows, cols, group_rows, x_train, nullptr, false, guide, scales,
-                    gscale, y, codes_opt, nullptr, 0, nullptr, 0, stream);
+                    gscale, y, codes_opt, nullptr, nullptr, 0, nullptr, 0, stream);
 }
 
 int guided_fake_quant_stats(int fmt, int bits, int64_t rows, int64_t cols, int64_t group_rows,
                             const uint16_t* x_train, const uint16_t* x_rollout,
                             const uint8_t* guide, const uint8_t* scales, const float* gscale,
-                            uint16_t* y, uint8_t* codes_opt, double* acc3, int accumulate,
-                            void* work, int64_t work_bytes, void* stream) {
+                            uint16_t* y, uint8_t* codes_opt, double* acc3, int64_t* counts_opt,
+                            int accumulate, void* work, int64_t work_bytes, void* stream) {
   return run_guided(fmt, bits, rows, cols, group_rows, x_train, x_rollout, true, guide, scales,
-                    gscale, y, codes_opt, acc3, accumulate, work, work_bytes, stream);
+                    gscale, y, codes_opt, acc3, counts_opt, accumulate, work, work_bytes, stream);
 }
 
 int discrepancy_stats(int64_t n, const uint16_t* x_t, const uint16_t* x_r, const uint16_t* y_t,

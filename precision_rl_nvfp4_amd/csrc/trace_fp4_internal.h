@@ -18,6 +18,10 @@ constexpr int64_t kTileUnits = (int64_t)kThreads * kUPT;
 // amax pass).
 constexpr int kPartMax = 1024;
 
+// Mismatch diagnostics of guided_fake_quant_stats: two 15-bin distance
+// histograms and two direction counts.
+constexpr int kMismatchCounts = 32;
+
 // Shape of one call: G groups of `upg` units each (units = G * upg), every
 // group with its own FP32 global scale (NVFP4). Blocks never straddle groups.
 struct Shape {
@@ -44,11 +48,13 @@ hipError_t launch_quantize(int fmt, int plane_mode, const Shape& sh, const uint1
 
 // Guided rounding under the rollout scales (guided_fake_quant), Reconstruct
 // alone (decode_guidance: decode_only, bits 1, writes reference codes), and
-// the fused discrepancy sums (xr and acc3 non-NULL).
+// the fused discrepancy sums (xr and acc3 non-NULL) with, when counts is also
+// non-NULL, the mismatch diagnostics.
 hipError_t launch_guided(int fmt, int bits, bool decode_only, const Shape& sh,
                          const uint16_t* x, const uint8_t* guide, const uint8_t* scales,
                          const float* gscale, uint16_t* y, uint8_t* codes, const uint16_t* xr,
-                         double* acc3, int accumulate, void* work, hipStream_t stream);
+                         double* acc3, int64_t* counts, int accumulate, void* work,
+                         hipStream_t stream);
 
 // Groups per batch of NVFP4 encoding with scales from the amax (each launch
 // quantizes one batch and reads the next for its amax); 0 = sized for the

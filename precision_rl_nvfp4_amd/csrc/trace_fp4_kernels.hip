@@ -48,6 +48,7 @@ typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kFltMax = 3.40282346638528859812e+38f;
 constexpr int kMidGroups = 64;          // first level of the partial-sum reduction
+constexpr int kMismatchBins = 15;       // signed-grid distances 0..14
 
 // ------------------------------------------------------------ lane exchange
 
@@ -169,6 +170,31 @@ __device__ __forceinline__ uint32_t select_codes(const float (&t)[8], uint32_t g
         return L + up - dn;
       }
     }
+  }
+}
+
+// ------------------------------------------------------------ mismatch diagnostics
+
+// Position of a code on the signed grid (-7..7; +-0 both 0).
+__device__ __forceinline__ int code_pos(uint32_t c) {
+  const int k = (int)(c & 7u);
+  return (c & 8u) ? -k : k;
+}
+
+// Adds one unit's 8 elements to the workgroup histograms: distance between
+// the guided and rollout codes (bins 1..14), between the RTN and rollout
+// codes (bins 16..29), and the direction of guided vs RTN magnitudes (30, 31).
+// Distance 0 is not counted here (it is the remainder of the tile).
+__device__ __forceinline__ void mismatch_unit(uint32_t K, uint32_t KR, uint32_t K0, uint32_t* hist) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t kt = (K >> (4 * i)) & 15u, kr = (KR >> (4 * i)) & 15u, kb = (K0 >> (4 * i)) & 15u;
+    const int pr = code_pos(kr);
+    const int d1 = abs(code_pos(kt) - pr), d2 = abs(code_pos(kb) - pr);
+    if (d1) atomicAdd(&hist[d1], 1u);
+    if (d2) atomicAdd(&hist[kMismatchBins + d2], 1u);
+    const uint32_t mt = kt & 7u, mb = kb & 7u;
+    if (mt != mb) atomicAdd(&hist[mt > mb ? 2 * kMismatchBins : 2 * kMismatchBins + 1], 1u);
   }
 }
 
@@ -351,6 +377,7 @@ struct GuidedArgs {
   uint32_t* codes;
   const uint4* xr;           // rollout input (stats)
   double* partials;          // 2 per workgroup (stats)
+  uint32_t* cpart;           // [kMismatchCounts][tiles] mismatch counts (diagnostics)
 };
 
 
@@ -480,11 +507,15 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
 // alone (DECODE: reference codes, no y), and the fused discrepancy sums
 // (STATS: SB = sum (x_t - x_r)^2 over the inputs; SF = sum (y_t - y_r)^2 with
 // y_r the rollout's RTN output under the same scales, recomputed from x_r).
-template <int FMT, int BITS, bool DECODE, bool WCODES, bool STATS>
+template <int FMT, int BITS, bool DECODE, bool WCODES, bool STATS, bool DIAG>
 __global__ __launch_bounds__(kThreads) void guided_kernel(GuidedArgs a) {
   __shared__ float2 lut[128];
+  __shared__ uint32_t hist[DIAG ? kMismatchCounts : 1];
   int64_t g, tbase;
   tile_of(a.map, g, tbase);
+  if constexpr (DIAG) {
+    if (threadIdx.x < kMismatchCounts) hist[threadIdx.x] = 0u;
+  }
   const int64_t gbase = g * a.map.upg;
   // Issue the tile's loads first; the factor table is built while they fly.
   uint4 v[kUPT];
@@ -502,10 +533,8 @@ __global__ __launch_bounds__(kThreads) void guided_kernel(GuidedArgs a) {
     else if constexpr (BITS == 4) gv[j] = ok ? reinterpret_cast<const uint32_t*>(a.guide)[gu] : 0u;
     else gv[j] = 0u;
   }
-  if constexpr (FMT == 0) {
-    build_factor_lut(lut, a.gscale[2 * g]);
-    __syncthreads();
-  }
+  if constexpr (FMT == 0) build_factor_lut(lut, a.gscale[2 * g]);
+  if constexpr (FMT == 0 || DIAG) __syncthreads();
   double acc_b = 0.0, acc_f = 0.0;
 #pragma unroll
   for (int j = 0; j < kUPT; ++j) {
@@ -540,6 +569,10 @@ __global__ __launch_bounds__(kThreads) void guided_kernel(GuidedArgs a) {
         unit_f32(yr, fq);
         acc_f += sq_diff_sum(ft, fq);
       }
+      if constexpr (DIAG) {
+        const uint32_t K0 = BITS == 0 ? K : rtn_codes(t);
+        if (u < a.map.upg && (K != KR || K0 != KR)) mismatch_unit(K, KR, K0, hist);
+      }
     }
     if (u < a.map.upg) {
       const int64_t gu = gbase + u;
@@ -553,6 +586,40 @@ __global__ __launch_bounds__(kThreads) void guided_kernel(GuidedArgs a) {
       a.partials[2 * blockIdx.x] = acc_b;
       a.partials[2 * blockIdx.x + 1] = acc_f;
     }
+  }
+  if constexpr (DIAG) {
+    __syncthreads();
+    if (threadIdx.x < kMismatchCounts) {
+      // Distance 0 (bins 0 and 15) is the rest of the tile's elements.
+      const int64_t valid = min((int64_t)kTileUnits, a.map.upg - tbase) * kUnitElems;
+      const int b = threadIdx.x;
+      uint32_t hv = hist[b];
+      if (b == 0 || b == kMismatchBins) {
+        uint32_t others = 0;
+        for (int i = 1; i < kMismatchBins; ++i) others += hist[b + i];
+        hv = (uint32_t)valid - others;
+      }
+      a.cpart[(int64_t)b * gridDim.x + blockIdx.x] = hv;
+    }
+  }
+}
+
+// Sums the per-tile mismatch counts of bin blockIdx.x into counts (int64).
+__global__ __launch_bounds__(kThreads) void counts_final_kernel(const uint32_t* __restrict__ cpart,
+                                                                int64_t tiles, int64_t* counts,
+                                                                int accumulate) {
+  const uint32_t* p = cpart + (int64_t)blockIdx.x * tiles;
+  unsigned long long s = 0;
+  for (int64_t i = threadIdx.x; i < tiles; i += kThreads) s += p[i];
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+  __shared__ unsigned long long ws[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long t = 0;
+    for (int w = 0; w < kThreads / 64; ++w) t += ws[w];
+    if (accumulate) counts[blockIdx.x] += (int64_t)t;
+    else counts[blockIdx.x] = (int64_t)t;
   }
 }
 
@@ -692,27 +759,31 @@ hipError_t quant_wy(bool wy, int ssrc, const QuantArgs& a, int64_t blocks, hipSt
   }
 }
 
-template <int FMT, int BITS, bool DECODE, bool WCODES, bool STATS>
+template <int FMT, int BITS, bool DECODE, bool WCODES, bool STATS, bool DIAG>
 hipError_t guided_go(const GuidedArgs& a, const Shape& sh, hipStream_t s) {
-  return launch(guided_kernel<FMT, BITS, DECODE, WCODES, STATS>, dim3(tile_grid(sh)), dim3(kThreads), s, a);
+  return launch(guided_kernel<FMT, BITS, DECODE, WCODES, STATS, DIAG>, dim3(tile_grid(sh)),
+                dim3(kThreads), s, a);
 }
 
 template <int FMT, int BITS>
-hipError_t guided_bits(bool wc, bool stats, const GuidedArgs& a, const Shape& sh, hipStream_t s) {
-  if (stats) return wc ? guided_go<FMT, BITS, false, true, true>(a, sh, s)
-                       : guided_go<FMT, BITS, false, false, true>(a, sh, s);
-  return wc ? guided_go<FMT, BITS, false, true, false>(a, sh, s)
-            : guided_go<FMT, BITS, false, false, false>(a, sh, s);
+hipError_t guided_bits(bool wc, bool stats, bool diag, const GuidedArgs& a, const Shape& sh,
+                       hipStream_t s) {
+  if (diag) return wc ? guided_go<FMT, BITS, false, true, true, true>(a, sh, s)
+                      : guided_go<FMT, BITS, false, false, true, true>(a, sh, s);
+  if (stats) return wc ? guided_go<FMT, BITS, false, true, true, false>(a, sh, s)
+                       : guided_go<FMT, BITS, false, false, true, false>(a, sh, s);
+  return wc ? guided_go<FMT, BITS, false, true, false, false>(a, sh, s)
+            : guided_go<FMT, BITS, false, false, false, false>(a, sh, s);
 }
 
 template <int FMT>
-hipError_t guided_fmt(int bits, bool decode, bool wc, bool stats, const GuidedArgs& a,
+hipError_t guided_fmt(int bits, bool decode, bool wc, bool stats, bool diag, const GuidedArgs& a,
                       const Shape& sh, hipStream_t s) {
-  if (decode) return guided_go<FMT, 1, true, true, false>(a, sh, s);
+  if (decode) return guided_go<FMT, 1, true, true, false, false>(a, sh, s);
   switch (bits) {
-    case 0: return guided_bits<FMT, 0>(wc, stats, a, sh, s);
-    case 1: return guided_bits<FMT, 1>(wc, stats, a, sh, s);
-    default: return guided_bits<FMT, 4>(wc, stats, a, sh, s);
+    case 0: return guided_bits<FMT, 0>(wc, stats, diag, a, sh, s);
+    case 1: return guided_bits<FMT, 1>(wc, stats, diag, a, sh, s);
+    default: return guided_bits<FMT, 4>(wc, stats, diag, a, sh, s);
   }
 }
 
@@ -723,7 +794,9 @@ int64_t quant_work_bytes(const Shape& sh) {
 }
 
 int64_t guided_stats_work_bytes(const Shape& sh) {
-  return 2 * (int64_t)sizeof(double) * ((int64_t)tile_grid(sh) + kMidGroups);
+  const int64_t tiles = (int64_t)tile_grid(sh);
+  return 2 * (int64_t)sizeof(double) * (tiles + kMidGroups) +
+         (int64_t)sizeof(uint32_t) * kMismatchCounts * tiles;
 }
 
 int64_t stats_groups(int64_t n) {
@@ -799,13 +872,17 @@ hipError_t launch_quantize(int fmt, int plane_mode, const Shape& sh, const uint1
 hipError_t launch_guided(int fmt, int bits, bool decode_only, const Shape& sh, const uint16_t* x,
                          const uint8_t* guide, const uint8_t* scales, const float* gscale,
                          uint16_t* y, uint8_t* codes, const uint16_t* xr, double* acc3,
-                         int accumulate, void* work, hipStream_t stream) {
+                         int64_t* counts, int accumulate, void* work, hipStream_t stream) {
   const int64_t units = sh.groups * sh.upg;
   const bool stats = acc3 != nullptr;
+  const bool diag = stats && counts != nullptr;
   if (units == 0) {
     if (!stats) return hipSuccess;
-    return launch(sums_final_kernel, dim3(1), dim3(kThreads), stream, (const double*)nullptr,
-                  (int64_t)0, (int64_t)0, acc3, accumulate);
+    hipError_t e = launch(sums_final_kernel, dim3(1), dim3(kThreads), stream, (const double*)nullptr,
+                          (int64_t)0, (int64_t)0, acc3, accumulate);
+    if (e != hipSuccess || !diag) return e;
+    return launch(counts_final_kernel, dim3(kMismatchCounts), dim3(kThreads), stream,
+                  (const uint32_t*)nullptr, (int64_t)0, counts, accumulate);
   }
   GuidedArgs a{};
   a.map = tile_map(sh);
@@ -817,12 +894,18 @@ hipError_t launch_guided(int fmt, int bits, bool decode_only, const Shape& sh, c
   a.codes = reinterpret_cast<uint32_t*>(codes);
   a.xr = reinterpret_cast<const uint4*>(xr);
   a.partials = static_cast<double*>(work);
-  const bool wc = codes != nullptr;
-  hipError_t e = fmt == 0 ? guided_fmt<0>(bits, decode_only, wc, stats, a, sh, stream)
-                          : guided_fmt<1>(bits, decode_only, wc, stats, a, sh, stream);
-  if (e != hipSuccess || !stats) return e;
-  // Per-tile pairs -> kMidGroups pairs -> acc3, each level in a fixed order.
   const int64_t tiles = tile_grid(sh);
+  if (stats) a.cpart = reinterpret_cast<uint32_t*>(a.partials + 2 * (tiles + kMidGroups));
+  const bool wc = codes != nullptr;
+  hipError_t e = fmt == 0 ? guided_fmt<0>(bits, decode_only, wc, stats, diag, a, sh, stream)
+                          : guided_fmt<1>(bits, decode_only, wc, stats, diag, a, sh, stream);
+  if (e != hipSuccess || !stats) return e;
+  if (diag) {
+    e = launch(counts_final_kernel, dim3(kMismatchCounts), dim3(kThreads), stream,
+               (const uint32_t*)a.cpart, tiles, counts, accumulate);
+    if (e != hipSuccess) return e;
+  }
+  // Per-tile pairs -> kMidGroups pairs -> acc3, each level in a fixed order.
   const int64_t per = (tiles + kMidGroups - 1) / kMidGroups;
   double* mid = a.partials + 2 * tiles;
   e = launch(sums_mid_kernel, dim3(kMidGroups), dim3(kThreads), stream, (const double*)a.partials,

@@ -174,23 +174,74 @@ def check_guided(xt_bits, xr_bits, rows, cols, fmt, bits, with_codes=True, group
     return g, y, o_enc, o
 
 
+def unpack_codes(packed: np.ndarray) -> np.ndarray:
+    """uint8[N/2] code plane -> uint8[N] codes (element 2i in the low nibble)."""
+    p = np.asarray(packed, np.uint8).reshape(-1)
+    out = np.empty(2 * p.size, np.uint8)
+    out[0::2] = p & 15
+    out[1::2] = p >> 4
+    return out
+
+
+def oracle_mismatch(fmt, bits, xt_bits, xr_bits, rows, group_rows, o_guided):
+    """The oracle's mismatch counts for a guided result: rollout codes from a
+    full-code (bits=4) record of the rollout, RTN codes of the training input
+    under the same rollout scales (guided with bits=0)."""
+    enc4 = oracle_encode(fmt, 4, xr_bits, rows, group_rows)
+    rtn = o_guided if bits == 0 else oracle_guided(fmt, 0, xt_bits, enc4, rows, group_rows)
+    return ofp4.mismatch_counts(unpack_codes(o_guided["codes"]), unpack_codes(enc4["guide"]),
+                                unpack_codes(rtn["codes"]))
+
+
+def torch_mismatch_counts(ct: torch.Tensor, cr: torch.Tensor, cb: torch.Tensor) -> np.ndarray:
+    """The mismatch counts from three packed code planes with plain torch
+    ops (for full-size tensors whose planes are sample-checked against the
+    oracle): the same definition as the oracle's, chunk by chunk."""
+    def pos(p):
+        c = torch.stack([p & 15, p >> 4], -1).reshape(-1).to(torch.int16)
+        k = c & 7
+        return torch.where((c & 8) != 0, -k, k), k
+    out = torch.zeros(ofp4.MISMATCH_COUNTS, dtype=torch.int64, device=ct.device)
+    nb = ofp4.MISMATCH_BINS
+    a, b, c = ct.reshape(-1), cr.reshape(-1), cb.reshape(-1)
+    step = 1 << 26
+    for s0 in range(0, a.numel(), step):
+        pt, kt = pos(a[s0:s0 + step])
+        pr, _ = pos(b[s0:s0 + step])
+        pb, kb = pos(c[s0:s0 + step])
+        out[:nb] += torch.bincount((pt - pr).abs().long(), minlength=nb)[:nb]
+        out[nb:2 * nb] += torch.bincount((pb - pr).abs().long(), minlength=nb)[:nb]
+        out[2 * nb] += (kt > kb).sum()
+        out[2 * nb + 1] += (kt < kb).sum()
+    return out.cpu().numpy()
+
+
 def check_guided_stats(xt_bits, xr_bits, rows, cols, fmt, bits, group_rows=0, tol=1e-6):
     """guided_fake_quant_stats: y and codes bit-exact; {SB, SF, n} within tol
-    of the oracle's sums over (x_t, x_r, guided y, rollout y)."""
+    of the oracle's sums over (x_t, x_r, guided y, rollout y); the mismatch
+    counts exactly the oracle's; a call without counts gives the same y, codes
+    and sums bit for bit."""
     rec_bits = 4 if bits == 0 else bits
     xr = to_dev(xr_bits, rows, cols)
     xt = to_dev(xt_bits, rows, cols)
     g = tq.encode_guidance(xr, fmt, rec_bits, with_y=False, group_rows=group_rows)
-    y, codes, acc = tq.guided_fake_quant_stats(xt, xr, g, bits=bits, with_codes=True)
+    y, codes, acc, counts = tq.guided_fake_quant_stats(xt, xr, g, bits=bits, with_codes=True,
+                                                       mismatch=True)
+    y2, codes2, acc2 = tq.guided_fake_quant_stats(xt, xr, g, bits=bits, with_codes=True)
     o_enc = oracle_encode(fmt, rec_bits, xr_bits, rows, group_rows)
     o = oracle_guided(fmt, bits, xt_bits, o_enc, rows, group_rows)
     assert_same(bits_of(y), o["y"], f"guided y (stats) bits={bits}")
     assert_same(u8(codes), o["codes"], f"guided codes (stats) bits={bits}")
+    assert_same(bits_of(y2), o["y"], f"guided y (stats, no counts) bits={bits}")
+    assert_same(u8(codes2), o["codes"], f"guided codes (stats, no counts) bits={bits}")
     sb, sf, n = ofp4.discrepancy_stats(xt_bits, xr_bits, o["y"], o_enc["y"])
     a = acc.cpu().numpy()
+    assert np.array_equal(a, acc2.cpu().numpy()), (a, acc2)
     assert a[2] == n, (a, n)
     assert rel_close(a[0], sb, tol), ("SB", a[0], sb)
     assert rel_close(a[1], sf, tol), ("SF", a[1], sf)
+    want = oracle_mismatch(fmt, bits, xt_bits, xr_bits, rows, group_rows, o)
+    assert_same(counts.cpu().numpy(), want, f"mismatch counts bits={bits}")
     return a, (sb, sf, n)
 
 

@@ -51,7 +51,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.trace_abi_version() == 2
+    assert lib.trace_abi_version() == _abi.ABI_VERSION == 3
     for code, name in [(0, "TRACE_OK"), (-1, "TRACE_EINVAL"), (-2, "TRACE_ESHAPE"),
                        (-3, "TRACE_EALIGN"), (-4, "TRACE_EALIAS"), (-5, "TRACE_EDEVICE"),
                        (-6, "TRACE_ELAUNCH"), (7, "unknown status")]:
@@ -77,8 +77,10 @@ def test_workspace_sizes(lib):
     assert lib.trace_quant_workspace_bytes(3, 4, 32, 0) == -1           # bad format
     # two float64 partial sums per workgroup tile of 2048 units (16384 elements),
     # plus 64 pairs for the first level of the reduction
-    assert lib.trace_guided_stats_workspace_bytes(0, 4, 32, 0) == 16 * (1 + 64)
-    assert lib.trace_guided_stats_workspace_bytes(0, 17 * 8192, 2048, 8192) == 16 * (17 * 1024 + 64)
+    # 16 bytes of sums per tile + 64 second-level pairs, 32 uint32 counts per tile
+    assert lib.trace_guided_stats_workspace_bytes(0, 4, 32, 0) == 16 * (1 + 64) + 128
+    assert lib.trace_guided_stats_workspace_bytes(0, 17 * 8192, 2048, 8192) == \
+        16 * (17 * 1024 + 64) + 128 * 17 * 1024
     assert lib.trace_guided_stats_workspace_bytes(0, 4, 24, 0) == -1    # cols % 16
 
 
@@ -161,19 +163,24 @@ def test_guided_fake_quant_rejects(lib, args, status):
 
 
 F = 0x700000            # a fake x_rollout address
-SW, SB = W + 4096, 16 * 65   # stats workspace address and bytes for [4, 32]
+K = 0x780000            # a fake counts address
+SW, SB = W + 4096, 16 * 65 + 4 * 32   # stats workspace address and bytes for [4, 32]
 # guided_fake_quant_stats(fmt, bits, rows, cols, group_rows, x, xr, guide, scales, gscale, y, codes,
-#                         acc3, accumulate, work, work_bytes, stream)
+#                         acc3, counts, accumulate, work, work_bytes, stream)
 @pytest.mark.parametrize("args,status", [
-    ((0, 1, 4, 32, 0, A, F, B, C, E, D, None, W, 2, SW, SB, None), _abi.EINVAL),        # flag
-    ((0, 1, 4, 32, 0, A, None, B, C, E, D, None, W, 0, SW, SB, None), _abi.EINVAL),     # NULL x_r
-    ((0, 1, 4, 32, 0, A, F, B, C, E, D, None, None, 0, SW, SB, None), _abi.EINVAL),     # NULL acc
-    ((0, 1, 4, 32, 0, A, F, B, C, E, D, None, W, 0, None, SB, None), _abi.EINVAL),      # NULL work
-    ((0, 1, 4, 32, 0, A, F, B, C, E, D, None, W, 0, SW, SB - 8, None), _abi.ESHAPE),    # work small
-    ((0, 1, 4, 32, 0, A, F + 8, B, C, E, D, None, W, 0, SW, SB, None), _abi.EALIGN),    # x_r align
-    ((0, 1, 4, 32, 0, A, F, B, C, E, D, None, W + 4, 0, SW, SB, None), _abi.EALIGN),    # acc align
-    ((0, 1, 4, 32, 0, A, F, B, C, E, F, None, W, 0, SW, SB, None), _abi.EALIAS),        # y over x_r
-    ((0, 1, 4, 32, 0, A, F, B, C, E, D, None, W, 0, W + 8, SB, None), _abi.EALIAS),     # work over acc
+    ((0, 1, 4, 32, 0, A, F, B, C, E, D, None, W, None, 2, SW, SB, None), _abi.EINVAL),     # flag
+    ((0, 1, 4, 32, 0, A, None, B, C, E, D, None, W, None, 0, SW, SB, None), _abi.EINVAL),  # NULL x_r
+    ((0, 1, 4, 32, 0, A, F, B, C, E, D, None, None, K, 0, SW, SB, None), _abi.EINVAL),     # NULL acc
+    ((0, 1, 4, 32, 0, A, F, B, C, E, D, None, W, None, 0, None, SB, None), _abi.EINVAL),   # NULL work
+    ((0, 1, 4, 32, 0, A, F, B, C, E, D, None, W, None, 0, SW, SB - 8, None), _abi.ESHAPE), # work small
+    ((0, 1, 4, 32, 0, A, F + 8, B, C, E, D, None, W, None, 0, SW, SB, None), _abi.EALIGN), # x_r align
+    ((0, 1, 4, 32, 0, A, F, B, C, E, D, None, W + 4, None, 0, SW, SB, None), _abi.EALIGN), # acc align
+    ((0, 1, 4, 32, 0, A, F, B, C, E, D, None, W, K + 4, 0, SW, SB, None), _abi.EALIGN),    # counts align
+    ((0, 1, 4, 32, 0, A, F, B, C, E, F, None, W, None, 0, SW, SB, None), _abi.EALIAS),     # y over x_r
+    ((0, 1, 4, 32, 0, A, F, B, C, E, D, None, W, None, 0, W + 8, SB, None), _abi.EALIAS),  # work over acc
+    ((0, 1, 4, 32, 0, A, F, B, C, E, D, None, W, W + 16, 0, SW, SB, None), _abi.EALIAS),   # counts over acc
+    ((0, 1, 4, 32, 0, A, F, B, C, E, D, None, W, F + 64, 0, SW, SB, None), _abi.EALIAS),   # counts in x_r
+    ((0, 1, 4, 32, 0, A, F, B, C, E, D, None, W, SW + 256, 0, SW, SB, None), _abi.EALIAS), # counts in work
 ])
 def test_guided_fake_quant_stats_rejects(lib, args, status):
     assert lib.guided_fake_quant_stats(*args) == status
@@ -200,7 +207,9 @@ def test_valid_call_without_gpu_is_edevice(lib):
     assert lib.quantize_rtn(0, 4, 32, 0, A, None, B, C, D, None, W, WB, None) == _abi.EDEVICE
     assert lib.encode_guidance(0, 1, 4, 32, 0, A, E, B, C, None, None, None, 0, None) == _abi.EDEVICE
     assert lib.guided_fake_quant(1, 1, 4, 32, 0, A, B, C, None, D, None, None) == _abi.EDEVICE
-    assert lib.guided_fake_quant_stats(0, 1, 4, 32, 0, A, F, B, C, E, D, None, W, 0, SW, SB,
+    assert lib.guided_fake_quant_stats(0, 1, 4, 32, 0, A, F, B, C, E, D, None, W, None, 0, SW, SB,
+                                       None) == _abi.EDEVICE
+    assert lib.guided_fake_quant_stats(0, 1, 4, 32, 0, A, F, B, C, E, D, None, W, K, 1, SW, SB,
                                        None) == _abi.EDEVICE
     assert lib.decode_guidance(0, 8, 32, 4, A, B, C, E, D, None) == _abi.EDEVICE
     assert lib.discrepancy_stats(64, A, B, C, D, E, 0, E + 64, 16, None) == _abi.EDEVICE

@@ -81,10 +81,18 @@ def test_stream_layer_bench_configuration():
         xt[c * CH:(c + 1) * CH].copy_(a)
         xr[c * CH:(c + 1) * CH].copy_(b)
     g = tq.encode_guidance(xr, NV, 1, with_y=True, group_rows=CH)
-    y, codes, acc = tq.guided_fake_quant_stats(xt, xr, g, with_codes=True)
+    y, codes, acc, counts = tq.guided_fake_quant_stats(xt, xr, g, with_codes=True, mismatch=True)
     y_plain, _ = tq.guided_fake_quant(xt, g)
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int16), y_plain.view(torch.int16))
+    # mismatch counts against plain torch over the code planes (rollout codes
+    # from a full-code record, RTN codes under the rollout scales), which the
+    # row samples below pin to the oracle
+    g4 = tq.encode_guidance(xr, NV, 4, group_rows=CH)
+    y_rtn, codes_rtn = tq.guided_fake_quant(xt, g, bits=0, with_codes=True)
+    want = G.torch_mismatch_counts(codes, g4.guide, codes_rtn)
+    G.assert_same(counts.cpu().numpy(), want, "mismatch counts, streamed layer")
+    assert want[:15].sum() == xt.numel()
     xt_b, xr_b = _bits(xt), _bits(xr)
     gs = G.f32(g.gscale).reshape(chunks, 2)
     n_chunk = CH * syn.HIDDEN
@@ -102,6 +110,9 @@ def test_stream_layer_bench_configuration():
             rr0, rr1 = c * CH + r0, c * CH + r1
             _check_rows(NV, 1, xt_b, xr_b, syn.HIDDEN, rr0, rr1, S_oracle[c], g, y_g=y, codes_g=codes,
                         y_r=g.y)
+            _check_rows(NV, 4, xt_b, xr_b, syn.HIDDEN, rr0, rr1, S_oracle[c], g4)
+            _check_rows(NV, 1, xt_b, xr_b, syn.HIDDEN, rr0, rr1, S_oracle[c], g, y_g=y_rtn,
+                        codes_g=codes_rtn, gbits=0)
     a = acc.cpu().numpy()
     assert a[2] == xt.numel()
     assert G.rel_close(a[0], sb_total), (a[0], sb_total)

@@ -361,10 +361,42 @@ def test_guided_fake_quant_stats_grouped_and_accumulated(fmt):
     # accumulate=True over two calls equals the sums of the two halves
     t, r = G.to_dev(xt, 111, 2048), G.to_dev(xr, 111, 2048)
     g = tq.encode_guidance(r, fmt, 1, group_rows=37)
-    _, _, acc = tq.guided_fake_quant_stats(t, r, g)
-    tq.guided_fake_quant_stats(t, r, g, acc=acc, accumulate=True)
+    _, _, acc, cnt = tq.guided_fake_quant_stats(t, r, g, mismatch=True)
+    one = cnt.clone()
+    tq.guided_fake_quant_stats(t, r, g, acc=acc, accumulate=True, counts=cnt)
     b = acc.cpu().numpy()
     assert b[2] == 2 * a[2] and G.rel_close(b[0], 2 * a[0], 1e-12) and G.rel_close(b[1], 2 * a[1], 1e-12)
+    assert torch.equal(cnt, 2 * one)
+    # counts with accumulate=False overwrite whatever the tensor held
+    cnt.fill_(-12345)
+    tq.guided_fake_quant_stats(t, r, g, counts=cnt)
+    assert torch.equal(cnt, one)
+
+
+@pytest.mark.parametrize("fmt", [NV, MX])
+def test_mismatch_counts_planted(fmt):
+    """Rollout = training with 4000 elements scaled by 1.5, so that both
+    histograms have entries beyond distance 1; each record width against the
+    oracle. With the full-code record (bits=4) the guided code is the bracket
+    end nearer the rollout code, so its total distance never exceeds RTN's."""
+    G.say(f"mismatch counts, planted differences fmt={fmt}")
+    xt, _ = _pair(64, 2048, 11, mx=(fmt == MX))
+    xt = xt.reshape(-1)
+    xr = xt.copy()
+    rng = np.random.default_rng(5)
+    idx = rng.choice(xt.size, 4000, replace=False)
+    f = ofp4.bf16_to_f32(xr[idx]).astype(np.float32) * np.float32(1.5)
+    xr[idx] = formats.f32_to_bf16(f)
+    for bits in (4, 1, 0):
+        G.check_guided_stats(xt, xr, 64, 2048, fmt, bits)
+    t, r = G.to_dev(xt, 64, 2048), G.to_dev(xr, 64, 2048)
+    *_, cnt = tq.guided_fake_quant_stats(t, r, tq.encode_guidance(r, fmt, 4), mismatch=True)
+    c = cnt.cpu().numpy()
+    d = np.arange(tq.MISMATCH_BINS)
+    assert c[:15].sum() == c[15:30].sum() == xt.size
+    assert (c[16:30] > 0).sum() >= 2                      # RTN: distances beyond 1 occur
+    assert (d * c[:15]).sum() <= (d * c[15:30]).sum()
+    assert (d * c[:15]).sum() < (d * c[15:30]).sum() or c[30] + c[31] == 0
 
 
 @pytest.mark.parametrize("fmt", [NV, MX])
