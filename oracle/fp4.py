@@ -191,18 +191,20 @@ def bracket(t):
     return lo.astype(np.uint8), hi.astype(np.uint8)
 
 
-def reconstruct(t, c) -> np.ndarray:
+def reconstruct(t, c, b=1) -> np.ndarray:
     """Compact rollout reference (Reconstruct, Algorithm 1 prose): the E2M1
-    magnitude nearest t whose low code bit equals c (b = 1: the mantissa bit).
-    Ties go to the larger magnitude. Returns the 3-bit index; the caller pairs
-    it with the training sign."""
+    magnitude nearest t whose low b bits of the 3-bit magnitude index equal c
+    (b = 1: the mantissa bit; b = 3: the whole magnitude). Ties go to the
+    larger magnitude. Returns the 3-bit index; the caller pairs it with the
+    training sign."""
     t = np.asarray(t, dtype=_F32).astype(np.float64)
     c = np.asarray(c, dtype=np.int64)
+    mask = (1 << b) - 1
     v = E2M1_F32.astype(np.float64)
     best_k = np.zeros(t.shape, dtype=np.int64)
     best_d = np.full(t.shape, np.inf)
     for k in range(8):                      # ascending, so "<=" keeps the larger on ties
-        ok = (k & 1) == c
+        ok = (k & mask) == c
         dk = np.abs(v[k] - t)
         take = ok & (dk <= best_d)
         best_k = np.where(take, k, best_k)
@@ -281,6 +283,30 @@ def unpack_bits(packed) -> np.ndarray:
     return np.stack([(p >> i) & 1 for i in range(8)], axis=1).reshape(-1).astype(np.uint8)
 
 
+def pack_low_bits(vals, b) -> np.ndarray:
+    """b-bit fields, LSB first, as one bit string: element i occupies bits
+    b*i .. b*i + b - 1 of the little-endian stream (b = 1: pack_bits; b = 2:
+    four elements per byte; b = 3: eight elements per three bytes)."""
+    v = np.asarray(vals, dtype=np.int64).reshape(-1)
+    bitstream = np.zeros(v.size * b, dtype=np.uint8)
+    for j in range(b):
+        bitstream[j::b] = (v >> j) & 1
+    return pack_bits(bitstream)
+
+
+def unpack_low_bits(packed, b, n) -> np.ndarray:
+    bitstream = unpack_bits(packed)[: n * b].astype(np.int64)
+    out = np.zeros(n, dtype=np.int64)
+    for j in range(b):
+        out |= bitstream[j::b] << j
+    return out.astype(np.uint8)
+
+
+def guide_bytes(bits, n) -> int:
+    """Bytes of a guidance plane for n elements: n * bits / 8 (bits 1..4)."""
+    return n * bits // 8
+
+
 # ------------------------------------------------------------------ the five calls
 
 def _scales(fmt, x, gscale_in):
@@ -317,14 +343,16 @@ def encode_guidance(fmt, bits, x_bits, gscale=None):
     "Key Design"; Algorithm 1 prose: packed low-bit rollout codes plus the
     rollout scales). bits=1 keeps the mantissa bit of each code (1 bit per
     element; with the amortized E4M3 scale 1.5 bits per element for NVFP4);
-    bits=4 keeps the full signed code (the full-information record).
+    bits=2 and 3 keep the low 2 or 3 bits of the magnitude index (Algorithm
+    1's parameter b); bits=4 keeps the full signed code (the full-information
+    record).
 
-    Returns dict(guide, scales, gscale, amax, y) with guide = packed bits
-    u8[N/8] (bits=1) or packed codes u8[N/2] (bits=4); y is the rollout's own
-    fake-quantized output."""
+    Returns dict(guide, scales, gscale, amax, y) with guide = the packed low
+    bits u8[N*bits/8] (bits 1..3, pack_low_bits) or the packed codes u8[N/2]
+    (bits=4); y is the rollout's own fake-quantized output."""
     q = quantize_rtn(fmt, x_bits, gscale)
-    if bits == 1:
-        guide = pack_bits(q["k"] & 1)
+    if bits in (1, 2, 3):
+        guide = pack_low_bits(q["k"] & ((1 << bits) - 1), bits)
     elif bits == 4:
         guide = q["codes"]
     else:
@@ -341,21 +369,22 @@ def train_normalized(fmt, x_bits, scales, gscale):
     return normalize(x, r, B), d, _sign(x)
 
 
-def decode_guidance(fmt, x_bits, mbits, scales, gscale=None):
+def decode_guidance(fmt, x_bits, guide, scales, gscale=None, bits=1):
     """Training side, compact record: Reconstruct the reference code of every
-    element from the training value under the rollout scale and the rollout
-    mantissa bit, with the training sign (Algorithm 1 prose). Returns packed
-    reference codes u8[N/2]."""
+    element from the training value under the rollout scale and the rollout's
+    low `bits` magnitude bits, with the training sign (Algorithm 1 prose).
+    Returns packed reference codes u8[N/2]."""
     t, _, sg = train_normalized(fmt, x_bits, scales, gscale)
-    c = unpack_bits(mbits)[: t.size]
-    return pack_codes(codes_of(sg, reconstruct(t, c)))
+    c = unpack_low_bits(guide, bits, t.size)
+    return pack_codes(codes_of(sg, reconstruct(t, c, bits)))
 
 
 def guided_fake_quant(fmt, bits, x_bits, guide, scales, gscale=None):
     """Training side, rollout-guided rounding (§3.1 "Key Design"; Algorithm 1
     prose). Under the rollout scale, bracket t = |x| * r and pick:
     bits=0: RTN (the comparison q_RTN of the local guarantee);
-    bits=1: the candidate nearest the reconstructed reference;
+    bits=1, 2, 3: the candidate nearest the reference reconstructed from the
+    rollout's low `bits` magnitude bits;
     bits=4: the candidate nearest the exact rollout codeword.
     The output keeps the training sign and is dequantized with the rollout
     decode factor. Returns dict(y=bf16 bits[N], codes=packed u8[N/2], k)."""
@@ -365,9 +394,9 @@ def guided_fake_quant(fmt, bits, x_bits, guide, scales, gscale=None):
         k = rtn(t)
     else:
         lo, hi = bracket(t)
-        if bits == 1:
-            c = unpack_bits(guide)[: t.size]
-            k = select_compact(lo, hi, reconstruct(t, c))
+        if bits in (1, 2, 3):
+            c = unpack_low_bits(guide, bits, t.size)
+            k = select_compact(lo, hi, reconstruct(t, c, bits))
         elif bits == 4:
             cr = unpack_codes(guide)[: t.size]
             k = select_full(lo, hi, sg, cr >> 3, cr & 7)

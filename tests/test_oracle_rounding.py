@@ -82,11 +82,11 @@ def test_bracket_invariants():
     assert np.all((k == lo) | (k == hi))
 
 
-def _brute_reconstruct(t, c):
+def _brute_reconstruct(t, c, b=1):
     ft = Fraction(float(t))
     best = None
     for k in range(8):
-        if (k & 1) != c:
+        if k % (2 ** b) != c:
             continue
         d = abs(V[k] - ft)
         if best is None or d < best[0] or (d == best[0] and k > best[1]):
@@ -101,6 +101,61 @@ def test_reconstruct_bruteforce():
         exp = np.array([_brute_reconstruct(x, c) for x in t])
         assert np.array_equal(r, exp)
         assert np.all((r & 1) == c)
+
+
+@pytest.mark.parametrize("b", [2, 3])
+def test_reconstruct_low_b_bits_bruteforce(b):
+    """Algorithm 1 prose with b = 2 and 3: nearest magnitude whose low b index
+    bits equal c, exact rationals, ties to the larger magnitude."""
+    t = _t_grid()[:3000]
+    for c in range(2 ** b):
+        r = fp4.reconstruct(t, np.full(t.shape, c), b)
+        exp = np.array([_brute_reconstruct(x, c, b) for x in t])
+        assert np.array_equal(r, exp)
+        assert np.all((r & (2 ** b - 1)) == c)
+
+
+def test_reconstruct_b3_is_the_rollout_magnitude():
+    """b = 3 keeps the whole magnitude index: one candidate, whatever t is."""
+    t = _t_grid()
+    for c in range(8):
+        assert np.all(fp4.reconstruct(t, np.full(t.shape, c), 3) == c)
+
+
+def test_reconstruct_b2_thresholds():
+    """b = 2 chooses between index c and c + 4 (magnitudes {0, 2}, {.5, 3},
+    {1, 4}, {1.5, 6}); the upper one from the midpoint 1, 1.75, 2.5, 3.75 on
+    (inclusive: ties go up). Derived by hand from the E2M1 table."""
+    mid = {0: 1.0, 1: 1.75, 2: 2.5, 3: 3.75}
+    for c, m in mid.items():
+        m32 = np.float32(m)
+        t = np.array([0, np.nextafter(m32, np.float32(0)), m32, np.nextafter(m32, np.float32(9)), 7],
+                     dtype=np.float32)
+        assert list(fp4.reconstruct(t, np.full(5, c), 2)) == [c, c, c + 4, c + 4, c + 4]
+
+
+@pytest.mark.parametrize("b", [1, 2, 3])
+def test_low_bit_guidance_adjacent_guarantee(b):
+    """For every b: where the rollout magnitude is a candidate, the guided
+    index is the rollout's or RTN's (local guarantee); with b = 3 it is always
+    the rollout's there, and b = 3 equals the full-code selection when the
+    signs agree."""
+    t = _t_grid()
+    t = t[t < 6]
+    lo, hi = fp4.bracket(t)
+    k_rtn = fp4.rtn(t)
+    zeros = np.zeros(t.shape, np.uint8)
+    v = np.array(formats.E2M1)
+    for k_r in range(8):
+        kr = np.full(t.shape, k_r, np.uint8)
+        kg = fp4.select_compact(lo, hi, fp4.reconstruct(t, kr & (2 ** b - 1), b))
+        assert np.all((kg == lo) | (kg == hi))
+        adj = (kr == lo) | (kr == hi)
+        assert np.all((kg[adj] == kr[adj]) | (kg[adj] == k_rtn[adj]))
+        assert np.all(np.abs(v[kg[adj]] - v[k_r]) <= np.abs(v[k_rtn[adj]] - v[k_r]))
+        if b == 3:
+            assert np.all(kg[adj] == kr[adj])
+            assert np.array_equal(kg, fp4.select_full(lo, hi, zeros, zeros, kr))
 
 
 def test_compact_select_table(golden):
@@ -198,3 +253,18 @@ def test_pack_layouts():
     bits = np.array([1, 0, 0, 0, 0, 0, 0, 1, 0, 1, 0, 0, 0, 0, 0, 0], dtype=np.uint8)
     assert list(fp4.pack_bits(bits)) == [0x81, 0x02]
     assert np.array_equal(fp4.unpack_bits(fp4.pack_bits(bits)), bits)
+    # b = 1 is pack_bits
+    assert np.array_equal(fp4.pack_low_bits(bits, 1), fp4.pack_bits(bits))
+    # b = 2: element 4j + i at bits 2i of byte j
+    two = np.array([1, 2, 3, 0, 0, 0, 0, 3], dtype=np.uint8)
+    assert list(fp4.pack_low_bits(two, 2)) == [0b00111001, 0b11000000]
+    # b = 3: element 8j + i at bits 3i of the 24-bit little-endian group j
+    three = np.array([7, 0, 5, 1, 2, 3, 4, 6], dtype=np.uint8)
+    word = sum(int(x) << (3 * i) for i, x in enumerate(three))
+    assert list(fp4.pack_low_bits(three, 3)) == [word & 0xFF, (word >> 8) & 0xFF, word >> 16]
+    rng = np.random.default_rng(3)
+    for b in (1, 2, 3):
+        vals = rng.integers(0, 2 ** b, 64).astype(np.uint8)
+        packed = fp4.pack_low_bits(vals, b)
+        assert packed.size == fp4.guide_bytes(b, 64) == 8 * b
+        assert np.array_equal(fp4.unpack_low_bits(packed, b, 64), vals)

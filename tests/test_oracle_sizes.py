@@ -39,9 +39,21 @@ def test_full_guidance_size(golden):
     assert act / compact == p["reduction_factor"]
 
 
-@pytest.mark.parametrize("fmt,bits,expect", [("nvfp4", 1, 1.5), ("nvfp4", 4, 4.5),
-                                             ("mxfp4", 1, 1.25), ("mxfp4", 4, 4.25)])
+@pytest.mark.parametrize("fmt,bits,expect", [("nvfp4", 1, 1.5), ("nvfp4", 2, 2.5), ("nvfp4", 3, 3.5),
+                                             ("nvfp4", 4, 4.5), ("mxfp4", 1, 1.25), ("mxfp4", 2, 2.25),
+                                             ("mxfp4", 3, 3.25), ("mxfp4", 4, 4.25)])
 def test_record_planes(fmt, bits, expect):
     n = 8192 * 2048
     p = sizes.record_plane_bytes(n, fmt, bits)
     assert (p["guide"] + p["scales"]) * 8 / n == expect
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_encode_writes_the_counted_planes(bits):
+    """The oracle's encode writes exactly the plane sizes counted above."""
+    import numpy as np
+    from oracle import fp4
+    x = np.random.default_rng(bits).integers(0, 0x7F00, 4096).astype(np.uint16)
+    o = fp4.encode_guidance(fp4.NVFP4, bits, x)
+    p = sizes.record_plane_bytes(x.size, "nvfp4", bits)
+    assert o["guide"].size == p["guide"] and o["scales"].size == p["scales"]
