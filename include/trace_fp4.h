@@ -22,9 +22,10 @@
  *
  * Pointers. Every pointer argument is a DEVICE pointer owned by the caller;
  * nothing is retained after the call returns. Input arrays are only read.
- * bf16 arrays must be 16-byte aligned; code planes 4-byte aligned; global
- * scales 4-byte aligned; workspaces and float64 accumulators 8-byte aligned.
- * Other planes have no alignment requirement. When N == 0 the data pointers
+ * bf16 arrays must be 16-byte aligned; code planes 4-byte aligned; 2-bit
+ * planes 2-byte aligned; global scales 4-byte aligned; workspaces, float64
+ * accumulators and int64 counts 8-byte aligned. Other planes have no
+ * alignment requirement. When N == 0 the data pointers
  * may be NULL.
  *
  * Planes written or read by the calls:
@@ -33,6 +34,11 @@
  *                       2i in the low nibble of byte i, 2i+1 in the high one.
  *   mbits   uint8[N/8]  one bit per element, the mantissa bit k & 1; element
  *                       8i+j in bit j of byte i (LSB first).
+ *   lowb    uint8[N*b/8] b = 1, 2 or 3 low bits of each magnitude index k
+ *                       (b = 1 is mbits), as one LSB-first bit string: element
+ *                       i occupies bits b*i .. b*i+b-1 (b = 2: element 4j+i at
+ *                       bits 2i of byte j; b = 3: element 8j+i at bits 3i of
+ *                       the little-endian 24-bit group in bytes 3j..3j+2).
  *   scales  uint8[N/B]  NVFP4: E4M3 (bias 7, OCP "fn") block scale; MXFP4:
  *                       E8M0 block scale (byte = E + 127). One byte per block,
  *                       block order. Bytes read by a call must be valid
@@ -82,7 +88,7 @@
 extern "C" {
 #endif
 
-#define TRACE_ABI_VERSION 3
+#define TRACE_ABI_VERSION 4
 
 /* Entries of the mismatch diagnostics of guided_fake_quant_stats. */
 #define TRACE_MISMATCH_COUNTS 32
@@ -153,6 +159,9 @@ int quantize_rtn(int fmt, int64_t rows, int64_t cols, int64_t group_rows, const 
  * scales).
  *
  *   bits    1: guide = mbits uint8[N/8] (mantissa bit of each rollout code)
+ *           2, 3: guide = lowb uint8[N*bits/8] (the low 2 or 3 magnitude
+ *              bits: Algorithm 1's parameter b; 2.5 and 3.5 bits per
+ *              element with the NVFP4 scale)
  *           4: guide = codes uint8[N/2] (the full signed rollout codes, the
  *              full-information record of §3.1)
  *   x_rollout      in   bf16[N]
@@ -169,18 +178,19 @@ int encode_guidance(int fmt, int bits, int64_t rows, int64_t cols, int64_t group
 /*
  * decode_guidance — training side, compact record: Reconstruct (Algorithm 1
  * prose). For each element, t = |x_train| * r under the ROLLOUT block scale;
- * the reference index is the E2M1 magnitude nearest t whose mantissa bit
- * equals the rollout bit, ties toward the larger magnitude; its sign is the
- * training sign. A rollout block whose scale is zero gives t = 0.
+ * the reference index is the E2M1 magnitude nearest t whose low `bits`
+ * magnitude bits equal the rollout's, ties toward the larger magnitude; its
+ * sign is the training sign. A rollout block whose scale is zero gives t = 0.
  *
+ *   bits      1, 2 or 3
  *   x_train   in   bf16[N]
- *   mbits     in   uint8[N/8]   from encode_guidance(bits=1)
+ *   guide     in   uint8[N*bits/8]   from encode_guidance(bits)
  *   scales    in   uint8[N/B]   rollout block scales
  *   gscale    in   float[2G]    NVFP4: rollout S of group g at [2g]; MXFP4: NULL
  *   ref_codes out  uint8[N/2]
  */
-int decode_guidance(int fmt, int64_t rows, int64_t cols, int64_t group_rows,
-                    const uint16_t* x_train, const uint8_t* mbits, const uint8_t* scales,
+int decode_guidance(int fmt, int bits, int64_t rows, int64_t cols, int64_t group_rows,
+                    const uint16_t* x_train, const uint8_t* guide, const uint8_t* scales,
                     const float* gscale, uint8_t* ref_codes, void* stream);
 
 /*
@@ -191,8 +201,9 @@ int decode_guidance(int fmt, int64_t rows, int64_t cols, int64_t group_rows,
  * {q-, q+} (a single one when t is a codeword or t >= 6) and one is chosen:
  *
  *   bits 0  RTN (the q_RTN of the local guarantee, §3.1); guide must be NULL
- *   bits 1  the candidate nearest the Reconstruct reference (decode fused);
- *           guide = mbits uint8[N/8]
+ *   bits 1, 2, 3  the candidate nearest the Reconstruct reference from the
+ *           low `bits` magnitude bits (decode fused); guide = lowb
+ *           uint8[N*bits/8]
  *   bits 4  the candidate nearest the exact rollout codeword, both signed
  *           (candidates carry the training sign); guide = codes uint8[N/2]
  *

@@ -166,22 +166,25 @@ def encode_guidance(x_rollout: torch.Tensor, fmt="nvfp4", bits: int = 1,
                     group_rows: int = 0, guide=None, scales=None, gscale_out=None, y=None,
                     work=None) -> Guidance:
     """Rollout side: RTN-quantize and emit the guidance record (bits=1: the
-    mantissa-bit plane; bits=4: the full code plane) plus the scales."""
+    mantissa-bit plane; 2, 3: the low magnitude bits; 4: the full code plane)
+    plus the scales."""
     f = fmt_id(fmt)
     rows, cols = _check_x(x_rollout, "x_rollout")
-    gcols = cols // 8 if bits == 1 else cols // 2
+    if bits not in (1, 2, 3, 4):
+        raise ValueError("bits must be 1, 2, 3 or 4")
+    gcols = cols * bits // 8
     c, s, g, yy = _rtn_call("encode_guidance", x_rollout, f, bits, group_rows, gscale,
                             (rows, gcols), with_y, guide, scales, gscale_out, y, work)
     return Guidance(f, int(bits), c, s, g, yy, int(group_rows))
 
 
 def decode_guidance(x_train: torch.Tensor, g: Guidance, ref_codes=None) -> torch.Tensor:
-    """Reconstruct the compact rollout reference codes (bits=1 records only)."""
-    if g.bits != 1:
-        raise ValueError("decode_guidance takes a bits=1 record")
+    """Reconstruct the compact rollout reference codes (records of 1..3 bits)."""
+    if g.bits not in (1, 2, 3):
+        raise ValueError("decode_guidance takes a record of 1, 2 or 3 bits")
     rows, cols = _check_x(x_train, "x_train")
     ref_codes = _empty((rows, cols // 2), torch.uint8, x_train, ref_codes)
-    _abi.call("decode_guidance", g.fmt, rows, cols, g.group_rows, _ptr(x_train), _ptr(g.guide),
+    _abi.call("decode_guidance", g.fmt, g.bits, rows, cols, g.group_rows, _ptr(x_train), _ptr(g.guide),
               _ptr(g.scales), _ptr(g.gscale), _ptr(ref_codes), _stream(x_train))
     return ref_codes
 
@@ -200,7 +203,7 @@ def _guided_common(x_train, g, bits, with_codes, y, codes):
 def guided_fake_quant(x_train: torch.Tensor, g: Guidance, bits: Optional[int] = None,
                       with_codes: bool = False, y=None, codes=None):
     """Training side: rollout-guided rounding under the rollout scales.
-    ``bits`` defaults to the record's (1 or 4); 0 gives RTN under the rollout
+    ``bits`` defaults to the record's (1..4); 0 gives RTN under the rollout
     scales. Returns (y, codes or None)."""
     b, rows, cols, y, codes, guide = _guided_common(x_train, g, bits, with_codes, y, codes)
     _abi.call("guided_fake_quant", g.fmt, b, rows, cols, g.group_rows, _ptr(x_train), _ptr(guide),

@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtrace_fp
 
 OK, EINVAL, ESHAPE, EALIGN, EALIAS, EDEVICE, ELAUNCH = 0, -1, -2, -3, -4, -5, -6
 NVFP4, MXFP4 = 0, 1
-ABI_VERSION = 3
+ABI_VERSION = 4
 MISMATCH_COUNTS = 32
 
 _i64 = ctypes.c_int64
@@ -32,8 +32,8 @@ SIGNATURES = {
     "quantize_rtn": (_int, [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp]),
     # fmt, bits, rows, cols, group_rows, x_r, gscale_in, guide, scales, gscale_out, y_r, work, work_bytes, stream
     "encode_guidance": (_int, [_int, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp]),
-    # fmt, rows, cols, group_rows, x_t, mbits, scales, gscale, ref_codes, stream
-    "decode_guidance": (_int, [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
+    # fmt, bits, rows, cols, group_rows, x_t, guide, scales, gscale, ref_codes, stream
+    "decode_guidance": (_int, [_int, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
     # fmt, bits, rows, cols, group_rows, x_t, guide, scales, gscale, y, codes, stream
     "guided_fake_quant": (_int, [_int, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     # fmt, bits, rows, cols, group_rows, x_t, x_r, guide, scales, gscale, y, codes, acc3, counts,

@@ -50,6 +50,12 @@ int block_of(int fmt) { return fmt == TRACE_FMT_NVFP4 ? 16 : 32; }
 
 bool valid_fmt(int fmt) { return fmt == TRACE_FMT_NVFP4 || fmt == TRACE_FMT_MXFP4; }
 
+// Guidance planes: bits 1..3 keep the low bits of each magnitude index (N*bits/8
+// bytes), 4 the full codes (N/2). Units of 8 elements are read whole, so a
+// plane is aligned to one unit's bytes when that is a power of two.
+int64_t guide_bytes(int bits, int64_t n) { return n * bits / 8; }
+uintptr_t guide_align(int bits) { return bits == 4 ? 4 : bits == 2 ? 2 : 1; }
+
 // A validated call shape: N elements in G groups of upg units.
 struct CallShape {
   int64_t n;
@@ -96,10 +102,9 @@ int launched(hipError_t e) { return e == hipSuccess ? TRACE_OK : TRACE_ELAUNCH; 
 
 // Shared by quantize_rtn and encode_guidance. `plane_bytes` is the size of
 // the code or bit plane, `plane_align` its alignment.
-int run_rtn(int fmt, int plane_mode, int64_t rows, int64_t cols, int64_t group_rows,
-            const uint16_t* x, const float* gin, uint8_t* plane, int64_t plane_div,
-            uint32_t plane_align, uint8_t* scales, float* gout, uint16_t* y, void* work,
-            int64_t work_bytes, void* stream) {
+int run_rtn(int fmt, int plane_bits, int64_t rows, int64_t cols, int64_t group_rows,
+            const uint16_t* x, const float* gin, uint8_t* plane, uint8_t* scales, float* gout,
+            uint16_t* y, void* work, int64_t work_bytes, void* stream) {
   CallShape cs;
   int st = shape_of(fmt, rows, cols, group_rows, &cs);
   if (st != TRACE_OK) return st;
@@ -114,23 +119,24 @@ int run_rtn(int fmt, int plane_mode, int64_t rows, int64_t cols, int64_t group_r
   const int64_t wneed = need_work ? tfp4::quant_work_bytes(cs.sh) : 0;
   if (need_work && work == nullptr) return TRACE_EINVAL;
   if (work_bytes < wneed) return TRACE_ESHAPE;
-  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(plane, plane_align) || !aligned(gin, 4) ||
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(plane, guide_align(plane_bits)) ||
+      !aligned(gin, 4) ||
       !aligned(gout, 4) || (need_work && !aligned(work, 8)))
     return TRACE_EALIGN;
   const Range ins[] = {{x, 2 * n}, {gin, 8 * G}};
-  const Range outs[] = {{plane, n / plane_div}, {scales, n / block_of(fmt)}, {gout, 8 * G},
+  const Range outs[] = {{plane, guide_bytes(plane_bits, n)}, {scales, n / block_of(fmt)}, {gout, 8 * G},
                         {y, 2 * n}, {need_work ? work : nullptr, wneed}};
   if (any_alias(outs, ins)) return TRACE_EALIAS;
   st = check_device();
   if (st != TRACE_OK) return st;
-  return launched(tfp4::launch_quantize(fmt, plane_mode, cs.sh, x, gin, gout, plane, scales, y,
+  return launched(tfp4::launch_quantize(fmt, plane_bits, cs.sh, x, gin, gout, plane, scales, y,
                                         need_work ? work : nullptr,
                                         static_cast<hipStream_t>(stream)));
 }
 
 // Checks shared by the training-side calls: scales, gscale, guide.
 int check_train(int fmt, int64_t n, const uint16_t* x, const uint8_t* guide, bool guide_needed,
-                uint32_t guide_align, const uint8_t* scales, const float* gscale) {
+                const uint8_t* scales, const float* gscale) {
   if (fmt == TRACE_FMT_NVFP4) {
     if (gscale == nullptr) return TRACE_EINVAL;
   } else if (gscale != nullptr) {
@@ -147,13 +153,13 @@ int run_guided(int fmt, int bits, int64_t rows, int64_t cols, int64_t group_rows
                const uint8_t* scales, const float* gscale, uint16_t* y, uint8_t* codes,
                double* acc3, int64_t* counts, int accumulate, void* work, int64_t work_bytes,
                void* stream) {
-  if (!valid_fmt(fmt) || (bits != 0 && bits != 1 && bits != 4)) return TRACE_EINVAL;
+  if (!valid_fmt(fmt) || bits < 0 || bits > 4) return TRACE_EINVAL;
   if (stats && accumulate != 0 && accumulate != 1) return TRACE_EINVAL;
   CallShape cs;
   int st = shape_of(fmt, rows, cols, group_rows, &cs);
   if (st != TRACE_OK) return st;
   const int64_t n = cs.n, G = cs.sh.groups;
-  st = check_train(fmt, n, x, guide, bits != 0, bits == 4 ? 4 : 1, scales, gscale);
+  st = check_train(fmt, n, x, guide, bits != 0, scales, gscale);
   if (st != TRACE_OK) return st;
   if (n > 0 && y == nullptr) return TRACE_EINVAL;
   int64_t wneed = 0;
@@ -164,10 +170,10 @@ int run_guided(int fmt, int bits, int64_t rows, int64_t cols, int64_t group_rows
     if (work_bytes < wneed) return TRACE_ESHAPE;
   }
   if (!aligned(x, 16) || !aligned(xr, 16) || !aligned(y, 16) || !aligned(codes, 4) ||
-      !aligned(guide, bits == 4 ? 4 : 1) || !aligned(gscale, 4) || !aligned(acc3, 8) ||
+      !aligned(guide, guide_align(bits)) || !aligned(gscale, 4) || !aligned(acc3, 8) ||
       !aligned(counts, 8) || (wneed > 0 && !aligned(work, 8)))
     return TRACE_EALIGN;
-  const int64_t gbytes = bits == 1 ? n / 8 : bits == 4 ? n / 2 : 0;
+  const int64_t gbytes = guide_bytes(bits, n);
   const Range ins[] = {{x, 2 * n}, {xr, stats ? 2 * n : 0}, {guide, gbytes},
                        {scales, n / block_of(fmt)}, {gscale, 8 * G}};
   const Range outs[] = {{y, 2 * n}, {codes, n / 2}, {acc3, stats ? 24 : 0},
@@ -229,38 +235,40 @@ int quantize_rtn(int fmt, int64_t rows, int64_t cols, int64_t group_rows, const 
                  const float* gscale_in, uint8_t* codes, uint8_t* scales, float* gscale_out,
                  uint16_t* y_opt, void* work, int64_t work_bytes, void* stream) {
   if (!valid_fmt(fmt)) return TRACE_EINVAL;
-  return run_rtn(fmt, 0, rows, cols, group_rows, x, gscale_in, codes, 2, 4, scales, gscale_out,
-                 y_opt, work, work_bytes, stream);
+  return run_rtn(fmt, 4, rows, cols, group_rows, x, gscale_in, codes, scales, gscale_out, y_opt,
+                 work, work_bytes, stream);
 }
 
 int encode_guidance(int fmt, int bits, int64_t rows, int64_t cols, int64_t group_rows,
                     const uint16_t* x_rollout, const float* gscale_in, uint8_t* guide,
                     uint8_t* scales, float* gscale_out, uint16_t* y_rollout_opt, void* work,
                     int64_t work_bytes, void* stream) {
-  if (!valid_fmt(fmt) || (bits != 1 && bits != 4)) return TRACE_EINVAL;
-  return run_rtn(fmt, bits == 1 ? 1 : 0, rows, cols, group_rows, x_rollout, gscale_in, guide,
-                 bits == 1 ? 8 : 2, bits == 1 ? 1 : 4, scales, gscale_out, y_rollout_opt, work,
-                 work_bytes, stream);
+  if (!valid_fmt(fmt) || bits < 1 || bits > 4) return TRACE_EINVAL;
+  return run_rtn(fmt, bits, rows, cols, group_rows, x_rollout, gscale_in, guide, scales,
+                 gscale_out, y_rollout_opt, work, work_bytes, stream);
 }
 
-int decode_guidance(int fmt, int64_t rows, int64_t cols, int64_t group_rows,
-                    const uint16_t* x_train, const uint8_t* mbits, const uint8_t* scales,
+int decode_guidance(int fmt, int bits, int64_t rows, int64_t cols, int64_t group_rows,
+                    const uint16_t* x_train, const uint8_t* guide, const uint8_t* scales,
                     const float* gscale, uint8_t* ref_codes, void* stream) {
-  if (!valid_fmt(fmt)) return TRACE_EINVAL;
+  if (!valid_fmt(fmt) || bits < 1 || bits > 3) return TRACE_EINVAL;
   CallShape cs;
   int st = shape_of(fmt, rows, cols, group_rows, &cs);
   if (st != TRACE_OK) return st;
   const int64_t n = cs.n, G = cs.sh.groups;
-  st = check_train(fmt, n, x_train, mbits, true, 1, scales, gscale);
+  st = check_train(fmt, n, x_train, guide, true, scales, gscale);
   if (st != TRACE_OK) return st;
   if (n > 0 && ref_codes == nullptr) return TRACE_EINVAL;
-  if (!aligned(x_train, 16) || !aligned(ref_codes, 4) || !aligned(gscale, 4)) return TRACE_EALIGN;
-  const Range ins[] = {{x_train, 2 * n}, {mbits, n / 8}, {scales, n / block_of(fmt)}, {gscale, 8 * G}};
+  if (!aligned(x_train, 16) || !aligned(ref_codes, 4) || !aligned(gscale, 4) ||
+      !aligned(guide, guide_align(bits)))
+    return TRACE_EALIGN;
+  const Range ins[] = {{x_train, 2 * n}, {guide, guide_bytes(bits, n)}, {scales, n / block_of(fmt)},
+                       {gscale, 8 * G}};
   const Range outs[] = {{ref_codes, n / 2}};
   if (any_alias(outs, ins)) return TRACE_EALIAS;
   st = check_device();
   if (st != TRACE_OK) return st;
-  return launched(tfp4::launch_guided(fmt, 1, true, cs.sh, x_train, mbits, scales, gscale, nullptr,
+  return launched(tfp4::launch_guided(fmt, bits, true, cs.sh, x_train, guide, scales, gscale, nullptr,
                                       ref_codes, nullptr, nullptr, nullptr, 0, nullptr,
                                       static_cast<hipStream_t>(stream)));
 }

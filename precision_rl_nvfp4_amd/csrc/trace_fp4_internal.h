@@ -38,16 +38,17 @@ int64_t guided_stats_work_bytes(const Shape& sh);
 int64_t stats_work_bytes(int64_t n);
 
 // RTN quantization of a tensor (quantize_rtn / encode_guidance).
-//   fmt 0 NVFP4 / 1 MXFP4; plane_mode 0 = code plane u8[N/2], 1 = mantissa-bit
-//   plane u8[N/8]. NVFP4: exactly one of gin (S of group g at gin[2g]) and
+//   fmt 0 NVFP4 / 1 MXFP4; plane_mode = bits of the plane: 4 = code plane
+//   u8[N/2], 1..3 = the low 1..3 magnitude bits, u8[N*bits/8]. NVFP4: exactly one of gin (S of group g at gin[2g]) and
 //   gout (receives {S, A} per group, computed from the amax) is non-NULL, and
 //   `work` holds quant_work_bytes when gout is used. MXFP4: both NULL.
 hipError_t launch_quantize(int fmt, int plane_mode, const Shape& sh, const uint16_t* x,
                            const float* gin, float* gout, uint8_t* plane, uint8_t* scales,
                            uint16_t* y, void* work, hipStream_t stream);
 
-// Guided rounding under the rollout scales (guided_fake_quant), Reconstruct
-// alone (decode_guidance: decode_only, bits 1, writes reference codes), and
+// Guided rounding under the rollout scales (guided_fake_quant, bits 0..4),
+// Reconstruct alone (decode_guidance: decode_only, bits 1..3, writes
+// reference codes), and
 // the fused discrepancy sums (xr and acc3 non-NULL) with, when counts is also
 // non-NULL, the mismatch diagnostics.
 hipError_t launch_guided(int fmt, int bits, bool decode_only, const Shape& sh,

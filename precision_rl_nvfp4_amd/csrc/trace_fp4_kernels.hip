@@ -124,6 +124,29 @@ __device__ __forceinline__ uint32_t spread_bits(uint32_t c) {
   return (c | (c << 3)) & 0x11111111u;
 }
 
+// Low 2 bits of each nibble -> 16 bits, element i at bits 2i..2i+1.
+__device__ __forceinline__ uint32_t gather_2bits(uint32_t k) {
+  uint32_t m = k & 0x33333333u;
+  m = (m | (m >> 2)) & 0x0F0F0F0Fu;
+  m = (m | (m >> 4)) & 0x00FF00FFu;
+  return (m | (m >> 8)) & 0xFFFFu;
+}
+__device__ __forceinline__ uint32_t spread_2bits(uint32_t c) {
+  c = (c | (c << 8)) & 0x00FF00FFu;
+  c = (c | (c << 4)) & 0x0F0F0F0Fu;
+  return (c | (c << 2)) & 0x33333333u;
+}
+
+// Low 3 bits of each nibble -> 24 bits, element i at bits 3i..3i+2.
+__device__ __forceinline__ uint32_t gather_3bits(uint32_t k) {
+  const uint32_t m = (k & 0x07070707u) | ((k & 0x70707070u) >> 1);  // 6 bits per byte
+  return (m & 0x3Fu) | ((m >> 2) & 0xFC0u) | ((m >> 4) & 0x3F000u) | ((m >> 6) & 0xFC0000u);
+}
+__device__ __forceinline__ uint32_t spread_3bits(uint32_t c) {
+  const uint32_t m = (c & 0x3Fu) | ((c & 0xFC0u) << 2) | ((c & 0x3F000u) << 4) | ((c & 0xFC0000u) << 6);
+  return (m & 0x07070707u) | ((m & 0x38383838u) << 1);
+}
+
 // Training-side selection under the rollout scale for the 8 elements of a
 // unit (t signed, carrying the training sign). Returns the chosen codes.
 //   BITS 0: RTN.
@@ -131,13 +154,43 @@ __device__ __forceinline__ uint32_t spread_bits(uint32_t c) {
 //           bracket {lo, hi} take hi when t lies strictly inside it, lo < 7,
 //           hi's mantissa bit is the rollout's, and t is not in a dead zone
 //           (2, 2.25) or (4, 4.5), where the Reconstruct reference is lo - 1.
+//   BITS 2: g = the rollout's low 2 magnitude bits c (16 bits). The
+//           reference is c + 4 when |t| reaches the midpoint of v(c) and
+//           v(c + 4) (1, 1.75, 2.5, 3.75), else c; take hi when t is inside,
+//           lo < 7 and the reference exceeds lo.
+//   BITS 3: g = the rollout magnitudes (24 bits), the reference itself.
 //   BITS 4: full record g = rollout codes (dword). Take hi when t is inside,
 //           lo < 7, the signs agree and the rollout magnitude exceeds lo.
-//   DECODE (BITS 1): the Reconstruct reference itself instead of the choice.
+//   DECODE (BITS 1..3): the Reconstruct reference itself instead of the choice.
 template <int BITS, bool DECODE>
 __device__ __forceinline__ uint32_t select_codes(const float (&t)[8], uint32_t g) {
   if constexpr (BITS == 0) {
     return rtn_codes(t);
+  } else if constexpr (BITS == 2 || BITS == 3) {
+    const uint32_t L = floor_codes(t);
+    uint32_t R;  // reference magnitudes, one per nibble
+    if constexpr (BITS == 3) {
+      R = spread_3bits(g);
+    } else {
+      R = spread_2bits(g);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t c = (R >> (4 * i)) & 3u;
+        const uint32_t thr = 0x3F8u + ((0xFA60u >> (4 * c)) & 15u);  // midpoint bits >> 20
+        R |= (uint32_t)(((__float_as_uint(t[i]) & 0x7FFFFFFFu) >> 20) >= thr) << (4 * i + 2);
+      }
+    }
+    if constexpr (DECODE) return (L & 0x88888888u) | R;
+    float tp[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tp[i] = __uint_as_float(__float_as_uint(t[i]) - 1u);
+    const uint32_t Lp = floor_codes(tp);
+    const uint32_t z = (L ^ Lp) & 0x77777777u;
+    const uint32_t X = (z | (z >> 1) | (z >> 2)) & 0x11111111u;  // t is a codeword
+    const uint32_t M = L & 0x77777777u;
+    const uint32_t gt = ~((M | 0x88888888u) - R) & 0x88888888u;  // reference > lo
+    // R > M is impossible when lo == 7, so no saturation mask is needed.
+    return L + ((gt >> 3) & ~X);
   } else {
     const uint32_t L = floor_codes(t);
     float tp[8];
@@ -419,8 +472,9 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(AmaxArgs a) {
 }
 
 // RTN quantization (quantize_rtn / encode_guidance).
-// FMT 0 NVFP4 / 1 MXFP4; PLANE 0 codes (u32 per unit) / 1 mantissa bits (u8
-// per unit); WY writes y; SSRC (NVFP4) 0: S = gin[2g]; 1: S from the amax
+// FMT 0 NVFP4 / 1 MXFP4; PLANE = bits of the guidance plane: 4 codes (u32 per
+// unit), 1 mantissa bits (u8 per unit), 2 / 3 the low 2 / 3 magnitude bits
+// (u16 / 3 bytes per unit); WY writes y; SSRC (NVFP4) 0: S = gin[2g]; 1: S from the amax
 // partials, {S, A} stored to gout by the group's first tile. With SSRC 1 the
 // workgroups past `qblocks` run the amax pass of the next batch of groups, so
 // one launch quantizes batch b while reading batch b + 1 for its amax.
@@ -491,8 +545,19 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
     const uint32_t K = rtn_codes(f);
     if (u < a.map.upg) {
       const int64_t gu = gbase + u;
-      if constexpr (PLANE == 0) reinterpret_cast<uint32_t*>(a.plane)[gu] = K;
-      else a.plane[gu] = (uint8_t)gather_mbits(K);
+      if constexpr (PLANE == 4) {
+        reinterpret_cast<uint32_t*>(a.plane)[gu] = K;
+      } else if constexpr (PLANE == 1) {
+        a.plane[gu] = (uint8_t)gather_mbits(K);
+      } else if constexpr (PLANE == 2) {
+        reinterpret_cast<uint16_t*>(a.plane)[gu] = (uint16_t)gather_2bits(K);
+      } else {
+        const uint32_t w = gather_3bits(K);
+        uint8_t* q = a.plane + 3 * gu;
+        q[0] = (uint8_t)w;
+        q[1] = (uint8_t)(w >> 8);
+        q[2] = (uint8_t)(w >> 16);
+      }
       if constexpr (FMT == 0) {
         if ((gu & 1) == 0) a.scales[gu >> 1] = (uint8_t)sb;
       } else {
@@ -529,9 +594,18 @@ __global__ __launch_bounds__(kThreads) void guided_kernel(GuidedArgs a) {
     v[j] = ok ? a.x[gu] : make_uint4(0u, 0u, 0u, 0u);
     if constexpr (STATS) vr[j] = ok ? a.xr[gu] : make_uint4(0u, 0u, 0u, 0u);
     sbv[j] = ok ? (uint32_t)a.scales[FMT == 0 ? (gu >> 1) : (gu >> 2)] : 0u;
-    if constexpr (BITS == 1) gv[j] = ok ? (uint32_t)a.guide[gu] : 0u;
-    else if constexpr (BITS == 4) gv[j] = ok ? reinterpret_cast<const uint32_t*>(a.guide)[gu] : 0u;
-    else gv[j] = 0u;
+    if constexpr (BITS == 1) {
+      gv[j] = ok ? (uint32_t)a.guide[gu] : 0u;
+    } else if constexpr (BITS == 2) {
+      gv[j] = ok ? (uint32_t)reinterpret_cast<const uint16_t*>(a.guide)[gu] : 0u;
+    } else if constexpr (BITS == 3) {
+      const uint8_t* q = a.guide + 3 * gu;
+      gv[j] = ok ? (uint32_t)q[0] | ((uint32_t)q[1] << 8) | ((uint32_t)q[2] << 16) : 0u;
+    } else if constexpr (BITS == 4) {
+      gv[j] = ok ? reinterpret_cast<const uint32_t*>(a.guide)[gu] : 0u;
+    } else {
+      gv[j] = 0u;
+    }
   }
   if constexpr (FMT == 0) build_factor_lut(lut, a.gscale[2 * g]);
   if constexpr (FMT == 0 || DIAG) __syncthreads();
@@ -759,6 +833,18 @@ hipError_t quant_wy(bool wy, int ssrc, const QuantArgs& a, int64_t blocks, hipSt
   }
 }
 
+// plane_mode = bits of the guidance plane (1..4; quantize_rtn writes codes, 4).
+template <int FMT>
+hipError_t quant_plane(int plane_mode, bool wy, int ssrc, const QuantArgs& a, int64_t blocks,
+                       hipStream_t s) {
+  switch (plane_mode) {
+    case 1: return quant_wy<FMT, 1>(wy, ssrc, a, blocks, s);
+    case 2: return quant_wy<FMT, 2>(wy, ssrc, a, blocks, s);
+    case 3: return quant_wy<FMT, 3>(wy, ssrc, a, blocks, s);
+    default: return quant_wy<FMT, 4>(wy, ssrc, a, blocks, s);
+  }
+}
+
 template <int FMT, int BITS, bool DECODE, bool WCODES, bool STATS, bool DIAG>
 hipError_t guided_go(const GuidedArgs& a, const Shape& sh, hipStream_t s) {
   return launch(guided_kernel<FMT, BITS, DECODE, WCODES, STATS, DIAG>, dim3(tile_grid(sh)),
@@ -779,10 +865,18 @@ hipError_t guided_bits(bool wc, bool stats, bool diag, const GuidedArgs& a, cons
 template <int FMT>
 hipError_t guided_fmt(int bits, bool decode, bool wc, bool stats, bool diag, const GuidedArgs& a,
                       const Shape& sh, hipStream_t s) {
-  if (decode) return guided_go<FMT, 1, true, true, false, false>(a, sh, s);
+  if (decode) {
+    switch (bits) {
+      case 1: return guided_go<FMT, 1, true, true, false, false>(a, sh, s);
+      case 2: return guided_go<FMT, 2, true, true, false, false>(a, sh, s);
+      default: return guided_go<FMT, 3, true, true, false, false>(a, sh, s);
+    }
+  }
   switch (bits) {
     case 0: return guided_bits<FMT, 0>(wc, stats, diag, a, sh, s);
     case 1: return guided_bits<FMT, 1>(wc, stats, diag, a, sh, s);
+    case 2: return guided_bits<FMT, 2>(wc, stats, diag, a, sh, s);
+    case 3: return guided_bits<FMT, 3>(wc, stats, diag, a, sh, s);
     default: return guided_bits<FMT, 4>(wc, stats, diag, a, sh, s);
   }
 }
@@ -829,10 +923,8 @@ hipError_t launch_quantize(int fmt, int plane_mode, const Shape& sh, const uint1
   const bool wy = y != nullptr;
   if (fmt == 1 || gout == nullptr) {
     a.qblocks = (int64_t)tile_grid(sh);
-    if (fmt == 0) return plane_mode == 0 ? quant_wy<0, 0>(wy, 0, a, a.qblocks, stream)
-                                         : quant_wy<0, 1>(wy, 0, a, a.qblocks, stream);
-    return plane_mode == 0 ? quant_wy<1, 0>(wy, 0, a, a.qblocks, stream)
-                           : quant_wy<1, 1>(wy, 0, a, a.qblocks, stream);
+    if (fmt == 0) return quant_plane<0>(plane_mode, wy, 0, a, a.qblocks, stream);
+    return quant_plane<1>(plane_mode, wy, 0, a, a.qblocks, stream);
   }
   // NVFP4 with S from the amax: the input is read twice (amax, then
   // quantize). Groups go in batches of about kCacheBatchBytes of input, and
@@ -863,8 +955,7 @@ hipError_t launch_quantize(int fmt, int plane_mode, const Shape& sh, const uint1
     a.side = m;
     a.side.g0 = g0 + nq;
     const int64_t blocks = a.qblocks + na * m.nparts;
-    e = plane_mode == 0 ? quant_wy<0, 0>(wy, 1, a, blocks, stream)
-                        : quant_wy<0, 1>(wy, 1, a, blocks, stream);
+    e = quant_plane<0>(plane_mode, wy, 1, a, blocks, stream);
   }
   return e;
 }

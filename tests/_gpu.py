@@ -65,11 +65,13 @@ def n_groups(rows, group_rows):
     return rows // group_rows if group_rows else 1
 
 
-def group_slices(n, G, fmt, plane_div):
-    """Element, plane-byte and scale-byte slices of each of G equal groups."""
+def group_slices(n, G, fmt, plane_bits):
+    """Element, plane-byte and scale-byte slices of each of G equal groups
+    (plane_bits: bits per element of the plane, 1..4)."""
     ng = n // G
     B = ofp4.BLOCK[fmt]
-    return [(slice(g * ng, (g + 1) * ng), slice(g * ng // plane_div, (g + 1) * ng // plane_div),
+    pb = lambda e: e * plane_bits // 8  # noqa: E731
+    return [(slice(g * ng, (g + 1) * ng), slice(pb(g * ng), pb((g + 1) * ng)),
              slice(g * ng // B, (g + 1) * ng // B)) for g in range(G)]
 
 
@@ -78,7 +80,7 @@ def oracle_quantize(fmt, xb, rows, group_rows=0, gscale=None):
     group or an array of per-group S."""
     G = n_groups(rows, group_rows)
     parts = []
-    for g, (es, _, _) in enumerate(group_slices(xb.size, G, fmt, 2)):
+    for g, (es, _, _) in enumerate(group_slices(xb.size, G, fmt, 4)):
         s = None if gscale is None else np.asarray(gscale, np.float32).reshape(-1)[g % np.size(gscale)]
         parts.append(ofp4.quantize_rtn(fmt, xb[es], s))
     cat = lambda k: np.concatenate([p[k] for p in parts]) if parts else np.zeros(0)
@@ -91,7 +93,7 @@ def oracle_quantize(fmt, xb, rows, group_rows=0, gscale=None):
 def oracle_encode(fmt, bits, xb, rows, group_rows=0):
     G = n_groups(rows, group_rows)
     parts = [ofp4.encode_guidance(fmt, bits, xb[es])
-             for es, _, _ in group_slices(xb.size, G, fmt, 8 if bits == 1 else 2)]
+             for es, _, _ in group_slices(xb.size, G, fmt, bits)]
     out = {k: np.concatenate([p[k] for p in parts]) for k in ("guide", "scales", "y")}
     out["gscale"] = np.array([p["gscale"] for p in parts], np.float32) if fmt == ofp4.NVFP4 else None
     return out
@@ -100,9 +102,8 @@ def oracle_encode(fmt, bits, xb, rows, group_rows=0):
 def oracle_guided(fmt, bits, xt, enc, rows, group_rows=0):
     """guided_fake_quant of the oracle per group against an oracle record."""
     G = n_groups(rows, group_rows)
-    div = 8 if bits == 1 else 2
     ys, cs = [], []
-    for g, (es, ps, ss) in enumerate(group_slices(xt.size, G, fmt, div)):
+    for g, (es, ps, ss) in enumerate(group_slices(xt.size, G, fmt, max(bits, 1))):
         guide = None if bits == 0 else enc["guide"][ps]
         S = None if enc["gscale"] is None else enc["gscale"][g]
         o = ofp4.guided_fake_quant(fmt, bits, xt[es], guide, enc["scales"][ss], S)
@@ -111,12 +112,12 @@ def oracle_guided(fmt, bits, xt, enc, rows, group_rows=0):
     return {"y": np.concatenate(ys), "codes": np.concatenate(cs)}
 
 
-def oracle_decode(fmt, xt, enc, rows, group_rows=0):
+def oracle_decode(fmt, xt, enc, rows, group_rows=0, bits=1):
     G = n_groups(rows, group_rows)
     out = []
-    for g, (es, ps, ss) in enumerate(group_slices(xt.size, G, fmt, 8)):
+    for g, (es, ps, ss) in enumerate(group_slices(xt.size, G, fmt, bits)):
         S = None if enc["gscale"] is None else enc["gscale"][g]
-        out.append(ofp4.decode_guidance(fmt, xt[es], enc["guide"][ps], enc["scales"][ss], S))
+        out.append(ofp4.decode_guidance(fmt, xt[es], enc["guide"][ps], enc["scales"][ss], S, bits))
     return np.concatenate(out)
 
 
@@ -245,11 +246,12 @@ def check_guided_stats(xt_bits, xr_bits, rows, cols, fmt, bits, group_rows=0, to
     return a, (sb, sf, n)
 
 
-def check_decode(xt_bits, xr_bits, rows, cols, fmt, group_rows=0):
+def check_decode(xt_bits, xr_bits, rows, cols, fmt, group_rows=0, bits=1):
     xr = to_dev(xr_bits, rows, cols)
     xt = to_dev(xt_bits, rows, cols)
-    g = tq.encode_guidance(xr, fmt, 1, group_rows=group_rows)
+    g = tq.encode_guidance(xr, fmt, bits, group_rows=group_rows)
     ref = tq.decode_guidance(xt, g)
-    o_enc = oracle_encode(fmt, 1, xr_bits, rows, group_rows)
-    o = oracle_decode(fmt, xt_bits, o_enc, rows, group_rows)
-    assert_same(u8(ref), o, "reference codes")
+    o_enc = oracle_encode(fmt, bits, xr_bits, rows, group_rows)
+    o = oracle_decode(fmt, xt_bits, o_enc, rows, group_rows, bits)
+    assert_same(u8(g.guide), o_enc["guide"], f"guide bits={bits}")
+    assert_same(u8(ref), o, f"reference codes bits={bits}")

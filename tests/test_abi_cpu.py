@@ -51,7 +51,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.trace_abi_version() == _abi.ABI_VERSION == 3
+    assert lib.trace_abi_version() == _abi.ABI_VERSION == 4
     for code, name in [(0, "TRACE_OK"), (-1, "TRACE_EINVAL"), (-2, "TRACE_ESHAPE"),
                        (-3, "TRACE_EALIGN"), (-4, "TRACE_EALIAS"), (-5, "TRACE_EDEVICE"),
                        (-6, "TRACE_ELAUNCH"), (7, "unknown status")]:
@@ -120,8 +120,11 @@ def test_quantize_rtn_rejects(lib, args, status):
 
 # encode_guidance(fmt, bits, rows, cols, group_rows, x, gin, guide, scales, gout, y, work, wb, stream)
 @pytest.mark.parametrize("args,status", [
-    ((0, 2, 4, 32, 0, A, None, B, C, D, None, W, WB, None), _abi.EINVAL),       # bits 2
+    ((0, 5, 4, 32, 0, A, None, B, C, D, None, W, WB, None), _abi.EINVAL),       # bits 5
     ((0, 0, 4, 32, 0, A, None, B, C, D, None, W, WB, None), _abi.EINVAL),       # bits 0
+    ((0, 2, 4, 32, 0, A, None, B + 1, C, D, None, W, WB, None), _abi.EALIGN),   # 2-bit plane alignment
+    ((0, 3, 4, 32, 0, A, None, B, B + 47, D, None, W, WB, None), _abi.EALIAS),  # 3-bit plane is 48 B
+    ((0, 2, 4, 32, 0, A, None, B, B + 31, D, None, W, WB, None), _abi.EALIAS),  # 2-bit plane is 32 B
     ((0, 4, 4, 32, 0, A, None, B + 1, C, D, None, W, WB, None), _abi.EALIGN),   # code plane alignment
     ((0, 1, 4, 32, 0, A, None, B, B + 8, D, None, W, WB, None), _abi.EALIAS),   # bit plane is 16 B here
     ((0, 1, 4, 32, 0, A, None, A + 100, C, D, None, W, WB, None), _abi.EALIAS),
@@ -130,15 +133,19 @@ def test_encode_guidance_rejects(lib, args, status):
     assert lib.encode_guidance(*args) == status
 
 
-# decode_guidance(fmt, rows, cols, group_rows, x, mbits, scales, gscale, ref, stream)
+# decode_guidance(fmt, bits, rows, cols, group_rows, x, guide, scales, gscale, ref, stream)
 @pytest.mark.parametrize("args,status", [
-    ((0, 4, 32, 0, A, B, C, None, D, None), _abi.EINVAL),               # NVFP4 needs rollout S
-    ((1, 4, 32, 0, A, B, C, E, D, None), _abi.EINVAL),                  # MXFP4 takes none
-    ((0, 4, 32, 0, A, None, C, E, D, None), _abi.EINVAL),               # NULL mbits
-    ((0, 4, 32, 0, A, B, C, E, None, None), _abi.EINVAL),               # NULL output
-    ((0, 4, 32, 3, A, B, C, E, D, None), _abi.ESHAPE),                  # grouping
-    ((0, 4, 32, 0, A, B, C, E, D + 1, None), _abi.EALIGN),
-    ((0, 4, 32, 0, A, B, C, E, B, None), _abi.EALIAS),                  # output on the bits
+    ((0, 1, 4, 32, 0, A, B, C, None, D, None), _abi.EINVAL),            # NVFP4 needs rollout S
+    ((1, 1, 4, 32, 0, A, B, C, E, D, None), _abi.EINVAL),               # MXFP4 takes none
+    ((0, 0, 4, 32, 0, A, B, C, E, D, None), _abi.EINVAL),               # bits 0 has no record
+    ((0, 4, 4, 32, 0, A, B, C, E, D, None), _abi.EINVAL),               # full codes need no decode
+    ((0, 1, 4, 32, 0, A, None, C, E, D, None), _abi.EINVAL),            # NULL guide
+    ((0, 1, 4, 32, 0, A, B, C, E, None, None), _abi.EINVAL),            # NULL output
+    ((0, 1, 4, 32, 3, A, B, C, E, D, None), _abi.ESHAPE),               # grouping
+    ((0, 1, 4, 32, 0, A, B, C, E, D + 1, None), _abi.EALIGN),
+    ((0, 2, 4, 32, 0, A, B + 1, C, E, D, None), _abi.EALIGN),           # 2-bit plane alignment
+    ((0, 1, 4, 32, 0, A, B, C, E, B, None), _abi.EALIAS),               # output on the bits
+    ((0, 3, 4, 32, 0, A, B, C, E, B + 44, None), _abi.EALIAS),          # 3-bit plane is 48 B here
 ])
 def test_decode_guidance_rejects(lib, args, status):
     assert lib.decode_guidance(*args) == status
@@ -146,8 +153,12 @@ def test_decode_guidance_rejects(lib, args, status):
 
 # guided_fake_quant(fmt, bits, rows, cols, group_rows, x, guide, scales, gscale, y, codes, stream)
 @pytest.mark.parametrize("args,status", [
-    ((0, 3, 4, 32, 0, A, B, C, E, D, None, None), _abi.EINVAL),          # bits 3
+    ((0, 5, 4, 32, 0, A, B, C, E, D, None, None), _abi.EINVAL),          # bits 5
+    ((0, -1, 4, 32, 0, A, B, C, E, D, None, None), _abi.EINVAL),         # bits -1
     ((0, 0, 4, 32, 0, A, B, C, E, D, None, None), _abi.EINVAL),          # bits 0 takes no guide
+    ((0, 3, 4, 32, 0, A, None, C, E, D, None, None), _abi.EINVAL),       # bits 3 needs a guide
+    ((0, 2, 4, 32, 0, A, B + 1, C, E, D, None, None), _abi.EALIGN),      # 2-bit guide alignment
+    ((0, 3, 4, 32, 0, A, B, C, E, D, B + 40, None), _abi.EALIAS),        # codes over the 3-bit guide
     ((0, 1, 4, 32, 0, A, None, C, E, D, None, None), _abi.EINVAL),       # bits 1 needs a guide
     ((0, 1, 4, 32, 0, A, B, C, E, None, None, None), _abi.EINVAL),       # NULL y
     ((0, 1, 4, 32, 8, A, B, C, E, D, None, None), _abi.ESHAPE),          # 8 does not divide 4
@@ -211,7 +222,7 @@ def test_valid_call_without_gpu_is_edevice(lib):
                                        None) == _abi.EDEVICE
     assert lib.guided_fake_quant_stats(0, 1, 4, 32, 0, A, F, B, C, E, D, None, W, K, 1, SW, SB,
                                        None) == _abi.EDEVICE
-    assert lib.decode_guidance(0, 8, 32, 4, A, B, C, E, D, None) == _abi.EDEVICE
+    assert lib.decode_guidance(0, 1, 8, 32, 4, A, B, C, E, D, None) == _abi.EDEVICE
     assert lib.discrepancy_stats(64, A, B, C, D, E, 0, E + 64, 16, None) == _abi.EDEVICE
 
 

@@ -49,8 +49,7 @@ def _check_rows(fmt, bits, xt_b, xr_b, cols, r0, r1, S, enc, y_g=None, codes_g=N
     B = ofp4.BLOCK[fmt]
     es = slice(r0 * cols, r1 * cols)
     o = ofp4.encode_guidance(fmt, bits, xr_b[es], S)
-    div = 8 if bits == 1 else 2
-    G.assert_same(G.u8(enc.guide).reshape(-1)[r0 * cols // div:r1 * cols // div], o["guide"],
+    G.assert_same(G.u8(enc.guide).reshape(-1)[r0 * cols * bits // 8:r1 * cols * bits // 8], o["guide"],
                   f"guide rows {r0}:{r1}")
     G.assert_same(G.u8(enc.scales).reshape(-1)[r0 * cols // B:r1 * cols // B], o["scales"],
                   f"scales rows {r0}:{r1}")
@@ -121,7 +120,7 @@ def test_stream_layer_bench_configuration():
     assert G.rel_close(a[1], ref[1]) and G.rel_close(a[0], ref[0])
 
 
-@pytest.mark.parametrize("bits", [0, 1, 4])
+@pytest.mark.parametrize("bits", [0, 1, 2, 3, 4])
 def test_moe_layer_full_size(bits):
     """Routed-expert inputs of one MoE layer: 65,536 permuted rows x 2048,
     NVFP4, one global scale for the tensor."""

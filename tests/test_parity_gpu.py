@@ -41,7 +41,7 @@ def test_quantize_rtn(fmt, rows, cols):
 
 
 @pytest.mark.parametrize("fmt", [NV, MX])
-@pytest.mark.parametrize("bits", [1, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
 @pytest.mark.parametrize("rows,cols", SHAPES)
 def test_encode_guidance(fmt, bits, rows, cols):
     G.say(f"encode_guidance fmt={fmt} bits={bits} shape=({rows},{cols})")
@@ -50,7 +50,7 @@ def test_encode_guidance(fmt, bits, rows, cols):
 
 
 @pytest.mark.parametrize("fmt", [NV, MX])
-@pytest.mark.parametrize("bits", [0, 1, 4])
+@pytest.mark.parametrize("bits", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("rows,cols", SHAPES)
 def test_guided_fake_quant(fmt, bits, rows, cols):
     G.say(f"guided_fake_quant fmt={fmt} bits={bits} shape=({rows},{cols})")
@@ -60,11 +60,12 @@ def test_guided_fake_quant(fmt, bits, rows, cols):
 
 
 @pytest.mark.parametrize("fmt", [NV, MX])
+@pytest.mark.parametrize("bits", [1, 2, 3])
 @pytest.mark.parametrize("rows,cols", SHAPES)
-def test_decode_guidance(fmt, rows, cols):
-    G.say(f"decode_guidance fmt={fmt} shape=({rows},{cols})")
+def test_decode_guidance(fmt, bits, rows, cols):
+    G.say(f"decode_guidance fmt={fmt} bits={bits} shape=({rows},{cols})")
     xt, xr = _pair(rows, cols, rows + 3, mx=(fmt == MX))
-    G.check_decode(xt, xr, rows, cols, fmt)
+    G.check_decode(xt, xr, rows, cols, fmt, bits=bits)
 
 
 def test_quantize_without_y_and_with_given_scale():
@@ -170,9 +171,10 @@ def test_enumerate_bf16_members_unit_scale():
         keep[0::16] = True
         xr = np.where(keep, xr, formats.f32_to_bf16(vals[pick]))
         for fmt in (NV, MX):
-            for bits in (0, 1, 4):
+            for bits in (0, 1, 2, 3, 4):
                 G.check_guided(xb, xr, rows, 32, fmt, bits)
-            G.check_decode(xb, xr, rows, 32, fmt)
+            for bits in (1, 2, 3):
+                G.check_decode(xb, xr, rows, 32, fmt, bits=bits)
 
 
 def test_enumerate_bf16_block_max():
@@ -325,7 +327,7 @@ def test_grouped_quantize_and_encode(fmt, G_, gr, cols):
     xt, xr = _grouped_pair(G_, gr, cols, 1, mx=(fmt == MX))
     rows = G_ * gr
     G.check_quantize(xt, rows, cols, fmt, group_rows=gr)
-    for bits in (1, 4):
+    for bits in (1, 2, 3, 4):
         G.check_encode(xr, rows, cols, fmt, bits, group_rows=gr)
     if fmt == NV:
         G.check_quantize(xt, rows, cols, fmt, gscale=np.float32(0.75), group_rows=gr)
@@ -337,15 +339,16 @@ def test_grouped_guided_and_decode(fmt, G_, gr, cols):
     G.say(f"grouped guided/decode fmt={fmt} groups={G_} x ({gr},{cols})")
     xt, xr = _grouped_pair(G_, gr, cols, 2, mx=(fmt == MX))
     rows = G_ * gr
-    for bits in (0, 1, 4):
+    for bits in (0, 1, 2, 3, 4):
         G.check_guided(xt, xr, rows, cols, fmt, bits, group_rows=gr)
-    G.check_decode(xt, xr, rows, cols, fmt, group_rows=gr)
+    for bits in (1, 2, 3):
+        G.check_decode(xt, xr, rows, cols, fmt, group_rows=gr, bits=bits)
 
 
 # ---------------------------------------------------------------- fused statistics
 
 @pytest.mark.parametrize("fmt", [NV, MX])
-@pytest.mark.parametrize("bits", [0, 1, 4])
+@pytest.mark.parametrize("bits", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("rows,cols", [(1, 32), (37, 2048), (256, 2048), (333, 256)])
 def test_guided_fake_quant_stats(fmt, bits, rows, cols):
     G.say(f"guided_fake_quant_stats fmt={fmt} bits={bits} shape=({rows},{cols})")
@@ -387,7 +390,7 @@ def test_mismatch_counts_planted(fmt):
     idx = rng.choice(xt.size, 4000, replace=False)
     f = ofp4.bf16_to_f32(xr[idx]).astype(np.float32) * np.float32(1.5)
     xr[idx] = formats.f32_to_bf16(f)
-    for bits in (4, 1, 0):
+    for bits in (4, 3, 2, 1, 0):
         G.check_guided_stats(xt, xr, 64, 2048, fmt, bits)
     t, r = G.to_dev(xt, 64, 2048), G.to_dev(xr, 64, 2048)
     *_, cnt = tq.guided_fake_quant_stats(t, r, tq.encode_guidance(r, fmt, 4), mismatch=True)
@@ -408,7 +411,7 @@ def test_guided_fake_quant_stats_extreme_values(fmt):
     b2 = b.copy()
     b2[::3] ^= 0x0001
     b2[1::7] ^= 0x8000                       # sign flips: (x_t - x_r)^2 ~ (2x)^2 overflows binary32
-    for bits in (0, 1, 4):
+    for bits in (0, 1, 2, 3, 4):
         G.check_guided_stats(b2, b, 16, 64, fmt, bits)
     tiny = np.zeros(64, np.uint16)
     tiny[:32] = np.arange(1, 33)             # bf16 subnormals: squares underflow binary32
