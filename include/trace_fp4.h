@@ -124,8 +124,10 @@ const char* trace_status_str(int status);
 int64_t trace_set_encode_batch(int64_t groups_per_batch);
 
 /* Workspace bytes quantize_rtn / encode_guidance need to derive the global
- * scales from the amax (NVFP4 with gscale_out); 0 for MXFP4. -1 for an
- * invalid shape. */
+ * scales from the amax (NVFP4 with gscale_out): 4096 per group, except 0 when
+ * a group's element count is a power of two from 16 to 8192 and G > 1 (such
+ * groups, e.g. one token's row for a per-token global scale, are reduced
+ * and quantized in one pass); 0 for MXFP4. -1 for an invalid shape. */
 int64_t trace_quant_workspace_bytes(int fmt, int64_t rows, int64_t cols, int64_t group_rows);
 
 /* Workspace bytes guided_fake_quant_stats needs. -1 for an invalid shape. */

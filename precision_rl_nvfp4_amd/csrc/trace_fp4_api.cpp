@@ -115,8 +115,8 @@ int run_rtn(int fmt, int plane_bits, int64_t rows, int64_t cols, int64_t group_r
     return TRACE_EINVAL;
   }
   if (n > 0 && (x == nullptr || plane == nullptr || scales == nullptr)) return TRACE_EINVAL;
-  const bool need_work = gout != nullptr && n > 0;
-  const int64_t wneed = need_work ? tfp4::quant_work_bytes(cs.sh) : 0;
+  const int64_t wneed = gout != nullptr && n > 0 ? tfp4::quant_work_bytes(fmt, cs.sh) : 0;
+  const bool need_work = wneed > 0;
   if (need_work && work == nullptr) return TRACE_EINVAL;
   if (work_bytes < wneed) return TRACE_ESHAPE;
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(plane, guide_align(plane_bits)) ||
@@ -165,7 +165,7 @@ int run_guided(int fmt, int bits, int64_t rows, int64_t cols, int64_t group_rows
   int64_t wneed = 0;
   if (stats) {
     if (acc3 == nullptr || (n > 0 && xr == nullptr)) return TRACE_EINVAL;
-    wneed = n > 0 ? tfp4::guided_stats_work_bytes(cs.sh) : 0;
+    wneed = n > 0 ? tfp4::guided_stats_work_bytes(fmt, cs.sh) : 0;
     if (wneed > 0 && work == nullptr) return TRACE_EINVAL;
     if (work_bytes < wneed) return TRACE_ESHAPE;
   }
@@ -216,14 +216,14 @@ int64_t trace_quant_workspace_bytes(int fmt, int64_t rows, int64_t cols, int64_t
   if (!valid_fmt(fmt)) return -1;
   CallShape cs;
   if (shape_of(fmt, rows, cols, group_rows, &cs) != TRACE_OK) return -1;
-  return fmt == TRACE_FMT_NVFP4 ? tfp4::quant_work_bytes(cs.sh) : 0;
+  return tfp4::quant_work_bytes(fmt, cs.sh);
 }
 
 int64_t trace_guided_stats_workspace_bytes(int fmt, int64_t rows, int64_t cols, int64_t group_rows) {
   if (!valid_fmt(fmt)) return -1;
   CallShape cs;
   if (shape_of(fmt, rows, cols, group_rows, &cs) != TRACE_OK) return -1;
-  return tfp4::guided_stats_work_bytes(cs.sh);
+  return tfp4::guided_stats_work_bytes(fmt, cs.sh);
 }
 
 int64_t trace_stats_workspace_bytes(int64_t n) {

@@ -30,18 +30,21 @@ struct Shape {
 };
 
 // Workspace of quantize_rtn / encode_guidance when S comes from the amax:
-// uint32 partial maxima [groups][kPartMax].
-int64_t quant_work_bytes(const Shape& sh);
-// Workspace of guided_fake_quant_stats: float64 partial sums, 2 per workgroup.
-int64_t guided_stats_work_bytes(const Shape& sh);
+// uint32 partial maxima [groups][kPartMax]; none for MXFP4 or for NVFP4
+// groups packed several to a tile (their amax is reduced inside the tile).
+int64_t quant_work_bytes(int fmt, const Shape& sh);
+// Workspace of guided_fake_quant_stats: float64 partial sums, 2 per workgroup,
+// 64 second-level pairs, and the per-workgroup mismatch counts.
+int64_t guided_stats_work_bytes(int fmt, const Shape& sh);
 // Workspace of discrepancy_stats.
 int64_t stats_work_bytes(int64_t n);
 
 // RTN quantization of a tensor (quantize_rtn / encode_guidance).
 //   fmt 0 NVFP4 / 1 MXFP4; plane_mode = bits of the plane: 4 = code plane
-//   u8[N/2], 1..3 = the low 1..3 magnitude bits, u8[N*bits/8]. NVFP4: exactly one of gin (S of group g at gin[2g]) and
-//   gout (receives {S, A} per group, computed from the amax) is non-NULL, and
-//   `work` holds quant_work_bytes when gout is used. MXFP4: both NULL.
+//   u8[N/2], 1..3 = the low 1..3 magnitude bits, u8[N*bits/8]. NVFP4:
+//   exactly one of gin (S of group g at gin[2g]) and gout (receives {S, A}
+//   per group, computed from the amax) is non-NULL, and `work` holds
+//   quant_work_bytes when gout is used. MXFP4: both NULL.
 hipError_t launch_quantize(int fmt, int plane_mode, const Shape& sh, const uint16_t* x,
                            const float* gin, float* gout, uint8_t* plane, uint8_t* scales,
                            uint16_t* y, void* work, hipStream_t stream);

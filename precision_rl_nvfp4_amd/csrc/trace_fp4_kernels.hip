@@ -49,6 +49,7 @@ typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
 constexpr float kFltMax = 3.40282346638528859812e+38f;
 constexpr int kMidGroups = 64;          // first level of the partial-sum reduction
 constexpr int kMismatchBins = 15;       // signed-grid distances 0..14
+constexpr int kPackGroups = kTileUnits / 2;  // most groups in a packed tile (NVFP4: >= 2 units each)
 
 // ------------------------------------------------------------ lane exchange
 
@@ -298,6 +299,18 @@ __device__ __forceinline__ float e4m3_value(uint32_t b) {
   return ex == 0u ? (float)m * 0x1p-9f : __uint_as_float(((ex + 120u) << 23) | (m << 20));
 }
 
+// NVFP4 factors of one E4M3 byte under S: r = min(S / e, FLT_MAX), d = e / S,
+// both 0 for e == 0 (the entries of build_factor_lut, for packed groups).
+__device__ __forceinline__ void nv_factors(uint32_t sb, float S, float& r, float& d) {
+  const float e = e4m3_value(sb & 0x7Fu);
+  r = 0.0f;
+  d = 0.0f;
+  if (e != 0.0f) {
+    d = e / S;
+    r = fminf(S / e, kFltMax);
+  }
+}
+
 // Workgroup table of the NVFP4 factors of every E4M3 byte under S:
 // lut[e] = {r = min(S / e, FLT_MAX), d = e / S}, {0, 0} for e == 0.
 __device__ __forceinline__ void build_factor_lut(float2* lut, float S) {
@@ -386,9 +399,17 @@ __device__ __forceinline__ double sq_diff_sum(const float (&a)[8], const float (
 
 // ------------------------------------------------------------ kernel arguments
 
+// Work split of a launch. Normally a tile of kTileUnits units lies in one
+// group (tiles = tiles per group). Packed (NVFP4 groups of a power-of-two
+// unit count below kTileUnits, e.g. one token's row): a tile holds
+// kTileUnits >> lg whole consecutive groups (tiles = tiles of the call).
 struct TileMap {
   int64_t upg;        // units per group
-  int64_t tiles;      // tiles per group
+  int64_t tiles;      // tiles per group, or of the call when packed
+  int64_t units;      // units of the call
+  int64_t groups;     // groups of the call
+  int lg;             // log2(upg) when packed
+  int packed;
 };
 
 __device__ __forceinline__ void tile_of(const TileMap& m, int64_t& g, int64_t& tbase) {
@@ -478,10 +499,17 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(AmaxArgs a) {
 // partials, {S, A} stored to gout by the group's first tile. With SSRC 1 the
 // workgroups past `qblocks` run the amax pass of the next batch of groups, so
 // one launch quantizes batch b while reading batch b + 1 for its amax.
-template <int FMT, int PLANE, bool WY, int SSRC>
+//
+// PACK (NVFP4): the tile holds whole groups (see TileMap). SSRC 0: S of each
+// group from gin; SSRC 2: from the group's own amax, reduced inside the
+// workgroup, so the input is read once; {S, A} go to gout. The block factors
+// are computed per block instead of from a table.
+template <int FMT, int PLANE, bool WY, int SSRC, bool PACK>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
-  __shared__ float2 lut[128];
+  __shared__ float2 lut[PACK ? 1 : 128];
   __shared__ uint32_t red[kThreads / 64];
+  __shared__ float gs[PACK ? kPackGroups : 1];                  // S of the tile's groups
+  __shared__ uint32_t ga[PACK && SSRC == 2 ? kPackGroups : 1];  // their amax (bf16 bits)
   if constexpr (SSRC == 1) {
     if ((int64_t)blockIdx.x >= a.qblocks) {
       amax_body(a.side, (int64_t)blockIdx.x - a.qblocks, red);
@@ -489,18 +517,57 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
     }
   }
   int64_t g, tbase;
-  tile_of(a.map, g, tbase);
-  g += a.g0;
-  const int64_t gbase = g * a.map.upg;
+  if constexpr (PACK) {
+    g = 0;
+    tbase = (int64_t)blockIdx.x * kTileUnits;
+  } else {
+    tile_of(a.map, g, tbase);
+    g += a.g0;
+  }
+  const int64_t gbase = PACK ? 0 : g * a.map.upg;
+  const int64_t lim = PACK ? a.map.units : a.map.upg;
   // Issue the tile's loads first; the scale and its factor table follow.
   uint4 v[kUPT];
 #pragma unroll
   for (int j = 0; j < kUPT; ++j) {
     const int64_t u = tbase + j * kThreads + threadIdx.x;
-    v[j] = u < a.map.upg ? a.x[gbase + u] : make_uint4(0u, 0u, 0u, 0u);
+    v[j] = u < lim ? a.x[gbase + u] : make_uint4(0u, 0u, 0u, 0u);
   }
   float S = 1.0f;
-  if constexpr (FMT == 0) {
+  if constexpr (PACK) {
+    const int lg = a.map.lg;
+    const int64_t g0t = tbase >> lg;                 // first group of the tile
+    const int gpt = kTileUnits >> lg;                // groups per tile
+    if constexpr (SSRC == 2) {
+      for (int i = threadIdx.x; i < gpt; i += kThreads) ga[i] = 0u;
+      __syncthreads();
+      // Segments of min(upg, 64) lanes hold one group's units for a given j.
+      const int w = lg < 6 ? 1 << lg : 64;
+#pragma unroll
+      for (int j = 0; j < kUPT; ++j) {
+        uint32_t bm = unit_amax_bits(v[j]);          // units past the end read as zero
+        for (int off = w >> 1; off > 0; off >>= 1) bm = max(bm, (uint32_t)__shfl_xor((int)bm, off));
+        if ((threadIdx.x & (w - 1)) == 0 && bm != 0u) atomicMax(&ga[(j * kThreads + threadIdx.x) >> lg], bm);
+      }
+      __syncthreads();
+      for (int i = threadIdx.x; i < gpt; i += kThreads) {
+        const float A = __uint_as_float(ga[i] << 16);
+        const float Sg = global_scale(A);
+        gs[i] = Sg;
+        const int64_t gg = g0t + i;
+        if (gg < a.map.groups) {
+          a.gout[2 * gg] = Sg;
+          a.gout[2 * gg + 1] = A;
+        }
+      }
+    } else {
+      for (int i = threadIdx.x; i < gpt; i += kThreads) {
+        const int64_t gg = g0t + i;
+        gs[i] = gg < a.map.groups ? a.gin[2 * gg] : 1.0f;
+      }
+    }
+    __syncthreads();
+  } else if constexpr (FMT == 0) {
     if constexpr (SSRC == 1) {
       uint32_t m = 0;
       for (int i = threadIdx.x; i < a.nparts; i += kThreads) m = max(m, a.part[g * kPartMax + i]);
@@ -528,7 +595,11 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
     if constexpr (FMT == 1) bm = max(bm, xor2(bm));
     float r, d = 0.0f, dsc = 0.0f;
     uint32_t sb;
-    if constexpr (FMT == 0) {
+    if constexpr (PACK) {
+      const float Sg = gs[(j * kThreads + threadIdx.x) >> a.map.lg];
+      sb = nv_scale_byte(bm, Sg);
+      nv_factors(sb, Sg, r, d);
+    } else if constexpr (FMT == 0) {
       sb = nv_scale_byte(bm, S);
       const float2 rd = lut[sb & 0x7Fu];
       r = rd.x;
@@ -543,7 +614,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) f[i] *= r;
     const uint32_t K = rtn_codes(f);
-    if (u < a.map.upg) {
+    if (u < lim) {
       const int64_t gu = gbase + u;
       if constexpr (PLANE == 4) {
         reinterpret_cast<uint32_t*>(a.plane)[gu] = K;
@@ -572,16 +643,23 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
 // alone (DECODE: reference codes, no y), and the fused discrepancy sums
 // (STATS: SB = sum (x_t - x_r)^2 over the inputs; SF = sum (y_t - y_r)^2 with
 // y_r the rollout's RTN output under the same scales, recomputed from x_r).
-template <int FMT, int BITS, bool DECODE, bool WCODES, bool STATS, bool DIAG>
+template <int FMT, int BITS, bool DECODE, bool WCODES, bool STATS, bool DIAG, bool PACK>
 __global__ __launch_bounds__(kThreads) void guided_kernel(GuidedArgs a) {
-  __shared__ float2 lut[128];
+  __shared__ float2 lut[PACK ? 1 : 128];
+  __shared__ float gs[PACK ? kPackGroups : 1];     // S of the tile's groups (packed)
   __shared__ uint32_t hist[DIAG ? kMismatchCounts : 1];
   int64_t g, tbase;
-  tile_of(a.map, g, tbase);
+  if constexpr (PACK) {
+    g = 0;
+    tbase = (int64_t)blockIdx.x * kTileUnits;
+  } else {
+    tile_of(a.map, g, tbase);
+  }
   if constexpr (DIAG) {
     if (threadIdx.x < kMismatchCounts) hist[threadIdx.x] = 0u;
   }
-  const int64_t gbase = g * a.map.upg;
+  const int64_t gbase = PACK ? 0 : g * a.map.upg;
+  const int64_t lim = PACK ? a.map.units : a.map.upg;
   // Issue the tile's loads first; the factor table is built while they fly.
   uint4 v[kUPT];
   uint4 vr[STATS ? kUPT : 1];
@@ -589,7 +667,7 @@ __global__ __launch_bounds__(kThreads) void guided_kernel(GuidedArgs a) {
 #pragma unroll
   for (int j = 0; j < kUPT; ++j) {
     const int64_t u = tbase + j * kThreads + threadIdx.x;
-    const bool ok = u < a.map.upg;
+    const bool ok = u < lim;
     const int64_t gu = gbase + u;
     v[j] = ok ? a.x[gu] : make_uint4(0u, 0u, 0u, 0u);
     if constexpr (STATS) vr[j] = ok ? a.xr[gu] : make_uint4(0u, 0u, 0u, 0u);
@@ -607,14 +685,24 @@ __global__ __launch_bounds__(kThreads) void guided_kernel(GuidedArgs a) {
       gv[j] = 0u;
     }
   }
-  if constexpr (FMT == 0) build_factor_lut(lut, a.gscale[2 * g]);
+  if constexpr (PACK) {
+    const int64_t g0t = tbase >> a.map.lg;
+    for (int i = threadIdx.x; i < (kTileUnits >> a.map.lg); i += kThreads) {
+      const int64_t gg = g0t + i;
+      gs[i] = gg < a.map.groups ? a.gscale[2 * gg] : 1.0f;
+    }
+  } else if constexpr (FMT == 0) {
+    build_factor_lut(lut, a.gscale[2 * g]);
+  }
   if constexpr (FMT == 0 || DIAG) __syncthreads();
   double acc_b = 0.0, acc_f = 0.0;
 #pragma unroll
   for (int j = 0; j < kUPT; ++j) {
     const int64_t u = tbase + j * kThreads + threadIdx.x;
     float r, d = 0.0f, dsc = 0.0f;
-    if constexpr (FMT == 0) {
+    if constexpr (PACK) {
+      nv_factors(sbv[j], gs[(j * kThreads + threadIdx.x) >> a.map.lg], r, d);
+    } else if constexpr (FMT == 0) {
       const float2 rd = lut[sbv[j] & 0x7Fu];
       r = rd.x;
       d = rd.y;
@@ -645,10 +733,10 @@ __global__ __launch_bounds__(kThreads) void guided_kernel(GuidedArgs a) {
       }
       if constexpr (DIAG) {
         const uint32_t K0 = BITS == 0 ? K : rtn_codes(t);
-        if (u < a.map.upg && (K != KR || K0 != KR)) mismatch_unit(K, KR, K0, hist);
+        if (u < lim && (K != KR || K0 != KR)) mismatch_unit(K, KR, K0, hist);
       }
     }
-    if (u < a.map.upg) {
+    if (u < lim) {
       const int64_t gu = gbase + u;
       if constexpr (DECODE || WCODES) a.codes[gu] = K;
       if constexpr (!DECODE) a.y[gu] = yv;
@@ -665,7 +753,7 @@ __global__ __launch_bounds__(kThreads) void guided_kernel(GuidedArgs a) {
     __syncthreads();
     if (threadIdx.x < kMismatchCounts) {
       // Distance 0 (bins 0 and 15) is the rest of the tile's elements.
-      const int64_t valid = min((int64_t)kTileUnits, a.map.upg - tbase) * kUnitElems;
+      const int64_t valid = min((int64_t)kTileUnits, lim - tbase) * kUnitElems;
       const int b = threadIdx.x;
       uint32_t hv = hist[b];
       if (b == 0 || b == kMismatchBins) {
@@ -798,14 +886,35 @@ hipError_t launch(void (*k)(P...), dim3 grid, dim3 block, hipStream_t s, A... ar
   return hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, argv, 0, s);
 }
 
-TileMap tile_map(const Shape& sh) {
-  TileMap m;
+// MXFP4 has no global scale, so a call's groups are one tensor to it.
+Shape effective(int fmt, const Shape& sh) {
+  if (fmt == 1 && sh.groups > 1) return Shape{1, sh.groups * sh.upg};
+  return sh;
+}
+
+// NVFP4 groups whose unit count is a power of two below a tile are packed
+// several to a tile (and their encode reads the input once).
+bool packable(int fmt, const Shape& sh) {
+  return fmt == 0 && sh.groups > 1 && sh.upg > 0 && sh.upg < kTileUnits && kTileUnits % sh.upg == 0;
+}
+
+TileMap tile_map(int fmt, const Shape& sh0) {
+  const Shape sh = effective(fmt, sh0);
+  TileMap m{};
   m.upg = sh.upg;
-  m.tiles = (sh.upg + kTileUnits - 1) / kTileUnits;
+  m.units = sh.groups * sh.upg;
+  m.groups = sh.groups;
+  if (packable(fmt, sh)) {
+    m.tiles = (m.units + kTileUnits - 1) / kTileUnits;
+    m.lg = __builtin_ctzll((unsigned long long)sh.upg);
+    m.packed = 1;
+  } else {
+    m.tiles = (sh.upg + kTileUnits - 1) / kTileUnits;
+  }
   return m;
 }
 
-unsigned tile_grid(const Shape& sh) { return (unsigned)(sh.groups * tile_map(sh).tiles); }
+int64_t tile_grid(const TileMap& m) { return m.packed ? m.tiles : m.groups * m.tiles; }
 
 std::atomic<int64_t> g_encode_batch{0};   // groups per batch; 0 = sized for the Infinity Cache
 constexpr int64_t kCacheBatchBytes = (int64_t)96 << 20;
@@ -817,78 +926,87 @@ int amax_parts(int64_t upg) {
   return (int)p;
 }
 
-template <int FMT, int PLANE, bool WY, int SSRC>
+template <int FMT, int PLANE, bool WY, int SSRC, bool PACK>
 hipError_t quant_go(const QuantArgs& a, int64_t blocks, hipStream_t s) {
-  return launch(quantize_kernel<FMT, PLANE, WY, SSRC>, dim3((unsigned)blocks), dim3(kThreads), s, a);
+  return launch(quantize_kernel<FMT, PLANE, WY, SSRC, PACK>, dim3((unsigned)blocks), dim3(kThreads), s, a);
 }
 
 // `blocks`: the launch's workgroups (quantize tiles, then side amax work).
-template <int FMT, int PLANE>
-hipError_t quant_wy(bool wy, int ssrc, const QuantArgs& a, int64_t blocks, hipStream_t s) {
+// ssrc: 0 S given, 1 S from amax partials, 2 S from the tile's own groups (packed).
+template <int FMT, int PLANE, bool WY>
+hipError_t quant_src(int ssrc, bool pack, const QuantArgs& a, int64_t blocks, hipStream_t s) {
   if constexpr (FMT == 1) {
-    return wy ? quant_go<1, PLANE, true, 0>(a, blocks, s) : quant_go<1, PLANE, false, 0>(a, blocks, s);
+    return quant_go<1, PLANE, WY, 0, false>(a, blocks, s);
   } else {
-    if (wy) return ssrc ? quant_go<0, PLANE, true, 1>(a, blocks, s) : quant_go<0, PLANE, true, 0>(a, blocks, s);
-    return ssrc ? quant_go<0, PLANE, false, 1>(a, blocks, s) : quant_go<0, PLANE, false, 0>(a, blocks, s);
+    if (pack) return ssrc ? quant_go<0, PLANE, WY, 2, true>(a, blocks, s)
+                          : quant_go<0, PLANE, WY, 0, true>(a, blocks, s);
+    return ssrc ? quant_go<0, PLANE, WY, 1, false>(a, blocks, s)
+                : quant_go<0, PLANE, WY, 0, false>(a, blocks, s);
   }
+}
+
+template <int FMT, int PLANE>
+hipError_t quant_wy(bool wy, int ssrc, bool pack, const QuantArgs& a, int64_t blocks, hipStream_t s) {
+  return wy ? quant_src<FMT, PLANE, true>(ssrc, pack, a, blocks, s)
+            : quant_src<FMT, PLANE, false>(ssrc, pack, a, blocks, s);
 }
 
 // plane_mode = bits of the guidance plane (1..4; quantize_rtn writes codes, 4).
 template <int FMT>
-hipError_t quant_plane(int plane_mode, bool wy, int ssrc, const QuantArgs& a, int64_t blocks,
-                       hipStream_t s) {
+hipError_t quant_plane(int plane_mode, bool wy, int ssrc, bool pack, const QuantArgs& a,
+                       int64_t blocks, hipStream_t s) {
   switch (plane_mode) {
-    case 1: return quant_wy<FMT, 1>(wy, ssrc, a, blocks, s);
-    case 2: return quant_wy<FMT, 2>(wy, ssrc, a, blocks, s);
-    case 3: return quant_wy<FMT, 3>(wy, ssrc, a, blocks, s);
-    default: return quant_wy<FMT, 4>(wy, ssrc, a, blocks, s);
+    case 1: return quant_wy<FMT, 1>(wy, ssrc, pack, a, blocks, s);
+    case 2: return quant_wy<FMT, 2>(wy, ssrc, pack, a, blocks, s);
+    case 3: return quant_wy<FMT, 3>(wy, ssrc, pack, a, blocks, s);
+    default: return quant_wy<FMT, 4>(wy, ssrc, pack, a, blocks, s);
   }
 }
 
-template <int FMT, int BITS, bool DECODE, bool WCODES, bool STATS, bool DIAG>
-hipError_t guided_go(const GuidedArgs& a, const Shape& sh, hipStream_t s) {
-  return launch(guided_kernel<FMT, BITS, DECODE, WCODES, STATS, DIAG>, dim3(tile_grid(sh)),
-                dim3(kThreads), s, a);
+template <int FMT, int BITS, bool DECODE, bool WCODES, bool STATS, bool DIAG, bool PACK>
+hipError_t guided_go(const GuidedArgs& a, hipStream_t s) {
+  return launch(guided_kernel<FMT, BITS, DECODE, WCODES, STATS, DIAG, PACK>,
+                dim3((unsigned)tile_grid(a.map)), dim3(kThreads), s, a);
 }
 
-template <int FMT, int BITS>
-hipError_t guided_bits(bool wc, bool stats, bool diag, const GuidedArgs& a, const Shape& sh,
+template <int FMT, int BITS, bool PACK>
+hipError_t guided_bits(bool wc, bool stats, bool diag, const GuidedArgs& a, hipStream_t s) {
+  if (diag) return wc ? guided_go<FMT, BITS, false, true, true, true, PACK>(a, s)
+                      : guided_go<FMT, BITS, false, false, true, true, PACK>(a, s);
+  if (stats) return wc ? guided_go<FMT, BITS, false, true, true, false, PACK>(a, s)
+                       : guided_go<FMT, BITS, false, false, true, false, PACK>(a, s);
+  return wc ? guided_go<FMT, BITS, false, true, false, false, PACK>(a, s)
+            : guided_go<FMT, BITS, false, false, false, false, PACK>(a, s);
+}
+
+template <int FMT, bool PACK>
+hipError_t guided_pack(int bits, bool decode, bool wc, bool stats, bool diag, const GuidedArgs& a,
                        hipStream_t s) {
-  if (diag) return wc ? guided_go<FMT, BITS, false, true, true, true>(a, sh, s)
-                      : guided_go<FMT, BITS, false, false, true, true>(a, sh, s);
-  if (stats) return wc ? guided_go<FMT, BITS, false, true, true, false>(a, sh, s)
-                       : guided_go<FMT, BITS, false, false, true, false>(a, sh, s);
-  return wc ? guided_go<FMT, BITS, false, true, false, false>(a, sh, s)
-            : guided_go<FMT, BITS, false, false, false, false>(a, sh, s);
-}
-
-template <int FMT>
-hipError_t guided_fmt(int bits, bool decode, bool wc, bool stats, bool diag, const GuidedArgs& a,
-                      const Shape& sh, hipStream_t s) {
   if (decode) {
     switch (bits) {
-      case 1: return guided_go<FMT, 1, true, true, false, false>(a, sh, s);
-      case 2: return guided_go<FMT, 2, true, true, false, false>(a, sh, s);
-      default: return guided_go<FMT, 3, true, true, false, false>(a, sh, s);
+      case 1: return guided_go<FMT, 1, true, true, false, false, PACK>(a, s);
+      case 2: return guided_go<FMT, 2, true, true, false, false, PACK>(a, s);
+      default: return guided_go<FMT, 3, true, true, false, false, PACK>(a, s);
     }
   }
   switch (bits) {
-    case 0: return guided_bits<FMT, 0>(wc, stats, diag, a, sh, s);
-    case 1: return guided_bits<FMT, 1>(wc, stats, diag, a, sh, s);
-    case 2: return guided_bits<FMT, 2>(wc, stats, diag, a, sh, s);
-    case 3: return guided_bits<FMT, 3>(wc, stats, diag, a, sh, s);
-    default: return guided_bits<FMT, 4>(wc, stats, diag, a, sh, s);
+    case 0: return guided_bits<FMT, 0, PACK>(wc, stats, diag, a, s);
+    case 1: return guided_bits<FMT, 1, PACK>(wc, stats, diag, a, s);
+    case 2: return guided_bits<FMT, 2, PACK>(wc, stats, diag, a, s);
+    case 3: return guided_bits<FMT, 3, PACK>(wc, stats, diag, a, s);
+    default: return guided_bits<FMT, 4, PACK>(wc, stats, diag, a, s);
   }
 }
 
 }  // namespace
 
-int64_t quant_work_bytes(const Shape& sh) {
+int64_t quant_work_bytes(int fmt, const Shape& sh) {
+  if (fmt != 0 || packable(fmt, sh)) return 0;
   return sh.groups * (int64_t)kPartMax * (int64_t)sizeof(uint32_t);
 }
 
-int64_t guided_stats_work_bytes(const Shape& sh) {
-  const int64_t tiles = (int64_t)tile_grid(sh);
+int64_t guided_stats_work_bytes(int fmt, const Shape& sh) {
+  const int64_t tiles = tile_grid(tile_map(fmt, sh));
   return 2 * (int64_t)sizeof(double) * (tiles + kMidGroups) +
          (int64_t)sizeof(uint32_t) * kMismatchCounts * tiles;
 }
@@ -913,7 +1031,7 @@ hipError_t launch_quantize(int fmt, int plane_mode, const Shape& sh, const uint1
                   sh.groups);
   }
   QuantArgs a{};
-  a.map = tile_map(sh);
+  a.map = tile_map(fmt, sh);
   a.x = reinterpret_cast<const uint4*>(x);
   a.gin = gin;
   a.gout = gout;
@@ -921,10 +1039,14 @@ hipError_t launch_quantize(int fmt, int plane_mode, const Shape& sh, const uint1
   a.scales = scales;
   a.y = reinterpret_cast<uint4*>(y);
   const bool wy = y != nullptr;
+  if (a.map.packed) {  // one pass: every group's amax is reduced inside its tile
+    a.qblocks = a.map.tiles;
+    return quant_plane<0>(plane_mode, wy, gout != nullptr ? 2 : 0, true, a, a.qblocks, stream);
+  }
   if (fmt == 1 || gout == nullptr) {
-    a.qblocks = (int64_t)tile_grid(sh);
-    if (fmt == 0) return quant_plane<0>(plane_mode, wy, 0, a, a.qblocks, stream);
-    return quant_plane<1>(plane_mode, wy, 0, a, a.qblocks, stream);
+    a.qblocks = tile_grid(a.map);
+    if (fmt == 0) return quant_plane<0>(plane_mode, wy, 0, false, a, a.qblocks, stream);
+    return quant_plane<1>(plane_mode, wy, 0, false, a, a.qblocks, stream);
   }
   // NVFP4 with S from the amax: the input is read twice (amax, then
   // quantize). Groups go in batches of about kCacheBatchBytes of input, and
@@ -955,7 +1077,7 @@ hipError_t launch_quantize(int fmt, int plane_mode, const Shape& sh, const uint1
     a.side = m;
     a.side.g0 = g0 + nq;
     const int64_t blocks = a.qblocks + na * m.nparts;
-    e = quant_plane<0>(plane_mode, wy, 1, a, blocks, stream);
+    e = quant_plane<0>(plane_mode, wy, 1, false, a, blocks, stream);
   }
   return e;
 }
@@ -976,7 +1098,7 @@ hipError_t launch_guided(int fmt, int bits, bool decode_only, const Shape& sh, c
                   (const uint32_t*)nullptr, (int64_t)0, counts, accumulate);
   }
   GuidedArgs a{};
-  a.map = tile_map(sh);
+  a.map = tile_map(fmt, sh);
   a.x = reinterpret_cast<const uint4*>(x);
   a.guide = guide;
   a.scales = scales;
@@ -985,11 +1107,13 @@ hipError_t launch_guided(int fmt, int bits, bool decode_only, const Shape& sh, c
   a.codes = reinterpret_cast<uint32_t*>(codes);
   a.xr = reinterpret_cast<const uint4*>(xr);
   a.partials = static_cast<double*>(work);
-  const int64_t tiles = tile_grid(sh);
+  const int64_t tiles = tile_grid(a.map);
   if (stats) a.cpart = reinterpret_cast<uint32_t*>(a.partials + 2 * (tiles + kMidGroups));
   const bool wc = codes != nullptr;
-  hipError_t e = fmt == 0 ? guided_fmt<0>(bits, decode_only, wc, stats, diag, a, sh, stream)
-                          : guided_fmt<1>(bits, decode_only, wc, stats, diag, a, sh, stream);
+  hipError_t e;
+  if (fmt == 1) e = guided_pack<1, false>(bits, decode_only, wc, stats, diag, a, stream);
+  else if (a.map.packed) e = guided_pack<0, true>(bits, decode_only, wc, stats, diag, a, stream);
+  else e = guided_pack<0, false>(bits, decode_only, wc, stats, diag, a, stream);
   if (e != hipSuccess || !stats) return e;
   if (diag) {
     e = launch(counts_final_kernel, dim3(kMismatchCounts), dim3(kThreads), stream,

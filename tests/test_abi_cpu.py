@@ -77,6 +77,16 @@ def test_workspace_sizes(lib):
     assert lib.trace_quant_workspace_bytes(3, 4, 32, 0) == -1           # bad format
     # two float64 partial sums per workgroup tile of 2048 units (16384 elements),
     # plus 64 pairs for the first level of the reduction
+    # packed groups (power-of-two units below a tile, G > 1) need no amax workspace
+    assert lib.trace_quant_workspace_bytes(0, 8, 32, 4) == 0           # 2 groups of 16 units
+    assert lib.trace_quant_workspace_bytes(0, 139264, 2048, 1) == 0    # per-token scales
+    assert lib.trace_quant_workspace_bytes(0, 6, 32, 3) == 2 * 4096    # 12 units: not a power of two
+    assert lib.trace_quant_workspace_bytes(0, 16, 2048, 8) == 2 * 4096  # 2048 units: a whole tile
+    assert lib.trace_quant_workspace_bytes(1, 16, 2048, 8) == 0
+    # per-token: 139264 rows x 256 units packed 8 to a tile
+    assert lib.trace_guided_stats_workspace_bytes(0, 139264, 2048, 1) == 16 * (17408 + 64) + 128 * 17408
+    # MXFP4 groups merge into one tensor: 4 groups of 300 units -> 1 tile
+    assert lib.trace_guided_stats_workspace_bytes(1, 4 * 75, 32, 75) == 16 * (1 + 64) + 128
     # 16 bytes of sums per tile + 64 second-level pairs, 32 uint32 counts per tile
     assert lib.trace_guided_stats_workspace_bytes(0, 4, 32, 0) == 16 * (1 + 64) + 128
     assert lib.trace_guided_stats_workspace_bytes(0, 17 * 8192, 2048, 8192) == \
@@ -104,7 +114,7 @@ WB = 4096               # quantize workspace bytes for one group
     ((0, 4, 32, 0, A, None, None, C, D, None, W, WB, None), _abi.EINVAL),       # NULL codes
     ((0, 4, 32, 0, A, None, B, C, D, None, None, WB, None), _abi.EINVAL),       # amax needs work
     ((0, 4, 32, 0, A, None, B, C, D, None, W, WB - 4, None), _abi.ESHAPE),      # work too small
-    ((0, 8, 32, 4, A, None, B, C, D, None, W, WB, None), _abi.ESHAPE),          # 2 groups need 2*WB
+    ((0, 6, 32, 3, A, None, B, C, D, None, W, WB, None), _abi.ESHAPE),          # 2 groups need 2*WB
     ((0, 4, 32, 0, A + 8, None, B, C, D, None, W, WB, None), _abi.EALIGN),      # x not 16-B aligned
     ((0, 4, 32, 0, A, None, B + 2, C, D, None, W, WB, None), _abi.EALIGN),      # codes not 4-B aligned
     ((0, 4, 32, 0, A, None, B, C, D, None, W + 4, WB, None), _abi.EALIGN),      # work not 8-B aligned

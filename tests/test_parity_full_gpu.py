@@ -120,6 +120,45 @@ def test_stream_layer_bench_configuration():
     assert G.rel_close(a[1], ref[1]) and G.rel_close(a[0], ref[0])
 
 
+def test_stream_layer_per_token_scales():
+    """One streamed layer, 139,264 x 2048, with a global scale per token
+    (group_rows = 1, the packed single-pass encode): every row's S against
+    the oracle's amax of that row, sampled rows block by block, fused sums
+    and mismatch counts against sums and counts over the library's outputs."""
+    G.say("full size: streamed layer, per-token global scales")
+    layer, chunks, CH = 20, 17, syn.STREAM_CHUNK
+    dev = G.DEV
+    sigma = syn.stream_sigma(layer, dev)
+    xt = torch.empty((chunks * CH, syn.HIDDEN), dtype=torch.bfloat16, device=dev)
+    xr = torch.empty_like(xt)
+    for c in range(chunks):
+        a, b = syn.stream_pair(layer, c, dev, sigma=sigma)
+        xt[c * CH:(c + 1) * CH].copy_(a)
+        xr[c * CH:(c + 1) * CH].copy_(b)
+    rows, cols = xt.shape
+    g = tq.encode_guidance(xr, NV, 1, with_y=True, group_rows=1)
+    y, codes, acc, counts = tq.guided_fake_quant_stats(xt, xr, g, with_codes=True, mismatch=True)
+    torch.cuda.synchronize()
+    # every row's global scale
+    amax_bits = (xr.view(torch.int16) & 0x7FFF).amax(dim=1).cpu().numpy().astype(np.uint16)
+    A = ofp4.bf16_to_f32(amax_bits)
+    S = np.array([ofp4.nvfp4_global_scale(a) for a in A], np.float32)
+    gs = G.f32(g.gscale).reshape(rows, 2)
+    G.assert_same(gs[:, 1], A, "per-token A")
+    G.assert_same(gs[:, 0], S, "per-token S")
+    xt_b, xr_b = _bits(xt), _bits(xr)
+    for r0, r1 in _samples(rows, span=24):
+        for r in range(r0, r1):
+            _check_rows(NV, 1, xt_b, xr_b, cols, r, r + 1, S[r], g, y_g=y, codes_g=codes, y_r=g.y)
+    ref = tq.discrepancy_stats(xt.view(-1), xr.view(-1), y.view(-1), g.y.view(-1)).cpu().numpy()
+    a = acc.cpu().numpy()
+    assert a[2] == ref[2] and G.rel_close(a[0], ref[0]) and G.rel_close(a[1], ref[1])
+    g4 = tq.encode_guidance(xr, NV, 4, group_rows=1)
+    _, codes_rtn = tq.guided_fake_quant(xt, g, bits=0, with_codes=True)
+    G.assert_same(counts.cpu().numpy(), G.torch_mismatch_counts(codes, g4.guide, codes_rtn),
+                  "mismatch counts, per-token scales")
+
+
 @pytest.mark.parametrize("bits", [0, 1, 2, 3, 4])
 def test_moe_layer_full_size(bits):
     """Routed-expert inputs of one MoE layer: 65,536 permuted rows x 2048,
