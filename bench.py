@@ -82,6 +82,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the plain guided_fake_quant timing")
     ap.add_argument("--no-diag", action="store_true", help="skip the mismatch-diagnostics pass")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the record-width and per-token-scale timings")
     ap.add_argument("--encode-batch", type=int, default=-1,
                     help="groups per batch of the two-pass NVFP4 encode (library default if < 0)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -141,6 +143,30 @@ def build_phases(lib, w, stream, qwork, swork):
     return step, extra, diag
 
 
+def variant_phases(lib, w, stream, qwork, torch, dev):
+    """Record widths 2, 3 and 4 (chunk scales) and the 1-bit record with one
+    global scale per token: (name, bytes/elem of encode, of guided, phases)."""
+    qb = qwork.numel() * qwork.element_size()
+    guide = torch.empty((w.layers, w.rows, HIDDEN // 2), dtype=torch.uint8, device=dev)
+    gtok = torch.empty((w.layers, w.rows, 2), dtype=torch.float32, device=dev)
+    out = []
+    for name, bits, gr in (("bits2", 2, CHUNK), ("bits3", 3, CHUNK), ("bits4", 4, CHUNK),
+                           ("bits1_per_token", 1, 1)):
+        gs = w.gscale if gr == CHUNK else gtok
+        enc, gfq = [], []
+        for i in range(w.layers):
+            p = lambda t: t[i].data_ptr()  # noqa: E731
+            enc.append((NV, bits, w.rows, HIDDEN, gr, p(w.xr), None, p(guide), p(w.scales), p(gs),
+                        None, qwork.data_ptr(), qb, stream))
+            gfq.append((NV, bits, w.rows, HIDDEN, gr, p(w.xt), p(guide), p(w.scales), p(gs), p(w.yt),
+                        None, stream))
+        gbytes = 8 / (gr * HIDDEN)                     # {S, A} per group
+        out.append((name, 2 + bits / 8 + 1 / 16 + gbytes, 2 + bits / 8 + 1 / 16 + 4 / (gr * HIDDEN) + 2,
+                    [("encode_guidance", lib.encode_guidance, enc),
+                     ("guided_fake_quant", lib.guided_fake_quant, gfq)]))
+    return out, (guide, gtok)
+
+
 def mismatch_report(counts):
     """Fig. 6-style summary of the per-layer mismatch counts: how often RTN
     under the rollout scales misses the rollout code, how many of those misses
@@ -186,11 +212,11 @@ def timed(torch, phases, steps):
     return wall, per
 
 
-def kernel_entry(name, ms_list, calls, n):
+def kernel_entry(name, ms_list, calls, n, bpe=None):
     steps = len(ms_list)
     ms = sum(ms_list)
     per_call_us = ms * 1e3 / (steps * calls)
-    algo = BPE[name] * n
+    algo = (BPE[name] if bpe is None else bpe) * n
     gbs = algo / (per_call_us * 1e-6) / 1e9
     return {"avg_us_per_call": round(per_call_us, 2), "calls_per_pass": calls,
             "elements_per_call": n, "algorithmic_bytes_per_call": int(algo),
@@ -336,6 +362,22 @@ def main():
         mismatch = mismatch_report(w.counts.cpu().tolist())
         log("bench: mismatch diagnostics done")
 
+    variants = None
+    if not args.no_variants:
+        # The record widths of Algorithm 1's parameter b and per-token scales,
+        # timed per call like the step, outside it.
+        variants = {}
+        vph, keep = variant_phases(lib, w, stream.cuda_stream, qwork, torch, dev)
+        for name, bpe_e, bpe_g, phases in vph:
+            run_phases(phases)
+            _, per_v = timed(torch, phases, max(3, args.steps // 4))
+            variants[name] = {
+                "encode_guidance": kernel_entry("encode_guidance", per_v[0], len(phases[0][2]), w.n, bpe_e),
+                "guided_fake_quant": kernel_entry("guided_fake_quant", per_v[1], len(phases[1][2]), w.n,
+                                                  bpe_g)}
+        del keep
+        log("bench: variants timed")
+
     elems_step = w.layers * w.n
     ms_step = wall * 1e3 / args.steps
     dom = max((k for k, _, _ in step), key=lambda k: kernels[k]["phase_ms_per_pass"])
@@ -387,6 +429,7 @@ def main():
         "step_GB_s": round(sum(BPE[k] for k, _, _ in step) * elems_step / (ms_step * 1e-3) / 1e9, 1),
         "rel_excess_mse_guided_per_layer": [round(r, 6) for r in rel],
         "mismatch": mismatch,
+        "variants": variants,
     }
     print(json.dumps(out), flush=True)
 
