@@ -24,6 +24,7 @@ Modules:
     fp4      the method: scales, RTN, guidance encode/decode, guided rounding,
              discrepancy sums
     sizes    the guidance-size arithmetic of §3.2 and §4.2
+    record   the page gather that collects a request's records
 
 Pins (tests marked ``not gpu``) tie every function here to something other
 than itself: values the paper prints, library casts (torch bf16 / float8),
