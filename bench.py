@@ -82,6 +82,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the plain guided_fake_quant timing")
     ap.add_argument("--no-diag", action="store_true", help="skip the mismatch-diagnostics pass")
+    ap.add_argument("--no-record", action="store_true", help="skip the record-path timings")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the record-width and per-token-scale timings")
     ap.add_argument("--encode-batch", type=int, default=-1,
@@ -165,6 +166,77 @@ def variant_phases(lib, w, stream, qwork, torch, dev):
                     [("encode_guidance", lib.encode_guidance, enc),
                      ("guided_fake_quant", lib.guided_fake_quant, gfq)]))
     return out, (guide, gtok)
+
+
+def record_path(torch, w, step, stream, dev, layers):
+    """Device-to-host transfer of each layer's compact record (mantissa-bit
+    plane, scales, chunk scales) through the pinned ring: alone, and pushed
+    right after each layer's encode while the step runs. Plus the gather of a
+    request's pages of an FP4 KV code plane."""
+    from precision_rl_nvfp4_amd.record import RecordRing, gather_pages
+
+    planes = [[w.guide[i], w.scales[i], w.gscale[i]] for i in range(layers)]
+    rec_bytes = sum(t.numel() * t.element_size() for t in planes[0])
+    depth = 4
+    out = {"bytes_per_layer": rec_bytes, "layers": layers, "ring_slots": depth}
+    with RecordRing(rec_bytes, depth) as ring:
+        def drain(pending, keep):
+            while len(pending) > keep:
+                s0 = pending.pop(0)
+                ring.wait(s0)
+                ring.release(s0)
+
+        for rep in range(2):                           # the first pass warms the path
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            pending = []
+            for i in range(layers):
+                drain(pending, depth - 1)
+                pending.append(ring.push(planes[i], stream=stream))
+            drain(pending, 0)
+            alone = time.perf_counter() - t0
+        out["d2h_GB_s"] = round(layers * rec_bytes / alone / 1e9, 2)
+
+        enc, gst = step[0][2], step[1][2]
+        for rep in range(2):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            pending = []
+            for i in range(layers):
+                st = step[0][1](*enc[i])
+                if st != 0:
+                    raise RuntimeError(f"encode_guidance returned {st}")
+                drain(pending, depth - 1)
+                pending.append(ring.push(planes[i], stream=stream))
+                st = step[1][1](*gst[i])
+                if st != 0:
+                    raise RuntimeError(f"guided_fake_quant_stats returned {st}")
+            torch.cuda.synchronize()
+            gpu_done = time.perf_counter() - t0
+            drain(pending, 0)
+            with_rec = time.perf_counter() - t0
+        out["step_ms_with_records"] = round(with_rec * 1e3, 3)
+        out["step_kernels_ms_with_records"] = round(gpu_done * 1e3, 3)
+
+    # FP4 KV cache: 4 KiB pages (16 tokens x 2 heads x 256 codes), a request
+    # owning 16,384 scattered pages of a 65,536-page pool.
+    page_bytes, npool, nreq = 4096, 65536, 16384
+    pool = torch.randint(0, 256, (npool * page_bytes,), dtype=torch.uint8, device=dev)
+    ids = torch.randperm(npool, device=dev)[:nreq].to(torch.int32)
+    outb = torch.empty(nreq * page_bytes, dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        gather_pages(pool, page_bytes, ids, out=outb)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        gather_pages(pool, page_bytes, ids, out=outb)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    out["kv_gather"] = {"bytes": nreq * page_bytes, "avg_us": round(us, 2),
+                        "GB_s": round(2 * nreq * page_bytes / (us * 1e-6) / 1e9, 1)}
+    return out
 
 
 def mismatch_report(counts):
@@ -378,6 +450,11 @@ def main():
         del keep
         log("bench: variants timed")
 
+    record = None
+    if not args.no_record:
+        record = record_path(torch, w, step, stream.cuda_stream, dev, w.layers)
+        log("bench: record path timed")
+
     elems_step = w.layers * w.n
     ms_step = wall * 1e3 / args.steps
     dom = max((k for k, _, _ in step), key=lambda k: kernels[k]["phase_ms_per_pass"])
@@ -430,6 +507,7 @@ def main():
         "rel_excess_mse_guided_per_layer": [round(r, 6) for r in rel],
         "mismatch": mismatch,
         "variants": variants,
+        "record_path": record,
     }
     print(json.dumps(out), flush=True)
 

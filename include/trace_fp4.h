@@ -88,7 +88,7 @@
 extern "C" {
 #endif
 
-#define TRACE_ABI_VERSION 4
+#define TRACE_ABI_VERSION 5
 
 /* Entries of the mismatch diagnostics of guided_fake_quant_stats. */
 #define TRACE_MISMATCH_COUNTS 32
@@ -103,7 +103,8 @@ enum trace_status {
   TRACE_EALIGN = -3,  /* a pointer misses its alignment */
   TRACE_EALIAS = -4,  /* an output overlaps an input or another output */
   TRACE_EDEVICE = -5, /* no current gfx950 device */
-  TRACE_ELAUNCH = -6  /* HIP reported an error when the kernels were enqueued */
+  TRACE_ELAUNCH = -6, /* HIP reported an error when the kernels were enqueued */
+  TRACE_EBUSY = -7    /* trace_ring_push: the next slot has not been released */
 };
 
 /* TRACE_ABI_VERSION of the built library. */
@@ -277,6 +278,75 @@ int guided_fake_quant_stats(int fmt, int bits, int64_t rows, int64_t cols, int64
 int discrepancy_stats(int64_t n, const uint16_t* x_t, const uint16_t* x_r,
                       const uint16_t* y_t, const uint16_t* y_r, double* acc3,
                       int accumulate, void* work, int64_t work_bytes, void* stream);
+
+/*
+ * Record path (paper §3.2 "Motivation": records are cached during generation
+ * and transferred to the training side; "Key Design": records are indexed by
+ * trajectory, token and site, and the KV guidance already sits in the FP4 KV
+ * cache). These calls move finished records off the GPU; the guidance calls
+ * above produce them.
+ *
+ * trace_ring — a ring of `slots` pinned host buffers of `slot_bytes` each,
+ * with its own copy stream (default priority) and one event per slot. Slots
+ * are used in ring order and cycle FREE -> IN FLIGHT (push) -> DONE (wait or
+ * query) -> FREE (release). A ring belongs to the device current at creation
+ * and is used from that device. Calls on one ring are thread-safe.
+ */
+typedef struct trace_ring trace_ring;
+
+/* Allocates the pinned slots (hipHostMalloc), the copy stream and the events.
+ * *ring receives the handle (NULL on error). ESHAPE: slot_bytes <= 0, slots
+ * outside [1, 4096] or more than 2^40 bytes in total; EDEVICE: the current
+ * device is not a gfx950; ELAUNCH: an allocation failed. */
+int trace_ring_create(int64_t slot_bytes, int32_t slots, trace_ring** ring);
+
+/* Waits for the ring's copies, then frees everything. */
+int trace_ring_destroy(trace_ring* ring);
+
+/* Copies n device buffers srcs[i] of bytes[i] bytes, back to back, into the
+ * next slot, after all work enqueued so far on after_stream (a hipStream_t,
+ * NULL = null stream); the producer stream is not blocked. *slot receives the
+ * slot index. ESHAPE: a negative size or more than slot_bytes in total;
+ * EBUSY: the next slot is still in flight or not released (nothing is
+ * enqueued); EDEVICE: called from another device. */
+int trace_ring_push(trace_ring* ring, const void* const* srcs, const int64_t* bytes, int32_t n,
+                    void* after_stream, int32_t* slot);
+
+/* Blocks until the slot's copies are done (slot becomes DONE). EINVAL for a
+ * FREE slot. */
+int trace_ring_wait(trace_ring* ring, int32_t slot);
+
+/* 1 when the slot's copies are done (slot becomes DONE), 0 when still in
+ * flight; EINVAL for a FREE slot. Never blocks. */
+int trace_ring_query(trace_ring* ring, int32_t slot);
+
+/* Host address of a DONE slot's bytes (valid until it is released) and, in
+ * *bytes (optional), how many were pushed; NULL when the slot is not DONE. */
+const void* trace_ring_slot(trace_ring* ring, int32_t slot, int64_t* bytes);
+
+/* Returns a DONE slot to the ring. EINVAL otherwise. */
+int trace_ring_release(trace_ring* ring, int32_t slot);
+
+/*
+ * trace_gather_pages — collects a finished request's pages of a paged record
+ * (for example the code or scale plane of the FP4 KV cache) into one
+ * contiguous buffer before its transfer: page i of out = page page_ids[i] of
+ * pool. An id outside [0, pool_pages) gives a page of zero bytes and adds 1 to
+ * *bad_ids (if given); the kernel never reads outside the pool.
+ *
+ *   pool       in   uint8[pool_pages * page_bytes]   device
+ *   page_ids   in   int32[n]                          device, 4-byte aligned
+ *   out        out  uint8[n * page_bytes]             device
+ *   bad_ids    in/out uint32 or NULL                  device, 4-byte aligned;
+ *                   incremented, never cleared
+ *
+ * Moves 16-byte words when page_bytes is a multiple of 16 and pool and out
+ * are 16-byte aligned, single bytes otherwise. ESHAPE: negative sizes,
+ * page_bytes <= 0, more than 2^46 bytes; EALIAS: out overlaps an input.
+ */
+int trace_gather_pages(const uint8_t* pool, int64_t pool_pages, int64_t page_bytes,
+                       const int32_t* page_ids, int64_t n, uint8_t* out, uint32_t* bad_ids,
+                       void* stream);
 
 #ifdef __cplusplus
 }

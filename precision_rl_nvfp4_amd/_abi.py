@@ -11,9 +11,9 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtrace_fp4.so")
 
-OK, EINVAL, ESHAPE, EALIGN, EALIAS, EDEVICE, ELAUNCH = 0, -1, -2, -3, -4, -5, -6
+OK, EINVAL, ESHAPE, EALIGN, EALIAS, EDEVICE, ELAUNCH, EBUSY = 0, -1, -2, -3, -4, -5, -6, -7
 NVFP4, MXFP4 = 0, 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 MISMATCH_COUNTS = 32
 
 _i64 = ctypes.c_int64
@@ -42,6 +42,17 @@ SIGNATURES = {
                                        _vp, _vp, _int, _vp, _i64, _vp]),
     # n, x_t, x_r, y_t, y_r, acc3, accumulate, work, work_bytes, stream
     "discrepancy_stats": (_int, [_i64, _vp, _vp, _vp, _vp, _vp, _int, _vp, _i64, _vp]),
+    # record path: slot_bytes, slots, &ring / ring / ring, srcs, bytes, n, stream, &slot / ...
+    "trace_ring_create": (_int, [_i64, ctypes.c_int32, ctypes.POINTER(_vp)]),
+    "trace_ring_destroy": (_int, [_vp]),
+    "trace_ring_push": (_int, [_vp, ctypes.POINTER(_vp), ctypes.POINTER(_i64), ctypes.c_int32, _vp,
+                               ctypes.POINTER(ctypes.c_int32)]),
+    "trace_ring_wait": (_int, [_vp, ctypes.c_int32]),
+    "trace_ring_query": (_int, [_vp, ctypes.c_int32]),
+    "trace_ring_slot": (_vp, [_vp, ctypes.c_int32, ctypes.POINTER(_i64)]),
+    "trace_ring_release": (_int, [_vp, ctypes.c_int32]),
+    # pool, pool_pages, page_bytes, page_ids, n, out, bad_ids, stream
+    "trace_gather_pages": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp]),
 }
 
 _lib = None

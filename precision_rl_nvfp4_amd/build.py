@@ -22,7 +22,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libtrace_fp4.so")
-SOURCES = [os.path.join(CSRC, "trace_fp4_kernels.hip"), os.path.join(CSRC, "trace_fp4_api.cpp")]
+SOURCES = [os.path.join(CSRC, "trace_fp4_kernels.hip"), os.path.join(CSRC, "trace_fp4_api.cpp"),
+           os.path.join(CSRC, "trace_fp4_record.hip")]
 ARCH = "gfx950"
 
 

@@ -83,7 +83,9 @@ int shape_of(int fmt, int64_t rows, int64_t cols, int64_t group_rows, CallShape*
 // Per-device result of the gfx950 check: 0 unknown, 1 yes, 2 no.
 std::atomic<int> g_dev_ok[64];
 
-int check_device() {
+}  // namespace
+
+int tfp4::check_device() {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return TRACE_EDEVICE;
   if (dev < 64) {
@@ -97,6 +99,10 @@ int check_device() {
   if (dev < 64) g_dev_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
   return ok ? TRACE_OK : TRACE_EDEVICE;
 }
+
+namespace {
+
+using tfp4::check_device;
 
 int launched(hipError_t e) { return e == hipSuccess ? TRACE_OK : TRACE_ELAUNCH; }
 
@@ -203,6 +209,7 @@ const char* trace_status_str(int status) {
     case TRACE_EALIAS: return "TRACE_EALIAS";
     case TRACE_EDEVICE: return "TRACE_EDEVICE";
     case TRACE_ELAUNCH: return "TRACE_ELAUNCH";
+    case TRACE_EBUSY: return "TRACE_EBUSY";
     default: return "unknown status";
   }
 }

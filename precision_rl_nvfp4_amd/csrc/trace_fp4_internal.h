@@ -60,6 +60,10 @@ hipError_t launch_guided(int fmt, int bits, bool decode_only, const Shape& sh,
                          double* acc3, int64_t* counts, int accumulate, void* work,
                          hipStream_t stream);
 
+// TRACE_OK when the current device is a gfx950, else TRACE_EDEVICE (cached
+// per device).
+int check_device();
+
 // Groups per batch of NVFP4 encoding with scales from the amax (each launch
 // quantizes one batch and reads the next for its amax); 0 = sized for the
 // Infinity Cache. Returns the previous value.

@@ -51,10 +51,10 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.trace_abi_version() == _abi.ABI_VERSION == 4
+    assert lib.trace_abi_version() == _abi.ABI_VERSION == 5
     for code, name in [(0, "TRACE_OK"), (-1, "TRACE_EINVAL"), (-2, "TRACE_ESHAPE"),
                        (-3, "TRACE_EALIGN"), (-4, "TRACE_EALIAS"), (-5, "TRACE_EDEVICE"),
-                       (-6, "TRACE_ELAUNCH"), (7, "unknown status")]:
+                       (-6, "TRACE_ELAUNCH"), (-7, "TRACE_EBUSY"), (7, "unknown status")]:
         assert _abi.status_str(code) == name
 
 
@@ -241,3 +241,53 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_abi, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         _abi.load()
+
+
+# ---------------------------------------------------------------- record path
+
+def test_ring_rejects_before_any_hip_call(lib):
+    h = ctypes.c_void_p(123)
+    assert lib.trace_ring_create(1 << 20, 4, None) == _abi.EINVAL
+    for sb, n in [(0, 4), (-1, 4), (1, 0), (1, 4097), (1 << 30, 2048)]:
+        assert lib.trace_ring_create(sb, n, ctypes.byref(h)) == _abi.ESHAPE, (sb, n)
+        assert h.value is None                      # cleared on error
+    slot = ctypes.c_int32()
+    srcs = (ctypes.c_void_p * 1)(A)
+    sizes = (ctypes.c_int64 * 1)(16)
+    assert lib.trace_ring_push(None, srcs, sizes, 1, None, ctypes.byref(slot)) == _abi.EINVAL
+    assert lib.trace_ring_wait(None, 0) == _abi.EINVAL
+    assert lib.trace_ring_query(None, 0) == _abi.EINVAL
+    assert lib.trace_ring_release(None, 0) == _abi.EINVAL
+    assert lib.trace_ring_slot(None, 0, None) is None
+    assert lib.trace_ring_destroy(None) == _abi.EINVAL
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is visible: a ring would be created")
+def test_ring_create_without_gpu_is_edevice(lib):
+    h = ctypes.c_void_p()
+    assert lib.trace_ring_create(1 << 20, 4, ctypes.byref(h)) == _abi.EDEVICE
+    assert h.value is None
+
+
+# trace_gather_pages(pool, pool_pages, page_bytes, ids, n, out, bad, stream)
+@pytest.mark.parametrize("args,status", [
+    ((A, 4, 0, B, 2, C, None, None), _abi.ESHAPE),           # page_bytes 0
+    ((A, -1, 16, B, 2, C, None, None), _abi.ESHAPE),         # negative pool
+    ((A, 4, 16, B, -2, C, None, None), _abi.ESHAPE),         # negative n
+    ((A, 4, 1 << 40, B, 1 << 10, C, None, None), _abi.ESHAPE),  # 2^50 bytes
+    ((A, 4, 16, None, 2, C, None, None), _abi.EINVAL),       # NULL ids
+    ((A, 4, 16, B, 2, None, None, None), _abi.EINVAL),       # NULL out
+    ((None, 4, 16, B, 2, C, None, None), _abi.EINVAL),       # NULL pool
+    ((A, 4, 16, B + 2, 2, C, None, None), _abi.EALIGN),      # ids alignment
+    ((A, 4, 16, B, 2, C, D + 1, None), _abi.EALIGN),         # counter alignment
+    ((A, 4, 16, B, 2, A + 48, None, None), _abi.EALIAS),     # out over the pool's last page
+    ((A, 4, 16, B, 2, B - 16, None, None), _abi.EALIAS),     # out over the ids
+    ((A, 4, 16, B, 2, C, C + 8, None), _abi.EALIAS),         # counter inside out
+])
+def test_gather_rejects(lib, args, status):
+    assert lib.trace_gather_pages(*args) == status
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is visible: valid calls would launch")
+def test_gather_without_gpu_is_edevice(lib):
+    assert lib.trace_gather_pages(A, 4, 16, B, 2, C, D, None) == _abi.EDEVICE
