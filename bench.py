@@ -410,6 +410,15 @@ def main():
         run_phases(step)
         torch.cuda.synchronize()
         log(f"bench: warmup step {i + 1}/{args.warmup} done")
+    # The single-pass encode publishes each chunk's S in its workspace (after
+    # the per-chunk slots); the two-pass schedule leaves those words alone.
+    if args.warmup > 0:
+        pub = qwork.view(torch.int32)[w.chunks * 1024:w.chunks * 2048:1024].cpu()
+        s_last = w.gscale[w.layers - 1, :, 0].contiguous().view(torch.int32).cpu()
+        encode_path = "single-pass" if torch.equal(pub, s_last) else "two-pass"
+    else:
+        encode_path = "unknown"
+    log(f"bench: encode schedule {encode_path}")
 
     wall, per = timed(torch, step, args.steps)
     log(f"bench: {args.steps} timed steps in {wall:.3f} s")
@@ -497,7 +506,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "stream_nvfp4_136k_tokens", "layers": w.layers, "chunks": w.chunks,
-                   "encode_batch": args.encode_batch,
+                   "encode_batch": args.encode_batch, "encode_schedule": encode_path,
                    "chunk_tokens": CHUNK, "hidden": HIDDEN, "format": "nvfp4", "guide_bits": 1,
                    "elements_per_side_per_step": elems_step},
         "roofline": roofline,

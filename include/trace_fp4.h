@@ -113,19 +113,26 @@ int trace_abi_version(void);
 /* Static name of a status code ("TRACE_OK", ...); "unknown status" otherwise. */
 const char* trace_status_str(int status);
 
-/* How NVFP4 calls that derive S from the amax schedule their two passes over
- * the input (amax, then quantize): the groups go in batches, and each launch
- * quantizes one batch while it reads the next batch for its amax, so a batch
- * is re-read while it is still in the Infinity Cache. groups_per_batch = 0
- * (the default) sizes batches to about 96 MiB of input; n > 0 uses n groups
- * per batch (n >= G: one amax pass over every group, then one quantize pass).
- * Results are bit-identical for every setting; the knob exists to exercise
- * and compare schedules. Process-wide. Returns the previous setting, or
- * TRACE_EINVAL for a negative value. */
+/* How NVFP4 calls that derive S from the amax schedule their work.
+ * groups_per_batch = 0 (the default): groups of at most 1024 tiles (16.8M
+ * elements, e.g. an 8192 x 2048 chunk) are encoded in ONE pass over the input
+ * by a cooperative launch whose workgroups hold their tiles in registers
+ * while the group's amax is combined (it needs 4 resident workgroups per CU;
+ * otherwise, and for larger groups, the two-pass schedule below is used).
+ * n > 0 forces two passes (amax, then quantize) with n groups per batch: each
+ * launch quantizes one batch while it reads the next batch for its amax
+ * (n >= G: one amax pass over every group, then one quantize pass); with 0,
+ * two-pass batches are about 96 MiB of input. Results are bit-identical for
+ * every setting; the knob exists to exercise and compare schedules.
+ * Process-wide. Returns the previous setting, or TRACE_EINVAL for a negative
+ * value. */
 int64_t trace_set_encode_batch(int64_t groups_per_batch);
 
 /* Workspace bytes quantize_rtn / encode_guidance need to derive the global
- * scales from the amax (NVFP4 with gscale_out): 4096 per group, except 0 when
+ * scales from the amax (NVFP4 with gscale_out): 4 * (2048 * G + 1) rounded up
+ * to a multiple of 8 (per group 1024 partial maxima and 1024 words for the
+ * published S, and one count of bounded waits of the single-pass encode that
+ * gave up, which stays 0; it is the int32 at index 2048 * G), except 0 when
  * a group's element count is a power of two from 16 to 8192 and G > 1 (such
  * groups, e.g. one token's row for a per-token global scale, are reduced
  * and quantized in one pass); 0 for MXFP4. -1 for an invalid shape. */

@@ -492,6 +492,32 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(AmaxArgs a) {
   amax_body(a, blockIdx.x, red);
 }
 
+// Outputs of one quantized unit (global unit index gu): its guidance-plane
+// bits, its block's scale byte (written by the block's first unit) and y.
+template <int FMT, int PLANE, bool WY>
+__device__ __forceinline__ void write_unit(uint32_t K, uint32_t sb, float d, float dsc, int64_t gu,
+                                           uint8_t* plane, uint8_t* scales, uint4* y) {
+  if constexpr (PLANE == 4) {
+    reinterpret_cast<uint32_t*>(plane)[gu] = K;
+  } else if constexpr (PLANE == 1) {
+    plane[gu] = (uint8_t)gather_mbits(K);
+  } else if constexpr (PLANE == 2) {
+    reinterpret_cast<uint16_t*>(plane)[gu] = (uint16_t)gather_2bits(K);
+  } else {
+    const uint32_t w = gather_3bits(K);
+    uint8_t* q = plane + 3 * gu;
+    q[0] = (uint8_t)w;
+    q[1] = (uint8_t)(w >> 8);
+    q[2] = (uint8_t)(w >> 16);
+  }
+  if constexpr (FMT == 0) {
+    if ((gu & 1) == 0) scales[gu >> 1] = (uint8_t)sb;
+  } else {
+    if ((gu & 3) == 0) scales[gu >> 2] = (uint8_t)sb;
+  }
+  if constexpr (WY) y[gu] = FMT == 0 ? dequant_nv(K, d) : dequant_mx(K, dsc);
+}
+
 // RTN quantization (quantize_rtn / encode_guidance).
 // FMT 0 NVFP4 / 1 MXFP4; PLANE = bits of the guidance plane: 4 codes (u32 per
 // unit), 1 mantissa bits (u8 per unit), 2 / 3 the low 2 / 3 magnitude bits
@@ -614,29 +640,179 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) f[i] *= r;
     const uint32_t K = rtn_codes(f);
-    if (u < lim) {
-      const int64_t gu = gbase + u;
-      if constexpr (PLANE == 4) {
-        reinterpret_cast<uint32_t*>(a.plane)[gu] = K;
-      } else if constexpr (PLANE == 1) {
-        a.plane[gu] = (uint8_t)gather_mbits(K);
-      } else if constexpr (PLANE == 2) {
-        reinterpret_cast<uint16_t*>(a.plane)[gu] = (uint16_t)gather_2bits(K);
-      } else {
-        const uint32_t w = gather_3bits(K);
-        uint8_t* q = a.plane + 3 * gu;
-        q[0] = (uint8_t)w;
-        q[1] = (uint8_t)(w >> 8);
-        q[2] = (uint8_t)(w >> 16);
+    if (u < lim) write_unit<FMT, PLANE, WY>(K, sb, d, dsc, gbase + u, a.plane, a.scales, a.y);
+  }
+}
+
+// Single-pass NVFP4 encode with S from each group's amax, for groups of at
+// most kOnePassTiles tiles. All workgroups are resident (cooperative
+// launch); Q sets of T workgroups each (T = tiles per group) take groups q,
+// q + Q, ... in turn, one tile per workgroup per group, kept on chip:
+//   * a tile's max goes to its slot, tagged (bit 31), by one store as soon
+//     as the tile has arrived;
+//   * the group's tile 0 workgroup waits for all T slots, derives S and A,
+//     writes {S, A} to gout and publishes S (nonzero) to kSCopies words;
+//     every other workgroup waits for one of them;
+//   * the tile is then quantized from on-chip storage.
+// Three tiles are in flight per workgroup: the one waiting for its S (in
+// LDS, each thread keeping its own words), the next one (registers, max
+// published) and the loads of the one after (registers), so a group's
+// combine has two tile-times to complete and a tile's loads one.
+// Slots and S words are zeroed by a fill kernel before the launch. Every wait
+// is bounded: past kSpinMax polls the workgroup records an error in *err and
+// carries on with S = NaN, so the grid always drains.
+struct OnePassArgs {
+  const uint4* x;
+  int64_t upg;               // units per group
+  int64_t groups;
+  int T;                     // tiles (workgroups) per group
+  int Q;                     // groups in flight
+  uint32_t* slots;           // [groups][kPartMax] tagged tile maxima
+  uint32_t* sword;           // [groups][kSCopies][64]: S bits at [.][c][0], 0 until published
+  uint32_t* err;             // bounded-wait failures
+  float* gout;
+  uint8_t* plane;
+  uint8_t* scales;
+  uint4* y;
+};
+
+constexpr int kSpinMax = 1 << 22;
+constexpr int kSCopies = 16;            // copies of each published S, one per 256-byte line
+
+__device__ __forceinline__ uint32_t load_agent(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int PLANE, bool WY>
+__global__ __launch_bounds__(kThreads, 4) void onepass_encode_kernel(OnePassArgs a) {
+  __shared__ float2 lut[128];
+  __shared__ uint32_t red[kThreads / 64];
+  __shared__ float sS;
+  __shared__ uint4 stash[kUPT * kThreads];   // the tile waiting for its S (thread-private words)
+  const int q = (int)blockIdx.x / a.T;
+  const int t = (int)blockIdx.x - q * a.T;
+  const int64_t tbase = (int64_t)t * kTileUnits;
+  const int64_t G = a.groups, Q = a.Q;
+  uint4 r0[kUPT], r1[kUPT];
+  auto load_tile = [&](uint4 (&v)[kUPT], int64_t g) {
+#pragma unroll
+    for (int j = 0; j < kUPT; ++j) {
+      const int64_t u = tbase + j * kThreads + threadIdx.x;
+      v[j] = u < a.upg ? a.x[g * a.upg + u] : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  // Tile max of group g -> its tagged slot.
+  auto publish_max = [&](const uint4 (&v)[kUPT], int64_t g) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < kUPT; ++j) m = max(m, unit_amax_bits(v[j]));
+    m = wave_max_u32(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0)
+      store_agent(&a.slots[g * kPartMax + t], 0x80000000u | max(max(red[0], red[1]), max(red[2], red[3])));
+    __syncthreads();  // red[] is reused
+  };
+  auto to_stash = [&](const uint4 (&v)[kUPT]) {
+#pragma unroll
+    for (int j = 0; j < kUPT; ++j) stash[j * kThreads + threadIdx.x] = v[j];
+  };
+
+  int64_t g = q;
+  if (g >= G) return;
+  load_tile(r0, g);
+  publish_max(r0, g);
+  to_stash(r0);
+  if (g + Q < G) {
+    load_tile(r0, g + Q);
+    publish_max(r0, g + Q);
+  }
+  if (g + 2 * Q < G) load_tile(r1, g + 2 * Q);
+  // Loop state: stash = tile of g (max published); r0 = tile of g + Q (max
+  // published); r1 = loads of g + 2Q in flight.
+  for (; g < G; g += Q) {
+    // S of group g
+    if (t == 0) {
+      uint32_t gm = 0;
+      for (int i = threadIdx.x; i < a.T; i += kThreads) {
+        uint32_t v;
+        int spins = 0;
+        while (((v = load_agent(&a.slots[g * kPartMax + i])) & 0x80000000u) == 0u) {
+          if (++spins > kSpinMax) {
+            atomicAdd(a.err, 1u);
+            v = 0x80000000u;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        gm = max(gm, v & 0x7FFFFFFFu);
       }
-      if constexpr (FMT == 0) {
-        if ((gu & 1) == 0) a.scales[gu >> 1] = (uint8_t)sb;
-      } else {
-        if ((gu & 3) == 0) a.scales[gu >> 2] = (uint8_t)sb;
+      gm = wave_max_u32(gm);
+      if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = gm;
+      __syncthreads();
+      const float A = __uint_as_float(max(max(red[0], red[1]), max(red[2], red[3])) << 16);
+      const float S = global_scale(A);
+      if (threadIdx.x < kSCopies) store_agent(&a.sword[(g * kSCopies + threadIdx.x) * 64], __float_as_uint(S));
+      if (threadIdx.x == 0) {
+        a.gout[2 * g] = S;
+        a.gout[2 * g + 1] = A;
+        sS = S;
       }
-      if constexpr (WY) a.y[gu] = FMT == 0 ? dequant_nv(K, d) : dequant_mx(K, dsc);
+    } else if (threadIdx.x == 0) {
+      const uint32_t* w = &a.sword[(g * kSCopies + (int)(blockIdx.x % kSCopies)) * 64];
+      uint32_t v;
+      int spins = 0;
+      while ((v = load_agent(w)) == 0u) {
+        if (++spins > kSpinMax) {
+          atomicAdd(a.err, 1u);
+          v = 0x7FC00000u;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      sS = __uint_as_float(v);
+    }
+    __syncthreads();
+    const float S = sS;
+    build_factor_lut(lut, S);
+    __syncthreads();
+    // quantize the stashed tile of g, one unit at a time (the next tile and
+    // the loads after it hold 64 VGPRs meanwhile)
+#pragma unroll 1
+    for (int j = 0; j < kUPT; ++j) {
+      const int64_t u = tbase + j * kThreads + threadIdx.x;
+      const uint4 v = stash[j * kThreads + threadIdx.x];
+      uint32_t bm = unit_amax_bits(v);
+      bm = max(bm, xor1(bm));
+      const uint32_t sb = nv_scale_byte(bm, S);
+      const float2 rd = lut[sb & 0x7Fu];
+      float f[8];
+      unit_f32(v, f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) f[i] *= rd.x;
+      const uint32_t K = rtn_codes(f);
+      if (u < a.upg) write_unit<0, PLANE, WY>(K, sb, rd.y, 0.0f, g * a.upg + u, a.plane, a.scales, a.y);
+    }
+    __syncthreads();  // lut, sS and red[] are rewritten below or next round
+    // advance: r0 -> stash, r1 -> r0 (max published), next loads -> r1
+    if (g + Q < G) {
+      to_stash(r0);
+      if (g + 2 * Q < G) {
+#pragma unroll
+        for (int j = 0; j < kUPT; ++j) r0[j] = r1[j];
+        publish_max(r0, g + 2 * Q);
+        if (g + 3 * Q < G) load_tile(r1, g + 3 * Q);
+      }
     }
   }
+}
+
+__global__ __launch_bounds__(kThreads) void zero_words_kernel(uint32_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads)
+    p[i] = 0u;
 }
 
 // Guided rounding under the rollout scales (guided_fake_quant), Reconstruct
@@ -963,6 +1139,69 @@ hipError_t quant_plane(int plane_mode, bool wy, int ssrc, bool pack, const Quant
   }
 }
 
+// ---- single-pass encode (onepass_encode_kernel)
+
+constexpr int kOnePassTiles = kPartMax;  // largest group: 1024 tiles = 16.8M elements
+constexpr int kOnePassPerCU = 4;         // resident workgroups per CU it is built for
+
+template <int PLANE, bool WY>
+const void* onepass_fn() {
+  return reinterpret_cast<const void*>(&onepass_encode_kernel<PLANE, WY>);
+}
+
+const void* onepass_kernel(int plane_mode, bool wy) {
+  switch (plane_mode) {
+    case 1: return wy ? onepass_fn<1, true>() : onepass_fn<1, false>();
+    case 2: return wy ? onepass_fn<2, true>() : onepass_fn<2, false>();
+    case 3: return wy ? onepass_fn<3, true>() : onepass_fn<3, false>();
+    default: return wy ? onepass_fn<4, true>() : onepass_fn<4, false>();
+  }
+}
+
+// Workgroups that may be resident at once for the kernel: kOnePassPerCU per
+// CU if the occupancy query allows that many, else 0 (not used).
+int64_t onepass_capacity(const void* k) {
+  int dev = -1, cus = 0, per = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k, kThreads, 0) != hipSuccess) return 0;
+  if (per < kOnePassPerCU) return 0;
+  return (int64_t)cus * kOnePassPerCU;
+}
+
+// Launches the single-pass encode when it applies; *used tells whether it did.
+hipError_t launch_onepass(int plane_mode, bool wy, const Shape& sh, const QuantArgs& qa, void* work,
+                          hipStream_t stream, bool* used) {
+  *used = false;
+  const int64_t T = (sh.upg + kTileUnits - 1) / kTileUnits;
+  if (T > kOnePassTiles) return hipSuccess;
+  const void* k = onepass_kernel(plane_mode, wy);
+  const int64_t cap = onepass_capacity(k);
+  const int64_t Q = min(sh.groups, cap / T);
+  if (Q < 1) return hipSuccess;
+  OnePassArgs a{};
+  a.x = qa.x;
+  a.upg = sh.upg;
+  a.groups = sh.groups;
+  a.T = (int)T;
+  a.Q = (int)Q;
+  a.slots = static_cast<uint32_t*>(work);
+  a.sword = a.slots + sh.groups * kPartMax;
+  a.err = a.sword + sh.groups * kSCopies * 64;
+  a.gout = qa.gout;
+  a.plane = qa.plane;
+  a.scales = qa.scales;
+  a.y = qa.y;
+  const int64_t words = sh.groups * ((int64_t)kPartMax + kSCopies * 64) + 1;
+  const int64_t zb = min((words + kThreads - 1) / kThreads, (int64_t)1024);
+  hipError_t e = launch(zero_words_kernel, dim3((unsigned)zb), dim3(kThreads), stream, a.slots, words);
+  if (e != hipSuccess) return e;
+  void* argv[] = {&a};
+  e = hipLaunchCooperativeKernel(k, dim3((unsigned)(Q * T)), dim3(kThreads), argv, 0, stream);
+  if (e == hipSuccess) *used = true;
+  return e == hipErrorCooperativeLaunchTooLarge ? hipSuccess : e;
+}
+
 template <int FMT, int BITS, bool DECODE, bool WCODES, bool STATS, bool DIAG, bool PACK>
 hipError_t guided_go(const GuidedArgs& a, hipStream_t s) {
   return launch(guided_kernel<FMT, BITS, DECODE, WCODES, STATS, DIAG, PACK>,
@@ -1002,7 +1241,10 @@ hipError_t guided_pack(int bits, bool decode, bool wc, bool stats, bool diag, co
 
 int64_t quant_work_bytes(int fmt, const Shape& sh) {
   if (fmt != 0 || packable(fmt, sh)) return 0;
-  return sh.groups * (int64_t)kPartMax * (int64_t)sizeof(uint32_t);
+  // amax partials or tagged tile maxima [G][kPartMax], S words [G][kSCopies * 64],
+  // error count
+  const int64_t words = sh.groups * ((int64_t)kPartMax + kSCopies * 64) + 1;
+  return (words * (int64_t)sizeof(uint32_t) + 7) / 8 * 8;
 }
 
 int64_t guided_stats_work_bytes(int fmt, const Shape& sh) {
@@ -1048,8 +1290,15 @@ hipError_t launch_quantize(int fmt, int plane_mode, const Shape& sh, const uint1
     if (fmt == 0) return quant_plane<0>(plane_mode, wy, 0, false, a, a.qblocks, stream);
     return quant_plane<1>(plane_mode, wy, 0, false, a, a.qblocks, stream);
   }
-  // NVFP4 with S from the amax: the input is read twice (amax, then
-  // quantize). Groups go in batches of about kCacheBatchBytes of input, and
+  // NVFP4 with S from the amax. Groups of at most kOnePassTiles tiles are
+  // encoded in one pass (unless a batch size was set); otherwise the input
+  // is read twice (amax, then quantize).
+  if (g_encode_batch.load(std::memory_order_relaxed) == 0) {
+    bool used = false;
+    hipError_t e1 = launch_onepass(plane_mode, wy, sh, a, work, stream, &used);
+    if (e1 != hipSuccess || used) return e1;
+  }
+  // Two passes: groups go in batches of about kCacheBatchBytes of input, and
   // the launch that quantizes batch b also runs the amax pass of batch b + 1,
   // so each batch is re-read one launch after its first read, while it still
   // sits in the 256 MB Infinity Cache. A caller-set batch size overrides the

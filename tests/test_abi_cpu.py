@@ -70,8 +70,11 @@ def test_workspace_sizes(lib):
     assert lib.trace_stats_workspace_bytes(8192 * 2048) == 16 * 1024
     assert lib.trace_stats_workspace_bytes(-1) == 0
     # one kPartMax (1024) array of uint32 partial maxima per global-scale group
-    assert lib.trace_quant_workspace_bytes(0, 4, 32, 0) == 4096
-    assert lib.trace_quant_workspace_bytes(0, 17 * 8192, 2048, 8192) == 17 * 4096
+    # per group 1024 partial (or tile) maxima + 16 S words on their own 256-byte
+    # lines, plus one error count, in 8-byte units
+    qwb = lambda G: (4 * (2048 * G + 1) + 7) // 8 * 8  # noqa: E731
+    assert lib.trace_quant_workspace_bytes(0, 4, 32, 0) == qwb(1) == 8200
+    assert lib.trace_quant_workspace_bytes(0, 17 * 8192, 2048, 8192) == qwb(17)
     assert lib.trace_quant_workspace_bytes(1, 4, 32, 0) == 0            # MXFP4: no amax pass
     assert lib.trace_quant_workspace_bytes(0, 5, 32, 2) == -1           # 2 does not divide 5
     assert lib.trace_quant_workspace_bytes(3, 4, 32, 0) == -1           # bad format
@@ -80,8 +83,8 @@ def test_workspace_sizes(lib):
     # packed groups (power-of-two units below a tile, G > 1) need no amax workspace
     assert lib.trace_quant_workspace_bytes(0, 8, 32, 4) == 0           # 2 groups of 16 units
     assert lib.trace_quant_workspace_bytes(0, 139264, 2048, 1) == 0    # per-token scales
-    assert lib.trace_quant_workspace_bytes(0, 6, 32, 3) == 2 * 4096    # 12 units: not a power of two
-    assert lib.trace_quant_workspace_bytes(0, 16, 2048, 8) == 2 * 4096  # 2048 units: a whole tile
+    assert lib.trace_quant_workspace_bytes(0, 6, 32, 3) == qwb(2)      # 12 units: not a power of two
+    assert lib.trace_quant_workspace_bytes(0, 16, 2048, 8) == qwb(2)   # 2048 units: a whole tile
     assert lib.trace_quant_workspace_bytes(1, 16, 2048, 8) == 0
     # per-token: 139264 rows x 256 units packed 8 to a tile
     assert lib.trace_guided_stats_workspace_bytes(0, 139264, 2048, 1) == 16 * (17408 + 64) + 128 * 17408
@@ -95,7 +98,7 @@ def test_workspace_sizes(lib):
 
 
 W = 0x600000            # a fake workspace address
-WB = 4096               # quantize workspace bytes for one group
+WB = 8200               # quantize workspace bytes for one group
 
 
 # quantize_rtn(fmt, rows, cols, group_rows, x, gin, codes, scales, gout, y, work, work_bytes, stream)

@@ -79,10 +79,13 @@ def test_stream_layer_bench_configuration():
         a, b = syn.stream_pair(layer, c, dev, sigma=sigma)
         xt[c * CH:(c + 1) * CH].copy_(a)
         xr[c * CH:(c + 1) * CH].copy_(b)
-    g = tq.encode_guidance(xr, NV, 1, with_y=True, group_rows=CH)
+    work = tq.quant_workspace(NV, chunks * CH, syn.HIDDEN, CH, device=dev)
+    g = tq.encode_guidance(xr, NV, 1, with_y=True, group_rows=CH, work=work)
     y, codes, acc, counts = tq.guided_fake_quant_stats(xt, xr, g, with_codes=True, mismatch=True)
     y_plain, _ = tq.guided_fake_quant(xt, g)
     torch.cuda.synchronize()
+    # the single-pass encode's count of bounded waits that gave up
+    assert work.view(torch.int32)[chunks * 2048].item() == 0
     assert torch.equal(y.view(torch.int16), y_plain.view(torch.int16))
     # mismatch counts against plain torch over the code planes (rollout codes
     # from a full-code record, RTN codes under the rollout scales), which the

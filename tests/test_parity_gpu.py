@@ -476,9 +476,9 @@ def test_one_batch_corner_cases(one_batch):
 
 
 def test_schedules_agree_on_streamed_chunks():
-    """The cache-sized batches and the single batch give identical encodings
-    of 17 streamed chunks."""
-    G.say("cache-sized batches vs one batch on [17 x 8192, 2048]")
+    """The single-pass encode (the default for chunks of 8192 x 2048) and the
+    two-pass schedule give identical encodings of 17 streamed chunks."""
+    G.say("single pass vs two passes on [17 x 8192, 2048]")
     CH = syn.STREAM_CHUNK
     xr = torch.cat([syn.stream_pair(21, c, G.DEV)[1] for c in range(17)])
     lib = tq.load()
@@ -494,3 +494,27 @@ def test_schedules_agree_on_streamed_chunks():
         outs.append([G.u8(g.guide), G.u8(g.scales), G.f32(g.gscale), G.bits_of(g.y), G.u8(q.codes)])
     for a, b in zip(*outs):
         assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("G_,gr,cols", [(1, 256, 2048), (17, 64, 2048), (3, 37, 2048), (2, 1024, 2048)])
+def test_single_pass_encode_waits_never_time_out(G_, gr, cols):
+    """The single-pass encode keeps a count of bounded waits that gave up in
+    its workspace (after the per-group words); it stays 0, and the result is
+    the oracle's."""
+    G.say(f"single-pass encode wait counter, {G_} groups x ({gr},{cols})")
+    xt, xr = _grouped_pair(G_, gr, cols, 8)
+    rows = G_ * gr
+    x = G.to_dev(xr, rows, cols)
+    work = tq.quant_workspace(NV, rows, cols, gr, device=G.DEV)
+    g = tq.encode_guidance(x, NV, 1, with_y=True, group_rows=gr, work=work)
+    torch.cuda.synchronize()
+    words = work.view(torch.int32).cpu().numpy()
+    assert words[G_ * 2048] == 0
+    # only the single pass publishes S (16 copies, 64 words apart, per group)
+    S_bits = g.gscale.reshape(-1, 2)[:, 0].cpu().numpy().view(np.int32)
+    pub = words[G_ * 1024:G_ * 2048].reshape(G_, 16, 64)[:, :, 0]
+    assert np.array_equal(pub, np.repeat(S_bits[:, None], 16, axis=1)), "single pass not used"
+    o = G.oracle_encode(NV, 1, xr, rows, gr)
+    G.assert_same(G.u8(g.guide), o["guide"], "guide")
+    G.assert_same(G.bits_of(g.y), o["y"], "rollout y")
+    G.assert_same(G.f32(g.gscale).reshape(-1, 2)[:, 0], o["gscale"], "S")
