@@ -63,6 +63,19 @@ __device__ __forceinline__ uint32_t xor2(uint32_t v) {
 
 // ------------------------------------------------------------ unit helpers
 
+typedef unsigned int v4u_t __attribute__((ext_vector_type(4)));
+
+// Streaming accesses (data touched once): nontemporal, so they do not
+// allocate in the caches.
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  const v4u_t v = __builtin_nontemporal_load(reinterpret_cast<const v4u_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_stream(uint4* p, const uint4& v) {
+  const v4u_t w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<v4u_t*>(p));
+}
+
 // Largest bf16 magnitude (bits & 0x7FFF) among the 8 elements of a unit.
 __device__ __forceinline__ uint32_t unit_amax_bits(const uint4& v) {
   typedef unsigned short us2 __attribute__((ext_vector_type(2)));
@@ -477,10 +490,11 @@ __device__ __forceinline__ void amax_body(const AmaxArgs& a, int64_t blk, uint32
   uint32_t m = 0;
   int64_t u = (int64_t)w * kThreads + threadIdx.x;
   for (; u + 3 * stride < a.upg; u += 4 * stride) {
-    const uint4 p = x[u], q = x[u + stride], r = x[u + 2 * stride], s = x[u + 3 * stride];
+    const uint4 p = load_stream(x + u), q = load_stream(x + u + stride), r = load_stream(x + u + 2 * stride),
+                s = load_stream(x + u + 3 * stride);
     m = max(m, max(max(unit_amax_bits(p), unit_amax_bits(q)), max(unit_amax_bits(r), unit_amax_bits(s))));
   }
-  for (; u < a.upg; u += stride) m = max(m, unit_amax_bits(x[u]));
+  for (; u < a.upg; u += stride) m = max(m, unit_amax_bits(load_stream(x + u)));
   m = wave_max_u32(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
@@ -498,11 +512,11 @@ template <int FMT, int PLANE, bool WY>
 __device__ __forceinline__ void write_unit(uint32_t K, uint32_t sb, float d, float dsc, int64_t gu,
                                            uint8_t* plane, uint8_t* scales, uint4* y) {
   if constexpr (PLANE == 4) {
-    reinterpret_cast<uint32_t*>(plane)[gu] = K;
+    __builtin_nontemporal_store(K, reinterpret_cast<uint32_t*>(plane) + gu);
   } else if constexpr (PLANE == 1) {
-    plane[gu] = (uint8_t)gather_mbits(K);
+    __builtin_nontemporal_store((uint8_t)gather_mbits(K), plane + gu);
   } else if constexpr (PLANE == 2) {
-    reinterpret_cast<uint16_t*>(plane)[gu] = (uint16_t)gather_2bits(K);
+    __builtin_nontemporal_store((uint16_t)gather_2bits(K), reinterpret_cast<uint16_t*>(plane) + gu);
   } else {
     const uint32_t w = gather_3bits(K);
     uint8_t* q = plane + 3 * gu;
@@ -511,11 +525,11 @@ __device__ __forceinline__ void write_unit(uint32_t K, uint32_t sb, float d, flo
     q[2] = (uint8_t)(w >> 16);
   }
   if constexpr (FMT == 0) {
-    if ((gu & 1) == 0) scales[gu >> 1] = (uint8_t)sb;
+    if ((gu & 1) == 0) __builtin_nontemporal_store((uint8_t)sb, scales + (gu >> 1));
   } else {
-    if ((gu & 3) == 0) scales[gu >> 2] = (uint8_t)sb;
+    if ((gu & 3) == 0) __builtin_nontemporal_store((uint8_t)sb, scales + (gu >> 2));
   }
-  if constexpr (WY) y[gu] = FMT == 0 ? dequant_nv(K, d) : dequant_mx(K, dsc);
+  if constexpr (WY) store_stream(y + gu, FMT == 0 ? dequant_nv(K, d) : dequant_mx(K, dsc));
 }
 
 // RTN quantization (quantize_rtn / encode_guidance).
@@ -557,7 +571,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
 #pragma unroll
   for (int j = 0; j < kUPT; ++j) {
     const int64_t u = tbase + j * kThreads + threadIdx.x;
-    v[j] = u < lim ? a.x[gbase + u] : make_uint4(0u, 0u, 0u, 0u);
+    v[j] = u < lim ? load_stream(a.x + gbase + u) : make_uint4(0u, 0u, 0u, 0u);
   }
   float S = 1.0f;
   if constexpr (PACK) {
@@ -701,7 +715,7 @@ __global__ __launch_bounds__(kThreads, 4) void onepass_encode_kernel(OnePassArgs
 #pragma unroll
     for (int j = 0; j < kUPT; ++j) {
       const int64_t u = tbase + j * kThreads + threadIdx.x;
-      v[j] = u < a.upg ? a.x[g * a.upg + u] : make_uint4(0u, 0u, 0u, 0u);
+      v[j] = u < a.upg ? load_stream(a.x + g * a.upg + u) : make_uint4(0u, 0u, 0u, 0u);
     }
   };
   // Tile max of group g -> its tagged slot.
@@ -845,18 +859,18 @@ __global__ __launch_bounds__(kThreads) void guided_kernel(GuidedArgs a) {
     const int64_t u = tbase + j * kThreads + threadIdx.x;
     const bool ok = u < lim;
     const int64_t gu = gbase + u;
-    v[j] = ok ? a.x[gu] : make_uint4(0u, 0u, 0u, 0u);
-    if constexpr (STATS) vr[j] = ok ? a.xr[gu] : make_uint4(0u, 0u, 0u, 0u);
-    sbv[j] = ok ? (uint32_t)a.scales[FMT == 0 ? (gu >> 1) : (gu >> 2)] : 0u;
+    v[j] = ok ? load_stream(a.x + gu) : make_uint4(0u, 0u, 0u, 0u);
+    if constexpr (STATS) vr[j] = ok ? load_stream(a.xr + gu) : make_uint4(0u, 0u, 0u, 0u);
+    sbv[j] = ok ? (uint32_t)__builtin_nontemporal_load(a.scales + (FMT == 0 ? (gu >> 1) : (gu >> 2))) : 0u;
     if constexpr (BITS == 1) {
-      gv[j] = ok ? (uint32_t)a.guide[gu] : 0u;
+      gv[j] = ok ? (uint32_t)__builtin_nontemporal_load(a.guide + gu) : 0u;
     } else if constexpr (BITS == 2) {
-      gv[j] = ok ? (uint32_t)reinterpret_cast<const uint16_t*>(a.guide)[gu] : 0u;
+      gv[j] = ok ? (uint32_t)__builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(a.guide) + gu) : 0u;
     } else if constexpr (BITS == 3) {
       const uint8_t* q = a.guide + 3 * gu;
       gv[j] = ok ? (uint32_t)q[0] | ((uint32_t)q[1] << 8) | ((uint32_t)q[2] << 16) : 0u;
     } else if constexpr (BITS == 4) {
-      gv[j] = ok ? reinterpret_cast<const uint32_t*>(a.guide)[gu] : 0u;
+      gv[j] = ok ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(a.guide) + gu) : 0u;
     } else {
       gv[j] = 0u;
     }
@@ -914,8 +928,8 @@ __global__ __launch_bounds__(kThreads) void guided_kernel(GuidedArgs a) {
     }
     if (u < lim) {
       const int64_t gu = gbase + u;
-      if constexpr (DECODE || WCODES) a.codes[gu] = K;
-      if constexpr (!DECODE) a.y[gu] = yv;
+      if constexpr (DECODE || WCODES) __builtin_nontemporal_store(K, a.codes + gu);
+      if constexpr (!DECODE) store_stream(a.y + gu, yv);
     }
   }
   if constexpr (STATS) {
@@ -1027,8 +1041,8 @@ __global__ __launch_bounds__(kThreads) void stats_partial_kernel(const uint16_t*
   double sb = 0.0, sf = 0.0;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < units; u += stride) {
-    accum_unit(xt4[u], xr4[u], sb);
-    accum_unit(yt4[u], yr4[u], sf);
+    accum_unit(load_stream(xt4 + u), load_stream(xr4 + u), sb);
+    accum_unit(load_stream(yt4 + u), load_stream(yr4 + u), sf);
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     for (int64_t i = units * kUnitElems; i < n; ++i) {
