@@ -116,8 +116,9 @@ const char* trace_status_str(int status);
 /* How NVFP4 calls that derive S from the amax schedule their work.
  * groups_per_batch = 0 (the default): groups of at most 1024 tiles (16.8M
  * elements, e.g. an 8192 x 2048 chunk) are encoded in ONE pass over the input
- * by a cooperative launch whose workgroups hold their tiles in registers
- * while the group's amax is combined (it needs 4 resident workgroups per CU;
+ * by a launch of at most as many workgroups as the device holds at once,
+ * which keep their tiles on chip while the group's amax is combined (it needs
+ * 4 resident workgroups per CU;
  * otherwise, and for larger groups, the two-pass schedule below is used).
  * n > 0 forces two passes (amax, then quantize) with n groups per batch: each
  * launch quantizes one batch while it reads the next batch for its amax

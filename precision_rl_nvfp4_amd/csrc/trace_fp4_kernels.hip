@@ -659,8 +659,9 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
 }
 
 // Single-pass NVFP4 encode with S from each group's amax, for groups of at
-// most kOnePassTiles tiles. All workgroups are resident (cooperative
-// launch); Q sets of T workgroups each (T = tiles per group) take groups q,
+// most kOnePassTiles tiles. The grid never exceeds the number of workgroups
+// the device holds at once, so all of them are resident; Q sets of T
+// workgroups each (T = tiles per group) take groups q,
 // q + Q, ... in turn, one tile per workgroup per group, kept on chip:
 //   * a tile's max goes to its slot, tagged (bit 31), by one store as soon
 //     as the tile has arrived;
@@ -1210,10 +1211,15 @@ hipError_t launch_onepass(int plane_mode, bool wy, const Shape& sh, const QuantA
   const int64_t zb = min((words + kThreads - 1) / kThreads, (int64_t)1024);
   hipError_t e = launch(zero_words_kernel, dim3((unsigned)zb), dim3(kThreads), stream, a.slots, words);
   if (e != hipSuccess) return e;
+  // An ordinary launch on the caller's queue: the grid is at most the
+  // resident capacity, and the workgroups wait only for each other, so every
+  // one of them becomes resident once earlier work on the device drains (a
+  // cooperative launch would guarantee the same but goes through another
+  // hardware queue, ~11 us of switching before and after the kernel).
   void* argv[] = {&a};
-  e = hipLaunchCooperativeKernel(k, dim3((unsigned)(Q * T)), dim3(kThreads), argv, 0, stream);
+  e = hipLaunchKernel(k, dim3((unsigned)(Q * T)), dim3(kThreads), argv, 0, stream);
   if (e == hipSuccess) *used = true;
-  return e == hipErrorCooperativeLaunchTooLarge ? hipSuccess : e;
+  return e;
 }
 
 template <int FMT, int BITS, bool DECODE, bool WCODES, bool STATS, bool DIAG, bool PACK>
