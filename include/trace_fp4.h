@@ -88,7 +88,7 @@
 extern "C" {
 #endif
 
-#define TRACE_ABI_VERSION 5
+#define TRACE_ABI_VERSION 6
 
 /* Entries of the mismatch diagnostics of guided_fake_quant_stats. */
 #define TRACE_MISMATCH_COUNTS 32
@@ -286,6 +286,41 @@ int guided_fake_quant_stats(int fmt, int bits, int64_t rows, int64_t cols, int64
 int discrepancy_stats(int64_t n, const uint16_t* x_t, const uint16_t* x_r,
                       const uint16_t* y_t, const uint16_t* y_r, double* acc3,
                       int accumulate, void* work, int64_t work_bytes, void* stream);
+
+/*
+ * Groups of unequal size: row-offset groups (paper Algorithm 1 prose: s
+ * combines block and token/global scales; here one FP32 global scale per
+ * expert of a grouped MoE input, whose routed rows are contiguous per
+ * expert). row_offsets is a DEVICE int64[groups + 1] array of row offsets,
+ * read on the device (it may come straight from routing); group g is rows
+ * [off[g], off[g + 1]). Offsets are clamped into [0, rows] and made
+ * nondecreasing (a running max), so a bad array cannot cause out-of-range
+ * accesses; rows outside [off[0], off[groups]) are not written. An empty
+ * group gets {S, A} = {1, 0}. Results equal separate calls on each group's
+ * rows. NVFP4 only matters here: for MXFP4 (no global scale) the offsets are
+ * not read and the call equals the ungrouped one (gscale pointers NULL).
+ * groups in [1, 2^24]; otherwise ESHAPE.
+ */
+
+/* Workspace bytes of the two calls below; 0 for MXFP4, -1 for an invalid
+ * shape or group count. */
+int64_t trace_grouped_workspace_bytes(int fmt, int64_t rows, int64_t cols, int64_t groups);
+
+/* encode_guidance with one global scale per row-offset group: gscale_out
+ * receives {S, A} of group g at [2g], [2g + 1] (required for NVFP4). Other
+ * arguments as in encode_guidance (bits 1..4; bits = 4 with y_rollout_opt
+ * is exactly quantize_rtn per group). */
+int encode_guidance_grouped(int fmt, int bits, int64_t rows, int64_t cols, int64_t groups,
+                            const int64_t* row_offsets, const uint16_t* x_rollout, uint8_t* guide,
+                            uint8_t* scales, float* gscale_out, uint16_t* y_rollout_opt, void* work,
+                            int64_t work_bytes, void* stream);
+
+/* guided_fake_quant under per-group rollout scales: gscale holds S of group g
+ * at [2g]. Other arguments as in guided_fake_quant (bits 0..4). */
+int guided_fake_quant_grouped(int fmt, int bits, int64_t rows, int64_t cols, int64_t groups,
+                              const int64_t* row_offsets, const uint16_t* x_train, const uint8_t* guide,
+                              const uint8_t* scales, const float* gscale, uint16_t* y, uint8_t* codes_opt,
+                              void* work, int64_t work_bytes, void* stream);
 
 /*
  * Record path (paper §3.2 "Motivation": records are cached during generation

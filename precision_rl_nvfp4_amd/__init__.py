@@ -32,7 +32,8 @@ from ._abi import MISMATCH_COUNTS, MXFP4, NVFP4, TraceError, load, status_str  #
 MISMATCH_BINS = MISMATCH_COUNTS // 2 - 1   # distances 0..14 per histogram
 
 __all__ = ["NVFP4", "MXFP4", "TraceError", "Quantized", "Guidance", "quantize_rtn",
-           "encode_guidance", "decode_guidance", "guided_fake_quant", "guided_fake_quant_stats",
+           "encode_guidance", "encode_guidance_grouped", "decode_guidance", "guided_fake_quant",
+           "guided_fake_quant_stats",
            "discrepancy_stats", "stats_workspace", "quant_workspace", "guided_stats_workspace",
            "derived_metrics", "mismatch_summary", "fmt_id", "BLOCK", "MISMATCH_COUNTS"]
 
@@ -62,6 +63,7 @@ class Guidance(NamedTuple):
     gscale: Optional[torch.Tensor]  # float32 [G, 2] (NVFP4) or None
     y: Optional[torch.Tensor]      # the rollout's own dequantized bf16 output, or None
     group_rows: int = 0
+    offsets: Optional[torch.Tensor] = None  # int64 [G + 1] device row offsets (row-offset groups)
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -178,10 +180,41 @@ def encode_guidance(x_rollout: torch.Tensor, fmt="nvfp4", bits: int = 1,
     return Guidance(f, int(bits), c, s, g, yy, int(group_rows))
 
 
+def _check_offsets(offsets: torch.Tensor, x: torch.Tensor) -> int:
+    if (offsets.dtype != torch.int64 or offsets.dim() != 1 or offsets.numel() < 2
+            or not offsets.is_contiguous() or offsets.device != x.device):
+        raise ValueError("row offsets must be a contiguous int64 [G + 1] tensor on x's device")
+    return offsets.numel() - 1
+
+
+def encode_guidance_grouped(x_rollout: torch.Tensor, offsets: torch.Tensor, fmt="nvfp4", bits: int = 1,
+                            with_y: bool = False, guide=None, scales=None, gscale_out=None, y=None,
+                            work=None) -> Guidance:
+    """encode_guidance with one global scale per row-offset group (e.g. per
+    expert of a grouped MoE input): group g is rows [offsets[g], offsets[g+1])."""
+    f = fmt_id(fmt)
+    rows, cols = _check_x(x_rollout, "x_rollout")
+    G = _check_offsets(offsets, x_rollout)
+    if bits not in (1, 2, 3, 4):
+        raise ValueError("bits must be 1, 2, 3 or 4")
+    guide = _empty((rows, cols * bits // 8), torch.uint8, x_rollout, guide)
+    scales = _empty((rows, cols // BLOCK[f]), torch.uint8, x_rollout, scales)
+    gscale_out = _empty((G, 2), torch.float32, x_rollout, gscale_out) if f == NVFP4 else None
+    y = _empty((rows, cols), torch.bfloat16, x_rollout, y) if with_y else None
+    need = int(load().trace_grouped_workspace_bytes(f, rows, cols, G))
+    work = _workspace(need, x_rollout.device, work)
+    _abi.call("encode_guidance_grouped", f, int(bits), rows, cols, G, _ptr(offsets), _ptr(x_rollout),
+              _ptr(guide), _ptr(scales), _ptr(gscale_out), _ptr(y), _ptr(work), _nbytes(work),
+              _stream(x_rollout))
+    return Guidance(f, int(bits), guide, scales, gscale_out, y, 0, offsets)
+
+
 def decode_guidance(x_train: torch.Tensor, g: Guidance, ref_codes=None) -> torch.Tensor:
     """Reconstruct the compact rollout reference codes (records of 1..3 bits)."""
     if g.bits not in (1, 2, 3):
         raise ValueError("decode_guidance takes a record of 1, 2 or 3 bits")
+    if g.offsets is not None:
+        raise ValueError("decode_guidance takes equal groups")
     rows, cols = _check_x(x_train, "x_train")
     ref_codes = _empty((rows, cols // 2), torch.uint8, x_train, ref_codes)
     _abi.call("decode_guidance", g.fmt, g.bits, rows, cols, g.group_rows, _ptr(x_train), _ptr(g.guide),
@@ -206,6 +239,14 @@ def guided_fake_quant(x_train: torch.Tensor, g: Guidance, bits: Optional[int] = 
     ``bits`` defaults to the record's (1..4); 0 gives RTN under the rollout
     scales. Returns (y, codes or None)."""
     b, rows, cols, y, codes, guide = _guided_common(x_train, g, bits, with_codes, y, codes)
+    if g.offsets is not None:   # row-offset groups
+        G = _check_offsets(g.offsets, x_train)
+        need = int(load().trace_grouped_workspace_bytes(g.fmt, rows, cols, G))
+        work = _workspace(need, x_train.device, None)
+        _abi.call("guided_fake_quant_grouped", g.fmt, b, rows, cols, G, _ptr(g.offsets), _ptr(x_train),
+                  _ptr(guide), _ptr(g.scales), _ptr(g.gscale), _ptr(y), _ptr(codes), _ptr(work),
+                  _nbytes(work), _stream(x_train))
+        return y, codes
     _abi.call("guided_fake_quant", g.fmt, b, rows, cols, g.group_rows, _ptr(x_train), _ptr(guide),
               _ptr(g.scales), _ptr(g.gscale), _ptr(y), _ptr(codes), _stream(x_train))
     return y, codes
@@ -221,6 +262,9 @@ def guided_fake_quant_stats(x_train: torch.Tensor, x_rollout: torch.Tensor, g: G
     (y, codes or None, acc float64[3]); with mismatch=True (or a counts
     tensor) also the int64[32] mismatch diagnostics, as a fourth element
     (layout in mismatch_summary)."""
+    if g.offsets is not None:
+        raise ValueError("guided_fake_quant_stats takes equal groups; for row-offset groups use "
+                         "guided_fake_quant and discrepancy_stats")
     b, rows, cols, y, codes, guide = _guided_common(x_train, g, bits, with_codes, y, codes)
     _check_x(x_rollout, "x_rollout")
     if tuple(x_rollout.shape) != (rows, cols):

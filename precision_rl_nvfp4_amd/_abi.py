@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtrace_fp
 
 OK, EINVAL, ESHAPE, EALIGN, EALIAS, EDEVICE, ELAUNCH, EBUSY = 0, -1, -2, -3, -4, -5, -6, -7
 NVFP4, MXFP4 = 0, 1
-ABI_VERSION = 5
+ABI_VERSION = 6
 MISMATCH_COUNTS = 32
 
 _i64 = ctypes.c_int64
@@ -42,6 +42,14 @@ SIGNATURES = {
                                        _vp, _vp, _int, _vp, _i64, _vp]),
     # n, x_t, x_r, y_t, y_r, acc3, accumulate, work, work_bytes, stream
     "discrepancy_stats": (_int, [_i64, _vp, _vp, _vp, _vp, _vp, _int, _vp, _i64, _vp]),
+    # row-offset groups: fmt, rows, cols, groups
+    "trace_grouped_workspace_bytes": (_i64, [_int, _i64, _i64, _i64]),
+    # fmt, bits, rows, cols, groups, offsets, x_r, guide, scales, gscale_out, y_r, work, work_bytes, stream
+    "encode_guidance_grouped": (_int, [_int, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       _i64, _vp]),
+    # fmt, bits, rows, cols, groups, offsets, x_t, guide, scales, gscale, y, codes, work, work_bytes, stream
+    "guided_fake_quant_grouped": (_int, [_int, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                         _vp, _i64, _vp]),
     # record path: slot_bytes, slots, &ring / ring / ring, srcs, bytes, n, stream, &slot / ...
     "trace_ring_create": (_int, [_i64, ctypes.c_int32, ctypes.POINTER(_vp)]),
     "trace_ring_destroy": (_int, [_vp]),

@@ -50,6 +50,8 @@ int block_of(int fmt) { return fmt == TRACE_FMT_NVFP4 ? 16 : 32; }
 
 bool valid_fmt(int fmt) { return fmt == TRACE_FMT_NVFP4 || fmt == TRACE_FMT_MXFP4; }
 
+constexpr int64_t kMaxOffsetGroups = (int64_t)1 << 24;  // row-offset groups per call
+
 // Guidance planes: bits 1..3 keep the low bits of each magnitude index (N*bits/8
 // bytes), 4 the full codes (N/2). Units of 8 elements are read whole, so a
 // plane is aligned to one unit's bytes when that is a power of two.
@@ -238,6 +240,14 @@ int64_t trace_stats_workspace_bytes(int64_t n) {
   return tfp4::stats_work_bytes(n);
 }
 
+int64_t trace_grouped_workspace_bytes(int fmt, int64_t rows, int64_t cols, int64_t groups) {
+  if (!valid_fmt(fmt)) return -1;
+  CallShape cs;
+  if (shape_of(fmt, rows, cols, 0, &cs) != TRACE_OK || groups < 1 || groups > kMaxOffsetGroups) return -1;
+  if (fmt == TRACE_FMT_MXFP4) return 0;
+  return tfp4::offs_work_bytes(rows, cols, groups);
+}
+
 int quantize_rtn(int fmt, int64_t rows, int64_t cols, int64_t group_rows, const uint16_t* x,
                  const float* gscale_in, uint8_t* codes, uint8_t* scales, float* gscale_out,
                  uint16_t* y_opt, void* work, int64_t work_bytes, void* stream) {
@@ -294,6 +304,79 @@ int guided_fake_quant_stats(int fmt, int bits, int64_t rows, int64_t cols, int64
                             int accumulate, void* work, int64_t work_bytes, void* stream) {
   return run_guided(fmt, bits, rows, cols, group_rows, x_train, x_rollout, true, guide, scales,
                     gscale, y, codes_opt, acc3, counts_opt, accumulate, work, work_bytes, stream);
+}
+
+int encode_guidance_grouped(int fmt, int bits, int64_t rows, int64_t cols, int64_t groups,
+                            const int64_t* row_offsets, const uint16_t* x_rollout, uint8_t* guide,
+                            uint8_t* scales, float* gscale_out, uint16_t* y_rollout_opt, void* work,
+                            int64_t work_bytes, void* stream) {
+  if (!valid_fmt(fmt) || bits < 1 || bits > 4) return TRACE_EINVAL;
+  if (groups < 1 || groups > kMaxOffsetGroups) return TRACE_ESHAPE;
+  if (row_offsets == nullptr) return TRACE_EINVAL;
+  if (fmt == TRACE_FMT_MXFP4) {  // no global scale: the groups do not change anything
+    if (gscale_out != nullptr) return TRACE_EINVAL;
+    return run_rtn(fmt, bits, rows, cols, 0, x_rollout, nullptr, guide, scales, nullptr, y_rollout_opt,
+                   nullptr, 0, stream);
+  }
+  CallShape cs;
+  int st = shape_of(fmt, rows, cols, 0, &cs);
+  if (st != TRACE_OK) return st;
+  if (groups < 1 || groups > kMaxOffsetGroups) return TRACE_ESHAPE;
+  const int64_t n = cs.n;
+  if (row_offsets == nullptr || gscale_out == nullptr) return TRACE_EINVAL;
+  if (n > 0 && (x_rollout == nullptr || guide == nullptr || scales == nullptr)) return TRACE_EINVAL;
+  const int64_t wneed = tfp4::offs_work_bytes(rows, cols, groups);
+  if (tfp4::offs_entries(rows, cols, groups) > INT32_MAX) return TRACE_ESHAPE;
+  if (work == nullptr) return TRACE_EINVAL;
+  if (work_bytes < wneed) return TRACE_ESHAPE;
+  if (!aligned(x_rollout, 16) || !aligned(y_rollout_opt, 16) || !aligned(guide, guide_align(bits)) ||
+      !aligned(gscale_out, 4) || !aligned(row_offsets, 8) || !aligned(work, 8))
+    return TRACE_EALIGN;
+  const Range ins[] = {{x_rollout, 2 * n}, {row_offsets, 8 * (groups + 1)}};
+  const Range outs[] = {{guide, guide_bytes(bits, n)}, {scales, n / block_of(fmt)},
+                        {gscale_out, 8 * groups}, {y_rollout_opt, 2 * n}, {work, wneed}};
+  if (any_alias(outs, ins)) return TRACE_EALIAS;
+  st = check_device();
+  if (st != TRACE_OK) return st;
+  return launched(tfp4::launch_encode_offsets(bits, rows, cols, groups, row_offsets, x_rollout, guide,
+                                              scales, gscale_out, y_rollout_opt, work,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int guided_fake_quant_grouped(int fmt, int bits, int64_t rows, int64_t cols, int64_t groups,
+                              const int64_t* row_offsets, const uint16_t* x_train, const uint8_t* guide,
+                              const uint8_t* scales, const float* gscale, uint16_t* y, uint8_t* codes_opt,
+                              void* work, int64_t work_bytes, void* stream) {
+  if (!valid_fmt(fmt) || bits < 0 || bits > 4) return TRACE_EINVAL;
+  if (groups < 1 || groups > kMaxOffsetGroups) return TRACE_ESHAPE;
+  if (row_offsets == nullptr) return TRACE_EINVAL;
+  if (fmt == TRACE_FMT_MXFP4)
+    return run_guided(fmt, bits, rows, cols, 0, x_train, nullptr, false, guide, scales, gscale, y,
+                      codes_opt, nullptr, nullptr, 0, nullptr, 0, stream);
+  CallShape cs;
+  int st = shape_of(fmt, rows, cols, 0, &cs);
+  if (st != TRACE_OK) return st;
+  if (groups < 1 || groups > kMaxOffsetGroups) return TRACE_ESHAPE;
+  const int64_t n = cs.n;
+  st = check_train(fmt, n, x_train, guide, bits != 0, scales, gscale);
+  if (st != TRACE_OK) return st;
+  if (row_offsets == nullptr || (n > 0 && y == nullptr)) return TRACE_EINVAL;
+  const int64_t wneed = tfp4::offs_work_bytes(rows, cols, groups);
+  if (tfp4::offs_entries(rows, cols, groups) > INT32_MAX) return TRACE_ESHAPE;
+  if (work == nullptr) return TRACE_EINVAL;
+  if (work_bytes < wneed) return TRACE_ESHAPE;
+  if (!aligned(x_train, 16) || !aligned(y, 16) || !aligned(codes_opt, 4) ||
+      !aligned(guide, guide_align(bits)) || !aligned(gscale, 4) || !aligned(row_offsets, 8) ||
+      !aligned(work, 8))
+    return TRACE_EALIGN;
+  const Range ins[] = {{x_train, 2 * n}, {guide, guide_bytes(bits, n)}, {scales, n / block_of(fmt)},
+                       {gscale, 8 * groups}, {row_offsets, 8 * (groups + 1)}};
+  const Range outs[] = {{y, 2 * n}, {codes_opt, n / 2}, {work, wneed}};
+  if (any_alias(outs, ins)) return TRACE_EALIAS;
+  st = check_device();
+  if (st != TRACE_OK) return st;
+  return launched(tfp4::launch_guided_offsets(bits, rows, cols, groups, row_offsets, x_train, guide, scales,
+                                              gscale, y, codes_opt, work, static_cast<hipStream_t>(stream)));
 }
 
 int discrepancy_stats(int64_t n, const uint16_t* x_t, const uint16_t* x_r, const uint16_t* y_t,

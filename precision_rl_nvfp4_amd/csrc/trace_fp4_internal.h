@@ -60,6 +60,21 @@ hipError_t launch_guided(int fmt, int bits, bool decode_only, const Shape& sh,
                          double* acc3, int64_t* counts, int accumulate, void* work,
                          hipStream_t stream);
 
+// Row-offset groups (NVFP4): groups are the row ranges [off[g], off[g + 1])
+// given by a device array of G + 1 row offsets (clamped into [0, rows] and
+// made nondecreasing on the device; rows outside [off[0], off[G]) are not
+// touched). Workspace: offs_work_bytes; the launches use offs_entries
+// workgroups (tiles of every group, plus slack of one per group).
+int64_t offs_work_bytes(int64_t rows, int64_t cols, int64_t groups);
+int64_t offs_entries(int64_t rows, int64_t cols, int64_t groups);
+hipError_t launch_encode_offsets(int bits, int64_t rows, int64_t cols, int64_t G, const int64_t* off_in,
+                                 const uint16_t* x, uint8_t* plane, uint8_t* scales, float* gout,
+                                 uint16_t* y, void* work, hipStream_t stream);
+hipError_t launch_guided_offsets(int bits, int64_t rows, int64_t cols, int64_t G, const int64_t* off_in,
+                                 const uint16_t* x, const uint8_t* guide, const uint8_t* scales,
+                                 const float* gscale, uint16_t* y, uint8_t* codes, void* work,
+                                 hipStream_t stream);
+
 // TRACE_OK when the current device is a gfx950, else TRACE_EDEVICE (cached
 // per device).
 int check_device();

@@ -416,6 +416,10 @@ __device__ __forceinline__ double sq_diff_sum(const float (&a)[8], const float (
 // group (tiles = tiles per group). Packed (NVFP4 groups of a power-of-two
 // unit count below kTileUnits, e.g. one token's row): a tile holds
 // kTileUnits >> lg whole consecutive groups (tiles = tiles of the call).
+// Row-offset groups (groups of any size, e.g. the experts of a grouped MoE
+// input): a device table gives each workgroup its (group, tile); groups are
+// the row ranges [offs[g], offs[g + 1]), tiles of group g are table entries
+// tstart[g] .. tstart[g + 1] - 1, and entries past the last are (-1, 0).
 struct TileMap {
   int64_t upg;        // units per group
   int64_t tiles;      // tiles per group, or of the call when packed
@@ -423,6 +427,12 @@ struct TileMap {
   int64_t groups;     // groups of the call
   int lg;             // log2(upg) when packed
   int packed;
+  // row-offset groups
+  const int64_t* offs;   // [groups + 1] row offsets (clamped, nondecreasing)
+  const int32_t* tstart; // [groups + 1] first table entry of each group
+  const int2* table;     // [entries] (group, tile within the group)
+  const uint32_t* tpart; // [entries] tile maxima (bf16 magnitude bits)
+  int64_t upr;           // units per row
 };
 
 __device__ __forceinline__ void tile_of(const TileMap& m, int64_t& g, int64_t& tbase) {
@@ -556,16 +566,27 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
       return;
     }
   }
-  int64_t g, tbase;
+  int64_t g, tbase, gbase, lim;
+  int tk = 0;  // tile within the group (row-offset groups)
   if constexpr (PACK) {
     g = 0;
     tbase = (int64_t)blockIdx.x * kTileUnits;
+    gbase = 0;
+    lim = a.map.units;
+  } else if constexpr (SSRC == 3) {
+    const int2 e = a.map.table[blockIdx.x];
+    if (e.x < 0) return;
+    g = e.x;
+    tk = e.y;
+    tbase = (int64_t)e.y * kTileUnits;
+    gbase = a.map.offs[g] * a.map.upr;
+    lim = a.map.offs[g + 1] * a.map.upr - gbase;
   } else {
     tile_of(a.map, g, tbase);
     g += a.g0;
+    gbase = g * a.map.upg;
+    lim = a.map.upg;
   }
-  const int64_t gbase = PACK ? 0 : g * a.map.upg;
-  const int64_t lim = PACK ? a.map.units : a.map.upg;
   // Issue the tile's loads first; the scale and its factor table follow.
   uint4 v[kUPT];
 #pragma unroll
@@ -608,7 +629,21 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
     }
     __syncthreads();
   } else if constexpr (FMT == 0) {
-    if constexpr (SSRC == 1) {
+    if constexpr (SSRC == 3) {
+      uint32_t m = 0;
+      const int32_t t0 = a.map.tstart[g], t1 = a.map.tstart[g + 1];
+      for (int i = t0 + (int)threadIdx.x; i < t1; i += kThreads) m = max(m, a.map.tpart[i]);
+      m = wave_max_u32(m);
+      if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+      __syncthreads();
+      m = max(max(red[0], red[1]), max(red[2], red[3]));
+      const float A = __uint_as_float(m << 16);
+      S = global_scale(A);
+      if (tk == 0 && threadIdx.x == 0) {
+        a.gout[2 * g] = S;
+        a.gout[2 * g + 1] = A;
+      }
+    } else if constexpr (SSRC == 1) {
       uint32_t m = 0;
       for (int i = threadIdx.x; i < a.nparts; i += kThreads) m = max(m, a.part[g * kPartMax + i]);
       m = wave_max_u32(m);
@@ -830,27 +865,143 @@ __global__ __launch_bounds__(kThreads) void zero_words_kernel(uint32_t* p, int64
     p[i] = 0u;
 }
 
+// ---- row-offset groups (e.g. one global scale per expert of a grouped MoE input)
+
+// One workgroup. From the caller's row offsets (read only here) it derives
+// offs = the running max of clamp(off, 0, rows), so groups are disjoint row
+// ranges, and tstart = the exclusive prefix sum of each group's tile count.
+// Empty groups get {S, A} = {1, 0} in gout (if given): no tile writes them.
+__global__ __launch_bounds__(kThreads) void offs_prep_kernel(const int64_t* __restrict__ off_in,
+                                                            int64_t G, int64_t rows, int64_t upr,
+                                                            int64_t* offs, int32_t* tstart, float* gout) {
+  __shared__ int64_t part[kThreads];
+  const int64_t n = G + 1;
+  const int64_t per = (n + kThreads - 1) / kThreads;
+  const int64_t i0 = min((int64_t)threadIdx.x * per, n), i1 = min(i0 + per, n);
+  // 1. running max of the clamped offsets
+  int64_t m = 0;
+  for (int64_t i = i0; i < i1; ++i) m = max(m, min(max(off_in[i], (int64_t)0), rows));
+  part[threadIdx.x] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int64_t run = 0;
+    for (int k = 0; k < kThreads; ++k) {
+      const int64_t v = part[k];
+      part[k] = run;   // max over the chunks before k
+      run = max(run, v);
+    }
+  }
+  __syncthreads();
+  m = part[threadIdx.x];
+  for (int64_t i = i0; i < i1; ++i) {
+    m = max(m, min(max(off_in[i], (int64_t)0), rows));
+    offs[i] = m;
+  }
+  __syncthreads();
+  // 2. tiles per group, exclusive prefix sum
+  const int64_t gper = (G + kThreads - 1) / kThreads;
+  const int64_t g0 = min((int64_t)threadIdx.x * gper, G), g1 = min(g0 + gper, G);
+  int64_t t = 0;
+  for (int64_t g = g0; g < g1; ++g) t += ((offs[g + 1] - offs[g]) * upr + kTileUnits - 1) / kTileUnits;
+  __syncthreads();
+  part[threadIdx.x] = t;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int64_t run = 0;
+    for (int k = 0; k < kThreads; ++k) {
+      const int64_t v = part[k];
+      part[k] = run;
+      run += v;
+    }
+    tstart[G] = (int32_t)run;
+  }
+  __syncthreads();
+  t = part[threadIdx.x];
+  for (int64_t g = g0; g < g1; ++g) {
+    tstart[g] = (int32_t)t;
+    const int64_t tg = ((offs[g + 1] - offs[g]) * upr + kTileUnits - 1) / kTileUnits;
+    if (tg == 0 && gout != nullptr) {
+      gout[2 * g] = 1.0f;
+      gout[2 * g + 1] = 0.0f;
+    }
+    t += tg;
+  }
+}
+
+// table[e] = (group, tile within the group) for e < tstart[G], (-1, 0) after.
+__global__ __launch_bounds__(kThreads) void tile_table_kernel(const int32_t* __restrict__ tstart,
+                                                             int64_t G, int64_t entries, int2* table) {
+  const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (e >= entries) return;
+  const int32_t total = tstart[G];
+  if (e >= total) {
+    table[e] = make_int2(-1, 0);
+    return;
+  }
+  // last g with tstart[g] <= e (empty groups share their start with the next)
+  int64_t lo = 0, hi = G - 1;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) >> 1;
+    if (tstart[mid] <= e) lo = mid;
+    else hi = mid - 1;
+  }
+  table[e] = make_int2((int)lo, (int)(e - tstart[lo]));
+}
+
+// Tile maxima of row-offset groups: tpart[e] for table entry e.
+__global__ __launch_bounds__(kThreads) void tile_amax_kernel(TileMap m, const uint4* __restrict__ x,
+                                                            uint32_t* tpart) {
+  __shared__ uint32_t red[kThreads / 64];
+  const int2 e = m.table[blockIdx.x];
+  if (e.x < 0) return;
+  const int64_t gbase = m.offs[e.x] * m.upr;
+  const int64_t lim = m.offs[e.x + 1] * m.upr - gbase;
+  const int64_t tbase = (int64_t)e.y * kTileUnits;
+  uint32_t mx = 0;
+#pragma unroll
+  for (int j = 0; j < kUPT; ++j) {
+    const int64_t u = tbase + j * kThreads + threadIdx.x;
+    if (u < lim) mx = max(mx, unit_amax_bits(load_stream(x + gbase + u)));
+  }
+  mx = wave_max_u32(mx);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0) tpart[blockIdx.x] = max(max(red[0], red[1]), max(red[2], red[3]));
+}
+
 // Guided rounding under the rollout scales (guided_fake_quant), Reconstruct
 // alone (DECODE: reference codes, no y), and the fused discrepancy sums
 // (STATS: SB = sum (x_t - x_r)^2 over the inputs; SF = sum (y_t - y_r)^2 with
 // y_r the rollout's RTN output under the same scales, recomputed from x_r).
-template <int FMT, int BITS, bool DECODE, bool WCODES, bool STATS, bool DIAG, bool PACK>
+template <int FMT, int BITS, bool DECODE, bool WCODES, bool STATS, bool DIAG, int MAP>
 __global__ __launch_bounds__(kThreads) void guided_kernel(GuidedArgs a) {
+  // MAP 0: one group per tile; 1: packed small groups; 2: row-offset groups.
+  constexpr bool PACK = MAP == 1;
+  static_assert(!(MAP == 2 && STATS), "row-offset groups take no fused statistics");
   __shared__ float2 lut[PACK ? 1 : 128];
   __shared__ float gs[PACK ? kPackGroups : 1];     // S of the tile's groups (packed)
   __shared__ uint32_t hist[DIAG ? kMismatchCounts : 1];
-  int64_t g, tbase;
+  int64_t g, tbase, gbase, lim;
   if constexpr (PACK) {
     g = 0;
     tbase = (int64_t)blockIdx.x * kTileUnits;
+    gbase = 0;
+    lim = a.map.units;
+  } else if constexpr (MAP == 2) {
+    const int2 e = a.map.table[blockIdx.x];
+    if (e.x < 0) return;
+    g = e.x;
+    tbase = (int64_t)e.y * kTileUnits;
+    gbase = a.map.offs[g] * a.map.upr;
+    lim = a.map.offs[g + 1] * a.map.upr - gbase;
   } else {
     tile_of(a.map, g, tbase);
+    gbase = g * a.map.upg;
+    lim = a.map.upg;
   }
   if constexpr (DIAG) {
     if (threadIdx.x < kMismatchCounts) hist[threadIdx.x] = 0u;
   }
-  const int64_t gbase = PACK ? 0 : g * a.map.upg;
-  const int64_t lim = PACK ? a.map.units : a.map.upg;
   // Issue the tile's loads first; the factor table is built while they fly.
   uint4 v[kUPT];
   uint4 vr[STATS ? kUPT : 1];
@@ -1123,7 +1274,8 @@ hipError_t quant_go(const QuantArgs& a, int64_t blocks, hipStream_t s) {
 }
 
 // `blocks`: the launch's workgroups (quantize tiles, then side amax work).
-// ssrc: 0 S given, 1 S from amax partials, 2 S from the tile's own groups (packed).
+// ssrc: 0 S given, 1 S from amax partials, 2 S from the tile's own groups
+// (packed), 3 S from the tile maxima of row-offset groups.
 template <int FMT, int PLANE, bool WY>
 hipError_t quant_src(int ssrc, bool pack, const QuantArgs& a, int64_t blocks, hipStream_t s) {
   if constexpr (FMT == 1) {
@@ -1131,6 +1283,7 @@ hipError_t quant_src(int ssrc, bool pack, const QuantArgs& a, int64_t blocks, hi
   } else {
     if (pack) return ssrc ? quant_go<0, PLANE, WY, 2, true>(a, blocks, s)
                           : quant_go<0, PLANE, WY, 0, true>(a, blocks, s);
+    if (ssrc == 3) return quant_go<0, PLANE, WY, 3, false>(a, blocks, s);
     return ssrc ? quant_go<0, PLANE, WY, 1, false>(a, blocks, s)
                 : quant_go<0, PLANE, WY, 0, false>(a, blocks, s);
   }
@@ -1222,38 +1375,41 @@ hipError_t launch_onepass(int plane_mode, bool wy, const Shape& sh, const QuantA
   return e;
 }
 
-template <int FMT, int BITS, bool DECODE, bool WCODES, bool STATS, bool DIAG, bool PACK>
-hipError_t guided_go(const GuidedArgs& a, hipStream_t s) {
-  return launch(guided_kernel<FMT, BITS, DECODE, WCODES, STATS, DIAG, PACK>,
-                dim3((unsigned)tile_grid(a.map)), dim3(kThreads), s, a);
+template <int FMT, int BITS, bool DECODE, bool WCODES, bool STATS, bool DIAG, int MAP>
+hipError_t guided_go(const GuidedArgs& a, int64_t blocks, hipStream_t s) {
+  return launch(guided_kernel<FMT, BITS, DECODE, WCODES, STATS, DIAG, MAP>, dim3((unsigned)blocks),
+                dim3(kThreads), s, a);
 }
 
-template <int FMT, int BITS, bool PACK>
-hipError_t guided_bits(bool wc, bool stats, bool diag, const GuidedArgs& a, hipStream_t s) {
-  if (diag) return wc ? guided_go<FMT, BITS, false, true, true, true, PACK>(a, s)
-                      : guided_go<FMT, BITS, false, false, true, true, PACK>(a, s);
-  if (stats) return wc ? guided_go<FMT, BITS, false, true, true, false, PACK>(a, s)
-                       : guided_go<FMT, BITS, false, false, true, false, PACK>(a, s);
-  return wc ? guided_go<FMT, BITS, false, true, false, false, PACK>(a, s)
-            : guided_go<FMT, BITS, false, false, false, false, PACK>(a, s);
-}
-
-template <int FMT, bool PACK>
-hipError_t guided_pack(int bits, bool decode, bool wc, bool stats, bool diag, const GuidedArgs& a,
+template <int FMT, int BITS, int MAP>
+hipError_t guided_bits(bool wc, bool stats, bool diag, const GuidedArgs& a, int64_t blocks,
                        hipStream_t s) {
+  if constexpr (MAP != 2) {
+    if (diag) return wc ? guided_go<FMT, BITS, false, true, true, true, MAP>(a, blocks, s)
+                        : guided_go<FMT, BITS, false, false, true, true, MAP>(a, blocks, s);
+    if (stats) return wc ? guided_go<FMT, BITS, false, true, true, false, MAP>(a, blocks, s)
+                         : guided_go<FMT, BITS, false, false, true, false, MAP>(a, blocks, s);
+  }
+  return wc ? guided_go<FMT, BITS, false, true, false, false, MAP>(a, blocks, s)
+            : guided_go<FMT, BITS, false, false, false, false, MAP>(a, blocks, s);
+}
+
+template <int FMT, int MAP>
+hipError_t guided_pack(int bits, bool decode, bool wc, bool stats, bool diag, const GuidedArgs& a,
+                       int64_t blocks, hipStream_t s) {
   if (decode) {
     switch (bits) {
-      case 1: return guided_go<FMT, 1, true, true, false, false, PACK>(a, s);
-      case 2: return guided_go<FMT, 2, true, true, false, false, PACK>(a, s);
-      default: return guided_go<FMT, 3, true, true, false, false, PACK>(a, s);
+      case 1: return guided_go<FMT, 1, true, true, false, false, MAP>(a, blocks, s);
+      case 2: return guided_go<FMT, 2, true, true, false, false, MAP>(a, blocks, s);
+      default: return guided_go<FMT, 3, true, true, false, false, MAP>(a, blocks, s);
     }
   }
   switch (bits) {
-    case 0: return guided_bits<FMT, 0, PACK>(wc, stats, diag, a, s);
-    case 1: return guided_bits<FMT, 1, PACK>(wc, stats, diag, a, s);
-    case 2: return guided_bits<FMT, 2, PACK>(wc, stats, diag, a, s);
-    case 3: return guided_bits<FMT, 3, PACK>(wc, stats, diag, a, s);
-    default: return guided_bits<FMT, 4, PACK>(wc, stats, diag, a, s);
+    case 0: return guided_bits<FMT, 0, MAP>(wc, stats, diag, a, blocks, s);
+    case 1: return guided_bits<FMT, 1, MAP>(wc, stats, diag, a, blocks, s);
+    case 2: return guided_bits<FMT, 2, MAP>(wc, stats, diag, a, blocks, s);
+    case 3: return guided_bits<FMT, 3, MAP>(wc, stats, diag, a, blocks, s);
+    default: return guided_bits<FMT, 4, MAP>(wc, stats, diag, a, blocks, s);
   }
 }
 
@@ -1380,9 +1536,9 @@ hipError_t launch_guided(int fmt, int bits, bool decode_only, const Shape& sh, c
   if (stats) a.cpart = reinterpret_cast<uint32_t*>(a.partials + 2 * (tiles + kMidGroups));
   const bool wc = codes != nullptr;
   hipError_t e;
-  if (fmt == 1) e = guided_pack<1, false>(bits, decode_only, wc, stats, diag, a, stream);
-  else if (a.map.packed) e = guided_pack<0, true>(bits, decode_only, wc, stats, diag, a, stream);
-  else e = guided_pack<0, false>(bits, decode_only, wc, stats, diag, a, stream);
+  if (fmt == 1) e = guided_pack<1, 0>(bits, decode_only, wc, stats, diag, a, tiles, stream);
+  else if (a.map.packed) e = guided_pack<0, 1>(bits, decode_only, wc, stats, diag, a, tiles, stream);
+  else e = guided_pack<0, 0>(bits, decode_only, wc, stats, diag, a, tiles, stream);
   if (e != hipSuccess || !stats) return e;
   if (diag) {
     e = launch(counts_final_kernel, dim3(kMismatchCounts), dim3(kThreads), stream,
@@ -1414,4 +1570,89 @@ hipError_t launch_stats(int64_t n, const uint16_t* xt, const uint16_t* xr, const
 
 namespace tfp4 {
 int64_t set_encode_batch(int64_t groups) { return g_encode_batch.exchange(groups); }
+
+// ---- row-offset groups: workspace [offs | tstart | table | tile maxima]
+
+namespace {
+struct OffsLayout {
+  int64_t entries, b_offs, b_tstart, b_table, b_tpart, total;
+};
+OffsLayout offs_layout(int64_t rows, int64_t cols, int64_t G) {
+  OffsLayout L{};
+  const int64_t units = rows * (cols / kUnitElems);
+  L.entries = (units + kTileUnits - 1) / kTileUnits + G;
+  auto up8 = [](int64_t b) { return (b + 7) / 8 * 8; };
+  L.b_offs = 0;
+  L.b_tstart = up8(8 * (G + 1));
+  L.b_table = L.b_tstart + up8(4 * (G + 1));
+  L.b_tpart = L.b_table + 8 * L.entries;
+  L.total = L.b_tpart + up8(4 * L.entries);
+  return L;
+}
+
+// Derives offs / tstart / table in the workspace; fills the map's fields.
+hipError_t offs_prepare(int64_t rows, int64_t cols, int64_t G, const int64_t* off_in, float* gout,
+                        void* work, TileMap* m, hipStream_t stream) {
+  const OffsLayout L = offs_layout(rows, cols, G);
+  uint8_t* w = static_cast<uint8_t*>(work);
+  *m = TileMap{};
+  m->offs = reinterpret_cast<const int64_t*>(w + L.b_offs);
+  m->tstart = reinterpret_cast<const int32_t*>(w + L.b_tstart);
+  m->table = reinterpret_cast<const int2*>(w + L.b_table);
+  m->tpart = reinterpret_cast<const uint32_t*>(w + L.b_tpart);
+  m->upr = cols / kUnitElems;
+  m->groups = G;
+  m->units = rows * m->upr;
+  hipError_t e = launch(offs_prep_kernel, dim3(1), dim3(kThreads), stream, off_in, G, rows, m->upr,
+                        reinterpret_cast<int64_t*>(w + L.b_offs), reinterpret_cast<int32_t*>(w + L.b_tstart),
+                        gout);
+  if (e != hipSuccess) return e;
+  return launch(tile_table_kernel, dim3((unsigned)((L.entries + kThreads - 1) / kThreads)), dim3(kThreads),
+                stream, m->tstart, G, L.entries, reinterpret_cast<int2*>(w + L.b_table));
+}
+}  // namespace
+
+int64_t offs_work_bytes(int64_t rows, int64_t cols, int64_t groups) {
+  return offs_layout(rows, cols, groups).total;
+}
+
+int64_t offs_entries(int64_t rows, int64_t cols, int64_t groups) {
+  return offs_layout(rows, cols, groups).entries;
+}
+
+hipError_t launch_encode_offsets(int bits, int64_t rows, int64_t cols, int64_t G, const int64_t* off_in,
+                                 const uint16_t* x, uint8_t* plane, uint8_t* scales, float* gout,
+                                 uint16_t* y, void* work, hipStream_t stream) {
+  QuantArgs a{};
+  hipError_t e = offs_prepare(rows, cols, G, off_in, gout, work, &a.map, stream);
+  if (e != hipSuccess) return e;
+  const int64_t entries = offs_layout(rows, cols, G).entries;
+  a.x = reinterpret_cast<const uint4*>(x);
+  a.gout = gout;
+  a.plane = plane;
+  a.scales = scales;
+  a.y = reinterpret_cast<uint4*>(y);
+  a.qblocks = entries;
+  e = launch(tile_amax_kernel, dim3((unsigned)entries), dim3(kThreads), stream, a.map, a.x,
+             const_cast<uint32_t*>(a.map.tpart));
+  if (e != hipSuccess) return e;
+  return quant_plane<0>(bits, y != nullptr, 3, false, a, entries, stream);
+}
+
+hipError_t launch_guided_offsets(int bits, int64_t rows, int64_t cols, int64_t G, const int64_t* off_in,
+                                 const uint16_t* x, const uint8_t* guide, const uint8_t* scales,
+                                 const float* gscale, uint16_t* y, uint8_t* codes, void* work,
+                                 hipStream_t stream) {
+  GuidedArgs a{};
+  hipError_t e = offs_prepare(rows, cols, G, off_in, nullptr, work, &a.map, stream);
+  if (e != hipSuccess) return e;
+  const int64_t entries = offs_layout(rows, cols, G).entries;
+  a.x = reinterpret_cast<const uint4*>(x);
+  a.guide = guide;
+  a.scales = scales;
+  a.gscale = gscale;
+  a.y = reinterpret_cast<uint4*>(y);
+  a.codes = reinterpret_cast<uint32_t*>(codes);
+  return guided_pack<0, 2>(bits, false, codes != nullptr, false, false, a, entries, stream);
+}
 }  // namespace tfp4

@@ -51,7 +51,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.trace_abi_version() == _abi.ABI_VERSION == 5
+    assert lib.trace_abi_version() == _abi.ABI_VERSION == 6
     for code, name in [(0, "TRACE_OK"), (-1, "TRACE_EINVAL"), (-2, "TRACE_ESHAPE"),
                        (-3, "TRACE_EALIGN"), (-4, "TRACE_EALIAS"), (-5, "TRACE_EDEVICE"),
                        (-6, "TRACE_ELAUNCH"), (-7, "TRACE_EBUSY"), (7, "unknown status")]:
@@ -294,3 +294,63 @@ def test_gather_rejects(lib, args, status):
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is visible: valid calls would launch")
 def test_gather_without_gpu_is_edevice(lib):
     assert lib.trace_gather_pages(A, 4, 16, B, 2, C, D, None) == _abi.EDEVICE
+
+
+# ---------------------------------------------------------------- row-offset groups
+
+def test_grouped_workspace_sizes(lib):
+    # [offs int64 G+1 | tstart int32 G+1 | table int2 x entries | tile maxima u32 x entries],
+    # entries = tiles of the call + one per group
+    up8 = lambda b: (b + 7) // 8 * 8  # noqa: E731
+    for rows, cols, G in [(1000, 2048, 9), (65536, 2048, 256), (4, 32, 1)]:
+        entries = (rows * cols // 8 + 2047) // 2048 + G
+        want = up8(8 * (G + 1)) + up8(4 * (G + 1)) + 8 * entries + up8(4 * entries)
+        assert lib.trace_grouped_workspace_bytes(0, rows, cols, G) == want
+    assert lib.trace_grouped_workspace_bytes(1, 64, 2048, 4) == 0
+    assert lib.trace_grouped_workspace_bytes(0, 64, 2048, 0) == -1
+    assert lib.trace_grouped_workspace_bytes(0, 64, 24, 2) == -1
+
+
+GW = 0x900000   # fake workspace for the grouped calls
+GWB = 1 << 16
+O = 0xA00000    # fake device offsets
+# encode_guidance_grouped(fmt, bits, rows, cols, G, offs, x, guide, scales, gout, y, work, wb, stream)
+@pytest.mark.parametrize("args,status", [
+    ((0, 0, 4, 32, 2, O, A, B, C, D, None, GW, GWB, None), _abi.EINVAL),     # bits 0
+    ((0, 1, 4, 32, 0, O, A, B, C, D, None, GW, GWB, None), _abi.ESHAPE),    # no groups
+    ((0, 1, 4, 32, 2, None, A, B, C, D, None, GW, GWB, None), _abi.EINVAL),  # NULL offsets
+    ((0, 1, 4, 32, 2, O, A, B, C, None, None, GW, GWB, None), _abi.EINVAL),  # NVFP4 needs gscale_out
+    ((1, 1, 4, 32, 2, O, A, B, C, D, None, None, 0, None), _abi.EINVAL),    # MXFP4 takes none
+    ((0, 1, 4, 32, 2, O, A, B, C, D, None, None, GWB, None), _abi.EINVAL),  # NULL work
+    ((0, 1, 4, 32, 2, O, A, B, C, D, None, GW, 8, None), _abi.ESHAPE),      # work too small
+    ((0, 1, 4, 24, 2, O, A, B, C, D, None, GW, GWB, None), _abi.ESHAPE),    # cols % 16
+    ((0, 1, 4, 32, 2, O + 4, A, B, C, D, None, GW, GWB, None), _abi.EALIGN),  # offsets alignment
+    ((0, 1, 4, 32, 2, O, A, B, C, D, None, GW + 4, GWB, None), _abi.EALIGN),  # work alignment
+    ((0, 1, 4, 32, 2, O, A, B, C, O + 8, None, GW, GWB, None), _abi.EALIAS),  # gscale over offsets
+    ((0, 1, 4, 32, 2, O, A, B, C, D, None, A + 64, GWB, None), _abi.EALIAS),  # work over x
+])
+def test_encode_grouped_rejects(lib, args, status):
+    assert lib.encode_guidance_grouped(*args) == status
+
+
+# guided_fake_quant_grouped(fmt, bits, rows, cols, G, offs, x, guide, scales, gscale, y, codes, work, wb, stream)
+@pytest.mark.parametrize("args,status", [
+    ((0, 5, 4, 32, 2, O, A, B, C, E, D, None, GW, GWB, None), _abi.EINVAL),    # bits 5
+    ((0, 1, 4, 32, -1, O, A, B, C, E, D, None, GW, GWB, None), _abi.ESHAPE),  # negative groups
+    ((0, 1, 4, 32, 2, None, A, B, C, E, D, None, GW, GWB, None), _abi.EINVAL),  # NULL offsets
+    ((0, 1, 4, 32, 2, O, A, B, C, None, D, None, GW, GWB, None), _abi.EINVAL),  # NVFP4 needs gscale
+    ((0, 0, 4, 32, 2, O, A, B, C, E, D, None, GW, GWB, None), _abi.EINVAL),    # bits 0 takes no guide
+    ((0, 1, 4, 32, 2, O, A, B, C, E, None, None, GW, GWB, None), _abi.EINVAL),  # NULL y
+    ((0, 1, 4, 32, 2, O, A, B, C, E, D, None, GW, 8, None), _abi.ESHAPE),      # work too small
+    ((0, 1, 4, 32, 2, O, A, B, C, E, D + 8, None, GW, GWB, None), _abi.EALIGN),  # y alignment
+    ((0, 1, 4, 32, 2, O, A, B, C, E, O, None, GW, GWB, None), _abi.EALIAS),    # y over offsets
+    ((0, 1, 4, 32, 2, O, A, B, C, E, D, None, E, GWB, None), _abi.EALIAS),     # work over gscale
+])
+def test_guided_grouped_rejects(lib, args, status):
+    assert lib.guided_fake_quant_grouped(*args) == status
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is visible: valid calls would launch")
+def test_grouped_without_gpu_is_edevice(lib):
+    assert lib.encode_guidance_grouped(0, 1, 4, 32, 2, O, A, B, C, D, None, GW, GWB, None) == _abi.EDEVICE
+    assert lib.guided_fake_quant_grouped(0, 1, 4, 32, 2, O, A, B, C, E, D, None, GW, GWB, None) == _abi.EDEVICE

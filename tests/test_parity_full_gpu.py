@@ -260,3 +260,33 @@ def test_tiny_pair_whole_tensor():
         G.check_guided_stats(xt_b, xr_b, 256, 2048, NV, bits)
     G.check_guided(xt_b, xr_b, 256, 2048, NV, 0)
     G.check_decode(xt_b, xr_b, 256, 2048, NV)
+
+
+def test_moe_layer_per_expert_scales():
+    """The MoE layer [65536, 2048] with one global scale per expert (256
+    experts, offsets straight from routing): every expert's S against the
+    oracle's amax of its rows; experts sampled whole against the oracle."""
+    G.say("full size: MoE layer, per-expert scales")
+    xt, xr, _, offsets = syn.moe_pair(20, device=G.DEV)
+    rows, cols = xt.shape
+    g = tq.encode_guidance_grouped(xr, offsets, NV, 1, with_y=True)
+    y, codes = tq.guided_fake_quant(xt, g, with_codes=True)
+    torch.cuda.synchronize()
+    offs = offsets.cpu().numpy()
+    amax = (xr.view(torch.int16) & 0x7FFF).amax(dim=1).cpu().numpy().astype(np.uint16)
+    gs = G.f32(g.gscale).reshape(-1, 2)
+    xt_b, xr_b = _bits(xt), _bits(xr)
+    for e in range(len(offs) - 1):
+        r0, r1 = int(offs[e]), int(offs[e + 1])
+        A = ofp4.bf16_to_f32(amax[r0:r1]).max() if r1 > r0 else np.float32(0)
+        assert gs[e, 1] == A and gs[e, 0] == ofp4.nvfp4_global_scale(A), e
+    for e in (0, 1, 77, 128, 255):
+        r0, r1 = int(offs[e]), int(offs[e + 1])
+        es = slice(r0 * cols, r1 * cols)
+        o = ofp4.encode_guidance(NV, 1, xr_b[es])
+        og = ofp4.guided_fake_quant(NV, 1, xt_b[es], o["guide"], o["scales"], o["gscale"])
+        G.assert_same(G.u8(g.guide).reshape(-1)[r0 * cols // 8:r1 * cols // 8], o["guide"], f"expert {e} guide")
+        G.assert_same(G.u8(g.scales).reshape(-1)[r0 * cols // 16:r1 * cols // 16], o["scales"], "scales")
+        G.assert_same(_bits(g.y)[es], o["y"], f"expert {e} rollout y")
+        G.assert_same(_bits(y)[es], og["y"], f"expert {e} guided y")
+        G.assert_same(G.u8(codes).reshape(-1)[r0 * cols // 2:r1 * cols // 2], og["codes"], "guided codes")

@@ -518,3 +518,105 @@ def test_single_pass_encode_waits_never_time_out(G_, gr, cols):
     G.assert_same(G.u8(g.guide), o["guide"], "guide")
     G.assert_same(G.bits_of(g.y), o["y"], "rollout y")
     G.assert_same(G.f32(g.gscale).reshape(-1, 2)[:, 0], o["gscale"], "S")
+
+
+# ---------------------------------------------------------------- row-offset groups
+
+def _offset_groups_pair(sizes, cols, seed):
+    """Consecutive groups of the given row counts (some empty), each with its
+    own magnitude."""
+    xs, rs = [], []
+    for g, n in enumerate(sizes):
+        if n == 0:
+            continue
+        xt, xr = syn.activation_pair(n, cols, (94, seed, g))
+        k = float(2.0 ** (3 * (g % 7) - 6)) * (1.0 + 0.29 * (g % 3))
+        xs.append((xt.float() * k).to(torch.bfloat16))
+        rs.append((xr.float() * k).to(torch.bfloat16))
+    return syn.bits_u16(torch.cat(xs)).reshape(-1), syn.bits_u16(torch.cat(rs)).reshape(-1)
+
+
+def _oracle_offsets(fmt, bits, xt_b, xr_b, cols, offs):
+    """The oracle per group: each group's rows as one tensor."""
+    enc, gd, S = [], [], []
+    for g in range(len(offs) - 1):
+        r0, r1 = int(offs[g]), int(offs[g + 1])
+        es = slice(r0 * cols, r1 * cols)
+        if r1 == r0:
+            S.append((1.0, 0.0))
+            continue
+        o = ofp4.encode_guidance(fmt, 4 if bits == 0 else bits, xr_b[es])
+        og = ofp4.guided_fake_quant(fmt, bits, xt_b[es], None if bits == 0 else o["guide"], o["scales"],
+                                    o["gscale"])
+        enc.append(o)
+        gd.append(og)
+        S.append((o["gscale"], o["amax"]))
+    cat = lambda parts, k: np.concatenate([p[k] for p in parts])  # noqa: E731
+    return cat(enc, "guide"), cat(enc, "scales"), cat(enc, "y"), cat(gd, "y"), cat(gd, "codes"), S
+
+
+@pytest.mark.parametrize("sizes,cols", [([0, 37, 1, 300, 0, 0, 512, 100, 50], 2048),
+                                        ([3, 0, 64, 1, 9], 256), ([7], 64), ([0, 0, 5], 16)])
+def test_row_offset_groups(sizes, cols):
+    """encode_guidance_grouped / guided_fake_quant_grouped against the oracle
+    run on each group's rows, every record width; empty groups get {1, 0}."""
+    G.say(f"row-offset groups {sizes} x {cols}")
+    xt_b, xr_b = _offset_groups_pair(sizes, cols, len(sizes))
+    rows = sum(sizes)
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    doffs = torch.from_numpy(offs).to(G.DEV)
+    xt, xr = G.to_dev(xt_b, rows, cols), G.to_dev(xr_b, rows, cols)
+    for bits in (1, 2, 3, 4):
+        g = tq.encode_guidance_grouped(xr, doffs, NV, bits, with_y=True)
+        guide, scales, yr, _, _, S = _oracle_offsets(NV, bits, xt_b, xr_b, cols, offs)
+        G.assert_same(G.u8(g.guide), guide, f"guide bits={bits}")
+        G.assert_same(G.u8(g.scales), scales, "scales")
+        G.assert_same(G.bits_of(g.y), yr, "rollout y")
+        gs = G.f32(g.gscale).reshape(-1, 2)
+        G.assert_same(gs, np.array(S, np.float32), "{S, A} per group")
+        for gb in (bits, 0):
+            y, codes = tq.guided_fake_quant(xt, g, bits=gb, with_codes=True)
+            _, _, _, yg, cg, _ = _oracle_offsets(NV, gb, xt_b, xr_b, cols, offs) if gb == 0 else \
+                _oracle_offsets(NV, bits, xt_b, xr_b, cols, offs)
+            G.assert_same(G.bits_of(y), yg, f"guided y bits={gb}")
+            G.assert_same(G.u8(codes), cg, f"guided codes bits={gb}")
+
+
+def test_row_offset_groups_bad_offsets_and_uncovered_rows():
+    """Offsets outside [0, rows] or decreasing are clamped and made
+    nondecreasing; rows outside [off[0], off[G]) are left untouched."""
+    G.say("row-offset groups: bad offsets, canaries")
+    cols, rows = 256, 40
+    xt_b, xr_b = _offset_groups_pair([rows], cols, 3)
+    xr = G.to_dev(xr_b, rows, cols)
+    bad = np.array([5, -3, 20, 12, 33, 90], np.int64)          # -> 5 5 20 20 33 40
+    eff = np.maximum.accumulate(np.clip(bad, 0, rows))
+    doffs = torch.from_numpy(bad).to(G.DEV)
+    guide = torch.full((rows, cols // 8), 0xA5, dtype=torch.uint8, device=G.DEV)
+    y = torch.full((rows, cols), 0x1234, dtype=torch.int16, device=G.DEV).view(torch.bfloat16)
+    g = tq.encode_guidance_grouped(xr, doffs, NV, 1, with_y=True, guide=guide, y=y)
+    torch.cuda.synchronize()
+    gu, yy = G.u8(g.guide).reshape(rows, -1), G.bits_of(g.y).reshape(rows, -1)
+    assert (gu[:5] == 0xA5).all() and (yy[:5] == 0x1234).all()      # rows before off[0]
+    for k in range(len(eff) - 1):
+        r0, r1 = int(eff[k]), int(eff[k + 1])
+        if r1 == r0:
+            assert tuple(G.f32(g.gscale).reshape(-1, 2)[k]) == (1.0, 0.0)
+            continue
+        o = ofp4.encode_guidance(NV, 1, xr_b[r0 * cols:r1 * cols])
+        G.assert_same(gu[r0:r1].reshape(-1), o["guide"], f"group {k} guide")
+        G.assert_same(yy[r0:r1].reshape(-1), o["y"], f"group {k} y")
+
+
+def test_row_offset_groups_mxfp4_equals_ungrouped():
+    G.say("row-offset groups, MXFP4")
+    xt_b, xr_b = _offset_groups_pair([10, 0, 22], 2048, 5)
+    xt, xr = G.to_dev(xt_b, 32, 2048), G.to_dev(xr_b, 32, 2048)
+    doffs = torch.tensor([0, 10, 10, 32], dtype=torch.int64, device=G.DEV)
+    g1 = tq.encode_guidance_grouped(xr, doffs, MX, 1, with_y=True)
+    g0 = tq.encode_guidance(xr, MX, 1, with_y=True)
+    assert g1.gscale is None
+    assert torch.equal(g1.guide, g0.guide) and torch.equal(g1.scales, g0.scales)
+    y1, _ = tq.guided_fake_quant(xt, g1)
+    y0, _ = tq.guided_fake_quant(xt, g0)
+    assert torch.equal(y1.view(torch.int16), y0.view(torch.int16))
