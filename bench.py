@@ -239,6 +239,37 @@ def record_path(torch, w, step, stream, dev, layers):
     return out
 
 
+def moe_per_expert(torch, syn, dev, reps):
+    """One MoE layer (65,536 routed rows x 2048, 256 experts) with one global
+    scale per expert from the routing offsets: encode (bits=1) and guided
+    rounding, each timed per call with events."""
+    import precision_rl_nvfp4_amd as tq
+
+    xt, xr, _, offsets = syn.moe_pair(20, device=dev)
+    n = xt.numel()
+    work = tq.grouped_workspace("nvfp4", xt.shape[0], xt.shape[1], offsets.numel() - 1, device=dev)
+    g = tq.encode_guidance_grouped(xr, offsets, "nvfp4", 1, work=work)
+    y = torch.empty_like(xt)
+    out = {}
+    for name, fn, bpe in (("encode_guidance_grouped", lambda: tq.encode_guidance_grouped(
+                               xr, offsets, "nvfp4", 1, guide=g.guide, scales=g.scales,
+                               gscale_out=g.gscale, work=work), 2 + 1 / 8 + 1 / 16),
+                          ("guided_fake_quant_grouped", lambda: tq.guided_fake_quant(xt, g, y=y, work=work),
+                           2 + 1 / 8 + 1 / 16 + 2)):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        gbs = bpe * n / (us * 1e-6) / 1e9
+        out[name] = {"avg_us_per_call": round(us, 2), "elements_per_call": n, "GB_s": round(gbs, 1),
+                     "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    return out
+
+
 def mismatch_report(counts):
     """Fig. 6-style summary of the per-layer mismatch counts: how often RTN
     under the rollout scales misses the rollout code, how many of those misses
@@ -457,6 +488,7 @@ def main():
                 "guided_fake_quant": kernel_entry("guided_fake_quant", per_v[1], len(phases[1][2]), w.n,
                                                   bpe_g)}
         del keep
+        variants["moe_per_expert"] = moe_per_expert(torch, syn, dev, max(3, args.steps // 4))
         log("bench: variants timed")
 
     record = None

@@ -35,6 +35,7 @@ __all__ = ["NVFP4", "MXFP4", "TraceError", "Quantized", "Guidance", "quantize_rt
            "encode_guidance", "encode_guidance_grouped", "decode_guidance", "guided_fake_quant",
            "guided_fake_quant_stats",
            "discrepancy_stats", "stats_workspace", "quant_workspace", "guided_stats_workspace",
+           "grouped_workspace",
            "derived_metrics", "mismatch_summary", "fmt_id", "BLOCK", "MISMATCH_COUNTS"]
 
 BLOCK = {NVFP4: 16, MXFP4: 32}
@@ -117,6 +118,12 @@ def _workspace(nbytes: int, device, work: Optional[torch.Tensor]) -> Optional[to
 def quant_workspace(fmt, rows: int, cols: int, group_rows: int = 0, device="cuda"):
     """Workspace tensor for quantize_rtn / encode_guidance with scales from the amax."""
     n = int(load().trace_quant_workspace_bytes(fmt_id(fmt), rows, cols, group_rows))
+    return _workspace(n, device, None)
+
+
+def grouped_workspace(fmt, rows: int, cols: int, groups: int, device="cuda"):
+    """Workspace tensor for the row-offset grouped calls."""
+    n = int(load().trace_grouped_workspace_bytes(fmt_id(fmt), rows, cols, groups))
     return _workspace(n, device, None)
 
 
@@ -234,7 +241,7 @@ def _guided_common(x_train, g, bits, with_codes, y, codes):
 
 
 def guided_fake_quant(x_train: torch.Tensor, g: Guidance, bits: Optional[int] = None,
-                      with_codes: bool = False, y=None, codes=None):
+                      with_codes: bool = False, y=None, codes=None, work=None):
     """Training side: rollout-guided rounding under the rollout scales.
     ``bits`` defaults to the record's (1..4); 0 gives RTN under the rollout
     scales. Returns (y, codes or None)."""
@@ -242,7 +249,7 @@ def guided_fake_quant(x_train: torch.Tensor, g: Guidance, bits: Optional[int] = 
     if g.offsets is not None:   # row-offset groups
         G = _check_offsets(g.offsets, x_train)
         need = int(load().trace_grouped_workspace_bytes(g.fmt, rows, cols, G))
-        work = _workspace(need, x_train.device, None)
+        work = _workspace(need, x_train.device, work)
         _abi.call("guided_fake_quant_grouped", g.fmt, b, rows, cols, G, _ptr(g.offsets), _ptr(x_train),
                   _ptr(guide), _ptr(g.scales), _ptr(g.gscale), _ptr(y), _ptr(codes), _ptr(work),
                   _nbytes(work), _stream(x_train))
