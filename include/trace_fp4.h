@@ -125,6 +125,14 @@ const char* trace_status_str(int status);
  * (n >= G: one amax pass over every group, then one quantize pass); with 0,
  * two-pass batches are about 96 MiB of input. Results are bit-identical for
  * every setting; the knob exists to exercise and compare schedules.
+ * Single-pass launches of a process run one after another on each device,
+ * whatever their streams (each needs the whole device at once): the first
+ * one on a second stream synchronizes the device once, later ones wait on
+ * the previous one's event. A graph capture adds no ordering (a graph runs
+ * in order); two graphs or processes that encode at the same time on one
+ * device are not ordered, and then a workgroup that waits too long counts a
+ * failure in the workspace (see trace_quant_workspace_bytes) instead of
+ * hanging.
  * Process-wide. Returns the previous setting, or TRACE_EINVAL for a negative
  * value. */
 int64_t trace_set_encode_batch(int64_t groups_per_batch);

@@ -36,7 +36,10 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <map>
+#include <mutex>
 #include <tuple>
+#include <utility>
 
 #include "trace_fp4_internal.h"
 
@@ -1327,15 +1330,43 @@ const void* onepass_kernel(int plane_mode, bool wy) {
 }
 
 // Workgroups that may be resident at once for the kernel: kOnePassPerCU per
-// CU if the occupancy query allows that many, else 0 (not used).
-int64_t onepass_capacity(const void* k) {
-  int dev = -1, cus = 0, per = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k, kThreads, 0) != hipSuccess) return 0;
-  if (per < kOnePassPerCU) return 0;
-  return (int64_t)cus * kOnePassPerCU;
+// CU if the occupancy query allows that many, else 0 (not used). Cached per
+// device and kernel.
+int64_t onepass_capacity(const void* k, int dev) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, int64_t> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find({dev, k});
+  if (it != cache.end()) return it->second;
+  int cus = 0, per = 0;
+  int64_t cap = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k, kThreads, 0) == hipSuccess &&
+      per >= kOnePassPerCU)
+    cap = (int64_t)cus * kOnePassPerCU;
+  cache[{dev, k}] = cap;
+  return cap;
 }
+
+// Single-pass launches of one process on one device run one after another,
+// whatever their streams: each needs the whole device resident at once, so
+// two running side by side could each hold part of it and wait on the other
+// (the bounded waits would end that, with wrong results). While every launch
+// comes on one stream, stream order suffices and nothing is added (an event
+// per launch costs ~7 us of the next kernel's start). The first launch on
+// another stream synchronizes the device once; from then on each launch
+// waits for the previous launch's event and records its own. Nothing is done
+// while the stream is being captured into a graph (a graph runs its nodes
+// in order).
+struct OnePassOrder {
+  std::mutex mu;
+  hipEvent_t ev = nullptr;
+  bool multi = false;          // launches seen on more than one stream
+  bool recorded = false;       // ev holds the last launch (multi mode)
+  bool any = false;            // a launch happened
+  hipStream_t last = nullptr;  // stream of the last launch
+};
+OnePassOrder g_onepass_order[64];
 
 // Launches the single-pass encode when it applies; *used tells whether it did.
 hipError_t launch_onepass(int plane_mode, bool wy, const Shape& sh, const QuantArgs& qa, void* work,
@@ -1343,10 +1374,28 @@ hipError_t launch_onepass(int plane_mode, bool wy, const Shape& sh, const QuantA
   *used = false;
   const int64_t T = (sh.upg + kTileUnits - 1) / kTileUnits;
   if (T > kOnePassTiles) return hipSuccess;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipSuccess;
   const void* k = onepass_kernel(plane_mode, wy);
-  const int64_t cap = onepass_capacity(k);
+  const int64_t cap = onepass_capacity(k, dev);
   const int64_t Q = min(sh.groups, cap / T);
   if (Q < 1) return hipSuccess;
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(stream, &capture);
+  if (e != hipSuccess) return e;
+  OnePassOrder& ord = g_onepass_order[dev];
+  std::unique_lock<std::mutex> lock(ord.mu, std::defer_lock);
+  if (capture == hipStreamCaptureStatusNone) {
+    lock.lock();
+    if (ord.any && ord.last != stream && !ord.multi) {
+      // first launch on a second stream: the previous launch left no event
+      if ((e = hipEventCreateWithFlags(&ord.ev, hipEventDisableTiming)) != hipSuccess) return e;
+      if ((e = hipDeviceSynchronize()) != hipSuccess) return e;
+      ord.multi = true;
+    }
+    if (ord.multi && ord.recorded && ord.last != stream && (e = hipStreamWaitEvent(stream, ord.ev, 0)) != hipSuccess)
+      return e;
+  }
   OnePassArgs a{};
   a.x = qa.x;
   a.upg = sh.upg;
@@ -1362,7 +1411,7 @@ hipError_t launch_onepass(int plane_mode, bool wy, const Shape& sh, const QuantA
   a.y = qa.y;
   const int64_t words = sh.groups * ((int64_t)kPartMax + kSCopies * 64) + 1;
   const int64_t zb = min((words + kThreads - 1) / kThreads, (int64_t)1024);
-  hipError_t e = launch(zero_words_kernel, dim3((unsigned)zb), dim3(kThreads), stream, a.slots, words);
+  e = launch(zero_words_kernel, dim3((unsigned)zb), dim3(kThreads), stream, a.slots, words);
   if (e != hipSuccess) return e;
   // An ordinary launch on the caller's queue: the grid is at most the
   // resident capacity, and the workgroups wait only for each other, so every
@@ -1371,8 +1420,17 @@ hipError_t launch_onepass(int plane_mode, bool wy, const Shape& sh, const QuantA
   // hardware queue, ~11 us of switching before and after the kernel).
   void* argv[] = {&a};
   e = hipLaunchKernel(k, dim3((unsigned)(Q * T)), dim3(kThreads), argv, 0, stream);
-  if (e == hipSuccess) *used = true;
-  return e;
+  if (e != hipSuccess) return e;
+  *used = true;
+  if (capture == hipStreamCaptureStatusNone) {
+    if (ord.multi) {
+      if ((e = hipEventRecord(ord.ev, stream)) != hipSuccess) return e;
+      ord.recorded = true;
+    }
+    ord.any = true;
+    ord.last = stream;
+  }
+  return hipSuccess;
 }
 
 template <int FMT, int BITS, bool DECODE, bool WCODES, bool STATS, bool DIAG, int MAP>
