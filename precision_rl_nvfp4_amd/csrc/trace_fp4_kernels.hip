@@ -932,11 +932,20 @@ __global__ __launch_bounds__(kThreads) void offs_prep_kernel(const int64_t* __re
 }
 
 // table[e] = (group, tile within the group) for e < tstart[G], (-1, 0) after.
+// Up to kTableLds groups the starts are searched in LDS, else in memory.
+constexpr int kTableLds = 8192;
 __global__ __launch_bounds__(kThreads) void tile_table_kernel(const int32_t* __restrict__ tstart,
                                                              int64_t G, int64_t entries, int2* table) {
+  __shared__ int32_t st[kTableLds + 1];
+  const bool in_lds = G <= kTableLds;
+  if (in_lds) {
+    for (int64_t i = threadIdx.x; i <= G; i += kThreads) st[i] = tstart[i];
+    __syncthreads();
+  }
+  const int32_t* ts = in_lds ? st : tstart;
   const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (e >= entries) return;
-  const int32_t total = tstart[G];
+  const int32_t total = ts[G];
   if (e >= total) {
     table[e] = make_int2(-1, 0);
     return;
@@ -945,10 +954,10 @@ __global__ __launch_bounds__(kThreads) void tile_table_kernel(const int32_t* __r
   int64_t lo = 0, hi = G - 1;
   while (lo < hi) {
     const int64_t mid = (lo + hi + 1) >> 1;
-    if (tstart[mid] <= e) lo = mid;
+    if (ts[mid] <= e) lo = mid;
     else hi = mid - 1;
   }
-  table[e] = make_int2((int)lo, (int)(e - tstart[lo]));
+  table[e] = make_int2((int)lo, (int)(e - ts[lo]));
 }
 
 // Tile maxima of row-offset groups: tpart[e] for table entry e.
