@@ -8,13 +8,18 @@
 //   Algorithm 1 prose: BracketFP4, Reconstruct, combined block/global scale.
 //   §4.3: the MXFP4 (E8M0, 32-element block) variant.
 //
-// Layout of the work. Every kernel streams its tensors once: a lane owns
-// "units" of 8 bf16 (one 16-byte load), consecutive lanes own consecutive
-// units, so a wave load is one contiguous 1 KiB run. An NVFP4 block (16
-// elements) spans two lanes and an MXFP4 block (32) four; block maxima are
-// exchanged with DPP quad permutations. A call may hold several global-scale
-// groups (e.g. the 8192-token chunks of a streamed layer); a workgroup tile
-// never straddles two groups. No MFMA: the path is bound by HBM bandwidth.
+// Layout of the work. Each kernel streams its tensors: a lane owns "units"
+// of 8 bf16 (one 16-byte load), consecutive lanes own consecutive units, so a
+// wave load is one contiguous 1 KiB run. An NVFP4 block (16 elements) spans
+// two lanes and an MXFP4 block (32) four; block maxima are exchanged with DPP
+// quad permutations. A call may hold several global-scale groups: a
+// workgroup tile lies inside one group (e.g. one 8192-token chunk of a
+// streamed layer), holds several whole small groups (packed, e.g. one token's
+// row), or is given by a table of row-offset groups (e.g. one expert's rows).
+// Encoding with S derived from a group's amax reads the input once (packed
+// groups, and chunk-sized groups in onepass_encode_kernel) or twice (larger
+// groups). Data touched once is read and written with nontemporal accesses.
+// No MFMA: the path is bound by HBM bandwidth.
 //
 // Per-element arithmetic. The budget at the HBM roofline is ~20 VALU
 // operations per element, so the E2M1 work runs on gfx950's conversion
