@@ -701,30 +701,53 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
   }
 }
 
-// Single-pass NVFP4 encode with S from each group's amax, for groups of at
-// most kOnePassTiles tiles. The grid never exceeds the number of workgroups
-// the device holds at once, so all of them are resident; Q sets of T
-// workgroups each (T = tiles per group) take groups q,
-// q + Q, ... in turn, one tile per workgroup per group, kept on chip:
-//   * a tile's max goes to its slot, tagged (bit 31), by one store as soon
-//     as the tile has arrived;
-//   * the group's tile 0 workgroup waits for all T slots, derives S and A,
-//     writes {S, A} to gout and publishes S (nonzero) to kSCopies words;
-//     every other workgroup waits for one of them;
-//   * the tile is then quantized from on-chip storage.
-// Three tiles are in flight per workgroup: the one waiting for its S (in
-// LDS, each thread keeping its own words), the next one (registers, max
-// published) and the loads of the one after (registers), so a group's
-// combine has two tile-times to complete and a tile's loads one.
+// Single-pass NVFP4 encode with S from each group's amax. The grid never
+// exceeds the number of workgroups the device holds at once (2 per CU), so
+// all of them are resident: Q sets of T workgroups (T tiles per group, sized
+// at launch so every CU gets the same work) take groups q, q + Q, ... in
+// turn, one tile per workgroup per group, kept on chip; one more workgroup
+// combines.
+//
+// A tile workgroup is seven data waves and one control wave (eight waves, so
+// every SIMD holds two). The data waves load, hold and quantize the tiles;
+// the control wave does every wait on other workgroups. This split matters:
+// a wait on memory is a wait on the wave's whole vector-memory counter,
+// which also covers the tile loads in flight, so a data wave that polled
+// would stall until its next tile had arrived.
+//   * Data waves: a tile's max goes to its slot, tagged (bit 31), by one
+//     store from the last of the seven waves to reduce it (an LDS counter),
+//     as soon as the tile has arrived; no barrier is involved.
+//   * Combining workgroup (the last one): its first wave takes the groups in
+//     order, waits for each group's T slots, derives S and A, writes {S, A}
+//     to gout and publishes S (nonzero) to kSCopies words. It runs ahead of
+//     the tiles, so S is combined as soon as the last tile max of its group
+//     is in, about a round before it is needed.
+//   * Control wave: waits for one S word of the group and builds the table of
+//     block factors under S.
+//   * One barrier per group: the data waves quantize group g from its table
+//     while the control wave prepares group g + Q's in the other half of a
+//     double buffer.
+// Three tiles are on chip per data wave: the one being quantized (in LDS,
+// each thread keeping its own words), the next one (registers, max
+// published) and the one after (registers, loads in flight). The two
+// register tiles swap roles each round; within a round, unit j of the
+// stashed tile is quantized, its LDS words refilled from the next tile and
+// that register reloaded from the tile three rounds ahead, so the loads
+// leave spread over the round rather than in one burst (a burst queues
+// ahead of every other access of the CU, the slot stores and S polls
+// included). Tiles are read through a buffer resource whose range is the
+// tile, so every load instruction is issued whatever the tile's length and
+// each wait covers exactly the older tile.
 // Slots and S words are zeroed by a fill kernel before the launch. Every wait
 // is bounded: past kSpinMax polls the workgroup records an error in *err and
 // carries on with S = NaN, so the grid always drains.
 struct OnePassArgs {
   const uint4* x;
-  int64_t upg;               // units per group
-  int64_t groups;
+  int upg;                   // units per group
+  int groups;
   int T;                     // tiles (workgroups) per group
   int Q;                     // groups in flight
+  int L;                     // units per tile (a multiple of 64, <= kOPTile); a group's last tile may be shorter
   uint32_t* slots;           // [groups][kPartMax] tagged tile maxima
   uint32_t* sword;           // [groups][kSCopies][64]: S bits at [.][c][0], 0 until published
   uint32_t* err;             // bounded-wait failures
@@ -736,6 +759,15 @@ struct OnePassArgs {
 
 constexpr int kSpinMax = 1 << 22;
 constexpr int kSCopies = 16;            // copies of each published S, one per 256-byte line
+constexpr int kOPDataWaves = 7;                      // data waves per workgroup
+constexpr int kOPData = kOPDataWaves * 64;           // data threads
+constexpr int kOnePassThreads = kOPData + 64;        // + the control wave: 8 waves, 2 per SIMD
+constexpr int kOPUnits = 10;                         // units per data thread and tile
+constexpr int kOPTile = kOPData * kOPUnits;          // most units per tile (4480, a multiple of 64)
+constexpr int kPublishAt = 10;                       // unit of the round before which the tile max is published
+constexpr int kSlotsPerLane = kPartMax / 64;
+constexpr int kRawBufferWord3 = 0x00020000;     // buffer descriptor word 3: untyped 32-bit data, no swizzle
+constexpr int kBufferNT = 2;                    // buffer load cache policy: nontemporal
 
 __device__ __forceinline__ uint32_t load_agent(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -745,126 +777,233 @@ __device__ __forceinline__ void store_agent(uint32_t* p, uint32_t v) {
 }
 
 template <int PLANE, bool WY>
-__global__ __launch_bounds__(kThreads, 4) void onepass_encode_kernel(OnePassArgs a) {
-  __shared__ float2 lut[128];
-  __shared__ uint32_t red[kThreads / 64];
-  __shared__ float sS;
-  __shared__ uint4 stash[kUPT * kThreads];   // the tile waiting for its S (thread-private words)
+__global__ __launch_bounds__(kOnePassThreads, 4) void onepass_encode_kernel(OnePassArgs a) {
+  __shared__ float2 lut[2][128];
+  __shared__ float sS[2];
+  __shared__ uint32_t wmax[2], wcnt[2];
+  __shared__ uint4 stash[kOPUnits * kOPData];   // the tile waiting for its S (thread-private words)
+  // Group indices fit 31 bits and a group at most kPartMax tiles (checked at
+  // launch), so the indexing here is 32-bit and mostly scalar.
+  const int G = a.groups, Q = a.Q, upg = a.upg;
+  if ((int)blockIdx.x == Q * a.T) {
+    // ---- the combining workgroup (the last one): its first wave derives S
+    // of every group, in order, as soon as the group's T slots are tagged.
+    if (threadIdx.x >= 64) return;
+    const int lane = (int)threadIdx.x;
+    for (int g = 0; g < G; ++g) {
+      const int64_t gs = (int64_t)g * kPartMax;
+      uint32_t v[kSlotsPerLane];
+#pragma unroll
+      for (int k2 = 0; k2 < kSlotsPerLane; ++k2) {
+        const int i = lane + 64 * k2;
+        v[k2] = i < a.T ? load_agent(&a.slots[gs + i]) : 0x80000000u;
+      }
+      int spins = 0;
+      for (;;) {
+        bool all = true;
+#pragma unroll
+        for (int k2 = 0; k2 < kSlotsPerLane; ++k2) all = all && (v[k2] & 0x80000000u) != 0u;
+        if (__all(all)) break;
+        if (++spins > kSpinMax) {
+          if (lane == 0) atomicAdd(a.err, 1u);
+#pragma unroll
+          for (int k2 = 0; k2 < kSlotsPerLane; ++k2) v[k2] |= 0x80000000u;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (int k2 = 0; k2 < kSlotsPerLane; ++k2)
+          if ((v[k2] & 0x80000000u) == 0u) v[k2] = load_agent(&a.slots[gs + lane + 64 * k2]);
+      }
+      uint32_t gm = 0;
+#pragma unroll
+      for (int k2 = 0; k2 < kSlotsPerLane; ++k2) gm = max(gm, v[k2] & 0x7FFFFFFFu);
+      gm = wave_max_u32(gm);
+      const float A = __uint_as_float(gm << 16);
+      const float S = global_scale(A);
+      if (lane < kSCopies) store_agent(&a.sword[((int64_t)g * kSCopies + lane) * 64], __float_as_uint(S));
+      if (lane == 0) {
+        a.gout[2 * (int64_t)g] = S;
+        a.gout[2 * (int64_t)g + 1] = A;
+      }
+    }
+    return;
+  }
   const int q = (int)blockIdx.x / a.T;
   const int t = (int)blockIdx.x - q * a.T;
-  const int64_t tbase = (int64_t)t * kTileUnits;
-  const int64_t G = a.groups, Q = a.Q;
-  uint4 r0[kUPT], r1[kUPT];
-  auto load_tile = [&](uint4 (&v)[kUPT], int64_t g) {
-#pragma unroll
-    for (int j = 0; j < kUPT; ++j) {
-      const int64_t u = tbase + j * kThreads + threadIdx.x;
-      v[j] = u < a.upg ? load_stream(a.x + g * a.upg + u) : make_uint4(0u, 0u, 0u, 0u);
-    }
-  };
-  // Tile max of group g -> its tagged slot.
-  auto publish_max = [&](const uint4 (&v)[kUPT], int64_t g) {
-    uint32_t m = 0;
-#pragma unroll
-    for (int j = 0; j < kUPT; ++j) m = max(m, unit_amax_bits(v[j]));
-    m = wave_max_u32(m);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-    __syncthreads();
-    if (threadIdx.x == 0)
-      store_agent(&a.slots[g * kPartMax + t], 0x80000000u | max(max(red[0], red[1]), max(red[2], red[3])));
-    __syncthreads();  // red[] is reused
-  };
-  auto to_stash = [&](const uint4 (&v)[kUPT]) {
-#pragma unroll
-    for (int j = 0; j < kUPT; ++j) stash[j * kThreads + threadIdx.x] = v[j];
-  };
-
-  int64_t g = q;
-  if (g >= G) return;
-  load_tile(r0, g);
-  publish_max(r0, g);
-  to_stash(r0);
-  if (g + Q < G) {
-    load_tile(r0, g + Q);
-    publish_max(r0, g + Q);
+  if (threadIdx.x == 0) {
+    wmax[0] = wmax[1] = 0u;
+    wcnt[0] = wcnt[1] = 0u;
   }
-  if (g + 2 * Q < G) load_tile(r1, g + 2 * Q);
-  // Loop state: stash = tile of g (max published); r0 = tile of g + Q (max
-  // published); r1 = loads of g + 2Q in flight.
-  for (; g < G; g += Q) {
-    // S of group g
-    if (t == 0) {
-      uint32_t gm = 0;
-      for (int i = threadIdx.x; i < a.T; i += kThreads) {
-        uint32_t v;
+  __syncthreads();
+
+  // Rounds this workgroup runs: one per group q, q + Q, ..., padded to an
+  // even number (the data waves run two rounds per iteration of a loop with
+  // one exit; a padding round quantizes nothing).
+  const int rounds = ((G - q + Q - 1) / Q + 1) & ~1;
+  // wave index as a scalar, so the roles split without exec masking
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  if (wave == kOPDataWaves) {
+    // ---- control wave
+    const int lane = (int)threadIdx.x - kOPData;
+    int par = 0;
+    for (int k = 0, g = q; k < rounds; ++k, g += Q, par ^= 1) {
+      if (g >= G) {   // the data waves' padding round
+        __syncthreads();
+        continue;
+      }
+      // S of group g, published by the combining workgroup
+      uint32_t v = 0u;
+      if (lane == 0) {
+        const uint32_t* w = &a.sword[((int64_t)g * kSCopies + (int)(blockIdx.x % kSCopies)) * 64];
         int spins = 0;
-        while (((v = load_agent(&a.slots[g * kPartMax + i])) & 0x80000000u) == 0u) {
+        while ((v = load_agent(w)) == 0u) {
           if (++spins > kSpinMax) {
             atomicAdd(a.err, 1u);
-            v = 0x80000000u;
+            v = 0x7FC00000u;
             break;
           }
           __builtin_amdgcn_s_sleep(1);
         }
-        gm = max(gm, v & 0x7FFFFFFFu);
       }
-      gm = wave_max_u32(gm);
-      if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = gm;
-      __syncthreads();
-      const float A = __uint_as_float(max(max(red[0], red[1]), max(red[2], red[3])) << 16);
-      const float S = global_scale(A);
-      if (threadIdx.x < kSCopies) store_agent(&a.sword[(g * kSCopies + threadIdx.x) * 64], __float_as_uint(S));
-      if (threadIdx.x == 0) {
-        a.gout[2 * g] = S;
-        a.gout[2 * g + 1] = A;
-        sS = S;
-      }
-    } else if (threadIdx.x == 0) {
-      const uint32_t* w = &a.sword[(g * kSCopies + (int)(blockIdx.x % kSCopies)) * 64];
-      uint32_t v;
-      int spins = 0;
-      while ((v = load_agent(w)) == 0u) {
-        if (++spins > kSpinMax) {
-          atomicAdd(a.err, 1u);
-          v = 0x7FC00000u;
-          break;
+      const float S = __uint_as_float((uint32_t)__shfl((int)v, 0));
+      // factor table of every E4M3 byte under S: {min(S / e, FLT_MAX), e / S}
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int i = lane + 64 * h;
+        const float e = e4m3_value((uint32_t)i);
+        float r = 0.0f, d = 0.0f;
+        if (e != 0.0f) {
+          d = e / S;
+          r = fminf(S / e, kFltMax);
         }
-        __builtin_amdgcn_s_sleep(1);
+        lut[par][i] = make_float2(r, d);
       }
-      sS = __uint_as_float(v);
+      if (lane == 0) sS[par] = S;
+      __syncthreads();   // group g's table is ready; group g - Q's is no longer read
     }
-    __syncthreads();
-    const float S = sS;
-    build_factor_lut(lut, S);
-    __syncthreads();
-    // quantize the stashed tile of g, one unit at a time (the next tile and
-    // the loads after it hold 64 VGPRs meanwhile)
-#pragma unroll 1
-    for (int j = 0; j < kUPT; ++j) {
-      const int64_t u = tbase + j * kThreads + threadIdx.x;
-      const uint4 v = stash[j * kThreads + threadIdx.x];
-      uint32_t bm = unit_amax_bits(v);
-      bm = max(bm, xor1(bm));
-      const uint32_t sb = nv_scale_byte(bm, S);
-      const float2 rd = lut[sb & 0x7Fu];
-      float f[8];
-      unit_f32(v, f);
+    return;
+  }
+
+  // ---- data waves
+  // The tile is units t0u .. t0u + tlen - 1 of its group; unit j of this
+  // thread's share is t0u + tid + j * kOPData. Tiles are read through a buffer
+  // resource whose range is the tile (empty past the last group), so units
+  // outside it read as zero without a memory access, and every tile load is
+  // the same kOPUnits instructions.
+  const int t0u = t * a.L;
+  const int tlen = min(upg - t0u, a.L);
+  uint4 r0[kOPUnits], r1[kOPUnits];
+  auto tile_rsrc = [&](int g) {
+    const bool in = g < G;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(a.x + (in ? (int64_t)g * upg + t0u : 0)), (short)0,
+                                             in ? tlen * 16 : 0, kRawBufferWord3);
+  };
+  auto load_tile = [&](uint4 (&v)[kOPUnits], int g) {
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(g);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) f[i] *= rd.x;
-      const uint32_t K = rtn_codes(f);
-      if (u < a.upg) write_unit<0, PLANE, WY>(K, sb, rd.y, 0.0f, g * a.upg + u, a.plane, a.scales, a.y);
-    }
-    __syncthreads();  // lut, sS and red[] are rewritten below or next round
-    // advance: r0 -> stash, r1 -> r0 (max published), next loads -> r1
-    if (g + Q < G) {
-      to_stash(r0);
-      if (g + 2 * Q < G) {
+    for (int j = 0; j < kOPUnits; ++j)
+      v[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)threadIdx.x * 16,
+                                                                              j * kOPData * 16, kBufferNT));
+  };
+  // Tile max of group g -> its tagged slot, stored by the last data wave to
+  // add its wave max (LDS counter `par`, reset by that wave).
+  auto publish_max = [&](const uint4 (&v)[kOPUnits], int g, int par) {
+    uint32_t m = 0;
 #pragma unroll
-        for (int j = 0; j < kUPT; ++j) r0[j] = r1[j];
-        publish_max(r0, g + 2 * Q);
-        if (g + 3 * Q < G) load_tile(r1, g + 3 * Q);
+    for (int j = 0; j < kOPUnits; ++j) m = max(m, unit_amax_bits(v[j]));
+    m = wave_max_u32(m);
+    if (g < G && (threadIdx.x & 63) == 0) {
+      __hip_atomic_fetch_max(&wmax[par], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      const uint32_t c = __hip_atomic_fetch_add(&wcnt[par], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (c == kOPDataWaves - 1) {
+        const uint32_t M = __hip_atomic_load(&wmax[par], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        wmax[par] = 0u;
+        wcnt[par] = 0u;
+        store_agent(&a.slots[(int64_t)g * kPartMax + t], 0x80000000u | M);
       }
     }
+  };
+  auto to_stash = [&](const uint4 (&v)[kOPUnits]) {
+#pragma unroll
+    for (int j = 0; j < kOPUnits; ++j) stash[j * kOPData + threadIdx.x] = v[j];
+  };
+  // One round on group g (publication counter `par` for g + 2Q). On entry:
+  // stash = tile of g (max published), ra = tile of g + Q (max published),
+  // rb = loads of g + 2Q in flight. On exit ra and rb have swapped roles.
+  auto encode_round = [&](uint4 (&ra)[kOPUnits], uint4 (&rb)[kOPUnits], int g, int par) {
+    __syncthreads();   // the control wave has group g's table ready
+    const bool live = g < G;
+    const float S = sS[par];
+    const float2* L = lut[par];
+    // Outputs of this tile of group g, through buffer resources whose range
+    // is the tile: stores past it are dropped by the range check, and every
+    // offset is 32-bit. The tile starts on an even unit, so a unit's parity
+    // (which decides who writes the block's scale byte) is the lane's.
+    constexpr int PB = PLANE == 4 ? 4 : PLANE == 3 ? 3 : PLANE == 2 ? 2 : 1;   // plane bytes per unit
+    const int64_t gb = (int64_t)(live ? g : 0) * upg + t0u;
+    const int tl = live ? tlen : 0;
+    const __amdgpu_buffer_rsrc_t rp =
+        __builtin_amdgcn_make_buffer_rsrc(a.plane + gb * PB, (short)0, tl * PB, kRawBufferWord3);
+    const __amdgpu_buffer_rsrc_t rsc =
+        __builtin_amdgcn_make_buffer_rsrc(a.scales + (gb >> 1), (short)0, tl >> 1, kRawBufferWord3);
+    const __amdgpu_buffer_rsrc_t ryy =
+        __builtin_amdgcn_make_buffer_rsrc(WY ? a.y + gb : a.y, (short)0, WY ? tl * 16 : 0, kRawBufferWord3);
+    const int lane_u = (int)threadIdx.x;
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(g + 3 * Q);
+    // Unit by unit: quantize stash[j], refill it from ra[j] and reload ra[j]
+    // from group g + 3Q, so the tile's loads leave over the whole round
+    // rather than in one burst (a burst queues ahead of every other access
+    // of the CU, the slot stores and S polls included).
+#pragma unroll
+    for (int j = 0; j < kOPUnits; ++j) {
+      if (j == kPublishAt) publish_max(rb, g + 2 * Q, par);
+      if (live) {
+        const uint4 v = stash[j * kOPData + threadIdx.x];
+        uint32_t bm = unit_amax_bits(v);
+        bm = max(bm, xor1(bm));
+        const uint32_t sb = nv_scale_byte(bm, S);
+        const float2 rd = L[sb & 0x7Fu];
+        float f[8];
+        unit_f32(v, f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] *= rd.x;
+        const uint32_t K = rtn_codes(f);
+        const int su = j * kOPData;   // the unit's offset in the tile, less the lane's
+        if constexpr (PLANE == 4) {
+          __builtin_amdgcn_raw_buffer_store_b32(K, rp, lane_u * 4, su * 4, kBufferNT);
+        } else if constexpr (PLANE == 1) {
+          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)gather_mbits(K), rp, lane_u, su, kBufferNT);
+        } else if constexpr (PLANE == 2) {
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)gather_2bits(K), rp, lane_u * 2, su * 2, kBufferNT);
+        } else {
+          const uint32_t w = gather_3bits(K);
+          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)w, rp, lane_u * 3, su * 3, kBufferNT);
+          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(w >> 8), rp, lane_u * 3 + 1, su * 3, kBufferNT);
+          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(w >> 16), rp, lane_u * 3 + 2, su * 3, kBufferNT);
+        }
+        if ((lane_u & 1) == 0) __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sb, rsc, lane_u >> 1, su >> 1, kBufferNT);
+        if constexpr (WY)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u_t, dequant_nv(K, rd.y)), ryy, lane_u * 16, su * 16,
+                                                 kBufferNT);
+      }
+      stash[j * kOPData + threadIdx.x] = ra[j];
+      ra[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)threadIdx.x * 16,
+                                                                              j * kOPData * 16, kBufferNT));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (kPublishAt >= kOPUnits) publish_max(rb, g + 2 * Q, par);
+  };
+
+  load_tile(r0, q);
+  publish_max(r0, q, 0);
+  to_stash(r0);
+  load_tile(r0, q + Q);
+  load_tile(r1, q + 2 * Q);
+  publish_max(r0, q + Q, 1);
+  for (int k = 0, g = q; k < rounds; k += 2, g += 2 * Q) {
+    encode_round(r0, r1, g, 0);
+    encode_round(r1, r0, g + Q, 1);
   }
 }
 
@@ -1326,8 +1465,8 @@ hipError_t quant_plane(int plane_mode, bool wy, int ssrc, bool pack, const Quant
 
 // ---- single-pass encode (onepass_encode_kernel)
 
-constexpr int kOnePassTiles = kPartMax;  // largest group: 1024 tiles = 16.8M elements
-constexpr int kOnePassPerCU = 4;         // resident workgroups per CU it is built for
+constexpr int kOnePassTiles = kPartMax;  // most tiles per group (slot layout); the grid bounds it further
+constexpr int kOnePassPerCU = 2;         // resident workgroups per CU it is built for
 
 template <int PLANE, bool WY>
 const void* onepass_fn() {
@@ -1355,7 +1494,7 @@ int64_t onepass_capacity(const void* k, int dev) {
   int cus = 0, per = 0;
   int64_t cap = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k, kThreads, 0) == hipSuccess &&
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k, kOnePassThreads, 0) == hipSuccess &&
       per >= kOnePassPerCU)
     cap = (int64_t)cus * kOnePassPerCU;
   cache[{dev, k}] = cap;
@@ -1386,14 +1525,21 @@ OnePassOrder g_onepass_order[64];
 hipError_t launch_onepass(int plane_mode, bool wy, const Shape& sh, const QuantArgs& qa, void* work,
                           hipStream_t stream, bool* used) {
   *used = false;
-  const int64_t T = (sh.upg + kTileUnits - 1) / kTileUnits;
-  if (T > kOnePassTiles) return hipSuccess;
+  const int64_t Tmin = (sh.upg + kOPTile - 1) / kOPTile;
+  if (Tmin > kOnePassTiles) return hipSuccess;
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipSuccess;
   const void* k = onepass_kernel(plane_mode, wy);
   const int64_t cap = onepass_capacity(k, dev);
-  const int64_t Q = min(sh.groups, cap / T);
-  if (Q < 1) return hipSuccess;
+  const int64_t Q = min(sh.groups, (cap - 1) / Tmin);   // + the combining workgroup
+  // the kernel indexes groups with 32-bit ints, up to groups + 4Q
+  if (Q < 1 || sh.groups + 5 * Q > INT32_MAX) return hipSuccess;
+  // Spread each group over as many tiles as the resident grid allows (equal
+  // work per CU), in multiples of 64 units: a wave's plane and y stores then
+  // start on whole 64-byte segments, and no NVFP4 block straddles two tiles.
+  const int64_t Tfit = min((cap - 1) / Q, (int64_t)kOnePassTiles);
+  const int64_t L = ((sh.upg + Tfit - 1) / Tfit + 63) / 64 * 64;
+  const int64_t T = (sh.upg + L - 1) / L;
   hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
   hipError_t e = hipStreamIsCapturing(stream, &capture);
   if (e != hipSuccess) return e;
@@ -1412,10 +1558,11 @@ hipError_t launch_onepass(int plane_mode, bool wy, const Shape& sh, const QuantA
   }
   OnePassArgs a{};
   a.x = qa.x;
-  a.upg = sh.upg;
-  a.groups = sh.groups;
+  a.upg = (int)sh.upg;
+  a.groups = (int)sh.groups;
   a.T = (int)T;
   a.Q = (int)Q;
+  a.L = (int)L;
   a.slots = static_cast<uint32_t*>(work);
   a.sword = a.slots + sh.groups * kPartMax;
   a.err = a.sword + sh.groups * kSCopies * 64;
@@ -1433,7 +1580,7 @@ hipError_t launch_onepass(int plane_mode, bool wy, const Shape& sh, const QuantA
   // cooperative launch would guarantee the same but goes through another
   // hardware queue, ~11 us of switching before and after the kernel).
   void* argv[] = {&a};
-  e = hipLaunchKernel(k, dim3((unsigned)(Q * T)), dim3(kThreads), argv, 0, stream);
+  e = hipLaunchKernel(k, dim3((unsigned)(Q * T + 1)), dim3(kOnePassThreads), argv, 0, stream);
   if (e != hipSuccess) return e;
   *used = true;
   if (capture == hipStreamCaptureStatusNone) {

@@ -496,7 +496,8 @@ def test_schedules_agree_on_streamed_chunks():
         assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("G_,gr,cols", [(1, 256, 2048), (17, 64, 2048), (3, 37, 2048), (2, 1024, 2048)])
+@pytest.mark.parametrize("G_,gr,cols", [(1, 256, 2048), (17, 64, 2048), (3, 37, 2048), (2, 1024, 2048),
+                                         (24, 1024, 2048)])
 def test_single_pass_encode_waits_never_time_out(G_, gr, cols):
     """The single-pass encode keeps a count of bounded waits that gave up in
     its workspace (after the per-group words); it stays 0, and the result is
