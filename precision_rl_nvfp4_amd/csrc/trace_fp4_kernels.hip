@@ -1014,6 +1014,33 @@ __global__ __launch_bounds__(kThreads) void zero_words_kernel(uint32_t* p, int64
 
 // ---- row-offset groups (e.g. one global scale per expert of a grouped MoE input)
 
+// Exclusive scan over the workgroup (max when MAXOP, else sum) of one value
+// per thread, in thread order; *total gets the whole reduction. Identity 0
+// (the values are >= 0).
+template <bool MAXOP>
+__device__ __forceinline__ int64_t block_exclusive_scan(int64_t v, int64_t* total) {
+  __shared__ int64_t wtot[kThreads / 64];
+  const int lane = (int)threadIdx.x & 63, w = (int)threadIdx.x >> 6;
+  int64_t incl = v;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int64_t o = __shfl_up(incl, d);
+    if (lane >= d) incl = MAXOP ? max(incl, o) : incl + o;
+  }
+  int64_t excl = __shfl_up(incl, 1);
+  if (lane == 0) excl = 0;
+  if (lane == 63) wtot[w] = incl;
+  __syncthreads();
+  int64_t pre = 0, all = 0;
+  for (int k = 0; k < kThreads / 64; ++k) {
+    const int64_t t = wtot[k];
+    if (k < w) pre = MAXOP ? max(pre, t) : pre + t;
+    all = MAXOP ? max(all, t) : all + t;
+  }
+  *total = all;
+  __syncthreads();   // wtot[] is reused by the next scan
+  return MAXOP ? max(pre, excl) : pre + excl;
+}
+
 // One workgroup. From the caller's row offsets (read only here) it derives
 // offs = the running max of clamp(off, 0, rows), so groups are disjoint row
 // ranges, and tstart = the exclusive prefix sum of each group's tile count.
@@ -1021,25 +1048,14 @@ __global__ __launch_bounds__(kThreads) void zero_words_kernel(uint32_t* p, int64
 __global__ __launch_bounds__(kThreads) void offs_prep_kernel(const int64_t* __restrict__ off_in,
                                                             int64_t G, int64_t rows, int64_t upr,
                                                             int64_t* offs, int32_t* tstart, float* gout) {
-  __shared__ int64_t part[kThreads];
   const int64_t n = G + 1;
   const int64_t per = (n + kThreads - 1) / kThreads;
   const int64_t i0 = min((int64_t)threadIdx.x * per, n), i1 = min(i0 + per, n);
+  int64_t total;
   // 1. running max of the clamped offsets
   int64_t m = 0;
   for (int64_t i = i0; i < i1; ++i) m = max(m, min(max(off_in[i], (int64_t)0), rows));
-  part[threadIdx.x] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int64_t run = 0;
-    for (int k = 0; k < kThreads; ++k) {
-      const int64_t v = part[k];
-      part[k] = run;   // max over the chunks before k
-      run = max(run, v);
-    }
-  }
-  __syncthreads();
-  m = part[threadIdx.x];
+  m = block_exclusive_scan<true>(m, &total);   // max over the entries before i0
   for (int64_t i = i0; i < i1; ++i) {
     m = max(m, min(max(off_in[i], (int64_t)0), rows));
     offs[i] = m;
@@ -1050,20 +1066,8 @@ __global__ __launch_bounds__(kThreads) void offs_prep_kernel(const int64_t* __re
   const int64_t g0 = min((int64_t)threadIdx.x * gper, G), g1 = min(g0 + gper, G);
   int64_t t = 0;
   for (int64_t g = g0; g < g1; ++g) t += ((offs[g + 1] - offs[g]) * upr + kTileUnits - 1) / kTileUnits;
-  __syncthreads();
-  part[threadIdx.x] = t;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int64_t run = 0;
-    for (int k = 0; k < kThreads; ++k) {
-      const int64_t v = part[k];
-      part[k] = run;
-      run += v;
-    }
-    tstart[G] = (int32_t)run;
-  }
-  __syncthreads();
-  t = part[threadIdx.x];
+  t = block_exclusive_scan<false>(t, &total);
+  if (threadIdx.x == 0) tstart[G] = (int32_t)total;
   for (int64_t g = g0; g < g1; ++g) {
     tstart[g] = (int32_t)t;
     const int64_t tg = ((offs[g + 1] - offs[g]) * upr + kTileUnits - 1) / kTileUnits;
