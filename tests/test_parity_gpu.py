@@ -521,6 +521,52 @@ def test_single_pass_encode_waits_never_time_out(G_, gr, cols):
     G.assert_same(G.f32(g.gscale).reshape(-1, 2)[:, 0], o["gscale"], "S")
 
 
+def _encode_schedule_check(G_, gr, cols, bits, seed, single):
+    """encode_guidance with one S per group against the oracle; `single`
+    says whether the single-pass encode must have run (it alone publishes S
+    to the workspace's S words) or the two-pass one."""
+    xt, xr = _grouped_pair(G_, gr, cols, seed)
+    rows = G_ * gr
+    x = G.to_dev(xr, rows, cols)
+    work = tq.quant_workspace(NV, rows, cols, gr, device=G.DEV)
+    work.zero_()
+    g = tq.encode_guidance(x, NV, bits, with_y=True, group_rows=gr, work=work)
+    torch.cuda.synchronize()
+    words = work.view(torch.int32).cpu().numpy()
+    S_bits = g.gscale.reshape(-1, 2)[:, 0].cpu().numpy().view(np.int32)
+    pub = words[G_ * 1024:G_ * 2048].reshape(G_, 16, 64)[:, :, 0]
+    assert np.array_equal(pub, np.repeat(S_bits[:, None], 16, axis=1)) == single, "unexpected schedule"
+    assert words[G_ * 2048] == 0
+    o = G.oracle_encode(NV, bits, xr, rows, gr)
+    G.assert_same(G.u8(g.guide), o["guide"], "guide")
+    G.assert_same(G.bits_of(g.y), o["y"], "rollout y")
+    G.assert_same(G.u8(g.scales), o["scales"], "scales")
+    G.assert_same(G.f32(g.gscale).reshape(-1, 2)[:, 0], o["gscale"], "S")
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("G_,gr,cols", [(40, 37, 48), (1200, 3, 2048)])
+def test_single_pass_tile_geometry(G_, gr, cols, bits):
+    """Single-pass encodes whose tiles are not whole 64-unit multiples of the
+    group (40 groups of 222 units: tiles of 64, 64, 64 and 30 units, 40 groups
+    in flight) and whose workgroups take several groups in turn (1200 groups
+    of 768 units, 511 in flight), for every plane width, with y."""
+    G.say(f"single-pass tile geometry, {G_} groups x ({gr},{cols}), bits {bits}")
+    _encode_schedule_check(G_, gr, cols, bits, 17 + bits, single=True)
+
+
+def test_single_pass_largest_group_and_the_next():
+    """The largest group the single-pass encode holds on chip at once
+    ((2 x CUs - 1) tiles of 4480 units) is encoded in one pass; a group a
+    few rows larger falls back to two passes. Both match the oracle."""
+    cus = torch.cuda.get_device_properties(G.DEV).multi_processor_count
+    cols = 2048
+    rows_max = (2 * cus - 1) * 4480 * 8 // cols
+    G.say(f"single-pass boundary: groups of {rows_max} and {rows_max + 3} rows x {cols} ({cus} CUs)")
+    _encode_schedule_check(2, rows_max, cols, 1, 41, single=True)
+    _encode_schedule_check(2, rows_max + 3, cols, 1, 42, single=False)
+
+
 # ---------------------------------------------------------------- row-offset groups
 
 def _offset_groups_pair(sizes, cols, seed):
