@@ -321,15 +321,20 @@ __device__ __forceinline__ float e4m3_value(uint32_t b) {
 }
 
 // NVFP4 factors of one E4M3 byte under S: r = min(S / e, FLT_MAX), d = e / S,
-// both 0 for e == 0 (the entries of build_factor_lut, for packed groups).
-__device__ __forceinline__ void nv_factors(uint32_t sb, float S, float& r, float& d) {
+// both 0 for e == 0 (the entries of build_factor_lut), for packed groups.
+// Called by the two lanes of one block (adjacent lanes, even first, both
+// active, with the same sb and S): each lane performs one of the two
+// divisions and they swap results.
+__device__ __forceinline__ void nv_factors_pair(uint32_t sb, float S, float& r, float& d) {
   const float e = e4m3_value(sb & 0x7Fu);
-  r = 0.0f;
-  d = 0.0f;
-  if (e != 0.0f) {
-    d = e / S;
-    r = fminf(S / e, kFltMax);
-  }
+  const bool odd = (threadIdx.x & 1u) != 0u;
+  const float num = odd ? e : S, den = odd ? S : e;
+  float q = num / den;                 // even lane: S / e; odd lane: e / S
+  if (!odd) q = fminf(q, kFltMax);
+  if (e == 0.0f) q = 0.0f;
+  const float o = __uint_as_float(xor1(__float_as_uint(q)));
+  r = odd ? o : q;
+  d = odd ? q : o;
 }
 
 // Workgroup table of the NVFP4 factors of every E4M3 byte under S:
@@ -681,7 +686,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
     if constexpr (PACK) {
       const float Sg = gs[(j * kThreads + threadIdx.x) >> a.map.lg];
       sb = nv_scale_byte(bm, Sg);
-      nv_factors(sb, Sg, r, d);
+      nv_factors_pair(sb, Sg, r, d);
     } else if constexpr (FMT == 0) {
       sb = nv_scale_byte(bm, S);
       const float2 rd = lut[sb & 0x7Fu];
@@ -1203,7 +1208,7 @@ __global__ __launch_bounds__(kThreads) void guided_kernel(GuidedArgs a) {
     const int64_t u = tbase + j * kThreads + threadIdx.x;
     float r, d = 0.0f, dsc = 0.0f;
     if constexpr (PACK) {
-      nv_factors(sbv[j], gs[(j * kThreads + threadIdx.x) >> a.map.lg], r, d);
+      nv_factors_pair(sbv[j], gs[(j * kThreads + threadIdx.x) >> a.map.lg], r, d);
     } else if constexpr (FMT == 0) {
       const float2 rd = lut[sbv[j] & 0x7Fu];
       r = rd.x;
