@@ -769,7 +769,6 @@ constexpr int kOPData = kOPDataWaves * 64;           // data threads
 constexpr int kOnePassThreads = kOPData + 64;        // + the control wave: 8 waves, 2 per SIMD
 constexpr int kOPUnits = 10;                         // units per data thread and tile
 constexpr int kOPTile = kOPData * kOPUnits;          // most units per tile (4480, a multiple of 64)
-constexpr int kPublishAt = 10;                       // unit of the round before which the tile max is published
 constexpr int kSlotsPerLane = kPartMax / 64;
 constexpr int kRawBufferWord3 = 0x00020000;     // buffer descriptor word 3: untyped 32-bit data, no swizzle
 constexpr int kBufferNT = 2;                    // buffer load cache policy: nontemporal
@@ -962,7 +961,6 @@ __global__ __launch_bounds__(kOnePassThreads, 4) void onepass_encode_kernel(OneP
     // of the CU, the slot stores and S polls included).
 #pragma unroll
     for (int j = 0; j < kOPUnits; ++j) {
-      if (j == kPublishAt) publish_max(rb, g + 2 * Q, par);
       if (live) {
         const uint4 v = stash[j * kOPData + threadIdx.x];
         uint32_t bm = unit_amax_bits(v);
@@ -997,7 +995,8 @@ __global__ __launch_bounds__(kOnePassThreads, 4) void onepass_encode_kernel(OneP
                                                                               j * kOPData * 16, kBufferNT));
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (kPublishAt >= kOPUnits) publish_max(rb, g + 2 * Q, par);
+    // the tile after next: its loads were issued a round ago
+    publish_max(rb, g + 2 * Q, par);
   };
 
   load_tile(r0, q);
