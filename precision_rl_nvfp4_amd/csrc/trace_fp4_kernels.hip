@@ -785,7 +785,7 @@ __global__ __launch_bounds__(kOnePassThreads, 4) void onepass_encode_kernel(OneP
   __shared__ float2 lut[2][128];
   __shared__ float sS[2];
   __shared__ uint32_t wmax[2], wcnt[2];
-  __shared__ uint4 stash[kOPUnits * kOPData];   // the tile waiting for its S (thread-private words)
+  __shared__ uint4 stash[kOPUnits * kOPData];   // the tile being quantized (thread-private words)
   // Group indices fit 31 bits and a group at most kPartMax tiles (checked at
   // launch), so the indexing here is 32-bit and mostly scalar.
   const int G = a.groups, Q = a.Q, upg = a.upg;
@@ -953,7 +953,7 @@ __global__ __launch_bounds__(kOnePassThreads, 4) void onepass_encode_kernel(OneP
         __builtin_amdgcn_make_buffer_rsrc(a.scales + (gb >> 1), (short)0, tl >> 1, kRawBufferWord3);
     const __amdgpu_buffer_rsrc_t ryy =
         __builtin_amdgcn_make_buffer_rsrc(WY ? a.y + gb : a.y, (short)0, WY ? tl * 16 : 0, kRawBufferWord3);
-    const int lane_u = (int)threadIdx.x;
+    const int lane_u = (int)threadIdx.x;   // the thread's unit offset in the tile, for j = 0
     const __amdgpu_buffer_rsrc_t rs = tile_rsrc(g + 3 * Q);
     // Unit by unit: quantize stash[j], refill it from ra[j] and reload ra[j]
     // from group g + 3Q, so the tile's loads leave over the whole round
