@@ -608,12 +608,26 @@ def test_row_offset_groups(sizes, cols):
     """encode_guidance_grouped / guided_fake_quant_grouped against the oracle
     run on each group's rows, every record width; empty groups get {1, 0}."""
     G.say(f"row-offset groups {sizes} x {cols}")
+    _check_row_offset_groups(sizes, cols, (1, 2, 3, 4))
+
+
+@pytest.mark.parametrize("n_groups", [3000, 9000])
+def test_row_offset_many_groups(n_groups):
+    """Thousands of small row-offset groups, a quarter of them empty: the
+    tile table comes from the prep kernel's LDS copy of the tile starts up to
+    8192 groups and from its own kernel beyond; both against the oracle."""
+    sizes = np.random.default_rng(n_groups).integers(0, 4, n_groups).tolist()
+    G.say(f"row-offset groups: {n_groups} groups of 0..3 rows x 16")
+    _check_row_offset_groups(sizes, 16, (1,))
+
+
+def _check_row_offset_groups(sizes, cols, widths):
     xt_b, xr_b = _offset_groups_pair(sizes, cols, len(sizes))
     rows = sum(sizes)
     offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
     doffs = torch.from_numpy(offs).to(G.DEV)
     xt, xr = G.to_dev(xt_b, rows, cols), G.to_dev(xr_b, rows, cols)
-    for bits in (1, 2, 3, 4):
+    for bits in widths:
         g = tq.encode_guidance_grouped(xr, doffs, NV, bits, with_y=True)
         guide, scales, yr, _, _, S = _oracle_offsets(NV, bits, xt_b, xr_b, cols, offs)
         G.assert_same(G.u8(g.guide), guide, f"guide bits={bits}")
