@@ -56,6 +56,7 @@ typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kFltMax = 3.40282346638528859812e+38f;
 constexpr int kMidGroups = 64;          // first level of the partial-sum reduction
+constexpr int64_t kDirectTiles = 32768; // up to this many per-tile pairs are summed by one workgroup
 constexpr int kMismatchBins = 15;       // signed-grid distances 0..14
 constexpr int kPackGroups = kTileUnits / 2;  // most groups in a packed tile (NVFP4: >= 2 units each)
 
@@ -1311,14 +1312,26 @@ __global__ __launch_bounds__(kThreads) void sums_mid_kernel(const double* __rest
 }
 
 // Fixed-order reduction of `groups` partial pairs into acc3 = {SB, SF, n}.
+// Each thread keeps four running sums (so four loads are in flight) and
+// adds them in a fixed order.
 __global__ __launch_bounds__(kThreads) void sums_final_kernel(const double* __restrict__ partials,
                                                               int64_t groups, int64_t n, double* acc3,
                                                               int accumulate) {
-  double sb = 0.0, sf = 0.0;
-  for (int64_t i = threadIdx.x; i < groups; i += kThreads) {
-    sb += partials[2 * i];
-    sf += partials[2 * i + 1];
+  double b4[4] = {0.0, 0.0, 0.0, 0.0}, f4[4] = {0.0, 0.0, 0.0, 0.0};
+  int64_t i = threadIdx.x;
+  for (; i + 3 * kThreads < groups; i += 4 * kThreads) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      b4[k] += partials[2 * (i + k * kThreads)];
+      f4[k] += partials[2 * (i + k * kThreads) + 1];
+    }
   }
+  for (; i < groups; i += kThreads) {
+    b4[0] += partials[2 * i];
+    f4[0] += partials[2 * i + 1];
+  }
+  double sb = (b4[0] + b4[1]) + (b4[2] + b4[3]);
+  double sf = (f4[0] + f4[1]) + (f4[2] + f4[3]);
   group_sum2(sb, sf);
   if (threadIdx.x == 0) {
     if (accumulate) {
@@ -1772,7 +1785,11 @@ hipError_t launch_guided(int fmt, int bits, bool decode_only, const Shape& sh, c
                (const uint32_t*)a.cpart, tiles, counts, accumulate);
     if (e != hipSuccess) return e;
   }
-  // Per-tile pairs -> kMidGroups pairs -> acc3, each level in a fixed order.
+  // Per-tile pairs -> acc3 in one workgroup (up to kDirectTiles pairs), else
+  // per-tile pairs -> kMidGroups pairs -> acc3; each level in a fixed order.
+  if (tiles <= kDirectTiles)
+    return launch(sums_final_kernel, dim3(1), dim3(kThreads), stream, (const double*)a.partials, tiles,
+                  units * kUnitElems, acc3, accumulate);
   const int64_t per = (tiles + kMidGroups - 1) / kMidGroups;
   double* mid = a.partials + 2 * tiles;
   e = launch(sums_mid_kernel, dim3(kMidGroups), dim3(kThreads), stream, (const double*)a.partials,
