@@ -3,7 +3,6 @@ value is the guided FP4 value, the gradient reaches the unquantized input
 unchanged): forward values bit-exact against the oracle, backward the
 identity, and a small QAT forward/backward through the guided-layer policy."""
 
-import numpy as np
 import pytest
 import torch
 

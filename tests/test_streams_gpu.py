@@ -3,7 +3,6 @@ same calls run one after another, and the step captured in a HIP graph gives,
 on every replay, the eager results (the library clears its flags with a
 kernel, not a memset, so captures replay correctly)."""
 
-import numpy as np
 import pytest
 import torch
 

@@ -6,7 +6,7 @@ import numpy as np
 import torch
 
 import synthetic as syn
-from oracle import formats, fp4
+from oracle import fp4
 
 
 def test_tiny_pair_deterministic_and_shaped():
