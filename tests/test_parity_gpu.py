@@ -567,6 +567,42 @@ def test_single_pass_largest_group_and_the_next():
     _encode_schedule_check(2, rows_max + 3, cols, 1, 42, single=False)
 
 
+def _random_cases(n, seed):
+    """Seeded random shapes: format, [rows, cols], group rows (0 or a divisor
+    of rows), record width, guided width (0 or the record's), with or without
+    y. At most ~2M elements each, so the oracle keeps up."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        fmt = NV if rng.random() < 0.7 else MX
+        cols = int(rng.choice([16, 32, 48, 64, 96, 128, 256, 512, 1024, 2048, 4096]))
+        if fmt == MX and cols % 32:
+            continue
+        rows = int(rng.integers(1, min(4096, 2_000_000 // cols) + 1))
+        divs = [d for d in range(1, rows + 1) if rows % d == 0]
+        gr = 0 if rng.random() < 0.25 else int(rng.choice(divs))
+        bits = int(rng.integers(1, 5))
+        out.append((fmt, rows, cols, gr, bits, int(rng.choice([0, bits])), bool(rng.random() < 0.5),
+                    int(rng.integers(1 << 30))))
+    return out
+
+
+def test_random_shapes():
+    """40 seeded random shapes through encode_guidance and guided_fake_quant
+    (single-pass, packed and two-pass schedules as the shapes fall), each
+    group with its own magnitude, against the oracle."""
+    for k, (fmt, rows, cols, gr, bits, gbits, with_y, seed) in enumerate(_random_cases(40, 2026)):
+        G.say(f"random case {k}: fmt {fmt} [{rows}, {cols}] group_rows {gr} bits {bits}/{gbits} y {with_y}")
+        xt, xr = syn.activation_pair(rows, cols, (97, seed))
+        n_g = rows // gr if gr else 1
+        mag = 2.0 ** np.random.default_rng(seed).integers(-8, 9, n_g).astype(np.float32)
+        scale = torch.from_numpy(np.repeat(mag, rows // n_g)).reshape(-1, 1)
+        xtb = syn.bits_u16((xt.float() * scale).to(torch.bfloat16)).reshape(-1)
+        xrb = syn.bits_u16((xr.float() * scale).to(torch.bfloat16)).reshape(-1)
+        G.check_encode(xrb, rows, cols, fmt, bits, with_y=with_y, group_rows=gr)
+        G.check_guided(xtb, xrb, rows, cols, fmt, gbits, group_rows=gr)
+
+
 # ---------------------------------------------------------------- row-offset groups
 
 def _offset_groups_pair(sizes, cols, seed):
