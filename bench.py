@@ -124,8 +124,13 @@ class Workload:
 
 
 def build_phases(lib, w, stream, qwork, swork):
-    """Argument tuples of every ABI call, grouped by phase."""
+    """Argument tuples of every ABI call, grouped by phase. The step encodes
+    the whole stream (every layer's chunks, one S per chunk) in one call, then
+    runs the guided pass with the statistics layer by layer; the per-layer
+    encode calls are timed outside the step (and feed the record path)."""
     qb, sb = qwork.numel() * qwork.element_size(), swork.numel() * swork.element_size()
+    enc_all = [(NV, 1, w.layers * w.rows, HIDDEN, CHUNK, w.xr.data_ptr(), None, w.guide.data_ptr(),
+                w.scales.data_ptr(), w.gscale.data_ptr(), None, qwork.data_ptr(), qb, stream)]
     enc, gst, gfq, dia = [], [], [], []
     for i in range(w.layers):
         p = lambda t: t[i].data_ptr()  # noqa: E731
@@ -137,11 +142,12 @@ def build_phases(lib, w, stream, qwork, swork):
                     p(w.yt), None, stream))
         dia.append((NV, 1, w.rows, HIDDEN, CHUNK, p(w.xt), p(w.xr), p(w.guide), p(w.scales),
                     p(w.gscale), p(w.yt), None, p(w.acc), p(w.counts), 0, swork.data_ptr(), sb, stream))
-    step = [("encode_guidance", lib.encode_guidance, enc),
+    step = [("encode_guidance", lib.encode_guidance, enc_all),
             ("guided_fake_quant_stats", lib.guided_fake_quant_stats, gst)]
+    per_layer = [("encode_guidance", lib.encode_guidance, enc)]
     extra = [("guided_fake_quant", lib.guided_fake_quant, gfq)]
     diag = [("guided_fake_quant_stats+mismatch", lib.guided_fake_quant_stats, dia)]
-    return step, extra, diag
+    return step, per_layer, extra, diag
 
 
 def variant_phases(lib, w, stream, qwork, torch, dev):
@@ -168,7 +174,7 @@ def variant_phases(lib, w, stream, qwork, torch, dev):
     return out, (guide, gtok)
 
 
-def record_path(torch, w, step, stream, dev, layers):
+def record_path(torch, w, step, per_layer, stream, dev, layers):
     """Device-to-host transfer of each layer's compact record (mantissa-bit
     plane, scales, chunk scales) through the pinned ring: alone, and pushed
     right after each layer's encode while the step runs. Plus the gather of a
@@ -197,13 +203,13 @@ def record_path(torch, w, step, stream, dev, layers):
             alone = time.perf_counter() - t0
         out["d2h_GB_s"] = round(layers * rec_bytes / alone / 1e9, 2)
 
-        enc, gst = step[0][2], step[1][2]
+        enc, gst = per_layer[0][2], step[1][2]
         for rep in range(2):
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             pending = []
             for i in range(layers):
-                st = step[0][1](*enc[i])
+                st = per_layer[0][1](*enc[i])
                 if st != 0:
                     raise RuntimeError(f"encode_guidance returned {st}")
                 drain(pending, depth - 1)
@@ -430,7 +436,7 @@ def main():
     log(f"bench: generating {args.layers} layers x {args.chunks} chunks of [{CHUNK}, {HIDDEN}] pairs")
     t0 = time.perf_counter()
     w = Workload(torch, syn, args.layers, args.chunks, dev)
-    qn = int(lib.trace_quant_workspace_bytes(NV, w.rows, HIDDEN, CHUNK))
+    qn = int(lib.trace_quant_workspace_bytes(NV, w.layers * w.rows, HIDDEN, CHUNK))
     sn = int(lib.trace_guided_stats_workspace_bytes(NV, w.rows, HIDDEN, CHUNK))
     qwork = torch.empty(max(qn // 8, 1), dtype=torch.float64, device=dev)
     swork = torch.empty(max(sn // 8, 1), dtype=torch.float64, device=dev)
@@ -439,7 +445,7 @@ def main():
         f"{w.bytes_resident() / 2**30:.1f} GiB resident")
 
     stream = torch.cuda.current_stream(dev)
-    step, extra, diag = build_phases(lib, w, stream.cuda_stream, qwork, swork)
+    step, per_layer, extra, diag = build_phases(lib, w, stream.cuda_stream, qwork, swork)
 
     for i in range(args.warmup):
         run_phases(step)
@@ -448,9 +454,10 @@ def main():
     # The single-pass encode publishes each chunk's S in its workspace (after
     # the per-chunk slots); the two-pass schedule leaves those words alone.
     if args.warmup > 0:
-        pub = qwork.view(torch.int32)[w.chunks * 1024:w.chunks * 2048:1024].cpu()
-        s_last = w.gscale[w.layers - 1, :, 0].contiguous().view(torch.int32).cpu()
-        encode_path = "single-pass" if torch.equal(pub, s_last) else "two-pass"
+        G = w.layers * w.chunks
+        pub = qwork.view(torch.int32)[G * 1024:G * 2048:1024].cpu()
+        s_all = w.gscale[:, :, 0].contiguous().view(torch.int32).reshape(-1).cpu()
+        encode_path = "single-pass" if torch.equal(pub, s_all) else "two-pass"
     else:
         encode_path = "unknown"
     log(f"bench: encode schedule {encode_path}")
@@ -459,7 +466,16 @@ def main():
     log(f"bench: {args.steps} timed steps in {wall:.3f} s")
     acc = w.acc.cpu().tolist()               # sums of the last step
 
-    kernels = {name: kernel_entry(name, per[j], len(calls), w.n) for j, (name, _, calls) in enumerate(step)}
+    kernels = {name: kernel_entry(name, per[j], len(calls), w.layers * w.n // len(calls))
+               for j, (name, _, calls) in enumerate(step)}
+    kernels["encode_guidance"]["note"] = (f"one call over the whole stream: {w.layers * w.chunks} groups of "
+                                          f"{CHUNK} rows, one S each")
+    run_phases(per_layer)
+    _, per_l = timed(torch, per_layer, max(3, args.steps // 2))
+    kernels["encode_guidance_per_layer"] = kernel_entry("encode_guidance", per_l[0], len(per_layer[0][2]), w.n)
+    kernels["encode_guidance_per_layer"]["note"] = (f"timed outside the step: one call per layer "
+                                                    f"({w.chunks} groups of {CHUNK} rows)")
+    log("bench: per-layer encode timed")
     if not args.no_extra:
         run_phases(extra)
         _, per_x = timed(torch, extra, max(3, args.steps // 2))
@@ -497,7 +513,7 @@ def main():
 
     record = None
     if not args.no_record:
-        record = record_path(torch, w, step, stream.cuda_stream, dev, w.layers)
+        record = record_path(torch, w, step, per_layer, stream.cuda_stream, dev, w.layers)
         log("bench: record path timed")
 
     elems_step = w.layers * w.n

@@ -772,7 +772,7 @@ constexpr int kOPUnits = 10;                         // units per data thread an
 constexpr int kOPTile = kOPData * kOPUnits;          // most units per tile (4480, a multiple of 64)
 constexpr int kSlotsPerLane = kPartMax / 64;
 constexpr int kRawBufferWord3 = 0x00020000;     // buffer descriptor word 3: untyped 32-bit data, no swizzle
-constexpr int kBufferNT = 2;                    // buffer load cache policy: nontemporal
+constexpr int kBufferNT = 2;                    // buffer access cache policy: nontemporal
 
 __device__ __forceinline__ uint32_t load_agent(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1311,29 +1311,45 @@ __global__ __launch_bounds__(kThreads) void sums_mid_kernel(const double* __rest
   }
 }
 
-// Fixed-order reduction of `groups` partial pairs into acc3 = {SB, SF, n}.
-// Each thread keeps four running sums (so four loads are in flight) and
-// adds them in a fixed order.
-__global__ __launch_bounds__(kThreads) void sums_final_kernel(const double* __restrict__ partials,
-                                                              int64_t groups, int64_t n, double* acc3,
-                                                              int accumulate) {
-  double b4[4] = {0.0, 0.0, 0.0, 0.0}, f4[4] = {0.0, 0.0, 0.0, 0.0};
-  int64_t i = threadIdx.x;
-  for (; i + 3 * kThreads < groups; i += 4 * kThreads) {
+// Fixed-order reduction of `groups` partial pairs into acc3 = {SB, SF, n}, by
+// one workgroup of kSumThreads. Thread t sums pairs t, t + kSumThreads, ... in
+// order, loading kSumBatch pairs at a time so that a streamed layer's 17,408
+// pairs take two round trips to memory; the 16 wave sums are then added in
+// wave order. (Workspaces are only 8-byte aligned: the pair is two loads.)
+constexpr int kSumThreads = 1024;
+constexpr int kSumBatch = 16;
+__global__ __launch_bounds__(kSumThreads) void sums_final_kernel(const double* __restrict__ partials,
+                                                                 int64_t groups, int64_t n, double* acc3,
+                                                                 int accumulate) {
+  double sb = 0.0, sf = 0.0;
+  for (int64_t base = threadIdx.x; base < groups; base += (int64_t)kSumBatch * kSumThreads) {
+    double2 v[kSumBatch];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      b4[k] += partials[2 * (i + k * kThreads)];
-      f4[k] += partials[2 * (i + k * kThreads) + 1];
+    for (int k = 0; k < kSumBatch; ++k) {
+      const int64_t i = base + (int64_t)k * kSumThreads;
+      v[k] = i < groups ? make_double2(partials[2 * i], partials[2 * i + 1]) : make_double2(0.0, 0.0);
+    }
+#pragma unroll
+    for (int k = 0; k < kSumBatch; ++k) {
+      sb += v[k].x;
+      sf += v[k].y;
     }
   }
-  for (; i < groups; i += kThreads) {
-    b4[0] += partials[2 * i];
-    f4[0] += partials[2 * i + 1];
+  __shared__ double wb[kSumThreads / 64], wf[kSumThreads / 64];
+  sb = wave_sum(sb);
+  sf = wave_sum(sf);
+  if ((threadIdx.x & 63) == 0) {
+    wb[threadIdx.x >> 6] = sb;
+    wf[threadIdx.x >> 6] = sf;
   }
-  double sb = (b4[0] + b4[1]) + (b4[2] + b4[3]);
-  double sf = (f4[0] + f4[1]) + (f4[2] + f4[3]);
-  group_sum2(sb, sf);
+  __syncthreads();
   if (threadIdx.x == 0) {
+    sb = wb[0];
+    sf = wf[0];
+    for (int w = 1; w < kSumThreads / 64; ++w) {
+      sb += wb[w];
+      sf += wf[w];
+    }
     if (accumulate) {
       acc3[0] += sb;
       acc3[1] += sf;
@@ -1756,7 +1772,7 @@ hipError_t launch_guided(int fmt, int bits, bool decode_only, const Shape& sh, c
   const bool diag = stats && counts != nullptr;
   if (units == 0) {
     if (!stats) return hipSuccess;
-    hipError_t e = launch(sums_final_kernel, dim3(1), dim3(kThreads), stream, (const double*)nullptr,
+    hipError_t e = launch(sums_final_kernel, dim3(1), dim3(kSumThreads), stream, (const double*)nullptr,
                           (int64_t)0, (int64_t)0, acc3, accumulate);
     if (e != hipSuccess || !diag) return e;
     return launch(counts_final_kernel, dim3(kMismatchCounts), dim3(kThreads), stream,
@@ -1788,14 +1804,14 @@ hipError_t launch_guided(int fmt, int bits, bool decode_only, const Shape& sh, c
   // Per-tile pairs -> acc3 in one workgroup (up to kDirectTiles pairs), else
   // per-tile pairs -> kMidGroups pairs -> acc3; each level in a fixed order.
   if (tiles <= kDirectTiles)
-    return launch(sums_final_kernel, dim3(1), dim3(kThreads), stream, (const double*)a.partials, tiles,
+    return launch(sums_final_kernel, dim3(1), dim3(kSumThreads), stream, (const double*)a.partials, tiles,
                   units * kUnitElems, acc3, accumulate);
   const int64_t per = (tiles + kMidGroups - 1) / kMidGroups;
   double* mid = a.partials + 2 * tiles;
   e = launch(sums_mid_kernel, dim3(kMidGroups), dim3(kThreads), stream, (const double*)a.partials,
              tiles, per, mid);
   if (e != hipSuccess) return e;
-  return launch(sums_final_kernel, dim3(1), dim3(kThreads), stream, (const double*)mid,
+  return launch(sums_final_kernel, dim3(1), dim3(kSumThreads), stream, (const double*)mid,
                 (int64_t)kMidGroups, units * kUnitElems, acc3, accumulate);
 }
 
@@ -1806,7 +1822,7 @@ hipError_t launch_stats(int64_t n, const uint16_t* xt, const uint16_t* xr, const
   hipError_t e = launch(stats_partial_kernel, dim3(groups), dim3(kThreads), stream, xt, xr, yt, yr,
                         n, partials);
   if (e != hipSuccess) return e;
-  return launch(sums_final_kernel, dim3(1), dim3(kThreads), stream, (const double*)partials,
+  return launch(sums_final_kernel, dim3(1), dim3(kSumThreads), stream, (const double*)partials,
                 (int64_t)groups, n, acc3, accumulate);
 }
 

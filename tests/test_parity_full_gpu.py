@@ -123,6 +123,55 @@ def test_stream_layer_bench_configuration():
     assert G.rel_close(a[1], ref[1]) and G.rel_close(a[0], ref[0])
 
 
+def test_whole_stream_encode_one_call():
+    """The rollout side of the whole streamed workload in one call, as the
+    benchmark's step runs it: 20 layers x 17 chunks of [8192, 2048] (340
+    groups, one global scale each). Every group's {S, A} against the oracle's
+    scale of the exact amax, every layer bit for bit against a call of its
+    own, sampled rows of the first, middle and last group against the oracle."""
+    G.say("full size: whole stream, 20 x 17 x [8192, 2048] in one encode call")
+    layers, chunks, CH = len(syn.GUIDED_LAYERS), syn.STREAM_CHUNKS, syn.STREAM_CHUNK
+    rows_l, cols = chunks * CH, syn.HIDDEN
+    dev = G.DEV
+    xr = torch.empty((layers, rows_l, cols), dtype=torch.bfloat16, device=dev)
+    for li, layer in enumerate(syn.GUIDED_LAYERS):
+        sigma = syn.stream_sigma(layer, dev)
+        for c in range(chunks):
+            _, b = syn.stream_pair(layer, c, dev, sigma=sigma)
+            xr[li, c * CH:(c + 1) * CH].copy_(b)
+            del b
+    flat = xr.view(layers * rows_l, cols)
+    work = tq.quant_workspace(NV, layers * rows_l, cols, CH, device=dev)
+    g = tq.encode_guidance(flat, NV, 1, group_rows=CH, work=work)
+    torch.cuda.synchronize()
+    G_ = layers * chunks
+    assert work.view(torch.int32)[G_ * 2048].item() == 0
+    # every group's amax (plain torch, exact) and the oracle's S of it
+    amax = (flat.view(torch.int16) & 0x7FFF).view(G_, CH * cols).amax(dim=1).cpu().numpy().astype(np.uint16)
+    A = ofp4.bf16_to_f32(amax)
+    S = np.array([ofp4.nvfp4_global_scale(a) for a in A], np.float32)
+    gs = G.f32(g.gscale).reshape(G_, 2)
+    G.assert_same(gs[:, 1], A, "whole-stream A")
+    G.assert_same(gs[:, 0], S, "whole-stream S")
+    # each layer on its own gives the same planes and scales
+    guide = g.guide.view(layers, rows_l, -1)
+    scales = g.scales.view(layers, rows_l, -1)
+    for li in range(layers):
+        gl = tq.encode_guidance(xr[li], NV, 1, group_rows=CH)
+        assert torch.equal(gl.guide, guide[li]), li
+        assert torch.equal(gl.scales, scales[li]), li
+        assert torch.equal(gl.gscale.view(-1), g.gscale.view(G_, 2)[li * chunks:(li + 1) * chunks].reshape(-1)), li
+    B = ofp4.BLOCK[NV]
+    for grp in (0, G_ // 2, G_ - 1):
+        for r0, r1 in _samples(CH, span=32):
+            a0, a1 = grp * CH + r0, grp * CH + r1
+            xb = _bits(flat[a0:a1])
+            o = ofp4.encode_guidance(NV, 1, xb, S[grp])
+            G.assert_same(G.u8(g.guide[a0:a1]).reshape(-1), o["guide"], f"guide group {grp} rows {r0}:{r1}")
+            G.assert_same(G.u8(g.scales[a0:a1]).reshape(-1), o["scales"], f"scales group {grp} rows {r0}:{r1}")
+            assert o["scales"].size == (a1 - a0) * cols // B
+
+
 def test_stream_layer_per_token_scales():
     """One streamed layer, 139,264 x 2048, with a global scale per token
     (group_rows = 1, the packed single-pass encode): every row's S against
