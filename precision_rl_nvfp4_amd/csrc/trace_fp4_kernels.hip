@@ -1314,10 +1314,11 @@ __global__ __launch_bounds__(kThreads) void sums_mid_kernel(const double* __rest
 // Fixed-order reduction of `groups` partial pairs into acc3 = {SB, SF, n}, by
 // one workgroup of kSumThreads. Thread t sums pairs t, t + kSumThreads, ... in
 // order, loading kSumBatch pairs at a time so that a streamed layer's 17,408
-// pairs take two round trips to memory; the 16 wave sums are then added in
-// wave order. (Workspaces are only 8-byte aligned: the pair is two loads.)
+// pairs (17 per thread) take one round trip to memory; the 16 wave sums are
+// then added in wave order. (Workspaces are only 8-byte aligned: a pair is
+// two loads.)
 constexpr int kSumThreads = 1024;
-constexpr int kSumBatch = 16;
+constexpr int kSumBatch = 17;
 __global__ __launch_bounds__(kSumThreads) void sums_final_kernel(const double* __restrict__ partials,
                                                                  int64_t groups, int64_t n, double* acc3,
                                                                  int accumulate) {
