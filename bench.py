@@ -373,6 +373,22 @@ def _oracle_unit(args):
     return int(np.asarray(bt).size)
 
 
+def single_core_tiny(torch, target_s=2.0):
+    """The same oracle chain on the tiny pair (256 tokens x 2048, seed 0) in
+    this process, i.e. on one core, repeated for about `target_s` seconds."""
+    import synthetic as syn
+    xt, xr = syn.tiny_pair("cpu")
+    args = (syn.bits_u16(xt).reshape(-1), syn.bits_u16(xr).reshape(-1))
+    _oracle_unit(args)                                   # warm
+    reps, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < target_s:
+        n = _oracle_unit(args)
+        reps += 1
+    wall = time.perf_counter() - t0
+    return {"value": round(reps * n / wall / 1e9, 6), "unit": "Gelem/s", "cores": 1,
+            "sample": f"{reps} passes of encode(bits=1) -> guided(bits=1) -> sums over 256 x 2048, {wall:.1f} s"}
+
+
 def cpu_baseline(torch, w, workers, target_s):
     """The oracle, as it stands, over 1024-token slices of the streamed
     workload (each slice taken as one tensor with its own global scale),
@@ -401,10 +417,13 @@ def cpu_baseline(torch, w, workers, target_s):
             elems += sum(pool.map(_oracle_unit, jobs, chunksize=1))
             rounds += 1
         wall = time.perf_counter() - t0
+    single = single_core_tiny(torch)
     return {
         "value": round(elems / wall / 1e9, 6),
         "unit": "Gelem/s",
         "cores": workers,
+        "host_cpus": os.cpu_count(),
+        "single_core_tiny": single,
         "kind": "oracle",
         "sample": (f"{rounds * workers} slices of {rows} tokens x {HIDDEN} from the streamed workload "
                    f"({elems} elements per side), each one NVFP4 tensor: encode(bits=1) -> "
