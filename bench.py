@@ -174,6 +174,24 @@ def variant_phases(lib, w, stream, qwork, torch, dev):
     return out, (guide, gtok)
 
 
+def rtn_decode_phases(lib, w, stream, qwork, codes, gsq):
+    """The other steps of the path, per layer: vanilla fake quantization of
+    X_t (quantize_rtn with codes, scales and y, S from each chunk's amax),
+    RTN under the rollout scales (guided_fake_quant bits=0) and the 1-bit
+    Reconstruct alone (decode_guidance): (name, bytes/elem, phase)."""
+    qb = qwork.numel() * qwork.element_size()
+    q, g0, dec = [], [], []
+    for i in range(w.layers):
+        p = lambda t: t[i].data_ptr()  # noqa: E731
+        q.append((NV, w.rows, HIDDEN, CHUNK, p(w.xt), None, p(codes), p(w.scales), p(gsq), p(w.yt),
+                  qwork.data_ptr(), qb, stream))
+        g0.append((NV, 0, w.rows, HIDDEN, CHUNK, p(w.xt), None, p(w.scales), p(w.gscale), p(w.yt), None, stream))
+        dec.append((NV, 1, w.rows, HIDDEN, CHUNK, p(w.xt), p(w.guide), p(w.scales), p(w.gscale), p(codes), stream))
+    return [("quantize_rtn", 2 + 1 / 2 + 1 / 16 + 2, ("quantize_rtn", lib.quantize_rtn, q)),
+            ("guided_fake_quant_bits0", 2 + 1 / 16 + 2, ("guided_fake_quant", lib.guided_fake_quant, g0)),
+            ("decode_guidance", 2 + 1 / 8 + 1 / 16 + 1 / 2, ("decode_guidance", lib.decode_guidance, dec))]
+
+
 def record_path(torch, w, step, per_layer, stream, dev, layers):
     """Device-to-host transfer of each layer's compact record (mantissa-bit
     plane, scales, chunk scales) through the pinned ring: alone, and pushed
@@ -527,6 +545,21 @@ def main():
                 "guided_fake_quant": kernel_entry("guided_fake_quant", per_v[1], len(phases[1][2]), w.n,
                                                   bpe_g)}
         del keep
+        # The remaining steps of the path on the same layers: the 1-bit record
+        # of the step is re-encoded first, since the variants above rewrote
+        # the scale plane.
+        run_phases(step[:1])
+        codes = torch.empty((w.layers, w.rows, HIDDEN // 2), dtype=torch.uint8, device=dev)
+        gsq = torch.empty_like(w.gscale)
+        other = {}
+        for name, bpe, phase in rtn_decode_phases(lib, w, stream.cuda_stream, qwork, codes, gsq):
+            run_phases([phase])
+            _, per_o = timed(torch, [phase], max(3, args.steps // 4))
+            other[name] = kernel_entry(phase[0], per_o[0], len(phase[2]), w.n, bpe)
+            if name == "quantize_rtn":
+                run_phases(step[:1])          # the record again (quantize_rtn rewrote the scales)
+        variants["other_steps"] = other
+        del codes, gsq
         variants["moe_per_expert"] = moe_per_expert(torch, syn, dev, max(3, args.steps // 4))
         log("bench: variants timed")
 
