@@ -88,7 +88,7 @@
 extern "C" {
 #endif
 
-#define TRACE_ABI_VERSION 6
+#define TRACE_ABI_VERSION 7
 
 /* Entries of the mismatch diagnostics of guided_fake_quant_stats. */
 #define TRACE_MISMATCH_COUNTS 32
@@ -136,6 +136,17 @@ const char* trace_status_str(int status);
  * Process-wide. Returns the previous setting, or TRACE_EINVAL for a negative
  * value. */
 int64_t trace_set_encode_batch(int64_t groups_per_batch);
+
+/* Bound of every wait of the single-pass encode on other workgroups, in
+ * polls (0 = the default, 4,194,304 polls, about 0.25 s). A wait that reaches
+ * it gives up: the workgroup adds 1 to the workspace's failure count and
+ * carries on (with S = NaN where the scale had not arrived), so the launch
+ * always completes; that call's outputs are then undefined. The next call
+ * starts from a cleared workspace. For callers and tests that need the
+ * failure path to finish quickly (e.g. a limit of 1 makes the waits give up
+ * at once). Process-wide. Returns the previous setting, or TRACE_EINVAL for
+ * a value below 0 or above 2^31 - 1. */
+int64_t trace_set_wait_limit(int64_t polls);
 
 /* Workspace bytes quantize_rtn / encode_guidance need to derive the global
  * scales from the amax (NVFP4 with gscale_out): 4 * (2048 * G + 1) rounded up

@@ -221,6 +221,11 @@ int64_t trace_set_encode_batch(int64_t groups_per_batch) {
   return tfp4::set_encode_batch(groups_per_batch);
 }
 
+int64_t trace_set_wait_limit(int64_t polls) {
+  if (polls < 0 || polls > INT32_MAX) return TRACE_EINVAL;
+  return tfp4::set_wait_limit(polls);
+}
+
 int64_t trace_quant_workspace_bytes(int fmt, int64_t rows, int64_t cols, int64_t group_rows) {
   if (!valid_fmt(fmt)) return -1;
   CallShape cs;

@@ -80,9 +80,13 @@ hipError_t launch_guided_offsets(int bits, int64_t rows, int64_t cols, int64_t G
 int check_device();
 
 // Groups per batch of NVFP4 encoding with scales from the amax (each launch
-// quantizes one batch and reads the next for its amax); 0 = sized for the
-// Infinity Cache. Returns the previous value.
+// quantizes one batch and reads the next for its amax); 0 = automatic.
+// Returns the previous value.
 int64_t set_encode_batch(int64_t groups);
+
+// Polls after which a bounded wait of the single-pass encode gives up; 0 =
+// the default. Returns the previous value.
+int64_t set_wait_limit(int64_t polls);
 
 // Deterministic float64 sums of discrepancy_stats into acc3.
 hipError_t launch_stats(int64_t n, const uint16_t* xt, const uint16_t* xr, const uint16_t* yt,

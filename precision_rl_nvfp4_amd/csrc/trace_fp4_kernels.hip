@@ -747,7 +747,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
 // tile, so every load instruction is issued whatever the tile's length and
 // each wait covers exactly the older tile.
 // Slots and S words are zeroed by a fill kernel before the launch. Every wait
-// is bounded: past kSpinMax polls the workgroup records an error in *err and
+// is bounded: past spin_max polls the workgroup records an error in *err and
 // carries on with S = NaN, so the grid always drains.
 struct OnePassArgs {
   const uint4* x;
@@ -759,13 +759,14 @@ struct OnePassArgs {
   uint32_t* slots;           // [groups][kPartMax] tagged tile maxima
   uint32_t* sword;           // [groups][kSCopies][64]: S bits at [.][c][0], 0 until published
   uint32_t* err;             // bounded-wait failures
+  int spin_max;              // polls before a wait gives up
   float* gout;
   uint8_t* plane;
   uint8_t* scales;
   uint4* y;
 };
 
-constexpr int kSpinMax = 1 << 22;
+constexpr int kSpinMax = 1 << 22;      // default bound of every wait, in polls (~0.25 s)
 constexpr int kSCopies = 16;            // copies of each published S, one per 256-byte line
 constexpr int kOPDataWaves = 7;                      // data waves per workgroup
 constexpr int kOPData = kOPDataWaves * 64;           // data threads
@@ -811,7 +812,7 @@ __global__ __launch_bounds__(kOnePassThreads, 4) void onepass_encode_kernel(OneP
 #pragma unroll
         for (int k2 = 0; k2 < kSlotsPerLane; ++k2) all = all && (v[k2] & 0x80000000u) != 0u;
         if (__all(all)) break;
-        if (++spins > kSpinMax) {
+        if (++spins > a.spin_max) {
           if (lane == 0) atomicAdd(a.err, 1u);
 #pragma unroll
           for (int k2 = 0; k2 < kSlotsPerLane; ++k2) v[k2] |= 0x80000000u;
@@ -865,7 +866,7 @@ __global__ __launch_bounds__(kOnePassThreads, 4) void onepass_encode_kernel(OneP
         const uint32_t* w = &a.sword[((int64_t)g * kSCopies + (int)(blockIdx.x % kSCopies)) * 64];
         int spins = 0;
         while ((v = load_agent(w)) == 0u) {
-          if (++spins > kSpinMax) {
+          if (++spins > a.spin_max) {
             atomicAdd(a.err, 1u);
             v = 0x7FC00000u;
             break;
@@ -1461,7 +1462,8 @@ TileMap tile_map(int fmt, const Shape& sh0) {
 
 int64_t tile_grid(const TileMap& m) { return m.packed ? m.tiles : m.groups * m.tiles; }
 
-std::atomic<int64_t> g_encode_batch{0};   // groups per batch; 0 = sized for the Infinity Cache
+std::atomic<int64_t> g_encode_batch{0};   // groups per batch; 0 = automatic (kCacheBatchBytes of input)
+std::atomic<int64_t> g_wait_limit{0};     // polls per bounded wait; 0 = kSpinMax
 constexpr int64_t kCacheBatchBytes = (int64_t)96 << 20;
 
 int amax_parts(int64_t upg) {
@@ -1613,6 +1615,8 @@ hipError_t launch_onepass(int plane_mode, bool wy, const Shape& sh, const QuantA
   a.slots = static_cast<uint32_t*>(work);
   a.sword = a.slots + sh.groups * kPartMax;
   a.err = a.sword + sh.groups * kSCopies * 64;
+  const int64_t wl = g_wait_limit.load(std::memory_order_relaxed);
+  a.spin_max = wl > 0 ? (int)wl : kSpinMax;
   a.gout = qa.gout;
   a.plane = qa.plane;
   a.scales = qa.scales;
@@ -1742,9 +1746,10 @@ hipError_t launch_quantize(int fmt, int plane_mode, const Shape& sh, const uint1
   }
   // Two passes: groups go in batches of about kCacheBatchBytes of input, and
   // the launch that quantizes batch b also runs the amax pass of batch b + 1,
-  // so each batch is re-read one launch after its first read, while it still
-  // sits in the 256 MB Infinity Cache. A caller-set batch size overrides the
-  // automatic one (trace_set_encode_batch).
+  // so each batch is re-read one launch after its first read. (On MI355X the
+  // re-read runs at the plain HBM rate, not from the Infinity Cache, for any
+  // batch size measured.) A caller-set batch size overrides the automatic one
+  // (trace_set_encode_batch).
   AmaxArgs m{};
   m.x = a.x;
   m.upg = sh.upg;
@@ -1840,6 +1845,7 @@ hipError_t launch_stats(int64_t n, const uint16_t* xt, const uint16_t* xr, const
 
 namespace tfp4 {
 int64_t set_encode_batch(int64_t groups) { return g_encode_batch.exchange(groups); }
+int64_t set_wait_limit(int64_t polls) { return g_wait_limit.exchange(polls); }
 
 // ---- row-offset groups: workspace [offs | tstart | table | tile maxima]
 

@@ -51,7 +51,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.trace_abi_version() == _abi.ABI_VERSION == 6
+    assert lib.trace_abi_version() == _abi.ABI_VERSION == 7
     for code, name in [(0, "TRACE_OK"), (-1, "TRACE_EINVAL"), (-2, "TRACE_ESHAPE"),
                        (-3, "TRACE_EALIGN"), (-4, "TRACE_EALIAS"), (-5, "TRACE_EDEVICE"),
                        (-6, "TRACE_ELAUNCH"), (-7, "TRACE_EBUSY"), (7, "unknown status")]:
@@ -63,6 +63,14 @@ def test_encode_batch_setting(lib):
     assert lib.trace_set_encode_batch(0) == 3
     assert lib.trace_set_encode_batch(-1) == _abi.EINVAL
     assert lib.trace_set_encode_batch(0) == 0
+
+
+def test_wait_limit_setting(lib):
+    assert lib.trace_set_wait_limit(5) == 0
+    assert lib.trace_set_wait_limit(0) == 5
+    assert lib.trace_set_wait_limit(-1) == _abi.EINVAL
+    assert lib.trace_set_wait_limit(1 << 31) == _abi.EINVAL
+    assert lib.trace_set_wait_limit(0) == 0
 
 
 def test_workspace_sizes(lib):
