@@ -505,22 +505,32 @@ __global__ __launch_bounds__(64) void fill_gscale_kernel(float* g, int64_t group
 }
 
 // Partial group amax: workgroup w of group g writes the max bf16 magnitude
-// (as binary32 bits) of its strided share of the group to part[g][w].
-// `blk` is the workgroup's index within the amax pass.
+// (as binary32 bits) of its share of the group to part[g][w]. The share is a
+// contiguous range of whole 8-unit-per-thread tiles, read a tile (8 loads
+// per thread, 32 KB per workgroup) at a time. `blk` is the workgroup's index
+// within the amax pass.
 __device__ __forceinline__ void amax_body(const AmaxArgs& a, int64_t blk, uint32_t* red) {
   const int64_t gi = blk / a.nparts;
   const int w = (int)(blk - gi * a.nparts);
   const int64_t g = a.g0 + gi;
   const uint4* x = a.x + g * a.upg;
-  const int64_t stride = (int64_t)a.nparts * kThreads;
+  constexpr int64_t kTile = (int64_t)kThreads * 8;
+  const int64_t tiles = (a.upg + kTile - 1) / kTile;
+  const int64_t per = (tiles + a.nparts - 1) / a.nparts;   // tiles of this workgroup
+  const int64_t t0 = (int64_t)w * per;
+  const int64_t t1 = min(t0 + per, tiles);
   uint32_t m = 0;
-  int64_t u = (int64_t)w * kThreads + threadIdx.x;
-  for (; u + 3 * stride < a.upg; u += 4 * stride) {
-    const uint4 p = load_stream(x + u), q = load_stream(x + u + stride), r = load_stream(x + u + 2 * stride),
-                s = load_stream(x + u + 3 * stride);
-    m = max(m, max(max(unit_amax_bits(p), unit_amax_bits(q)), max(unit_amax_bits(r), unit_amax_bits(s))));
+  for (int64_t t = t0; t < t1; ++t) {
+    const int64_t base = t * kTile + threadIdx.x;
+    uint4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int64_t u = base + k * kThreads;
+      v[k] = u < a.upg ? load_stream(x + u) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) m = max(m, unit_amax_bits(v[k]));
   }
-  for (; u < a.upg; u += stride) m = max(m, unit_amax_bits(load_stream(x + u)));
   m = wave_max_u32(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
