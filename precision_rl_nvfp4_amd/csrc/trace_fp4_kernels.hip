@@ -585,7 +585,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
   __shared__ float2 lut[PACK ? 1 : 128];
   __shared__ uint32_t red[kThreads / 64];
   __shared__ float gs[PACK ? kPackGroups : 1];                  // S of the tile's groups
-  __shared__ uint32_t ga[PACK && SSRC == 2 ? kPackGroups : 1];  // their amax (bf16 bits)
+  __shared__ uint32_t ga[PACK && SSRC == 2 ? kPackGroups : 1];  // segment maxima (bf16 bits)
   if constexpr (SSRC == 1) {
     if ((int64_t)blockIdx.x >= a.qblocks) {
       amax_body(a.side, (int64_t)blockIdx.x - a.qblocks, red);
@@ -626,19 +626,24 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
     const int64_t g0t = tbase >> lg;                 // first group of the tile
     const int gpt = kTileUnits >> lg;                // groups per tile
     if constexpr (SSRC == 2) {
-      for (int i = threadIdx.x; i < gpt; i += kThreads) ga[i] = 0u;
-      __syncthreads();
-      // Segments of min(upg, 64) lanes hold one group's units for a given j.
-      const int w = lg < 6 ? 1 << lg : 64;
+      // Segments of min(upg, 64) lanes hold one group's units for a given j;
+      // each writes its max to its own slot (tile unit >> lgs), so every slot
+      // is written once and no atomics or clearing are needed. A group of
+      // more than 64 units combines its 2^(lg - 6) slots.
+      const int lgs = lg < 6 ? lg : 6;
+      const int w = 1 << lgs;
 #pragma unroll
       for (int j = 0; j < kUPT; ++j) {
         uint32_t bm = unit_amax_bits(v[j]);          // units past the end read as zero
         for (int off = w >> 1; off > 0; off >>= 1) bm = max(bm, (uint32_t)__shfl_xor((int)bm, off));
-        if ((threadIdx.x & (w - 1)) == 0 && bm != 0u) atomicMax(&ga[(j * kThreads + threadIdx.x) >> lg], bm);
+        if ((threadIdx.x & (w - 1)) == 0) ga[(j * kThreads + threadIdx.x) >> lgs] = bm;
       }
       __syncthreads();
+      const int spg = 1 << (lg - lgs);               // slots per group
       for (int i = threadIdx.x; i < gpt; i += kThreads) {
-        const float A = __uint_as_float(ga[i] << 16);
+        uint32_t gm = 0u;
+        for (int k = 0; k < spg; ++k) gm = max(gm, ga[i * spg + k]);
+        const float A = __uint_as_float(gm << 16);
         const float Sg = global_scale(A);
         gs[i] = Sg;
         const int64_t gg = g0t + i;
