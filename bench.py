@@ -174,22 +174,28 @@ def variant_phases(lib, w, stream, qwork, torch, dev):
     return out, (guide, gtok)
 
 
-def rtn_decode_phases(lib, w, stream, qwork, codes, gsq):
+def rtn_decode_phases(lib, w, stream, qwork, codes, gsq, dwork):
     """The other steps of the path, per layer: vanilla fake quantization of
     X_t (quantize_rtn with codes, scales and y, S from each chunk's amax),
-    RTN under the rollout scales (guided_fake_quant bits=0) and the 1-bit
-    Reconstruct alone (decode_guidance): (name, bytes/elem, phase)."""
+    RTN under the rollout scales (guided_fake_quant bits=0), the 1-bit
+    Reconstruct alone (decode_guidance) and the discrepancy sums alone
+    (discrepancy_stats over four distinct layer-sized bf16 arrays):
+    (name, bytes/elem, phase)."""
     qb = qwork.numel() * qwork.element_size()
-    q, g0, dec = [], [], []
+    db = dwork.numel() * dwork.element_size()
+    q, g0, dec, st = [], [], [], []
     for i in range(w.layers):
         p = lambda t: t[i].data_ptr()  # noqa: E731
         q.append((NV, w.rows, HIDDEN, CHUNK, p(w.xt), None, p(codes), p(w.scales), p(gsq), p(w.yt),
                   qwork.data_ptr(), qb, stream))
         g0.append((NV, 0, w.rows, HIDDEN, CHUNK, p(w.xt), None, p(w.scales), p(w.gscale), p(w.yt), None, stream))
         dec.append((NV, 1, w.rows, HIDDEN, CHUNK, p(w.xt), p(w.guide), p(w.scales), p(w.gscale), p(codes), stream))
+        yr = w.xt[(i + 1) % w.layers].data_ptr()     # a fourth array of the layer's size
+        st.append((w.n, p(w.xt), p(w.xr), p(w.yt), yr, p(w.acc), 0, dwork.data_ptr(), db, stream))
     return [("quantize_rtn", 2 + 1 / 2 + 1 / 16 + 2, ("quantize_rtn", lib.quantize_rtn, q)),
             ("guided_fake_quant_bits0", 2 + 1 / 16 + 2, ("guided_fake_quant", lib.guided_fake_quant, g0)),
-            ("decode_guidance", 2 + 1 / 8 + 1 / 16 + 1 / 2, ("decode_guidance", lib.decode_guidance, dec))]
+            ("decode_guidance", 2 + 1 / 8 + 1 / 16 + 1 / 2, ("decode_guidance", lib.decode_guidance, dec)),
+            ("discrepancy_stats", 8, ("discrepancy_stats", lib.discrepancy_stats, st))]
 
 
 def record_path(torch, w, step, per_layer, stream, dev, layers):
@@ -551,15 +557,17 @@ def main():
         run_phases(step[:1])
         codes = torch.empty((w.layers, w.rows, HIDDEN // 2), dtype=torch.uint8, device=dev)
         gsq = torch.empty_like(w.gscale)
+        dn = int(lib.trace_stats_workspace_bytes(w.n))
+        dwork = torch.empty(max(dn // 8, 1), dtype=torch.float64, device=dev)
         other = {}
-        for name, bpe, phase in rtn_decode_phases(lib, w, stream.cuda_stream, qwork, codes, gsq):
+        for name, bpe, phase in rtn_decode_phases(lib, w, stream.cuda_stream, qwork, codes, gsq, dwork):
             run_phases([phase])
             _, per_o = timed(torch, [phase], max(3, args.steps // 4))
             other[name] = kernel_entry(phase[0], per_o[0], len(phase[2]), w.n, bpe)
             if name == "quantize_rtn":
                 run_phases(step[:1])          # the record again (quantize_rtn rewrote the scales)
         variants["other_steps"] = other
-        del codes, gsq
+        del codes, gsq, dwork
         variants["moe_per_expert"] = moe_per_expert(torch, syn, dev, max(3, args.steps // 4))
         log("bench: variants timed")
 
