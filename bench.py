@@ -304,6 +304,74 @@ def moe_per_expert(torch, syn, dev, reps):
     return out
 
 
+def other_configs(torch, syn, dev, reps):
+    """The MXFP4 and FP4 KV-cache workloads, timed per call with events (the
+    Infinity Cache flushed before each call): MXFP4 encode (bits=1) and
+    guided rounding on [65536, 2048] pairs with midpoint ties; the KV cache's
+    full-code record (bits=4) and guided rounding on the 40 K and V tensors of
+    20 layers ([65536, 256] each), as one call over all 40 (one S per tensor)
+    and as one call per tensor."""
+    import precision_rl_nvfp4_amd as tq
+
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def timeit(fn, n, bpe, calls=1):
+        fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in ev:
+            flush.fill_(1)
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        us = sum(e0.elapsed_time(e1) for e0, e1 in ev) * 1e3 / reps / calls
+        gbs = bpe * n / (us * 1e-6) / 1e9
+        return {"avg_us_per_call": round(us, 2), "calls_per_pass": calls, "elements_per_call": n,
+                "GB_s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+    out = {}
+    xt, xr = syn.mxfp4_pair(device=dev)
+    n = xt.numel()
+    g = tq.encode_guidance(xr, "mxfp4", 1)
+    y = torch.empty_like(xt)
+    out["mxfp4_65536x2048"] = {
+        "encode_guidance": timeit(lambda: tq.encode_guidance(xr, "mxfp4", 1, guide=g.guide, scales=g.scales),
+                                  n, 2 + 1 / 8 + 1 / 32),
+        "guided_fake_quant": timeit(lambda: tq.guided_fake_quant(xt, g, y=y), n, 2 + 1 / 8 + 1 / 32 + 2)}
+    del xt, xr, g, y
+    layers = 20
+    kt = torch.empty((2 * layers, 65536, 256), dtype=torch.bfloat16, device=dev)
+    kr = torch.empty_like(kt)
+    for li in range(layers):
+        for which in (0, 1):
+            a, b = syn.kv_pair(20 + li, which, device=dev)
+            kt[2 * li + which].copy_(a)
+            kr[2 * li + which].copy_(b)
+            del a, b
+    ft, fr = kt.view(-1, 256), kr.view(-1, 256)
+    n_all, n_one = ft.numel(), kt[0].numel()
+    work = tq.quant_workspace("nvfp4", ft.shape[0], 256, 65536, device=dev)
+    g = tq.encode_guidance(fr, "nvfp4", 4, group_rows=65536, work=work)
+    y = torch.empty_like(ft)
+    be, bg = 2 + 1 / 2 + 1 / 16, 2 + 1 / 2 + 1 / 16 + 2
+    out["kv_40x65536x256"] = {
+        "encode_guidance_one_call": timeit(lambda: tq.encode_guidance(
+            fr, "nvfp4", 4, group_rows=65536, guide=g.guide, scales=g.scales, gscale_out=g.gscale, work=work),
+            n_all, be),
+        "guided_fake_quant_one_call": timeit(lambda: tq.guided_fake_quant(ft, g, bits=4, y=y), n_all, bg)}
+    w1 = tq.quant_workspace("nvfp4", 65536, 256, 0, device=dev)
+    gs = [tq.encode_guidance(kr[i], "nvfp4", 4, work=w1) for i in range(2 * layers)]
+    ys = [torch.empty_like(kt[i]) for i in range(2 * layers)]
+    out["kv_40x65536x256"]["encode_guidance_per_tensor"] = timeit(
+        lambda: [tq.encode_guidance(kr[i], "nvfp4", 4, guide=gs[i].guide, scales=gs[i].scales,
+                                    gscale_out=gs[i].gscale, work=w1) for i in range(2 * layers)],
+        n_one, be, calls=2 * layers)
+    out["kv_40x65536x256"]["guided_fake_quant_per_tensor"] = timeit(
+        lambda: [tq.guided_fake_quant(kt[i], gs[i], bits=4, y=ys[i]) for i in range(2 * layers)],
+        n_one, bg, calls=2 * layers)
+    return out
+
+
 def mismatch_report(counts):
     """Fig. 6-style summary of the per-layer mismatch counts: how often RTN
     under the rollout scales misses the rollout code, how many of those misses
@@ -569,6 +637,7 @@ def main():
         variants["other_steps"] = other
         del codes, gsq, dwork
         variants["moe_per_expert"] = moe_per_expert(torch, syn, dev, max(3, args.steps // 4))
+        variants["other_configs"] = other_configs(torch, syn, dev, max(3, args.steps // 4))
         log("bench: variants timed")
 
     record = None
