@@ -114,12 +114,14 @@ int trace_abi_version(void);
 const char* trace_status_str(int status);
 
 /* How NVFP4 calls that derive S from the amax schedule their work.
- * groups_per_batch = 0 (the default): groups of at most (2 x CUs - 1) x 35840
- * elements (18.3M on a 256-CU MI355X, e.g. an 8192 x 2048 chunk) are encoded
- * in ONE pass over the input by a launch of at most as many workgroups as the
- * device holds at once, which keep their tiles on chip while the group's amax
- * is combined (it needs 2 resident workgroups of 512 threads per CU;
- * otherwise, and for larger groups, the two-pass schedule below is used).
+ * groups_per_batch = 0 (the default): a call of two or more groups of at
+ * most (2 x CUs - 1) x 35840 elements (18.3M on a 256-CU MI355X, e.g. 8192 x
+ * 2048 chunks) is encoded in ONE pass over the input by a launch of at most
+ * as many workgroups as the device holds at once, which keep their tiles on
+ * chip while each group's amax is combined (it needs 2 resident workgroups
+ * of 512 threads per CU; otherwise, for larger groups, and for a call of a
+ * single group, which is faster in two launches, the two-pass schedule
+ * below is used).
  * n > 0 forces two passes (amax, then quantize) with n groups per batch: each
  * launch quantizes one batch while it reads the next batch for its amax
  * (n >= G: one amax pass over every group, then one quantize pass); with 0,

@@ -493,7 +493,7 @@ def test_schedules_agree_on_streamed_chunks():
         assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("G_,gr,cols", [(1, 256, 2048), (17, 64, 2048), (3, 37, 2048), (2, 1024, 2048),
+@pytest.mark.parametrize("G_,gr,cols", [(2, 256, 2048), (17, 64, 2048), (3, 37, 2048), (2, 1024, 2048),
                                          (24, 1024, 2048)])
 def test_single_pass_encode_waits_never_time_out(G_, gr, cols):
     """The single-pass encode keeps a count of bounded waits that gave up in
@@ -550,6 +550,14 @@ def test_single_pass_tile_geometry(G_, gr, cols, bits):
     of 768 units, 511 in flight), for every plane width, with y."""
     G.say(f"single-pass tile geometry, {G_} groups x ({gr},{cols}), bits {bits}")
     _encode_schedule_check(G_, gr, cols, bits, 17 + bits, single=True)
+
+
+def test_single_group_uses_two_passes():
+    """A call of one group (one chunk, or one KV tensor) goes through the
+    two-pass schedule, which is faster there; the results are the oracle's."""
+    G.say("one group: two-pass schedule")
+    _encode_schedule_check(1, 512, 2048, 1, 43, single=False)
+    _encode_schedule_check(1, 4096, 256, 4, 44, single=False)
 
 
 def test_single_pass_largest_group_and_the_next():
