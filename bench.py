@@ -55,9 +55,10 @@ BPE = {
     "guided_fake_quant": 2 + 1 / 8 + 1 / 16 + 2,           # x_t, bits, scales in; y_t out
     "guided_fake_quant_stats+mismatch": 2 + 2 + 1 / 8 + 1 / 16 + 2,
 }
-# rocprofv3 kernel names of each call's main kernel.
+# rocprofv3 kernel names of each call's main kernel (the counter summary of
+# the dominant one is profiles/<name>_stream_nvfp4_pmc.txt).
 KERNEL_NAME = {
-    "encode_guidance": "quantize_kernel",
+    "encode_guidance": "onepass_encode_kernel",
     "guided_fake_quant_stats": "guided_kernel",
     "guided_fake_quant": "guided_kernel",
     "guided_fake_quant_stats+mismatch": "guided_kernel",
