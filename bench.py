@@ -184,19 +184,23 @@ def rtn_decode_phases(lib, w, stream, qwork, codes, gsq, dwork):
     (name, bytes/elem, phase)."""
     qb = qwork.numel() * qwork.element_size()
     db = dwork.numel() * dwork.element_size()
-    q, g0, dec, st = [], [], [], []
+    q, g0, dec, st, eg = [], [], [], [], []
     for i in range(w.layers):
         p = lambda t: t[i].data_ptr()  # noqa: E731
         q.append((NV, w.rows, HIDDEN, CHUNK, p(w.xt), None, p(codes), p(w.scales), p(gsq), p(w.yt),
                   qwork.data_ptr(), qb, stream))
         g0.append((NV, 0, w.rows, HIDDEN, CHUNK, p(w.xt), None, p(w.scales), p(w.gscale), p(w.yt), None, stream))
         dec.append((NV, 1, w.rows, HIDDEN, CHUNK, p(w.xt), p(w.guide), p(w.scales), p(w.gscale), p(codes), stream))
+        # the rollout encode with each chunk's S supplied (one read, no combine)
+        eg.append((NV, 1, w.rows, HIDDEN, CHUNK, p(w.xr), p(w.gscale), p(w.guide), p(w.scales), None, None,
+                   None, 0, stream))
         yr = w.xt[(i + 1) % w.layers].data_ptr()     # a fourth array of the layer's size
         st.append((w.n, p(w.xt), p(w.xr), p(w.yt), yr, p(w.acc), 0, dwork.data_ptr(), db, stream))
     return [("quantize_rtn", 2 + 1 / 2 + 1 / 16 + 2, ("quantize_rtn", lib.quantize_rtn, q)),
             ("guided_fake_quant_bits0", 2 + 1 / 16 + 2, ("guided_fake_quant", lib.guided_fake_quant, g0)),
             ("decode_guidance", 2 + 1 / 8 + 1 / 16 + 1 / 2, ("decode_guidance", lib.decode_guidance, dec)),
-            ("discrepancy_stats", 8, ("discrepancy_stats", lib.discrepancy_stats, st))]
+            ("discrepancy_stats", 8, ("discrepancy_stats", lib.discrepancy_stats, st)),
+            ("encode_guidance_S_supplied", 2 + 1 / 8 + 1 / 16, ("encode_guidance", lib.encode_guidance, eg))]
 
 
 def record_path(torch, w, step, per_layer, stream, dev, layers):

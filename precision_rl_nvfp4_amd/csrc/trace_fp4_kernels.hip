@@ -580,8 +580,18 @@ __device__ __forceinline__ void write_unit(uint32_t K, uint32_t sb, float d, flo
 // group from gin; SSRC 2: from the group's own amax, reduced inside the
 // workgroup, so the input is read once; {S, A} go to gout. The block factors
 // are computed per block instead of from a table.
+// Threads of a quantize_kernel workgroup; its tile is kTileUnits units either
+// way. With S supplied per group (and for MXFP4) the kernel runs 512 threads
+// of 4 units (33 VGPRs, 8 waves per SIMD: 102.9 against 107.3 us for a
+// streamed layer); the modes that reduce inside the workgroup (packed
+// groups, the amax partials and tile maxima of the two-pass and row-offset
+// schedules) keep 256 threads of 8 units (512 were slower for packed groups:
+// 131 against 116 us), and their reductions assume 4 waves.
+constexpr int quant_threads(int ssrc, bool pack) { return (ssrc == 0 && !pack) ? 2 * kThreads : kThreads; }
+
 template <int FMT, int PLANE, bool WY, int SSRC, bool PACK>
-__global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
+__global__ __launch_bounds__(quant_threads(SSRC, PACK)) void quantize_kernel(QuantArgs a) {
+  constexpr int QT = quant_threads(SSRC, PACK), QU = (int)(kTileUnits / QT);
   __shared__ float2 lut[PACK ? 1 : 128];
   __shared__ uint32_t red[kThreads / 64];
   __shared__ float gs[PACK ? kPackGroups : 1];                  // S of the tile's groups
@@ -614,10 +624,10 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
     lim = a.map.upg;
   }
   // Issue the tile's loads first; the scale and its factor table follow.
-  uint4 v[kUPT];
+  uint4 v[QU];
 #pragma unroll
-  for (int j = 0; j < kUPT; ++j) {
-    const int64_t u = tbase + j * kThreads + threadIdx.x;
+  for (int j = 0; j < QU; ++j) {
+    const int64_t u = tbase + j * QT + threadIdx.x;
     v[j] = u < lim ? load_stream(a.x + gbase + u) : make_uint4(0u, 0u, 0u, 0u);
   }
   float S = 1.0f;
@@ -633,14 +643,14 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
       const int lgs = lg < 6 ? lg : 6;
       const int w = 1 << lgs;
 #pragma unroll
-      for (int j = 0; j < kUPT; ++j) {
+      for (int j = 0; j < QU; ++j) {
         uint32_t bm = unit_amax_bits(v[j]);          // units past the end read as zero
         for (int off = w >> 1; off > 0; off >>= 1) bm = max(bm, (uint32_t)__shfl_xor((int)bm, off));
-        if ((threadIdx.x & (w - 1)) == 0) ga[(j * kThreads + threadIdx.x) >> lgs] = bm;
+        if ((threadIdx.x & (w - 1)) == 0) ga[(j * QT + threadIdx.x) >> lgs] = bm;
       }
       __syncthreads();
       const int spg = 1 << (lg - lgs);               // slots per group
-      for (int i = threadIdx.x; i < gpt; i += kThreads) {
+      for (int i = threadIdx.x; i < gpt; i += QT) {
         uint32_t gm = 0u;
         for (int k = 0; k < spg; ++k) gm = max(gm, ga[i * spg + k]);
         const float A = __uint_as_float(gm << 16);
@@ -653,7 +663,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
         }
       }
     } else {
-      for (int i = threadIdx.x; i < gpt; i += kThreads) {
+      for (int i = threadIdx.x; i < gpt; i += QT) {
         const int64_t gg = g0t + i;
         gs[i] = gg < a.map.groups ? a.gin[2 * gg] : 1.0f;
       }
@@ -663,7 +673,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
     if constexpr (SSRC == 3) {
       uint32_t m = 0;
       const int32_t t0 = a.map.tstart[g], t1 = a.map.tstart[g + 1];
-      for (int i = t0 + (int)threadIdx.x; i < t1; i += kThreads) m = max(m, a.map.tpart[i]);
+      for (int i = t0 + (int)threadIdx.x; i < t1; i += QT) m = max(m, a.map.tpart[i]);
       m = wave_max_u32(m);
       if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
       __syncthreads();
@@ -676,7 +686,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
       }
     } else if constexpr (SSRC == 1) {
       uint32_t m = 0;
-      for (int i = threadIdx.x; i < a.nparts; i += kThreads) m = max(m, a.part[g * kPartMax + i]);
+      for (int i = threadIdx.x; i < a.nparts; i += QT) m = max(m, a.part[g * kPartMax + i]);
       m = wave_max_u32(m);
       if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
       __syncthreads();
@@ -694,15 +704,15 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
     __syncthreads();
   }
 #pragma unroll
-  for (int j = 0; j < kUPT; ++j) {
-    const int64_t u = tbase + j * kThreads + threadIdx.x;
+  for (int j = 0; j < QU; ++j) {
+    const int64_t u = tbase + j * QT + threadIdx.x;
     uint32_t bm = unit_amax_bits(v[j]);
     bm = max(bm, xor1(bm));
     if constexpr (FMT == 1) bm = max(bm, xor2(bm));
     float r, d = 0.0f, dsc = 0.0f;
     uint32_t sb;
     if constexpr (PACK) {
-      const float Sg = gs[(j * kThreads + threadIdx.x) >> a.map.lg];
+      const float Sg = gs[(j * QT + threadIdx.x) >> a.map.lg];
       sb = nv_scale_byte(bm, Sg);
       nv_factors_pair(sb, Sg, r, d);
     } else if constexpr (FMT == 0) {
@@ -1490,7 +1500,8 @@ int amax_parts(int64_t upg) {
 
 template <int FMT, int PLANE, bool WY, int SSRC, bool PACK>
 hipError_t quant_go(const QuantArgs& a, int64_t blocks, hipStream_t s) {
-  return launch(quantize_kernel<FMT, PLANE, WY, SSRC, PACK>, dim3((unsigned)blocks), dim3(kThreads), s, a);
+  return launch(quantize_kernel<FMT, PLANE, WY, SSRC, PACK>, dim3((unsigned)blocks),
+                dim3(quant_threads(SSRC, PACK)), s, a);
 }
 
 // `blocks`: the launch's workgroups (quantize tiles, then side amax work).
