@@ -506,9 +506,10 @@ __global__ __launch_bounds__(64) void fill_gscale_kernel(float* g, int64_t group
 
 // Partial group amax: workgroup w of group g writes the max bf16 magnitude
 // (as binary32 bits) of its share of the group to part[g][w]. The share is a
-// contiguous range of whole 8-unit-per-thread tiles, read a tile (8 loads
-// per thread, 32 KB per workgroup) at a time. `blk` is the workgroup's index
-// within the amax pass.
+// contiguous range of whole tiles of kThreads * 8 units, read a tile (32 KB
+// per workgroup of NT threads) at a time. `blk` is the workgroup's index
+// within the amax pass; `red` holds NT / 64 words.
+template <int NT>
 __device__ __forceinline__ void amax_body(const AmaxArgs& a, int64_t blk, uint32_t* red) {
   const int64_t gi = blk / a.nparts;
   const int w = (int)(blk - gi * a.nparts);
@@ -521,25 +522,30 @@ __device__ __forceinline__ void amax_body(const AmaxArgs& a, int64_t blk, uint32
   const int64_t t1 = min(t0 + per, tiles);
   uint32_t m = 0;
   for (int64_t t = t0; t < t1; ++t) {
+    constexpr int U = (int)(kTile / NT);
     const int64_t base = t * kTile + threadIdx.x;
-    uint4 v[8];
+    uint4 v[U];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int64_t u = base + k * kThreads;
+    for (int k = 0; k < U; ++k) {
+      const int64_t u = base + k * NT;
       v[k] = u < a.upg ? load_stream(x + u) : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) m = max(m, unit_amax_bits(v[k]));
+    for (int k = 0; k < U; ++k) m = max(m, unit_amax_bits(v[k]));
   }
   m = wave_max_u32(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
-  if (threadIdx.x == 0) a.part[g * kPartMax + w] = max(max(red[0], red[1]), max(red[2], red[3])) << 16;
+  if (threadIdx.x == 0) {
+    uint32_t r = red[0];
+    for (int i = 1; i < NT / 64; ++i) r = max(r, red[i]);
+    a.part[g * kPartMax + w] = r << 16;
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void amax_kernel(AmaxArgs a) {
   __shared__ uint32_t red[kThreads / 64];
-  amax_body(a, blockIdx.x, red);
+  amax_body<kThreads>(a, blockIdx.x, red);
 }
 
 // Outputs of one quantized unit (global unit index gu): its guidance-plane
@@ -581,24 +587,23 @@ __device__ __forceinline__ void write_unit(uint32_t K, uint32_t sb, float d, flo
 // workgroup, so the input is read once; {S, A} go to gout. The block factors
 // are computed per block instead of from a table.
 // Threads of a quantize_kernel workgroup; its tile is kTileUnits units either
-// way. With S supplied per group (and for MXFP4) the kernel runs 512 threads
-// of 4 units (33 VGPRs, 8 waves per SIMD: 102.9 against 107.3 us for a
-// streamed layer); the modes that reduce inside the workgroup (packed
-// groups, the amax partials and tile maxima of the two-pass and row-offset
-// schedules) keep 256 threads of 8 units (512 were slower for packed groups:
-// 131 against 116 us), and their reductions assume 4 waves.
-constexpr int quant_threads(int ssrc, bool pack) { return (ssrc == 0 && !pack) ? 2 * kThreads : kThreads; }
+// way. One group per tile (S supplied, from the amax partials or from the
+// tile maxima of row-offset groups; MXFP4) runs 512 threads of 4 units (8
+// waves per SIMD: 102.9 against 107.3 us for a streamed layer with S
+// supplied); packed small groups keep 256 threads of 8 units (512 were
+// slower there: 131 against 116 us).
+constexpr int quant_threads(int ssrc, bool pack) { return (ssrc != 2 && !pack) ? 2 * kThreads : kThreads; }
 
 template <int FMT, int PLANE, bool WY, int SSRC, bool PACK>
 __global__ __launch_bounds__(quant_threads(SSRC, PACK)) void quantize_kernel(QuantArgs a) {
   constexpr int QT = quant_threads(SSRC, PACK), QU = (int)(kTileUnits / QT);
   __shared__ float2 lut[PACK ? 1 : 128];
-  __shared__ uint32_t red[kThreads / 64];
+  __shared__ uint32_t red[QT / 64];
   __shared__ float gs[PACK ? kPackGroups : 1];                  // S of the tile's groups
   __shared__ uint32_t ga[PACK && SSRC == 2 ? kPackGroups : 1];  // segment maxima (bf16 bits)
   if constexpr (SSRC == 1) {
     if ((int64_t)blockIdx.x >= a.qblocks) {
-      amax_body(a.side, (int64_t)blockIdx.x - a.qblocks, red);
+      amax_body<QT>(a.side, (int64_t)blockIdx.x - a.qblocks, red);
       return;
     }
   }
@@ -677,7 +682,8 @@ __global__ __launch_bounds__(quant_threads(SSRC, PACK)) void quantize_kernel(Qua
       m = wave_max_u32(m);
       if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
       __syncthreads();
-      m = max(max(red[0], red[1]), max(red[2], red[3]));
+      m = red[0];
+      for (int i = 1; i < QT / 64; ++i) m = max(m, red[i]);
       const float A = __uint_as_float(m << 16);
       S = global_scale(A);
       if (tk == 0 && threadIdx.x == 0) {
@@ -690,7 +696,8 @@ __global__ __launch_bounds__(quant_threads(SSRC, PACK)) void quantize_kernel(Qua
       m = wave_max_u32(m);
       if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
       __syncthreads();
-      m = max(max(red[0], red[1]), max(red[2], red[3]));
+      m = red[0];
+      for (int i = 1; i < QT / 64; ++i) m = max(m, red[i]);
       const float A = __uint_as_float(m);
       S = global_scale(A);
       if (tbase == 0 && threadIdx.x == 0) {
