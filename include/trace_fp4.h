@@ -115,11 +115,11 @@ const char* trace_status_str(int status);
 
 /* How NVFP4 calls that derive S from the amax schedule their work.
  * groups_per_batch = 0 (the default): a call of two or more groups of at
- * most (2 x CUs - 1) x 35840 elements (18.3M on a 256-CU MI355X, e.g. 8192 x
+ * most (2 x CUs - 1) x 33792 elements (17.3M on a 256-CU MI355X, e.g. 8192 x
  * 2048 chunks) is encoded in ONE pass over the input by a launch of at most
  * as many workgroups as the device holds at once, which keep their tiles on
  * chip while each group's amax is combined (it needs 2 resident workgroups
- * of 512 threads per CU; otherwise, for larger groups, and for a call of a
+ * of 768 threads per CU; otherwise, for larger groups, and for a call of a
  * single group, which is faster in two launches, the two-pass schedule
  * below is used).
  * n > 0 forces two passes (amax, then quantize) with n groups per batch: each

@@ -748,14 +748,15 @@ __global__ __launch_bounds__(quant_threads(SSRC, PACK)) void quantize_kernel(Qua
 // turn, one tile per workgroup per group, kept on chip; one more workgroup
 // combines.
 //
-// A tile workgroup is seven data waves and one control wave (eight waves, so
-// every SIMD holds two). The data waves load, hold and quantize the tiles;
+// A tile workgroup is eleven data waves and one control wave (twelve waves:
+// with two workgroups per CU every SIMD holds six, at most 85 VGPRs each).
+// The data waves load, hold and quantize the tiles;
 // the control wave does every wait on other workgroups. This split matters:
 // a wait on memory is a wait on the wave's whole vector-memory counter,
 // which also covers the tile loads in flight, so a data wave that polled
 // would stall until its next tile had arrived.
 //   * Data waves: a tile's max goes to its slot, tagged (bit 31), by one
-//     store from the last of the seven waves to reduce it (an LDS counter),
+//     store from the last of the eleven waves to reduce it (an LDS counter),
 //     as soon as the tile has arrived; no barrier is involved.
 //   * Combining workgroup (the last one): its first wave takes the groups in
 //     order, waits for each group's T slots, derives S and A, writes {S, A}
@@ -800,11 +801,11 @@ struct OnePassArgs {
 
 constexpr int kSpinMax = 1 << 22;      // default bound of every wait, in polls (~0.25 s)
 constexpr int kSCopies = 16;            // copies of each published S, one per 256-byte line
-constexpr int kOPDataWaves = 7;                      // data waves per workgroup
+constexpr int kOPDataWaves = 11;                     // data waves per workgroup
 constexpr int kOPData = kOPDataWaves * 64;           // data threads
 constexpr int kOnePassThreads = kOPData + 64;        // + the control wave: 8 waves, 2 per SIMD
-constexpr int kOPUnits = 10;                         // units per data thread and tile
-constexpr int kOPTile = kOPData * kOPUnits;          // most units per tile (4480, a multiple of 64)
+constexpr int kOPUnits = 6;                          // units per data thread and tile
+constexpr int kOPTile = kOPData * kOPUnits;          // most units per tile (4224, a multiple of 64)
 constexpr int kSlotsPerLane = kPartMax / 64;
 constexpr int kRawBufferWord3 = 0x00020000;     // buffer descriptor word 3: untyped 32-bit data, no swizzle
 constexpr int kBufferNT = 2;                    // buffer access cache policy: nontemporal
@@ -817,7 +818,7 @@ __device__ __forceinline__ void store_agent(uint32_t* p, uint32_t v) {
 }
 
 template <int PLANE, bool WY>
-__global__ __launch_bounds__(kOnePassThreads, 4) void onepass_encode_kernel(OnePassArgs a) {
+__global__ __launch_bounds__(kOnePassThreads, 6) void onepass_encode_kernel(OnePassArgs a) {
   __shared__ float2 lut[2][128];
   __shared__ float sS[2];
   __shared__ uint32_t wmax[2], wcnt[2];

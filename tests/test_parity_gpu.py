@@ -562,11 +562,11 @@ def test_single_group_uses_two_passes():
 
 def test_single_pass_largest_group_and_the_next():
     """The largest group the single-pass encode holds on chip at once
-    ((2 x CUs - 1) tiles of 4480 units) is encoded in one pass; a group a
+    ((2 x CUs - 1) tiles of 4224 units) is encoded in one pass; a group a
     few rows larger falls back to two passes. Both match the oracle."""
     cus = torch.cuda.get_device_properties(G.DEV).multi_processor_count
     cols = 2048
-    rows_max = (2 * cus - 1) * 4480 * 8 // cols
+    rows_max = (2 * cus - 1) * 4224 * 8 // cols
     G.say(f"single-pass boundary: groups of {rows_max} and {rows_max + 3} rows x {cols} ({cus} CUs)")
     _encode_schedule_check(2, rows_max, cols, 1, 41, single=True)
     _encode_schedule_check(2, rows_max + 3, cols, 1, 42, single=False)
