@@ -806,6 +806,12 @@ constexpr int kOPData = kOPDataWaves * 64;           // data threads
 constexpr int kOnePassThreads = kOPData + 64;        // + the control wave: 8 waves, 2 per SIMD
 constexpr int kOPUnits = 6;                          // units per data thread and tile
 constexpr int kOPTile = kOPData * kOPUnits;          // most units per tile (4224, a multiple of 64)
+// Every workgroup must become resident at once. Its waves are spread over a
+// CU's 4 SIMDs, so a wave count that is not a multiple of 4 fills them
+// unevenly, and a second workgroup per CU may not fit even where the
+// occupancy query says it does (14 waves per workgroup: the launch stalls on
+// its bounded waits).
+static_assert((kOPDataWaves + 1) % 4 == 0, "single-pass workgroups must fill the 4 SIMDs of a CU evenly");
 constexpr int kSlotsPerLane = kPartMax / 64;
 constexpr int kRawBufferWord3 = 0x00020000;     // buffer descriptor word 3: untyped 32-bit data, no swizzle
 constexpr int kBufferNT = 2;                    // buffer access cache policy: nontemporal
