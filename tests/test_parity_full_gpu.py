@@ -267,6 +267,52 @@ def test_kv_full_size(which):
         assert a[2] == ref[2] and G.rel_close(a[0], ref[0]) and G.rel_close(a[1], ref[1])
 
 
+def test_kv_cache_one_call_over_all_layers():
+    """The FP4 KV cache of 20 layers, K and V, as the benchmark times it: one
+    encode (full codes, bits=4) over the 40 tensors of [65536, 256] with one
+    global scale each, and one guided call. Every tensor's {S, A} against the
+    oracle's scale of the exact amax; the encode and the guided outputs of
+    every tensor bit for bit against calls of their own; sampled rows of the
+    first and last tensor against the oracle."""
+    G.say("full size: KV cache, 40 x [65536, 256] in one call")
+    n_t, rows_t, cols = 40, 65536, 256
+    kt = torch.empty((n_t, rows_t, cols), dtype=torch.bfloat16, device=G.DEV)
+    kr = torch.empty_like(kt)
+    for li in range(20):
+        for which in (0, 1):
+            a, b = syn.kv_pair(20 + li, which, device=G.DEV)
+            kt[2 * li + which].copy_(a)
+            kr[2 * li + which].copy_(b)
+            del a, b
+    ft, fr = kt.view(-1, cols), kr.view(-1, cols)
+    work = tq.quant_workspace(NV, ft.shape[0], cols, rows_t, device=G.DEV)
+    g = tq.encode_guidance(fr, NV, 4, group_rows=rows_t, work=work)
+    y, _ = tq.guided_fake_quant(ft, g, bits=4)
+    torch.cuda.synchronize()
+    assert work.view(torch.int32)[n_t * 2048].item() == 0
+    amax = (fr.view(torch.int16) & 0x7FFF).view(n_t, -1).amax(dim=1).cpu().numpy().astype(np.uint16)
+    A = ofp4.bf16_to_f32(amax)
+    S = np.array([ofp4.nvfp4_global_scale(v) for v in A], np.float32)
+    gs = G.f32(g.gscale).reshape(n_t, 2)
+    G.assert_same(gs[:, 1], A, "KV A")
+    G.assert_same(gs[:, 0], S, "KV S")
+    guide = g.guide.view(n_t, rows_t, -1)
+    scales = g.scales.view(n_t, rows_t, -1)
+    yv = y.view(n_t, rows_t, cols)
+    for i in range(n_t):
+        gi = tq.encode_guidance(kr[i], NV, 4)
+        yi, _ = tq.guided_fake_quant(kt[i], gi, bits=4)
+        assert torch.equal(gi.guide, guide[i]), i
+        assert torch.equal(gi.scales, scales[i]), i
+        assert torch.equal(gi.gscale.view(-1), g.gscale.view(n_t, 2)[i]), i
+        assert torch.equal(yi.view(torch.int16), yv[i].view(torch.int16)), i
+    for i in (0, n_t - 1):
+        xt_b, xr_b = _bits(kt[i]), _bits(kr[i])
+        gi = tq.encode_guidance(kr[i], NV, 4)
+        for r0, r1 in _samples(rows_t, span=256):
+            _check_rows(NV, 4, xt_b, xr_b, cols, r0, r1, S[i], gi, y_g=yv[i])
+
+
 def test_mxfp4_full_size_with_ties():
     """MXFP4 W4A4: [65536, 2048] pairs with 0.1% of the elements exactly on
     E2M1 rounding midpoints."""
