@@ -115,6 +115,28 @@ def test_stream_layer_bench_configuration():
             _check_rows(NV, 4, xt_b, xr_b, syn.HIDDEN, rr0, rr1, S_oracle[c], g4)
             _check_rows(NV, 1, xt_b, xr_b, syn.HIDDEN, rr0, rr1, S_oracle[c], g, y_g=y_rtn,
                         codes_g=codes_rtn, gbits=0)
+    # vanilla fake quantization of X_t with its own chunk scales (codes, y) and
+    # the 1-bit Reconstruct alone, as the benchmark times them per layer
+    q = tq.quantize_rtn(xt, NV, group_rows=CH, with_y=True)
+    ref = tq.decode_guidance(xt, g)
+    torch.cuda.synchronize()
+    qs = G.f32(q.gscale).reshape(chunks, 2)
+    cols = syn.HIDDEN
+    for c in (0, 16):
+        es = slice(c * n_chunk, (c + 1) * n_chunk)
+        St = ofp4.nvfp4_global_scale(ofp4.tensor_amax(xt_b[es]))
+        assert qs[c, 0] == St, (c, qs[c])
+        for r0, r1 in _samples(CH, span=32):
+            rr0, rr1 = c * CH + r0, c * CH + r1
+            e2 = slice(rr0 * cols, rr1 * cols)
+            oq = ofp4.quantize_rtn(NV, xt_b[e2], St)
+            G.assert_same(G.u8(q.codes).reshape(-1)[rr0 * cols // 2:rr1 * cols // 2], oq["codes"],
+                          f"rtn codes chunk {c} rows {r0}:{r1}")
+            G.assert_same(_bits(q.y)[e2], oq["y"], f"rtn y chunk {c} rows {r0}:{r1}")
+            o_enc = ofp4.encode_guidance(NV, 1, xr_b[e2], S_oracle[c])
+            od = ofp4.decode_guidance(NV, xt_b[e2], o_enc["guide"], o_enc["scales"], S_oracle[c], bits=1)
+            G.assert_same(G.u8(ref).reshape(-1)[rr0 * cols // 2:rr1 * cols // 2], od,
+                          f"decode chunk {c} rows {r0}:{r1}")
     a = acc.cpu().numpy()
     assert a[2] == xt.numel()
     assert G.rel_close(a[0], sb_total), (a[0], sb_total)
