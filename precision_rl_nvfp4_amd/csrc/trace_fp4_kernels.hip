@@ -367,9 +367,18 @@ __device__ __forceinline__ float mx_dscale(uint32_t sb) { return __uint_as_float
 
 // ------------------------------------------------------------ reductions
 
+// Max over the wave's 64 lanes, returned to every lane; all lanes must be
+// active. DPP within each row of 16 lanes (quad swaps, then rotations by 4
+// and 8), then the four row maxima read as scalars: 4 DPP steps and 4 lane
+// reads instead of 6 LDS permutes and their address arithmetic.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t m) {
-  for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-  return m;
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp((int)m, (int)m, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp((int)m, (int)m, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp((int)m, (int)m, 0x124, 0xF, 0xF, false));  // row_ror:4
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp((int)m, (int)m, 0x128, 0xF, 0xF, false));  // row_ror:8
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)m, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)m, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)m, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)m, 48);
+  return max(max(a, b), max(c, d));
 }
 __device__ __forceinline__ double wave_sum(double v) {
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
@@ -650,7 +659,11 @@ __global__ __launch_bounds__(quant_threads(SSRC, PACK)) void quantize_kernel(Qua
 #pragma unroll
       for (int j = 0; j < QU; ++j) {
         uint32_t bm = unit_amax_bits(v[j]);          // units past the end read as zero
-        for (int off = w >> 1; off > 0; off >>= 1) bm = max(bm, (uint32_t)__shfl_xor((int)bm, off));
+        if (w == 64) {
+          bm = wave_max_u32(bm);
+        } else {
+          for (int off = w >> 1; off > 0; off >>= 1) bm = max(bm, (uint32_t)__shfl_xor((int)bm, off));
+        }
         if ((threadIdx.x & (w - 1)) == 0) ga[(j * QT + threadIdx.x) >> lgs] = bm;
       }
       __syncthreads();
