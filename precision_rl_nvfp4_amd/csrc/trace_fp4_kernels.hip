@@ -1005,6 +1005,9 @@ __global__ __launch_bounds__(kOnePassThreads, 6) void onepass_encode_kernel(OneP
     const int tl = live ? tlen : 0;
     const __amdgpu_buffer_rsrc_t rp =
         __builtin_amdgcn_make_buffer_rsrc(a.plane + gb * PB, (short)0, tl * PB, kRawBufferWord3);
+    // 3-bit planes are stored a dword at a time where the tile's plane bytes
+    // start on a dword; su and the wave offsets are multiples of 64 units.
+    const bool al3 = PLANE == 3 && ((reinterpret_cast<uintptr_t>(a.plane + gb * PB) & 3u) == 0);
     const __amdgpu_buffer_rsrc_t rsc =
         __builtin_amdgcn_make_buffer_rsrc(a.scales + (gb >> 1), (short)0, tl >> 1, kRawBufferWord3);
     const __amdgpu_buffer_rsrc_t ryy =
@@ -1037,9 +1040,23 @@ __global__ __launch_bounds__(kOnePassThreads, 6) void onepass_encode_kernel(OneP
           __builtin_amdgcn_raw_buffer_store_b16((uint16_t)gather_2bits(K), rp, lane_u * 2, su * 2, kBufferNT);
         } else {
           const uint32_t w = gather_3bits(K);
-          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)w, rp, lane_u * 3, su * 3, kBufferNT);
-          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(w >> 8), rp, lane_u * 3 + 1, su * 3, kBufferNT);
-          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(w >> 16), rp, lane_u * 3 + 2, su * 3, kBufferNT);
+          const int wu = lane_u & ~63;   // the wave's first unit, less su
+          if (al3 && su + wu + 64 <= tl) {
+            // The wave's 64 units are 192 contiguous, dword-aligned plane
+            // bytes: lane l < 48 stores dword l, which starts at bit 32 l,
+            // i.e. bit off = 32 l - 24 c of unit c = 4 l / 3, and takes the
+            // rest of its 32 bits from unit c + 1.
+            const int l = lane_u & 63;
+            const int c = (4 * l) / 3;
+            const int off = 32 * l - 24 * c;
+            const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * c, (int)w);
+            const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (c + 1), (int)w);
+            if (l < 48) __builtin_amdgcn_raw_buffer_store_b32((lo >> off) | (hi << (24 - off)), rp, wu * 3 + 4 * l, su * 3, kBufferNT);
+          } else {
+            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)w, rp, lane_u * 3, su * 3, kBufferNT);
+            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(w >> 8), rp, lane_u * 3 + 1, su * 3, kBufferNT);
+            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(w >> 16), rp, lane_u * 3 + 2, su * 3, kBufferNT);
+          }
         }
         if ((lane_u & 1) == 0) __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sb, rsc, lane_u >> 1, su >> 1, kBufferNT);
         if constexpr (WY)
