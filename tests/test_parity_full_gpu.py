@@ -145,6 +145,36 @@ def test_stream_layer_bench_configuration():
     assert G.rel_close(a[1], ref[1]) and G.rel_close(a[0], ref[0])
 
 
+@pytest.mark.parametrize("bits", [2, 3])
+def test_stream_layer_wider_records(bits):
+    """The 2- and 3-bit records of one streamed layer as the benchmark times
+    them: 17 chunks of [8192, 2048] in one single-pass encode (chunk scales,
+    no rollout y), then guided_fake_quant with that record; sampled rows of
+    three chunks against the oracle."""
+    G.say(f"full size: streamed layer, bits {bits}, 17 x [8192, 2048]")
+    layer, chunks, CH = 3, 17, syn.STREAM_CHUNK
+    dev = G.DEV
+    sigma = syn.stream_sigma(layer, dev)
+    xt = torch.empty((chunks * CH, syn.HIDDEN), dtype=torch.bfloat16, device=dev)
+    xr = torch.empty_like(xt)
+    for c in range(chunks):
+        a, b = syn.stream_pair(layer, c, dev, sigma=sigma)
+        xt[c * CH:(c + 1) * CH].copy_(a)
+        xr[c * CH:(c + 1) * CH].copy_(b)
+    work = tq.quant_workspace(NV, chunks * CH, syn.HIDDEN, CH, device=dev)
+    g = tq.encode_guidance(xr, NV, bits, group_rows=CH, work=work)
+    y, codes = tq.guided_fake_quant(xt, g, with_codes=True)
+    torch.cuda.synchronize()
+    assert work.view(torch.int32)[chunks * 2048].item() == 0
+    xt_b, xr_b = _bits(xt), _bits(xr)
+    n_chunk = CH * syn.HIDDEN
+    for c in (0, 9, 16):
+        S = ofp4.nvfp4_global_scale(ofp4.tensor_amax(xr_b[c * n_chunk:(c + 1) * n_chunk]))
+        assert G.f32(g.gscale).reshape(chunks, 2)[c, 0] == S
+        for r0, r1 in _samples(CH):
+            _check_rows(NV, bits, xt_b, xr_b, syn.HIDDEN, c * CH + r0, c * CH + r1, S, g, y_g=y, codes_g=codes)
+
+
 def test_whole_stream_encode_one_call():
     """The rollout side of the whole streamed workload in one call, as the
     benchmark's step runs it: 20 layers x 17 chunks of [8192, 2048] (340
