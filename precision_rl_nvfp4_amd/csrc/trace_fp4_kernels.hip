@@ -562,7 +562,9 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(AmaxArgs a) {
 template <int FMT, int PLANE, bool WY>
 __device__ __forceinline__ void write_unit(uint32_t K, uint32_t sb, float d, float dsc, int64_t gu,
                                            uint8_t* plane, uint8_t* scales, uint4* y) {
-  if constexpr (PLANE == 4) {
+  if constexpr (PLANE == 0) {
+    // plane stored by the caller
+  } else if constexpr (PLANE == 4) {
     __builtin_nontemporal_store(K, reinterpret_cast<uint32_t*>(plane) + gu);
   } else if constexpr (PLANE == 1) {
     __builtin_nontemporal_store((uint8_t)gather_mbits(K), plane + gu);
@@ -750,6 +752,24 @@ __global__ __launch_bounds__(quant_threads(SSRC, PACK)) void quantize_kernel(Qua
 #pragma unroll
     for (int i = 0; i < 8; ++i) f[i] *= r;
     const uint32_t K = rtn_codes(f);
+    if constexpr (PLANE == 3) {
+      // A wave whose 64 units are all in range and whose 192 plane bytes
+      // start on a dword stores them as 48 dwords: dword l starts at bit
+      // off = 32 l - 24 c of unit c = 4 l / 3 and ends in unit c + 1.
+      const int64_t u0 = tbase + j * QT + (threadIdx.x & ~63);
+      uint8_t* wp = a.plane + 3 * (gbase + u0);
+      if (u0 + 64 <= lim && (reinterpret_cast<uintptr_t>(wp) & 3u) == 0) {
+        const uint32_t w = gather_3bits(K);
+        const int l = (int)threadIdx.x & 63;
+        const int c = (4 * l) / 3;
+        const int off = 32 * l - 24 * c;
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * c, (int)w);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (c + 1), (int)w);
+        if (l < 48) __builtin_nontemporal_store((lo >> off) | (hi << (24 - off)), reinterpret_cast<uint32_t*>(wp) + l);
+        write_unit<FMT, 0, WY>(K, sb, d, dsc, gbase + u, a.plane, a.scales, a.y);
+        continue;
+      }
+    }
     if (u < lim) write_unit<FMT, PLANE, WY>(K, sb, d, dsc, gbase + u, a.plane, a.scales, a.y);
   }
 }
