@@ -367,19 +367,30 @@ def test_kv_cache_one_call_over_all_layers():
 
 def test_mxfp4_full_size_with_ties():
     """MXFP4 W4A4: [65536, 2048] pairs with 0.1% of the elements exactly on
-    E2M1 rounding midpoints."""
+    E2M1 rounding midpoints; every record width (1 to 4 bits) with guided
+    rounding, Reconstruct alone for 1 to 3 bits and RTN under the rollout
+    scales, on sampled rows against the oracle."""
     G.say("full size: MXFP4 [65536, 2048] with midpoint ties")
     xt, xr = syn.mxfp4_pair(device=G.DEV)
     rows, cols = xt.shape
     xt_b, xr_b = _bits(xt), _bits(xr)
     q = tq.quantize_rtn(xt, MX)
     torch.cuda.synchronize()
-    for bits in (1, 4):
+    for bits in (1, 2, 3, 4):
         g = tq.encode_guidance(xr, MX, bits, with_y=True)
         y, codes = tq.guided_fake_quant(xt, g, with_codes=True)
+        ref = tq.decode_guidance(xt, g) if bits < 4 else None
+        y0, codes0 = tq.guided_fake_quant(xt, g, bits=0, with_codes=True) if bits == 1 else (None, None)
         torch.cuda.synchronize()
         for r0, r1 in _samples(rows):
-            _check_rows(MX, bits, xt_b, xr_b, cols, r0, r1, None, g, y_g=y, codes_g=codes, y_r=g.y)
+            o = _check_rows(MX, bits, xt_b, xr_b, cols, r0, r1, None, g, y_g=y, codes_g=codes, y_r=g.y)
+            es = slice(r0 * cols, r1 * cols)
+            if ref is not None:
+                od = ofp4.decode_guidance(MX, xt_b[es], o["guide"], o["scales"], None, bits=bits)
+                G.assert_same(G.u8(ref).reshape(-1)[r0 * cols // 2:r1 * cols // 2], od,
+                              f"mx decode bits {bits} rows {r0}:{r1}")
+            if y0 is not None:
+                _check_rows(MX, bits, xt_b, xr_b, cols, r0, r1, None, g, y_g=y0, codes_g=codes0, gbits=0)
     for r0, r1 in _samples(rows):
         es = slice(r0 * cols, r1 * cols)
         oq = ofp4.quantize_rtn(MX, xt_b[es])
