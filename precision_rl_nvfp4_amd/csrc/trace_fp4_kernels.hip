@@ -1210,6 +1210,71 @@ __global__ __launch_bounds__(kThreads) void tile_table_kernel(const int32_t* __r
   table[e] = make_int2((int)lo, (int)(e - ts[lo]));
 }
 
+// Up to kMergeGroups groups, offs_prep_kernel and tile_table_kernel in one
+// launch: every workgroup derives offs and tstart in LDS from the caller's
+// offsets with the same two scans, workgroup 0 also stores them (and {1, 0}
+// for empty groups), and each workgroup writes its kThreads table entries.
+constexpr int kMergeGroups = 4096;
+__global__ __launch_bounds__(kThreads) void offs_table_kernel(const int64_t* __restrict__ off_in, int64_t G,
+                                                             int64_t rows, int64_t upr, int64_t entries,
+                                                             int64_t* offs, int32_t* tstart, float* gout,
+                                                             int2* table) {
+  __shared__ int64_t so[kMergeGroups + 1];
+  __shared__ int32_t st[kMergeGroups + 1];
+  const bool first = blockIdx.x == 0;
+  const int64_t n = G + 1;
+  const int64_t per = (n + kThreads - 1) / kThreads;
+  const int64_t i0 = min((int64_t)threadIdx.x * per, n), i1 = min(i0 + per, n);
+  int64_t total;
+  // 1. running max of the clamped offsets
+  int64_t m = 0;
+  for (int64_t i = i0; i < i1; ++i) m = max(m, min(max(off_in[i], (int64_t)0), rows));
+  m = block_exclusive_scan<true>(m, &total);
+  for (int64_t i = i0; i < i1; ++i) {
+    m = max(m, min(max(off_in[i], (int64_t)0), rows));
+    so[i] = m;
+    if (first) offs[i] = m;
+  }
+  __syncthreads();
+  // 2. tiles per group, exclusive prefix sum
+  const int64_t gper = (G + kThreads - 1) / kThreads;
+  const int64_t g0 = min((int64_t)threadIdx.x * gper, G), g1 = min(g0 + gper, G);
+  int64_t t = 0;
+  for (int64_t g = g0; g < g1; ++g) t += ((so[g + 1] - so[g]) * upr + kTileUnits - 1) / kTileUnits;
+  t = block_exclusive_scan<false>(t, &total);
+  if (threadIdx.x == 0) {
+    st[G] = (int32_t)total;
+    if (first) tstart[G] = (int32_t)total;
+  }
+  for (int64_t g = g0; g < g1; ++g) {
+    st[g] = (int32_t)t;
+    const int64_t tg = ((so[g + 1] - so[g]) * upr + kTileUnits - 1) / kTileUnits;
+    if (first) {
+      tstart[g] = (int32_t)t;
+      if (tg == 0 && gout != nullptr) {
+        gout[2 * g] = 1.0f;
+        gout[2 * g + 1] = 0.0f;
+      }
+    }
+    t += tg;
+  }
+  __syncthreads();
+  // 3. this workgroup's table entries
+  const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (e >= entries) return;
+  if (e >= total) {
+    table[e] = make_int2(-1, 0);
+    return;
+  }
+  int64_t lo = 0, hi = G - 1;   // last g with tstart[g] <= e
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) >> 1;
+    if (st[mid] <= e) lo = mid;
+    else hi = mid - 1;
+  }
+  table[e] = make_int2((int)lo, (int)(e - st[lo]));
+}
+
 // Tile maxima of row-offset groups: tpart[e] for table entry e.
 __global__ __launch_bounds__(kThreads) void tile_amax_kernel(TileMap m, const uint4* __restrict__ x,
                                                             uint32_t* tpart) {
@@ -1977,6 +2042,11 @@ hipError_t offs_prepare(int64_t rows, int64_t cols, int64_t G, const int64_t* of
   m->upr = cols / kUnitElems;
   m->groups = G;
   m->units = rows * m->upr;
+  if (G <= kMergeGroups)
+    return launch(offs_table_kernel, dim3((unsigned)max((L.entries + kThreads - 1) / kThreads, (int64_t)1)),
+                  dim3(kThreads), stream, off_in, G, rows, m->upr, L.entries,
+                  reinterpret_cast<int64_t*>(w + L.b_offs), reinterpret_cast<int32_t*>(w + L.b_tstart), gout,
+                  reinterpret_cast<int2*>(w + L.b_table));
   hipError_t e = launch(offs_prep_kernel, dim3(1), dim3(kThreads), stream, off_in, G, rows, m->upr,
                         reinterpret_cast<int64_t*>(w + L.b_offs), reinterpret_cast<int32_t*>(w + L.b_tstart),
                         gout);

@@ -654,9 +654,10 @@ def test_row_offset_groups(sizes, cols):
 
 @pytest.mark.parametrize("n_groups", [3000, 9000])
 def test_row_offset_many_groups(n_groups):
-    """Thousands of small row-offset groups, a quarter of them empty: the
-    tile table comes from the prep kernel's LDS copy of the tile starts up to
-    8192 groups and from its own kernel beyond; both against the oracle."""
+    """Thousands of small row-offset groups, a quarter of them empty. Up to
+    4096 groups one kernel derives the offsets, tile starts and tile table
+    (3000); beyond that the prep kernel and the table kernel, whose search
+    runs in memory past 8192 groups (9000); both against the oracle."""
     sizes = np.random.default_rng(n_groups).integers(0, 4, n_groups).tolist()
     G.say(f"row-offset groups: {n_groups} groups of 0..3 rows x 16")
     _check_row_offset_groups(sizes, 16, (1,))
