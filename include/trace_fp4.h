@@ -88,7 +88,7 @@
 extern "C" {
 #endif
 
-#define TRACE_ABI_VERSION 7
+#define TRACE_ABI_VERSION 8
 
 /* Entries of the mismatch diagnostics of guided_fake_quant_stats. */
 #define TRACE_MISMATCH_COUNTS 32
@@ -128,34 +128,45 @@ const char* trace_status_str(int status);
  * two-pass batches are about 96 MiB of input. Results are bit-identical for
  * every setting; the knob exists to exercise and compare schedules.
  * Single-pass launches of a process run one after another on each device,
- * whatever their streams (each needs the whole device at once): the first
- * one on a second stream synchronizes the device once, later ones wait on
- * the previous one's event. A graph capture adds no ordering (a graph runs
- * in order); two graphs or processes that encode at the same time on one
- * device are not ordered, and then a workgroup that waits too long counts a
- * failure in the workspace (see trace_quant_workspace_bytes) instead of
- * hanging.
+ * whatever their streams (each needs the whole device at once), without any
+ * host synchronization: the first one on a second stream waits (on the
+ * device) for an event recorded at that moment on the stream of the previous
+ * single-pass launch, so that stream must not have been destroyed yet; later
+ * ones wait on the previous one's event. A graph capture adds no ordering (a
+ * graph runs in order). Two graphs or processes that encode at the same time
+ * on one device are not ordered: a workgroup whose wait on another then runs
+ * too long stops waiting and reads what it waited for from the input itself,
+ * so the results stay exact and only the time grows (see
+ * trace_set_wait_limit and trace_encode_wait_failures).
  * Process-wide. Returns the previous setting, or TRACE_EINVAL for a negative
  * value. */
 int64_t trace_set_encode_batch(int64_t groups_per_batch);
 
 /* Bound of every wait of the single-pass encode on other workgroups, in
  * polls (0 = the default, 4,194,304 polls, about 0.25 s). A wait that reaches
- * it gives up: the workgroup adds 1 to the workspace's failure count and
- * carries on (with S = NaN where the scale had not arrived), so the launch
- * always completes; that call's outputs are then undefined. The next call
- * starts from a cleared workspace. For callers and tests that need the
- * failure path to finish quickly (e.g. a limit of 1 makes the waits give up
- * at once). Process-wide. Returns the previous setting, or TRACE_EINVAL for
- * a value below 0 or above 2^31 - 1. */
+ * it gives up and takes what it waited for from the input instead: the
+ * combining wave reads the tiles whose maxima were not published, a
+ * workgroup whose group scale did not arrive reduces the group's amax
+ * itself. Both give the exact maximum, so every output is the same as
+ * without the give-up; the call only runs longer. Each give-up adds 1 to the
+ * device's count (trace_encode_wait_failures). For callers and tests that
+ * exercise that path (a limit of 1 makes nearly every wait give up at once).
+ * Process-wide. Returns the previous setting, or TRACE_EINVAL for a value
+ * below 0 or above 2^31 - 1. */
 int64_t trace_set_wait_limit(int64_t polls);
 
+/* *count = number of bounded waits of the single-pass encode that gave up on
+ * the current device since the library was loaded (0 when every launch had
+ * the whole device to itself). Reads device memory with a synchronous copy
+ * on the null stream: synchronize the streams of the encode calls first.
+ * EINVAL: count is NULL; EDEVICE: no gfx950 device is current; ELAUNCH: the
+ * copy failed. */
+int trace_encode_wait_failures(uint64_t* count);
+
 /* Workspace bytes quantize_rtn / encode_guidance need to derive the global
- * scales from the amax (NVFP4 with gscale_out): 4 * (2048 * G + 1) rounded up
- * to a multiple of 8 (per group 1024 partial maxima and 1024 words for the
- * published S, and one count of bounded waits of the single-pass encode that
- * gave up, which stays 0; it is the int32 at index 2048 * G), except 0 when
- * a group's element count is a power of two from 16 to 8192 and G > 1 (such
+ * scales from the amax (NVFP4 with gscale_out): 8192 * G (per group 1024
+ * partial maxima and 1024 words for the published S), except 0 when a
+ * group's element count is a power of two from 16 to 8192 and G > 1 (such
  * groups, e.g. one token's row for a per-token global scale, are reduced
  * and quantized in one pass); 0 for MXFP4. -1 for an invalid shape. */
 int64_t trace_quant_workspace_bytes(int fmt, int64_t rows, int64_t cols, int64_t group_rows);
@@ -370,9 +381,14 @@ int trace_ring_destroy(trace_ring* ring);
 /* Copies n device buffers srcs[i] of bytes[i] bytes, back to back, into the
  * next slot, after all work enqueued so far on after_stream (a hipStream_t,
  * NULL = null stream); the producer stream is not blocked. *slot receives the
- * slot index. ESHAPE: a negative size or more than slot_bytes in total;
- * EBUSY: the next slot is still in flight or not released (nothing is
- * enqueued); EDEVICE: called from another device. */
+ * slot index. The copies run later, on the ring's stream: every source
+ * buffer must stay allocated and unmodified until the slot's copies are done
+ * (trace_ring_wait returned, or trace_ring_query returned 1); freeing or
+ * reusing one earlier (e.g. through a caching allocator that hands it to the
+ * producer stream's next allocation) leaves undefined bytes in the slot.
+ * ESHAPE: a negative size or more than slot_bytes in total; EBUSY: the next
+ * slot is still in flight or not released (nothing is enqueued); EDEVICE:
+ * called from another device. */
 int trace_ring_push(trace_ring* ring, const void* const* srcs, const int64_t* bytes, int32_t n,
                     void* after_stream, int32_t* slot);
 

@@ -96,7 +96,3 @@ def floor_log2(a: np.ndarray) -> np.ndarray:
     _, e = np.frexp(np.asarray(a, dtype=np.float64))
     return e.astype(np.int64) - 1
 
-
-def e8m0_value(byte: np.ndarray) -> np.ndarray:
-    """E8M0 byte -> the power of two 2^(byte - 127), as float64."""
-    return np.exp2(np.asarray(byte, dtype=np.int64) - 127.0)

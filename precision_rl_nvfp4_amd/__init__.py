@@ -35,6 +35,7 @@ __all__ = ["NVFP4", "MXFP4", "TraceError", "Quantized", "Guidance", "quantize_rt
            "encode_guidance", "encode_guidance_grouped", "decode_guidance", "guided_fake_quant",
            "guided_fake_quant_stats",
            "discrepancy_stats", "stats_workspace", "quant_workspace", "guided_stats_workspace",
+           "encode_wait_failures",
            "grouped_workspace",
            "derived_metrics", "mismatch_summary", "fmt_id", "BLOCK", "MISMATCH_COUNTS"]
 
@@ -113,6 +114,17 @@ def _workspace(nbytes: int, device, work: Optional[torch.Tensor]) -> Optional[to
     if nbytes == 0:
         return None
     return torch.empty((nbytes + 7) // 8, dtype=torch.float64, device=device)
+
+
+def encode_wait_failures() -> int:
+    """Bounded waits of the single-pass encode that gave up on the current
+    device since the library was loaded. Each one was recovered exactly (the
+    missing maxima were read from the input), so a nonzero count means slower
+    calls, not wrong results. Synchronize the encode calls' streams first."""
+    import ctypes
+    v = ctypes.c_uint64()
+    _abi.call("trace_encode_wait_failures", ctypes.byref(v))
+    return int(v.value)
 
 
 def quant_workspace(fmt, rows: int, cols: int, group_rows: int = 0, device="cuda"):

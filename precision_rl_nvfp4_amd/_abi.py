@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtrace_fp
 
 OK, EINVAL, ESHAPE, EALIGN, EALIAS, EDEVICE, ELAUNCH, EBUSY = 0, -1, -2, -3, -4, -5, -6, -7
 NVFP4, MXFP4 = 0, 1
-ABI_VERSION = 7
+ABI_VERSION = 8
 MISMATCH_COUNTS = 32
 
 _i64 = ctypes.c_int64
@@ -26,6 +26,7 @@ SIGNATURES = {
     "trace_status_str": (ctypes.c_char_p, [_int]),
     "trace_set_encode_batch": (_i64, [_i64]),
     "trace_set_wait_limit": (_i64, [_i64]),
+    "trace_encode_wait_failures": (_int, [ctypes.POINTER(ctypes.c_uint64)]),
     "trace_quant_workspace_bytes": (_i64, [_int, _i64, _i64, _i64]),
     "trace_guided_stats_workspace_bytes": (_i64, [_int, _i64, _i64, _i64]),
     "trace_stats_workspace_bytes": (_i64, [_i64]),

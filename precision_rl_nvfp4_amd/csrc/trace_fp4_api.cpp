@@ -226,6 +226,13 @@ int64_t trace_set_wait_limit(int64_t polls) {
   return tfp4::set_wait_limit(polls);
 }
 
+int trace_encode_wait_failures(uint64_t* count) {
+  if (count == nullptr) return TRACE_EINVAL;
+  const int st = check_device();
+  if (st != TRACE_OK) return st;
+  return launched(tfp4::read_wait_failures(count));
+}
+
 int64_t trace_quant_workspace_bytes(int fmt, int64_t rows, int64_t cols, int64_t group_rows) {
   if (!valid_fmt(fmt)) return -1;
   CallShape cs;

@@ -30,8 +30,10 @@ struct Shape {
 };
 
 // Workspace of quantize_rtn / encode_guidance when S comes from the amax:
-// uint32 partial maxima [groups][kPartMax]; none for MXFP4 or for NVFP4
-// groups packed several to a tile (their amax is reduced inside the tile).
+// uint32 partial maxima (two passes) or tagged tile maxima (single pass)
+// [groups][kPartMax], then the single pass's published S words
+// [groups][1024]; none for MXFP4 or for NVFP4 groups packed several to a
+// tile (their amax is reduced inside the tile).
 int64_t quant_work_bytes(int fmt, const Shape& sh);
 // Workspace of guided_fake_quant_stats: float64 partial sums, 2 per workgroup,
 // 64 second-level pairs, and the per-workgroup mismatch counts.
@@ -87,6 +89,10 @@ int64_t set_encode_batch(int64_t groups);
 // Polls after which a bounded wait of the single-pass encode gives up; 0 =
 // the default. Returns the previous value.
 int64_t set_wait_limit(int64_t polls);
+
+// The current device's count of single-pass waits that gave up since the
+// library was loaded (a synchronous device-to-host copy).
+hipError_t read_wait_failures(uint64_t* out);
 
 // Deterministic float64 sums of discrepancy_stats into acc3.
 hipError_t launch_stats(int64_t n, const uint16_t* xt, const uint16_t* xr, const uint16_t* yt,

@@ -818,8 +818,11 @@ __global__ __launch_bounds__(quant_threads(SSRC, PACK)) void quantize_kernel(Qua
 // tile, so every load instruction is issued whatever the tile's length and
 // each wait covers exactly the older tile.
 // Slots and S words are zeroed by a fill kernel before the launch. Every wait
-// is bounded: past spin_max polls the workgroup records an error in *err and
-// carries on with S = NaN, so the grid always drains.
+// is bounded: past spin_max polls the waiting wave stops waiting, counts the
+// give-up in *fails and takes what it waited for from the input itself (the
+// maxima of the tiles whose slots were not tagged, or the whole group's
+// amax), so the grid always drains and the results stay exact; only the
+// time grows.
 struct OnePassArgs {
   const uint4* x;
   int upg;                   // units per group
@@ -829,7 +832,7 @@ struct OnePassArgs {
   int L;                     // units per tile (a multiple of 64, <= kOPTile); a group's last tile may be shorter
   uint32_t* slots;           // [groups][kPartMax] tagged tile maxima
   uint32_t* sword;           // [groups][kSCopies][64]: S bits at [.][c][0], 0 until published
-  uint32_t* err;             // bounded-wait failures
+  unsigned long long* fails; // bounded waits that gave up (device-wide count)
   int spin_max;              // polls before a wait gives up
   float* gout;
   uint8_t* plane;
@@ -861,6 +864,22 @@ __device__ __forceinline__ void store_agent(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Largest bf16 magnitude bits over units [u0, u1) of xg, read by one whole
+// wave (all 64 lanes active, u0 and u1 the same in every lane) and returned
+// to every lane: the slow path of a bounded wait that gave up. Four loads per
+// lane are in flight at a time.
+__device__ __forceinline__ uint32_t wave_units_amax(const uint4* xg, int64_t u0, int64_t u1) {
+  const int64_t lane = threadIdx.x & 63;
+  uint32_t m = 0;
+  int64_t u = u0 + lane;
+  for (; u + 3 * 64 < u1; u += 4 * 64) {
+    const uint4 a = xg[u], b = xg[u + 64], c = xg[u + 128], d = xg[u + 192];
+    m = max(max(m, unit_amax_bits(a)), max(unit_amax_bits(b), max(unit_amax_bits(c), unit_amax_bits(d))));
+  }
+  for (; u < u1; u += 64) m = max(m, unit_amax_bits(xg[u]));
+  return wave_max_u32(m);
+}
+
 template <int PLANE, bool WY>
 __global__ __launch_bounds__(kOnePassThreads, 6) void onepass_encode_kernel(OnePassArgs a) {
   __shared__ float2 lut[2][128];
@@ -884,15 +903,29 @@ __global__ __launch_bounds__(kOnePassThreads, 6) void onepass_encode_kernel(OneP
         v[k2] = i < a.T ? load_agent(&a.slots[gs + i]) : 0x80000000u;
       }
       int spins = 0;
+      uint32_t late = 0;   // maxima of the tiles read here after a wait gave up
       for (;;) {
         bool all = true;
 #pragma unroll
         for (int k2 = 0; k2 < kSlotsPerLane; ++k2) all = all && (v[k2] & 0x80000000u) != 0u;
         if (__all(all)) break;
         if (++spins > a.spin_max) {
-          if (lane == 0) atomicAdd(a.err, 1u);
+          // Some tiles' workgroups have not published (not resident beside
+          // this one): take those tiles' maxima from x. An untagged slot still
+          // holds 0 (cleared before the launch), so it adds nothing itself.
+          if (lane == 0) atomicAdd(a.fails, 1ull);
+          const uint4* xg = a.x + (int64_t)g * upg;
 #pragma unroll
-          for (int k2 = 0; k2 < kSlotsPerLane; ++k2) v[k2] |= 0x80000000u;
+          for (int k2 = 0; k2 < kSlotsPerLane; ++k2) {
+            uint64_t miss = __ballot(lane + 64 * k2 < a.T && (v[k2] & 0x80000000u) == 0u);
+            while (miss != 0u) {
+              const int i = __builtin_ctzll(miss) + 64 * k2;
+              miss &= miss - 1u;
+              const int64_t u0 = (int64_t)i * a.L;
+              late = max(late, wave_units_amax(xg, u0, min(u0 + a.L, (int64_t)upg)));
+            }
+            v[k2] |= 0x80000000u;
+          }
           break;
         }
         __builtin_amdgcn_s_sleep(1);
@@ -900,7 +933,7 @@ __global__ __launch_bounds__(kOnePassThreads, 6) void onepass_encode_kernel(OneP
         for (int k2 = 0; k2 < kSlotsPerLane; ++k2)
           if ((v[k2] & 0x80000000u) == 0u) v[k2] = load_agent(&a.slots[gs + lane + 64 * k2]);
       }
-      uint32_t gm = 0;
+      uint32_t gm = late;
 #pragma unroll
       for (int k2 = 0; k2 < kSlotsPerLane; ++k2) gm = max(gm, v[k2] & 0x7FFFFFFFu);
       gm = wave_max_u32(gm);
@@ -937,21 +970,28 @@ __global__ __launch_bounds__(kOnePassThreads, 6) void onepass_encode_kernel(OneP
         __syncthreads();
         continue;
       }
-      // S of group g, published by the combining workgroup
+      // S of group g, published by the combining workgroup (never 0)
       uint32_t v = 0u;
       if (lane == 0) {
         const uint32_t* w = &a.sword[((int64_t)g * kSCopies + (int)(blockIdx.x % kSCopies)) * 64];
         int spins = 0;
         while ((v = load_agent(w)) == 0u) {
           if (++spins > a.spin_max) {
-            atomicAdd(a.err, 1u);
-            v = 0x7FC00000u;
+            atomicAdd(a.fails, 1ull);
             break;
           }
           __builtin_amdgcn_s_sleep(1);
         }
       }
-      const float S = __uint_as_float((uint32_t)__shfl((int)v, 0));
+      v = (uint32_t)__shfl((int)v, 0);
+      if (v == 0u) {
+        // The wait gave up (the combining workgroup is not resident yet):
+        // this wave reduces the whole group's amax from x itself; the same
+        // exact maximum gives the same S the combining wave publishes.
+        const uint32_t gm = wave_units_amax(a.x + (int64_t)g * upg, 0, upg);
+        v = __float_as_uint(global_scale(__uint_as_float(gm << 16)));
+      }
+      const float S = __uint_as_float(v);
       // factor table of every E4M3 byte under S: {min(S / e, FLT_MAX), e / S}
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -1710,16 +1750,46 @@ int64_t onepass_capacity(const void* k, int dev) {
   return cap;
 }
 
+// Count of the single-pass encode's bounded waits that gave up, per device,
+// since the library was loaded (read by trace_encode_wait_failures).
+__device__ unsigned long long g_wait_fails;
+
+// Device addresses of the library's own device variables, looked up once per
+// device with that device current (in host code a __device__ variable's name
+// stands for a host-side shadow, not for its device memory).
+struct DeviceSyms {
+  bool ready = false;
+  unsigned long long* fails = nullptr;
+};
+std::mutex g_syms_mu;
+DeviceSyms g_syms[64];
+
+hipError_t device_syms(int dev, const DeviceSyms** out) {
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_syms_mu);
+  DeviceSyms& d = g_syms[dev];
+  if (!d.ready) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_wait_fails));
+    if (e != hipSuccess) return e;
+    d.fails = static_cast<unsigned long long*>(p);
+    d.ready = true;
+  }
+  *out = &d;
+  return hipSuccess;
+}
+
 // Single-pass launches of one process on one device run one after another,
 // whatever their streams: each needs the whole device resident at once, so
 // two running side by side could each hold part of it and wait on the other
-// (the bounded waits would end that, with wrong results). While every launch
-// comes on one stream, stream order suffices and nothing is added (an event
-// per launch costs ~7 us of the next kernel's start). The first launch on
-// another stream synchronizes the device once; from then on each launch
-// waits for the previous launch's event and records its own. Nothing is done
-// while the stream is being captured into a graph (a graph runs its nodes
-// in order).
+// (the bounded waits end that, through the slow exact path). While every
+// launch comes on one stream, stream order suffices and nothing is added (an
+// event per launch costs ~7 us of the next kernel's start). The first launch
+// on another stream is ordered after the previous launch by an event recorded
+// on that launch's stream at that moment; from then on each launch records
+// its own event and the next launch on another stream waits for it. No host
+// synchronization is involved. Nothing is done while the stream is being
+// captured into a graph (a graph runs its nodes in order).
 struct OnePassOrder {
   std::mutex mu;
   hipEvent_t ev = nullptr;
@@ -1757,10 +1827,13 @@ hipError_t launch_onepass(int plane_mode, bool wy, const Shape& sh, const QuantA
   if (capture == hipStreamCaptureStatusNone) {
     lock.lock();
     if (ord.any && ord.last != stream && !ord.multi) {
-      // first launch on a second stream: the previous launch left no event
-      if ((e = hipEventCreateWithFlags(&ord.ev, hipEventDisableTiming)) != hipSuccess) return e;
-      if ((e = hipDeviceSynchronize()) != hipSuccess) return e;
+      // first launch on a second stream: the previous launch left no event,
+      // so one is recorded now on its stream (after everything enqueued there)
+      if (ord.ev == nullptr && (e = hipEventCreateWithFlags(&ord.ev, hipEventDisableTiming)) != hipSuccess)
+        return e;
+      if ((e = hipEventRecord(ord.ev, ord.last)) != hipSuccess) return e;
       ord.multi = true;
+      ord.recorded = true;
     }
     if (ord.multi && ord.recorded && ord.last != stream && (e = hipStreamWaitEvent(stream, ord.ev, 0)) != hipSuccess)
       return e;
@@ -1772,16 +1845,18 @@ hipError_t launch_onepass(int plane_mode, bool wy, const Shape& sh, const QuantA
   a.T = (int)T;
   a.Q = (int)Q;
   a.L = (int)L;
+  const DeviceSyms* syms = nullptr;
+  if ((e = device_syms(dev, &syms)) != hipSuccess) return e;
   a.slots = static_cast<uint32_t*>(work);
   a.sword = a.slots + sh.groups * kPartMax;
-  a.err = a.sword + sh.groups * kSCopies * 64;
+  a.fails = syms->fails;
   const int64_t wl = g_wait_limit.load(std::memory_order_relaxed);
   a.spin_max = wl > 0 ? (int)wl : kSpinMax;
   a.gout = qa.gout;
   a.plane = qa.plane;
   a.scales = qa.scales;
   a.y = qa.y;
-  const int64_t words = sh.groups * ((int64_t)kPartMax + kSCopies * 64) + 1;
+  const int64_t words = sh.groups * ((int64_t)kPartMax + kSCopies * 64);
   const int64_t zb = min((words + kThreads - 1) / kThreads, (int64_t)1024);
   e = launch(zero_words_kernel, dim3((unsigned)zb), dim3(kThreads), stream, a.slots, words);
   if (e != hipSuccess) return e;
@@ -1847,9 +1922,8 @@ hipError_t guided_pack(int bits, bool decode, bool wc, bool stats, bool diag, co
 
 int64_t quant_work_bytes(int fmt, const Shape& sh) {
   if (fmt != 0 || packable(fmt, sh)) return 0;
-  // amax partials or tagged tile maxima [G][kPartMax], S words [G][kSCopies * 64],
-  // error count
-  const int64_t words = sh.groups * ((int64_t)kPartMax + kSCopies * 64) + 1;
+  // amax partials or tagged tile maxima [G][kPartMax], S words [G][kSCopies * 64]
+  const int64_t words = sh.groups * ((int64_t)kPartMax + kSCopies * 64);
   return (words * (int64_t)sizeof(uint32_t) + 7) / 8 * 8;
 }
 
@@ -2009,6 +2083,18 @@ hipError_t launch_stats(int64_t n, const uint16_t* xt, const uint16_t* xr, const
 namespace tfp4 {
 int64_t set_encode_batch(int64_t groups) { return g_encode_batch.exchange(groups); }
 int64_t set_wait_limit(int64_t polls) { return g_wait_limit.exchange(polls); }
+
+hipError_t read_wait_failures(uint64_t* out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const DeviceSyms* syms = nullptr;
+  if ((e = device_syms(dev, &syms)) != hipSuccess) return e;
+  unsigned long long v = 0;
+  if ((e = hipMemcpy(&v, syms->fails, sizeof(v), hipMemcpyDeviceToHost)) != hipSuccess) return e;
+  *out = (uint64_t)v;
+  return hipSuccess;
+}
 
 // ---- row-offset groups: workspace [offs | tstart | table | tile maxima]
 

@@ -22,7 +22,13 @@ def _stream_of(t: torch.Tensor):
 
 class RecordRing:
     """`slots` pinned host buffers of `slot_bytes` each, filled in ring order
-    by device-to-host copies on the ring's own stream."""
+    by device-to-host copies on the ring's own stream.
+
+    The copies of a push run later, on the ring's stream, so the ring keeps a
+    reference to the pushed tensors until the slot's copies are known to be
+    done (wait, ready returning True, release or close): a caller may drop
+    them, or reuse their memory through torch's caching allocator, right
+    after push."""
 
     def __init__(self, slot_bytes: int, slots: int):
         self._lib = _abi.load()
@@ -31,11 +37,13 @@ class RecordRing:
         self._h = h
         self.slot_bytes = int(slot_bytes)
         self.slots = int(slots)
+        self._held = [[] for _ in range(self.slots)]   # sources of each slot's copies in flight
 
     def push(self, tensors: Sequence[torch.Tensor], stream: Optional[int] = None) -> int:
         """Queue copies of the (contiguous, device) tensors, back to back, into
         the next slot, after the work already enqueued on `stream` (default:
-        torch's current stream of the first tensor). Returns the slot."""
+        torch's current stream of the first tensor). Returns the slot. The
+        tensors are kept alive by the ring until the copies are done."""
         if not tensors:
             raise ValueError("push needs at least one tensor")
         for t in tensors:
@@ -47,15 +55,19 @@ class RecordRing:
         slot = ctypes.c_int32()
         s = _stream_of(tensors[0]) if stream is None else stream
         _abi.call("trace_ring_push", self._h, srcs, sizes, n, s, ctypes.byref(slot))
+        self._held[slot.value] = list(tensors)
         return slot.value
 
     def wait(self, slot: int) -> None:
         _abi.call("trace_ring_wait", self._h, int(slot))
+        self._held[int(slot)] = []
 
     def ready(self, slot: int) -> bool:
         r = self._lib.trace_ring_query(self._h, int(slot))
         if r < 0:
             raise _abi.TraceError("trace_ring_query", r)
+        if r == 1:
+            self._held[int(slot)] = []
         return r == 1
 
     def view(self, slot: int) -> np.ndarray:
@@ -71,11 +83,13 @@ class RecordRing:
 
     def release(self, slot: int) -> None:
         _abi.call("trace_ring_release", self._h, int(slot))
+        self._held[int(slot)] = []
 
     def close(self) -> None:
         if self._h is not None:
-            _abi.call("trace_ring_destroy", self._h)
+            _abi.call("trace_ring_destroy", self._h)   # waits for the ring's copies
             self._h = None
+            self._held = [[] for _ in range(self.slots)]
 
     def __enter__(self):
         return self

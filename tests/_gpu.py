@@ -194,27 +194,34 @@ def oracle_mismatch(fmt, bits, xt_bits, xr_bits, rows, group_rows, o_guided):
                                 unpack_codes(rtn["codes"]))
 
 
-def torch_mismatch_counts(ct: torch.Tensor, cr: torch.Tensor, cb: torch.Tensor) -> np.ndarray:
-    """The mismatch counts from three packed code planes with plain torch
-    ops (for full-size tensors whose planes are sample-checked against the
-    oracle): the same definition as the oracle's, chunk by chunk."""
-    def pos(p):
-        c = torch.stack([p & 15, p >> 4], -1).reshape(-1).to(torch.int16)
-        k = c & 7
-        return torch.where((c & 8) != 0, -k, k), k
-    out = torch.zeros(ofp4.MISMATCH_COUNTS, dtype=torch.int64, device=ct.device)
-    nb = ofp4.MISMATCH_BINS
-    a, b, c = ct.reshape(-1), cr.reshape(-1), cb.reshape(-1)
-    step = 1 << 26
-    for s0 in range(0, a.numel(), step):
-        pt, kt = pos(a[s0:s0 + step])
-        pr, _ = pos(b[s0:s0 + step])
-        pb, kb = pos(c[s0:s0 + step])
-        out[:nb] += torch.bincount((pt - pr).abs().long(), minlength=nb)[:nb]
-        out[nb:2 * nb] += torch.bincount((pb - pr).abs().long(), minlength=nb)[:nb]
-        out[2 * nb] += (kt > kb).sum()
-        out[2 * nb + 1] += (kt < kb).sum()
-    return out.cpu().numpy()
+CHUNK_ELEMS = 1 << 21   # host-side chunk of the full-size checks (keeps numpy's buffers reused)
+
+
+def oracle_plane_counts(codes_t: torch.Tensor, codes_r: torch.Tensor, codes_b: torch.Tensor,
+                        step: int = CHUNK_ELEMS) -> np.ndarray:
+    """The oracle's mismatch counts (oracle.fp4.mismatch_counts) over three
+    packed device code planes of any size, chunk by chunk on the CPU: the
+    guided codes, the rollout codes and the RTN codes under the rollout scales."""
+    out = np.zeros(ofp4.MISMATCH_COUNTS, np.int64)
+    a, b, c = codes_t.reshape(-1), codes_r.reshape(-1), codes_b.reshape(-1)
+    half = step // 2
+    for s0 in range(0, a.numel(), half):
+        out += ofp4.mismatch_counts(ofp4.unpack_codes(u8(a[s0:s0 + half])), ofp4.unpack_codes(u8(b[s0:s0 + half])),
+                                    ofp4.unpack_codes(u8(c[s0:s0 + half])))
+    return out
+
+
+def oracle_plane_sums(x_t: torch.Tensor, x_r: torch.Tensor, y_t: torch.Tensor, y_r: torch.Tensor,
+                      step: int = CHUNK_ELEMS):
+    """The oracle's discrepancy sums (oracle.fp4.discrepancy_stats, float64)
+    over four device bf16 tensors of any size, chunk by chunk on the CPU:
+    (SB, SF, n)."""
+    fl = [t.reshape(-1) for t in (x_t, x_r, y_t, y_r)]
+    sb = sf = n = 0.0
+    for s0 in range(0, fl[0].numel(), step):
+        a, b, c = ofp4.discrepancy_stats(*(bits_of(t[s0:s0 + step]) for t in fl))
+        sb, sf, n = sb + a, sf + b, n + c
+    return sb, sf, n
 
 
 def check_guided_stats(xt_bits, xr_bits, rows, cols, fmt, bits, group_rows=0, tol=1e-6):

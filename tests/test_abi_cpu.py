@@ -51,7 +51,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.trace_abi_version() == _abi.ABI_VERSION == 7
+    assert lib.trace_abi_version() == _abi.ABI_VERSION == 8
     for code, name in [(0, "TRACE_OK"), (-1, "TRACE_EINVAL"), (-2, "TRACE_ESHAPE"),
                        (-3, "TRACE_EALIGN"), (-4, "TRACE_EALIAS"), (-5, "TRACE_EDEVICE"),
                        (-6, "TRACE_ELAUNCH"), (-7, "TRACE_EBUSY"), (7, "unknown status")]:
@@ -63,6 +63,14 @@ def test_encode_batch_setting(lib):
     assert lib.trace_set_encode_batch(0) == 3
     assert lib.trace_set_encode_batch(-1) == _abi.EINVAL
     assert lib.trace_set_encode_batch(0) == 0
+
+
+def test_wait_failure_query_without_a_device(lib):
+    """The give-up count needs a gfx950 device; a NULL output is rejected first."""
+    assert lib.trace_encode_wait_failures(None) == _abi.EINVAL
+    v = ctypes.c_uint64(7)
+    assert lib.trace_encode_wait_failures(ctypes.byref(v)) == _abi.EDEVICE
+    assert v.value == 7
 
 
 def test_wait_limit_setting(lib):
@@ -77,11 +85,10 @@ def test_workspace_sizes(lib):
     assert lib.trace_stats_workspace_bytes(0) == 16
     assert lib.trace_stats_workspace_bytes(8192 * 2048) == 16 * 1024
     assert lib.trace_stats_workspace_bytes(-1) == 0
-    # one kPartMax (1024) array of uint32 partial maxima per global-scale group
-    # per group 1024 partial (or tile) maxima + 16 S words on their own 256-byte
-    # lines, plus one error count, in 8-byte units
-    qwb = lambda G: (4 * (2048 * G + 1) + 7) // 8 * 8  # noqa: E731
-    assert lib.trace_quant_workspace_bytes(0, 4, 32, 0) == qwb(1) == 8200
+    # per global-scale group 1024 uint32 partial (or tile) maxima + 16 published
+    # S words on their own 256-byte lines (1024 words)
+    qwb = lambda G: 8192 * G  # noqa: E731
+    assert lib.trace_quant_workspace_bytes(0, 4, 32, 0) == qwb(1) == 8192
     assert lib.trace_quant_workspace_bytes(0, 17 * 8192, 2048, 8192) == qwb(17)
     assert lib.trace_quant_workspace_bytes(1, 4, 32, 0) == 0            # MXFP4: no amax pass
     assert lib.trace_quant_workspace_bytes(0, 5, 32, 2) == -1           # 2 does not divide 5
@@ -106,7 +113,7 @@ def test_workspace_sizes(lib):
 
 
 W = 0x600000            # a fake workspace address
-WB = 8200               # quantize workspace bytes for one group
+WB = 8192               # quantize workspace bytes for one group
 
 
 # quantize_rtn(fmt, rows, cols, group_rows, x, gin, codes, scales, gout, y, work, work_bytes, stream)

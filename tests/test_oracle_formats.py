@@ -97,11 +97,6 @@ def test_floor_log2_exact_all_bf16():
         assert formats.floor_log2(np.array([v]))[0] == math.frexp(v)[1] - 1
 
 
-def test_e8m0_value():
-    b = np.arange(255)
-    assert np.array_equal(formats.e8m0_value(b), 2.0 ** (b - 127.0))
-
-
 def test_e2m1_table_is_textbook():
     # E2M1, bias 1: exponent 0 subnormal (0, 0.5); otherwise (1 + m/2) * 2^(e-1).
     vals = []

@@ -80,21 +80,23 @@ def test_stream_layer_bench_configuration():
         xt[c * CH:(c + 1) * CH].copy_(a)
         xr[c * CH:(c + 1) * CH].copy_(b)
     work = tq.quant_workspace(NV, chunks * CH, syn.HIDDEN, CH, device=dev)
+    fails0 = tq.encode_wait_failures()
     g = tq.encode_guidance(xr, NV, 1, with_y=True, group_rows=CH, work=work)
     y, codes, acc, counts = tq.guided_fake_quant_stats(xt, xr, g, with_codes=True, mismatch=True)
     y_plain, _ = tq.guided_fake_quant(xt, g)
     torch.cuda.synchronize()
-    # the single-pass encode's count of bounded waits that gave up
-    assert work.view(torch.int32)[chunks * 2048].item() == 0
+    # no bounded wait of the single-pass encode gave up
+    assert tq.encode_wait_failures() == fails0
     assert torch.equal(y.view(torch.int16), y_plain.view(torch.int16))
-    # mismatch counts against plain torch over the code planes (rollout codes
-    # from a full-code record, RTN codes under the rollout scales), which the
-    # row samples below pin to the oracle
+    # mismatch counts: the oracle's count over the whole code planes (rollout
+    # codes from a full-code record, RTN codes under the rollout scales), whose
+    # codes the row samples below pin to the oracle
     g4 = tq.encode_guidance(xr, NV, 4, group_rows=CH)
     y_rtn, codes_rtn = tq.guided_fake_quant(xt, g, bits=0, with_codes=True)
-    want = G.torch_mismatch_counts(codes, g4.guide, codes_rtn)
+    want = G.oracle_plane_counts(codes, g4.guide, codes_rtn)
     G.assert_same(counts.cpu().numpy(), want, "mismatch counts, streamed layer")
     assert want[:15].sum() == xt.numel()
+    G.say("  mismatch counts equal the oracle's")
     xt_b, xr_b = _bits(xt), _bits(xr)
     gs = G.f32(g.gscale).reshape(chunks, 2)
     n_chunk = CH * syn.HIDDEN
@@ -140,9 +142,57 @@ def test_stream_layer_bench_configuration():
     a = acc.cpu().numpy()
     assert a[2] == xt.numel()
     assert G.rel_close(a[0], sb_total), (a[0], sb_total)
-    # SF against the sum over the library's own outputs (sample-verified above)
-    ref = tq.discrepancy_stats(xt.view(-1), xr.view(-1), y.view(-1), g.y.view(-1)).cpu().numpy()
-    assert G.rel_close(a[1], ref[1]) and G.rel_close(a[0], ref[0])
+    # SF: the oracle's sums over the guided and rollout outputs (sample-verified above)
+    sb, sf, n = G.oracle_plane_sums(xt, xr, y, g.y)
+    assert a[2] == n and G.rel_close(a[0], sb) and G.rel_close(a[1], sf), (a, (sb, sf, n))
+
+
+def test_guided_stats_two_layers_in_one_call():
+    """guided_fake_quant_stats over two streamed layers in one call (34
+    chunks of [8192, 2048]: 34,816 tiles, past the 32,768 that one reduction
+    workgroup sums, so the per-tile sums go through the two-level
+    reduction). SB and SF against the oracle's float64 sums over the inputs
+    and the (row-sampled) outputs; the same sums from the two per-layer calls,
+    which take the one-level reduction."""
+    G.say("full size: guided_fake_quant_stats over 2 streamed layers in one call")
+    chunks, CH = 17, syn.STREAM_CHUNK
+    dev = G.DEV
+    xt = torch.empty((2 * chunks * CH, syn.HIDDEN), dtype=torch.bfloat16, device=dev)
+    xr = torch.empty_like(xt)
+    for li, layer in enumerate((20, 21)):
+        sigma = syn.stream_sigma(layer, dev)
+        for c in range(chunks):
+            a, b = syn.stream_pair(layer, c, dev, sigma=sigma)
+            r0 = (li * chunks + c) * CH
+            xt[r0:r0 + CH].copy_(a)
+            xr[r0:r0 + CH].copy_(b)
+            del a, b
+    rows = xt.shape[0]
+    assert rows * syn.HIDDEN // 16384 > 32768
+    g = tq.encode_guidance(xr, NV, 1, with_y=True, group_rows=CH)
+    y, _, acc = tq.guided_fake_quant_stats(xt, xr, g)
+    half = rows // 2
+    gl = [tq.Guidance(NV, 1, g.guide[s], g.scales[s], g.gscale[k], None, CH)
+          for s, k in ((slice(0, half), slice(0, chunks)), (slice(half, rows), slice(chunks, 2 * chunks)))]
+    acc_l = torch.zeros(3, dtype=torch.float64, device=dev)
+    y_l = torch.empty_like(y)
+    tq.guided_fake_quant_stats(xt[:half], xr[:half], gl[0], acc=acc_l, y=y_l[:half])
+    tq.guided_fake_quant_stats(xt[half:], xr[half:], gl[1], acc=acc_l, accumulate=True, y=y_l[half:])
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y_l.view(torch.int16))
+    xt_b, xr_b = _bits(xt), _bits(xr)
+    n_chunk = CH * syn.HIDDEN
+    for grp in (0, chunks, 2 * chunks - 1):
+        S = ofp4.nvfp4_global_scale(ofp4.tensor_amax(xr_b[grp * n_chunk:(grp + 1) * n_chunk]))
+        for r0, r1 in _samples(CH, span=16):
+            _check_rows(NV, 1, xt_b, xr_b, syn.HIDDEN, grp * CH + r0, grp * CH + r1, S, g, y_g=y, y_r=g.y)
+    del xt_b, xr_b
+    sb, sf, n = G.oracle_plane_sums(xt, xr, y, g.y)
+    a, b = acc.cpu().numpy(), acc_l.cpu().numpy()
+    G.say(f"  one call {a.tolist()}, two calls {b.tolist()}, oracle {(sb, sf, n)}")
+    assert a[2] == b[2] == n == xt.numel()
+    assert G.rel_close(a[0], sb) and G.rel_close(a[1], sf), (a, (sb, sf))
+    assert G.rel_close(b[0], sb) and G.rel_close(b[1], sf), (b, (sb, sf))
 
 
 @pytest.mark.parametrize("bits", [2, 3])
@@ -162,10 +212,11 @@ def test_stream_layer_wider_records(bits):
         xt[c * CH:(c + 1) * CH].copy_(a)
         xr[c * CH:(c + 1) * CH].copy_(b)
     work = tq.quant_workspace(NV, chunks * CH, syn.HIDDEN, CH, device=dev)
+    fails0 = tq.encode_wait_failures()
     g = tq.encode_guidance(xr, NV, bits, group_rows=CH, work=work)
     y, codes = tq.guided_fake_quant(xt, g, with_codes=True)
     torch.cuda.synchronize()
-    assert work.view(torch.int32)[chunks * 2048].item() == 0
+    assert tq.encode_wait_failures() == fails0
     xt_b, xr_b = _bits(xt), _bits(xr)
     n_chunk = CH * syn.HIDDEN
     for c in (0, 9, 16):
@@ -194,10 +245,11 @@ def test_whole_stream_encode_one_call():
             del b
     flat = xr.view(layers * rows_l, cols)
     work = tq.quant_workspace(NV, layers * rows_l, cols, CH, device=dev)
+    fails0 = tq.encode_wait_failures()
     g = tq.encode_guidance(flat, NV, 1, group_rows=CH, work=work)
     torch.cuda.synchronize()
     G_ = layers * chunks
-    assert work.view(torch.int32)[G_ * 2048].item() == 0
+    assert tq.encode_wait_failures() == fails0
     # every group's amax (plain torch, exact) and the oracle's S of it
     amax = (flat.view(torch.int16) & 0x7FFF).view(G_, CH * cols).amax(dim=1).cpu().numpy().astype(np.uint16)
     A = ofp4.bf16_to_f32(amax)
@@ -254,12 +306,12 @@ def test_stream_layer_per_token_scales():
     for r0, r1 in _samples(rows, span=24):
         for r in range(r0, r1):
             _check_rows(NV, 1, xt_b, xr_b, cols, r, r + 1, S[r], g, y_g=y, codes_g=codes, y_r=g.y)
-    ref = tq.discrepancy_stats(xt.view(-1), xr.view(-1), y.view(-1), g.y.view(-1)).cpu().numpy()
+    sb, sf, n = G.oracle_plane_sums(xt, xr, y, g.y)
     a = acc.cpu().numpy()
-    assert a[2] == ref[2] and G.rel_close(a[0], ref[0]) and G.rel_close(a[1], ref[1])
+    assert a[2] == n and G.rel_close(a[0], sb) and G.rel_close(a[1], sf), (a, (sb, sf, n))
     g4 = tq.encode_guidance(xr, NV, 4, group_rows=1)
     _, codes_rtn = tq.guided_fake_quant(xt, g, bits=0, with_codes=True)
-    G.assert_same(counts.cpu().numpy(), G.torch_mismatch_counts(codes, g4.guide, codes_rtn),
+    G.assert_same(counts.cpu().numpy(), G.oracle_plane_counts(codes, g4.guide, codes_rtn),
                   "mismatch counts, per-token scales")
 
 
@@ -314,9 +366,9 @@ def test_kv_full_size(which):
         assert G.f32(g.gscale)[0] == S
         for r0, r1 in _samples(rows, span=256):
             _check_rows(NV, bits, xt_b, xr_b, cols, r0, r1, S, g, y_g=y, codes_g=codes, y_r=g.y)
-        ref = tq.discrepancy_stats(xt, xr, y, g.y).cpu().numpy()
+        sb, sf, n = G.oracle_plane_sums(xt, xr, y, g.y)
         a = acc.cpu().numpy()
-        assert a[2] == ref[2] and G.rel_close(a[0], ref[0]) and G.rel_close(a[1], ref[1])
+        assert a[2] == n and G.rel_close(a[0], sb) and G.rel_close(a[1], sf), (a, (sb, sf, n))
 
 
 def test_kv_cache_one_call_over_all_layers():
@@ -338,10 +390,11 @@ def test_kv_cache_one_call_over_all_layers():
             del a, b
     ft, fr = kt.view(-1, cols), kr.view(-1, cols)
     work = tq.quant_workspace(NV, ft.shape[0], cols, rows_t, device=G.DEV)
+    fails0 = tq.encode_wait_failures()
     g = tq.encode_guidance(fr, NV, 4, group_rows=rows_t, work=work)
     y, _ = tq.guided_fake_quant(ft, g, bits=4)
     torch.cuda.synchronize()
-    assert work.view(torch.int32)[n_t * 2048].item() == 0
+    assert tq.encode_wait_failures() == fails0
     amax = (fr.view(torch.int16) & 0x7FFF).view(n_t, -1).amax(dim=1).cpu().numpy().astype(np.uint16)
     A = ofp4.bf16_to_f32(amax)
     S = np.array([ofp4.nvfp4_global_scale(v) for v in A], np.float32)

@@ -142,39 +142,64 @@ def _enumeration_members():
     return bits[np.isfinite(f) & (np.abs(f) <= 6.0)]
 
 
+ROLLOUT_CODEWORDS = np.array([0, .5, 1, 1.5, 2, 3, 4, 6, -0.0, -.5, -1, -1.5, -2, -3, -4, -6], np.float32)
+
+
+def _members_tensor(members_t, members_r):
+    """Rows of 32 elements: row 0 is the tensor anchor [2688, 0, ...] (NVFP4:
+    A = 2688, S = 1); every other row holds two 16-element blocks, each with
+    6 at its first position (NVFP4 e = 1, so d = r = 1; MXFP4 E = 0 for the
+    32-element block) and 15 members. Returns (xt, xr, rows)."""
+    per = 15
+    nblk = -(-members_t.size // per)
+    nblk += nblk % 2                          # whole rows of two blocks
+    six = formats.f32_to_bf16(np.array([6.0], np.float32))[0]
+    out = []
+    for members in (members_t, members_r):
+        x = np.zeros((nblk, 16), np.uint16)
+        x[:, 0] = six
+        flat = np.zeros(nblk * per, np.uint16)
+        flat[: members.size] = members
+        x[:, 1:] = flat.reshape(nblk, per)
+        head = np.zeros(32, np.uint16)
+        head[0] = formats.f32_to_bf16(np.array([2688.0], np.float32))[0]
+        out.append(np.concatenate([head, x.reshape(-1)]))
+    rows = out[0].size // 32
+    return out[0], out[1], rows
+
+
 def test_enumerate_bf16_members_unit_scale():
     """Every finite bf16 value with |x| <= 6 as a non-max block member under
-    S = 1, e = 1 (and under MXFP4, E = 0): all five calls, GPU vs oracle."""
-    G.say("enumeration: block members")
+    S = 1, e = 1 (and under MXFP4, E = 0): quantize_rtn and encode_guidance,
+    GPU vs oracle."""
+    G.say("enumeration: block members, own scales")
     members = _enumeration_members()
-    per = 15
-    nblk = -(-members.size // per)
-    nblk += nblk % 2 == 0                    # anchor block + members: an even block count
-    x = np.zeros((nblk + 1, 16), np.uint16)
-    x[0, 0] = formats.f32_to_bf16(np.array([2688.0], np.float32))[0]
-    x[1:, 0] = formats.f32_to_bf16(np.array([6.0], np.float32))[0]
-    flat = np.zeros(nblk * per, np.uint16)
-    flat[: members.size] = members
-    x[1:, 1:] = flat.reshape(nblk, per)
-    rows = (nblk + 1) // 2
-    xb = x.reshape(-1)
-    assert xb.size == rows * 32
-    G.check_quantize(xb, rows, 32, NV)
-    G.check_quantize(xb, rows, 32, MX)
-    rng = np.random.default_rng(0)
-    for _ in range(2):
-        # rollout side: the same blocks with members replaced by random codewords
-        xr = xb.copy()
-        pick = rng.integers(0, 16, xr.size)
-        vals = np.array([0, .5, 1, 1.5, 2, 3, 4, 6, -0.0, -.5, -1, -1.5, -2, -3, -4, -6], np.float32)
-        keep = np.zeros(xr.size, bool)
-        keep[0::16] = True
-        xr = np.where(keep, xr, formats.f32_to_bf16(vals[pick]))
-        for fmt in (NV, MX):
-            for bits in (0, 1, 2, 3, 4):
-                G.check_guided(xb, xr, rows, 32, fmt, bits)
-            for bits in (1, 2, 3):
-                G.check_decode(xb, xr, rows, 32, fmt, bits=bits)
+    xb, _, rows = _members_tensor(members, members)
+    for fmt in (NV, MX):
+        G.check_quantize(xb, rows, 32, fmt)
+        for bits in (1, 2, 3, 4):
+            G.check_encode(xb, rows, 32, fmt, bits)
+
+
+@pytest.mark.parametrize("fmt", [NV, MX])
+def test_enumerate_bf16_train_values_all_rollout_codes(fmt):
+    """The whole training-side pipeline, exhaustively: every finite bf16 value
+    (65,280 of them, so t = |x| covers every bf16 magnitude, the saturated
+    range above 6 included) paired with each of the 16 signed rollout
+    codewords, under unit rollout scales. Guided rounding with records of
+    every width (bits 0 to 4) and Reconstruct (bits 1 to 3), GPU vs oracle,
+    bit for bit."""
+    G.say(f"enumeration: every bf16 training value x 16 rollout codes, fmt={fmt}")
+    allb = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    finite = allb[np.isfinite(formats.bf16_to_f32(allb))]
+    assert finite.size == 65280
+    train = np.repeat(finite, 16)
+    roll = np.tile(formats.f32_to_bf16(ROLLOUT_CODEWORDS), finite.size)
+    xt, xr, rows = _members_tensor(train, roll)
+    for bits in (0, 1, 2, 3, 4):
+        G.check_guided(xt, xr, rows, 32, fmt, bits)
+    for bits in (1, 2, 3):
+        G.check_decode(xt, xr, rows, 32, fmt, bits=bits)
 
 
 def test_enumerate_bf16_block_max():

@@ -9,6 +9,7 @@ import torch
 
 import precision_rl_nvfp4_amd as tq
 import synthetic as syn
+from oracle import fp4 as ofp4
 from oracle import record as orec
 from precision_rl_nvfp4_amd import _abi
 from precision_rl_nvfp4_amd.record import RecordRing, gather_pages
@@ -33,6 +34,35 @@ def test_ring_copies_encode_outputs_without_a_host_sync():
         assert host.size == want.size == 512 * 2048 // 8 + 512 * 2048 // 16 + 8
         G.assert_same(host, want, "slot bytes")
         ring.release(slot)
+
+
+def test_ring_keeps_pushed_tensors_until_copied():
+    """Push a record's planes and drop them at once, then let the producer
+    stream allocate and overwrite memory of the same sizes before the ring's
+    copies are waited on: the slot still holds the record's bytes (the ring
+    keeps the sources alive until the copies are done)."""
+    G.say("record ring: sources dropped right after push")
+    _, xr = syn.activation_pair(1024, 2048, (94, 0))
+    r = xr.to(G.DEV)
+    xr_b = G.bits_of(r)
+    o = ofp4.encode_guidance(ofp4.NVFP4, 1, xr_b)
+    want = np.concatenate([o["guide"], o["scales"], np.array([o["gscale"], o["amax"]], np.float32).view(np.uint8)])
+    with RecordRing(1 << 20, 2) as ring:
+        # keep the producer stream busy so the copies cannot start before
+        # the overwrites below are enqueued
+        busy = torch.empty(1 << 28, dtype=torch.uint8, device=G.DEV)
+        g = tq.encode_guidance(r, "nvfp4", 1)
+        for _ in range(8):
+            busy.fill_(3)
+        slot = ring.push([g.guide, g.scales, g.gscale])
+        sizes = [(t.numel(), t.dtype) for t in (g.guide, g.scales, g.gscale)]
+        del g
+        junk = [torch.full((n,), 0x5A, dtype=torch.uint8, device=G.DEV) if dt == torch.uint8 else
+                torch.full((n,), -1.0, dtype=dt, device=G.DEV) for n, dt in sizes]
+        ring.wait(slot)
+        G.assert_same(ring.view(slot), want, "slot bytes after the sources were dropped")
+        ring.release(slot)
+        del junk, busy
 
 
 def test_ring_slot_cycle():

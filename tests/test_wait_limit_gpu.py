@@ -1,14 +1,18 @@
 """The single-pass encode's bounded waits, forced from the host: with a wait
-limit of one poll the workgroups give up at once instead of waiting for each
-other's tile maxima and scales. The launch must still complete and count
-its failures in the workspace; with the limit restored the next call on the
-same workspace is exact again (bit-identical to a call made before)."""
+limit of one poll nearly every wait gives up at once instead of waiting for
+other workgroups' tile maxima and scales. A wait that gives up takes what it
+waited for from the input itself, so every output must still be bit-identical
+to the same call with the default limit, and the device's give-up count must
+have grown. Two launch shapes: one group in flight at a time (8192-row
+chunks) and several (1024-row groups)."""
 
+import numpy as np
 import pytest
 import torch
 
 import precision_rl_nvfp4_amd as tq
 import synthetic as syn
+from oracle import fp4 as ofp4
 from precision_rl_nvfp4_amd import _abi
 from tests import _gpu as G
 
@@ -17,28 +21,42 @@ pytestmark = pytest.mark.gpu
 NV = tq.NVFP4
 
 
-def test_waits_give_up_and_the_next_call_recovers():
-    G.say("single-pass encode with a wait limit of 1 poll, then the default")
+def _stream_rows(layer, chunks):
+    sigma = syn.stream_sigma(layer, G.DEV)
+    return torch.cat([syn.stream_pair(layer, c, G.DEV, sigma=sigma)[1] for c in range(chunks)])
+
+
+@pytest.mark.parametrize("group_rows,chunks,bits", [(8192, 2, 1), (1024, 2, 4)])
+def test_waits_give_up_and_results_stay_exact(group_rows, chunks, bits):
+    G.say(f"single-pass encode, wait limit 1 poll: group_rows={group_rows} chunks={chunks} bits={bits}")
     lib = _abi.load()
-    CH, chunks, cols = syn.STREAM_CHUNK, 2, syn.HIDDEN
-    sigma = syn.stream_sigma(20, G.DEV)
-    xr = torch.cat([syn.stream_pair(20, c, G.DEV, sigma=sigma)[1] for c in range(chunks)])
-    rows = xr.shape[0]
-    work = tq.quant_workspace(NV, rows, cols, CH, device=G.DEV)
-    fails = work.view(torch.int32)[chunks * 2048]
-    ref = tq.encode_guidance(xr, NV, 1, group_rows=CH, work=work)
+    xr = _stream_rows(20, chunks)
+    rows, cols = xr.shape
+    work = tq.quant_workspace(NV, rows, cols, group_rows, device=G.DEV)
+    ref = tq.encode_guidance(xr, NV, bits, with_y=True, group_rows=group_rows, work=work)
     torch.cuda.synchronize()
-    assert fails.item() == 0
+    fails0 = tq.encode_wait_failures()
     prev = lib.trace_set_wait_limit(1)
     try:
-        tq.encode_guidance(xr, NV, 1, group_rows=CH, work=work)
+        g = tq.encode_guidance(xr, NV, bits, with_y=True, group_rows=group_rows, work=work)
         torch.cuda.synchronize()
-        assert fails.item() > 0
     finally:
         assert lib.trace_set_wait_limit(prev) == 1
-    g = tq.encode_guidance(xr, NV, 1, group_rows=CH, work=work)
-    torch.cuda.synchronize()
-    assert fails.item() == 0
+    fails1 = tq.encode_wait_failures()
+    G.say(f"  waits that gave up: {fails1 - fails0}")
+    assert fails1 > fails0
     assert torch.equal(g.guide, ref.guide)
     assert torch.equal(g.scales, ref.scales)
     assert torch.equal(g.gscale, ref.gscale)
+    assert torch.equal(g.y.view(torch.int16), ref.y.view(torch.int16))
+    # and against the oracle's scales of the exact amax of every group
+    gs = G.f32(g.gscale).reshape(-1, 2)
+    amax = (xr.view(torch.int16) & 0x7FFF).view(rows // group_rows, -1).amax(dim=1).cpu().numpy()
+    A = ofp4.bf16_to_f32(amax.astype(np.uint16))
+    G.assert_same(gs[:, 1], A, "A after give-ups")
+    G.assert_same(gs[:, 0], np.array([ofp4.nvfp4_global_scale(a) for a in A], np.float32), "S after give-ups")
+    # the default limit again: no give-up, same results
+    g2 = tq.encode_guidance(xr, NV, bits, with_y=True, group_rows=group_rows, work=work)
+    torch.cuda.synchronize()
+    assert tq.encode_wait_failures() == fails1
+    assert torch.equal(g2.guide, ref.guide) and torch.equal(g2.gscale, ref.gscale)
