@@ -65,6 +65,22 @@ KERNEL_NAME = {
 }
 KERNEL_SRC = os.path.join(ROOT, "precision_rl_nvfp4_amd", "csrc", "trace_fp4_kernels.hip")
 PROFILES = os.path.join(ROOT, "profiles")
+MX = 1
+
+# The workloads other than the stream, as [layers, rows, cols] train/rollout
+# pairs of the 20 guided (deepest) layers. enc_gr: rows per global-scale
+# group (one S per layer tensor, or per K / V tensor); the step encodes every
+# layer's rollout tensor in one call, then runs the training side layer by
+# layer (guided_fake_quant_stats; for per-expert scales the grouped calls and
+# discrepancy_stats, since the fused statistics take equal groups only).
+CONFIGS = {
+    "stream": None,
+    "moe": dict(workload="moe_nvfp4_20x65536x2048", fmt=NV, bits=1, rows=65536, cols=HIDDEN, enc_gr=65536),
+    "moe_expert": dict(workload="moe_nvfp4_per_expert_20x65536x2048", fmt=NV, bits=1, rows=65536, cols=HIDDEN,
+                       enc_gr=0),
+    "kv": dict(workload="kv_nvfp4_20x2x65536x256", fmt=NV, bits=4, rows=2 * 65536, cols=256, enc_gr=65536),
+    "mxfp4": dict(workload="mxfp4_20x65536x2048", fmt=MX, bits=1, rows=65536, cols=HIDDEN, enc_gr=0),
+}
 
 
 def log(*a):
@@ -90,6 +106,10 @@ def parse():
                     help="groups per batch of the two-pass NVFP4 encode (library default if < 0)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain device copy of known size (counter calibration)")
+    ap.add_argument("--config", choices=sorted(CONFIGS), default="stream",
+                    help="workload: stream (the 136K-token stream, default), moe (routed-expert "
+                         "activations, one S per layer), moe_expert (one S per expert), kv (FP4 KV "
+                         "cache, full codes), mxfp4 (MXFP4 with midpoint ties)")
     return ap.parse_args()
 
 
@@ -437,11 +457,11 @@ def kernel_entry(name, ms_list, calls, n, bpe=None):
 
 # ---------------------------------------------------------------- counters
 
-def read_traffic(kernel):
+def read_traffic(kernel, workload="stream_nvfp4"):
     """HBM bytes per launch of ``kernel`` from the committed rocprofv3 --pmc
-    summary, or None when there is none or the kernel source changed since
-    the counters were taken."""
-    path = os.path.join(PROFILES, f"{kernel}_stream_nvfp4_pmc.txt")
+    summary of that workload, or None when there is none or the kernel source
+    changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_pmc.txt")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -461,11 +481,14 @@ def read_traffic(kernel):
 # ---------------------------------------------------------------- CPU baseline
 
 def _oracle_unit(args):
+    """encode (rollout) -> guided (training) -> discrepancy sums of one slice,
+    taken as one tensor: args = (train bits, rollout bits[, fmt, bits])."""
     import numpy as np
     from oracle import fp4 as ofp4
-    bt, br = args
-    e = ofp4.encode_guidance(ofp4.NVFP4, 1, br)
-    g = ofp4.guided_fake_quant(ofp4.NVFP4, 1, bt, e["guide"], e["scales"], e["gscale"])
+    bt, br = args[:2]
+    fmt, bits = (args[2], args[3]) if len(args) > 2 else (ofp4.NVFP4, 1)
+    e = ofp4.encode_guidance(fmt, bits, br)
+    g = ofp4.guided_fake_quant(fmt, bits, bt, e["guide"], e["scales"], e["gscale"])
     ofp4.discrepancy_stats(bt, br, g["y"], e["y"])
     return int(np.asarray(bt).size)
 
@@ -487,14 +510,17 @@ def single_core_tiny(torch, target_s=2.0):
 
 
 def cpu_baseline(torch, w, workers, target_s):
-    """The oracle, as it stands, over 1024-token slices of the streamed
-    workload (each slice taken as one tensor with its own global scale),
-    through the same encode -> guided -> discrepancy path, in rounds of one
-    slice per worker process until about `target_s` seconds have passed."""
+    """The oracle, as it stands, over slices of the workload (1024 rows of
+    2048, or as many rows of a narrower tensor; each slice taken as one tensor
+    with its own global scale), through the same encode -> guided ->
+    discrepancy path, in rounds of one slice per worker process until about
+    `target_s` seconds have passed."""
     import multiprocessing as mp
 
     import numpy as np
-    rows = 1024
+    cols = getattr(w, "cols", HIDDEN)
+    fmt, bits = getattr(w, "fmt", NV), getattr(w, "bits", 1)
+    rows = max(1024, 2 ** 21 // cols)
 
     def slice_bits(t, layer, r0):
         return t[layer, r0:r0 + rows].contiguous().view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1)
@@ -509,7 +535,7 @@ def cpu_baseline(torch, w, workers, target_s):
             for _ in range(workers):
                 layer = j % w.layers
                 r0 = ((j * 37) % (w.rows // rows)) * rows
-                jobs.append((slice_bits(w.xt, layer, r0), slice_bits(w.xr, layer, r0)))
+                jobs.append((slice_bits(w.xt, layer, r0), slice_bits(w.xr, layer, r0), fmt, bits))
                 j += 1
             elems += sum(pool.map(_oracle_unit, jobs, chunksize=1))
             rounds += 1
@@ -522,11 +548,217 @@ def cpu_baseline(torch, w, workers, target_s):
         "host_cpus": os.cpu_count(),
         "single_core_tiny": single,
         "kind": "oracle",
-        "sample": (f"{rounds * workers} slices of {rows} tokens x {HIDDEN} from the streamed workload "
-                   f"({elems} elements per side), each one NVFP4 tensor: encode(bits=1) -> "
-                   f"guided(bits=1) -> discrepancy sums; {workers} worker processes, {rounds} rounds, "
-                   f"{wall:.1f} s wall"),
+        "sample": (f"{rounds * workers} slices of {rows} rows x {cols} from the "
+                   f"{getattr(w, 'workload', 'streamed')} workload ({elems} elements per side), each one "
+                   f"{'NVFP4' if fmt == NV else 'MXFP4'} tensor: encode(bits={bits}) -> guided(bits={bits}) -> "
+                   f"discrepancy sums; {workers} worker processes, {rounds} rounds, {wall:.1f} s wall"),
     }
+
+
+# ---------------------------------------------------------------- ceiling
+
+def copy_ceiling(torch, dev, nbytes=1 << 30, reps=10):
+    """A plain device-to-device copy of `nbytes` (torch's copy kernel), timed
+    with events: the HBM rate a read + write stream reaches on this GPU,
+    reported beside the roofline (its `peak` stays the published 8 TB/s)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    gbs = 2 * nbytes / (us * 1e-6) / 1e9
+    del src, dst
+    return {"kernel": "torch copy_ (device to device)", "bytes_read_plus_written": 2 * nbytes,
+            "avg_us": round(us, 2), "GB_s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+# ---------------------------------------------------------------- other workloads
+
+class LayeredWorkload:
+    """One of the non-stream workloads (CONFIGS): `layers` train/rollout
+    pairs of [rows, cols], resident as [layers, rows, cols], plus the record
+    and output buffers of the step."""
+
+    def __init__(self, torch, syn, name, spec, layers, dev):
+        self.name, self.workload = name, spec["workload"]
+        self.fmt, self.bits = spec["fmt"], spec["bits"]
+        self.layers, self.rows, self.cols = layers, spec["rows"], spec["cols"]
+        self.enc_gr = spec["enc_gr"]
+        self.n = self.rows * self.cols
+        shape = (layers, self.rows, self.cols)
+        self.xt = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        self.xr = torch.empty_like(self.xt)
+        self.offsets = []
+        for li, layer in enumerate(syn.GUIDED_LAYERS[:layers]):
+            if name in ("moe", "moe_expert"):
+                a, b, _, offs = syn.moe_pair(layer, device=dev)
+                self.offsets.append(offs)
+                self.xt[li].copy_(a)
+                self.xr[li].copy_(b)
+            elif name == "kv":
+                for which in (0, 1):
+                    a, b = syn.kv_pair(layer, which, device=dev)
+                    self.xt[li, which * 65536:(which + 1) * 65536].copy_(a)
+                    self.xr[li, which * 65536:(which + 1) * 65536].copy_(b)
+            else:
+                a, b = syn.mxfp4_pair(self.rows, self.cols, device=dev, layer=layer)
+                self.xt[li].copy_(a)
+                self.xr[li].copy_(b)
+            del a, b
+        B = 16 if self.fmt == NV else 32
+        self.B = B
+        self.guide = torch.empty((layers, self.rows, self.cols * self.bits // 8), dtype=torch.uint8, device=dev)
+        self.scales = torch.empty((layers, self.rows, self.cols // B), dtype=torch.uint8, device=dev)
+        if name == "moe_expert":
+            E = self.offsets[0].numel() - 1
+            self.gscale = torch.empty((layers, E, 2), dtype=torch.float32, device=dev)
+            self.yr = torch.empty_like(self.xt)
+        elif self.fmt == NV:
+            self.gscale = torch.empty((layers, self.rows // self.enc_gr, 2), dtype=torch.float32, device=dev)
+            self.yr = None
+        else:
+            self.gscale, self.yr = None, None
+        self.yt = torch.empty_like(self.xt)
+        self.acc = torch.zeros((layers, 3), dtype=torch.float64, device=dev)
+
+    def bytes_resident(self):
+        ts = [self.xt, self.xr, self.guide, self.scales, self.yt, self.acc] + \
+            [t for t in (self.gscale, self.yr) if t is not None]
+        return sum(t.numel() * t.element_size() for t in ts)
+
+
+def layered_phases(lib, tq, w, stream):
+    """Argument tuples of the step's calls: (phases, bytes per element of
+    each phase's calls, workspaces kept alive)."""
+    p = lambda t, i: t[i].data_ptr()  # noqa: E731
+    L, R, C, b = w.layers, w.rows, w.cols, w.bits
+    plane = b / 8 + 1 / w.B
+    keep = []
+    if w.name == "moe_expert":
+        E = w.offsets[0].numel() - 1
+        gb = int(lib.trace_grouped_workspace_bytes(NV, R, C, E))
+        gwork = [tq._workspace(gb, w.xt.device, None) for _ in range(L)]
+        db = int(lib.trace_stats_workspace_bytes(w.n))
+        dwork = tq.stats_workspace(w.n, w.xt.device)
+        keep += gwork + [dwork]
+        enc, gfq, dst = [], [], []
+        for i in range(L):
+            enc.append((NV, b, R, C, E, w.offsets[i].data_ptr(), p(w.xr, i), p(w.guide, i), p(w.scales, i),
+                        p(w.gscale, i), p(w.yr, i), gwork[i].data_ptr(), gb, stream))
+            gfq.append((NV, b, R, C, E, w.offsets[i].data_ptr(), p(w.xt, i), p(w.guide, i), p(w.scales, i),
+                        p(w.gscale, i), p(w.yt, i), None, gwork[i].data_ptr(), gb, stream))
+            dst.append((w.n, p(w.xt, i), p(w.xr, i), p(w.yt, i), p(w.yr, i), p(w.acc, i), 0, dwork.data_ptr(),
+                        db, stream))
+        phases = [("encode_guidance_grouped", lib.encode_guidance_grouped, enc),
+                  ("guided_fake_quant_grouped", lib.guided_fake_quant_grouped, gfq),
+                  ("discrepancy_stats", lib.discrepancy_stats, dst)]
+        bpe = {"encode_guidance_grouped": 2 + plane + 2 + 8 * E / w.n,
+               "guided_fake_quant_grouped": 2 + plane + 4 * E / w.n + 2, "discrepancy_stats": 8}
+        return phases, bpe, keep
+    qb = int(lib.trace_quant_workspace_bytes(w.fmt, L * R, C, w.enc_gr))
+    qwork = tq._workspace(qb, w.xt.device, None)
+    sb = int(lib.trace_guided_stats_workspace_bytes(w.fmt, R, C, w.enc_gr))
+    swork = tq._workspace(sb, w.xt.device, None)
+    keep += [t for t in (qwork, swork) if t is not None]
+    gptr = lambda i: None if w.gscale is None else p(w.gscale, i)  # noqa: E731
+    enc = [(w.fmt, b, L * R, C, w.enc_gr, w.xr.data_ptr(), None, w.guide.data_ptr(), w.scales.data_ptr(),
+            None if w.gscale is None else w.gscale.data_ptr(), None,
+            None if qwork is None else qwork.data_ptr(), qb, stream)]
+    gst = [(w.fmt, b, R, C, w.enc_gr, p(w.xt, i), p(w.xr, i), p(w.guide, i), p(w.scales, i), gptr(i),
+            p(w.yt, i), None, p(w.acc, i), None, 0, None if swork is None else swork.data_ptr(), sb, stream)
+           for i in range(L)]
+    gs = 8 / (w.enc_gr * C) if (w.fmt == NV and w.enc_gr) else 0.0
+    phases = [("encode_guidance", lib.encode_guidance, enc),
+              ("guided_fake_quant_stats", lib.guided_fake_quant_stats, gst)]
+    bpe = {"encode_guidance": 2 + plane + gs, "guided_fake_quant_stats": 2 + 2 + plane + gs / 2 + 2}
+    return phases, bpe, keep
+
+
+LAYERED_KERNEL = {"encode_guidance": "quantize_kernel", "guided_fake_quant_stats": "guided_kernel",
+                  "encode_guidance_grouped": "quantize_kernel", "guided_fake_quant_grouped": "guided_kernel",
+                  "discrepancy_stats": "stats_partial_kernel"}
+
+
+def main_layered(args, torch, syn, tq, lib, dev):
+    """bench.py --config moe | moe_expert | kv | mxfp4: the step of that
+    workload, with the same timing, roofline and CPU-baseline fields as the
+    stream's line."""
+    spec = CONFIGS[args.config]
+    layers = min(args.layers, 20)
+    log(f"bench: generating {layers} layers of the {spec['workload']} workload")
+    t0 = time.perf_counter()
+    w = LayeredWorkload(torch, syn, args.config, spec, layers, dev)
+    stream = torch.cuda.current_stream(dev)
+    phases, bpe, keep = layered_phases(lib, tq, w, stream.cuda_stream)
+    torch.cuda.synchronize()
+    log(f"bench: workload ready in {time.perf_counter() - t0:.1f} s, {w.bytes_resident() / 2**30:.1f} GiB resident")
+    fails0 = tq.encode_wait_failures()
+    for i in range(args.warmup):
+        run_phases(phases)
+        torch.cuda.synchronize()
+        log(f"bench: warmup step {i + 1}/{args.warmup} done")
+    wall, per = timed(torch, phases, args.steps)
+    log(f"bench: {args.steps} timed steps in {wall:.3f} s")
+    total = layers * w.n
+    kernels = {}
+    for j, (name, _, calls) in enumerate(phases):
+        kernels[name] = kernel_entry(name, per[j], len(calls), total // len(calls), bpe[name])
+    dom = max(kernels, key=lambda k: kernels[k]["phase_ms_per_pass"])
+    d = kernels[dom]
+    roofline = {"bound": "hbm", "achieved": d["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": d["frac_of_peak"], "traffic": read_traffic(LAYERED_KERNEL[dom], spec["workload"]),
+                "kernel": dom, "algorithmic_bytes_per_launch": d["algorithmic_bytes_per_call"],
+                "avg_launch_us": d["avg_us_per_call"]}
+    acc = w.acc.cpu().tolist()
+    rel = [((sf - sb) / sb) if sb > 0 else math.nan for sb, sf, _ in acc]
+    fails = tq.encode_wait_failures() - fails0
+    ceiling = copy_ceiling(torch, dev)
+    cpu = None
+    if not args.no_cpu_baseline:
+        try:
+            aff = len(os.sched_getaffinity(0))
+        except AttributeError:
+            aff = os.cpu_count() or 1
+        workers = args.cpu_workers or max(1, min(16, aff))
+        log(f"bench: cpu baseline (oracle) on {workers} workers")
+        cpu = cpu_baseline(torch, w, workers, args.cpu_seconds)
+    ms_step = wall * 1e3 / args.steps
+    step_bytes = sum(bpe[name] * total for name, _, _ in phases)
+    out = {
+        "metric": "guided FP4 fake-quant Gelem/s + achieved HBM GB/s (% of peak), 1 GPU",
+        "value": round(total * args.steps / wall / 1e9, 2),
+        "unit": "Gelem/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": spec["workload"], "layers": layers, "rows": w.rows, "cols": w.cols,
+                   "format": "nvfp4" if w.fmt == NV else "mxfp4", "guide_bits": w.bits,
+                   "global_scale_rows": w.enc_gr if w.fmt == NV else None,
+                   "per_expert_scales": args.config == "moe_expert",
+                   "elements_per_side_per_step": total},
+        "roofline": roofline,
+        "copy_ceiling": ceiling,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "step_GB_s": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "encode_wait_failures": fails,
+        "rel_excess_mse_guided_per_layer": [round(r, 6) for r in rel],
+    }
+    del keep
+    print(json.dumps(out), flush=True)
 
 
 # ---------------------------------------------------------------- main
@@ -541,6 +773,7 @@ def main():
 
     import torch
 
+    import precision_rl_nvfp4_amd as tq
     import synthetic as syn
     from precision_rl_nvfp4_amd import _abi
 
@@ -549,6 +782,9 @@ def main():
         lib.trace_set_encode_batch(args.encode_batch)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.config != "stream":
+        return main_layered(args, torch, syn, tq, lib, dev)
+    fails0 = tq.encode_wait_failures()
     log(f"bench: generating {args.layers} layers x {args.chunks} chunks of [{CHUNK}, {HIDDEN}] pairs")
     t0 = time.perf_counter()
     w = Workload(torch, syn, args.layers, args.chunks, dev)
@@ -660,6 +896,8 @@ def main():
                 "avg_launch_us": d["avg_us_per_call"]}
     rel = [((sf - sb) / sb) if sb > 0 else math.nan for sb, sf, _ in acc]
 
+    fails = tq.encode_wait_failures() - fails0
+    ceiling = copy_ceiling(torch, dev)
     if args.copy_probe:
         src = torch.empty(2**30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -696,9 +934,11 @@ def main():
                    "chunk_tokens": CHUNK, "hidden": HIDDEN, "format": "nvfp4", "guide_bits": 1,
                    "elements_per_side_per_step": elems_step},
         "roofline": roofline,
+        "copy_ceiling": ceiling,
         "cpu_baseline": cpu,
         "kernels": kernels,
         "step_GB_s": round(sum(BPE[k] for k, _, _ in step) * elems_step / (ms_step * 1e-3) / 1e9, 1),
+        "encode_wait_failures": fails,
         "rel_excess_mse_guided_per_layer": [round(r, 6) for r in rel],
         "mismatch": mismatch,
         "variants": variants,

@@ -175,11 +175,13 @@ def _inject_midpoints(x: torch.Tensor, frac: float, block: int, g, device) -> to
     return out.reshape(x.shape).to(torch.bfloat16)
 
 
-def mxfp4_pair(rows: int = 65536, cols: int = HIDDEN, device="cpu", frac: float = 0.001):
+def mxfp4_pair(rows: int = 65536, cols: int = HIDDEN, device="cpu", frac: float = 0.001,
+               layer: int | None = None):
     """MXFP4 workload: the Student-t / log-normal pair plus 0.1% of the
     elements placed exactly on E2M1 rounding midpoints of their block, in the
-    train tensor and, independently, in the rollout tensor."""
-    g = _gen(device, CFG_MX, rows)
+    train tensor and, independently, in the rollout tensor. ``layer`` draws an
+    independent pair per deep layer (None: the single-tensor workload)."""
+    g = _gen(device, CFG_MX, rows) if layer is None else _gen(device, CFG_MX, rows, layer)
     sigma = channel_scales(cols, g, device)
     x_t = (_student_t4((rows, cols), g, device) * sigma).to(torch.bfloat16)
     x_t = _inject_midpoints(x_t, frac, 32, g, device)

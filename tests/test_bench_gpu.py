@@ -46,3 +46,27 @@ def test_bench_json_line_small():
     assert k["encode_guidance_per_layer"]["calls_per_pass"] == 2
     # guided rounding removes the train-rollout FP4 discrepancy on this data
     assert all(x < 0 for x in d["rel_excess_mse_guided_per_layer"])
+    # no bounded wait of the single-pass encode gave up; a measured copy rate
+    assert d["encode_wait_failures"] == 0
+    c = d["copy_ceiling"]
+    assert 0 < c["frac_of_peak"] < 1 and abs(c["GB_s"] - c["bytes_read_plus_written"] / (c["avg_us"] * 1e3)) \
+        <= 0.01 * c["GB_s"]
+
+
+@pytest.mark.parametrize("config,n_layer", [("kv", 2 * 65536 * 256), ("mxfp4", 65536 * 2048),
+                                            ("moe", 65536 * 2048), ("moe_expert", 65536 * 2048)])
+def test_bench_other_workloads(config, n_layer):
+    """--config selects the other workloads: one JSON line of the same
+    contract for a one-layer step of each."""
+    cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--config", config, "--layers", "1", "--steps", "2",
+           "--warmup", "1", "--no-cpu-baseline"]
+    print("bench:", " ".join(cmd[1:]), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=240, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
+    assert len(lines) == 1, r.stdout[-2000:]
+    d = json.loads(lines[0])
+    assert d["config"]["elements_per_side_per_step"] == n_layer
+    assert d["value"] > 0 and d["roofline"]["frac"] > 0 and d["encode_wait_failures"] == 0
+    assert abs(d["value"] - n_layer / (d["ms_per_step"] * 1e-3) / 1e9) <= 0.01 * d["value"]
+    assert all(x < 0 for x in d["rel_excess_mse_guided_per_layer"])
