@@ -93,6 +93,9 @@ extern "C" {
 /* Entries of the mismatch diagnostics of guided_fake_quant_stats. */
 #define TRACE_MISMATCH_COUNTS 32
 
+/* Bytes of the library's own per-device workspace of encode_guidance_noalloc. */
+#define TRACE_NOALLOC_SCRATCH_BYTES (4 << 20)
+
 enum trace_fmt { TRACE_FMT_NVFP4 = 0, TRACE_FMT_MXFP4 = 1 };
 
 enum trace_status {
@@ -217,6 +220,30 @@ int encode_guidance(int fmt, int bits, int64_t rows, int64_t cols, int64_t group
                     const uint16_t* x_rollout, const float* gscale_in, uint8_t* guide,
                     uint8_t* scales, float* gscale_out, uint16_t* y_rollout_opt, void* work,
                     int64_t work_bytes, void* stream);
+
+/*
+ * encode_guidance_noalloc — encode_guidance for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation. Same arguments (without work and work_bytes) and
+ * bit-identical results. Where encode_guidance needs a workspace (NVFP4 with
+ * gscale_out: S from each group's amax), this call uses the library's own
+ * device array of TRACE_NOALLOC_SCRATCH_BYTES (4 MiB) instead; each device
+ * holds its copy from the library's load until the process ends, and the call
+ * itself allocates nothing.
+ * Limit: trace_quant_workspace_bytes(fmt, rows, cols, group_rows) at most
+ * TRACE_NOALLOC_SCRATCH_BYTES, i.e. at most 512 global-scale groups that need
+ * the amax workspace (packed small groups, S supplied and MXFP4 need none);
+ * beyond it the call returns TRACE_ESHAPE and enqueues nothing.
+ * Every call on a device shares that device's array, and the array keeps what
+ * the last call left: each call clears what must start at zero itself (on its
+ * stream, with a kernel), so results never depend on earlier calls. Calls
+ * whose executions overlap on one device (on other streams or threads, or
+ * graphs replayed at the same time) race on the array and give undefined
+ * results: order them.
+ */
+int encode_guidance_noalloc(int fmt, int bits, int64_t rows, int64_t cols, int64_t group_rows,
+                            const uint16_t* x_rollout, const float* gscale_in, uint8_t* guide,
+                            uint8_t* scales, float* gscale_out, uint16_t* y_rollout_opt, void* stream);
 
 /*
  * decode_guidance — training side, compact record: Reconstruct (Algorithm 1

@@ -27,7 +27,8 @@ from typing import NamedTuple, Optional
 import torch
 
 from . import _abi
-from ._abi import MISMATCH_COUNTS, MXFP4, NVFP4, TraceError, load, status_str  # noqa: F401
+from ._abi import (MISMATCH_COUNTS, MXFP4, NOALLOC_SCRATCH_BYTES, NVFP4, TraceError, load,  # noqa: F401
+                   status_str)
 
 MISMATCH_BINS = MISMATCH_COUNTS // 2 - 1   # distances 0..14 per histogram
 
@@ -35,7 +36,7 @@ __all__ = ["NVFP4", "MXFP4", "TraceError", "Quantized", "Guidance", "quantize_rt
            "encode_guidance", "encode_guidance_grouped", "decode_guidance", "guided_fake_quant",
            "guided_fake_quant_stats",
            "discrepancy_stats", "stats_workspace", "quant_workspace", "guided_stats_workspace",
-           "encode_wait_failures",
+           "encode_wait_failures", "encode_guidance_noalloc", "NOALLOC_SCRATCH_BYTES",
            "grouped_workspace",
            "derived_metrics", "mismatch_summary", "fmt_id", "BLOCK", "MISMATCH_COUNTS"]
 
@@ -197,6 +198,37 @@ def encode_guidance(x_rollout: torch.Tensor, fmt="nvfp4", bits: int = 1,
     c, s, g, yy = _rtn_call("encode_guidance", x_rollout, f, bits, group_rows, gscale,
                             (rows, gcols), with_y, guide, scales, gscale_out, y, work)
     return Guidance(f, int(bits), c, s, g, yy, int(group_rows))
+
+
+def encode_guidance_noalloc(x_rollout: torch.Tensor, fmt="nvfp4", bits: int = 1,
+                            gscale: Optional[torch.Tensor] = None, group_rows: int = 0, *,
+                            guide: torch.Tensor, scales: torch.Tensor,
+                            gscale_out: Optional[torch.Tensor] = None,
+                            y: Optional[torch.Tensor] = None) -> Guidance:
+    """encode_guidance into caller buffers with no workspace argument: where a
+    workspace is needed the library uses its own per-device scratch array (up
+    to NOALLOC_SCRATCH_BYTES; larger calls raise). Nothing is allocated, so it
+    can run where allocation cannot (e.g. under graph capture). Calls that
+    overlap on one device share that array and must be ordered."""
+    f = fmt_id(fmt)
+    rows, cols = _check_x(x_rollout, "x_rollout")
+    if bits not in (1, 2, 3, 4):
+        raise ValueError("bits must be 1, 2, 3 or 4")
+    G = _groups(rows, group_rows)
+    guide = _empty((rows, cols * bits // 8), torch.uint8, x_rollout, guide)
+    scales = _empty((rows, cols // BLOCK[f]), torch.uint8, x_rollout, scales)
+    if f == NVFP4 and gscale is None:
+        if gscale_out is None:
+            raise ValueError("gscale_out (float32 [G, 2]) is required when gscale is not given")
+        gscale_out = _empty((G, 2), torch.float32, x_rollout, gscale_out)
+    else:
+        gscale_out = None
+    if y is not None:
+        y = _empty((rows, cols), torch.bfloat16, x_rollout, y)
+    _abi.call("encode_guidance_noalloc", f, int(bits), rows, cols, group_rows, _ptr(x_rollout), _ptr(gscale),
+              _ptr(guide), _ptr(scales), _ptr(gscale_out), _ptr(y), _stream(x_rollout))
+    return Guidance(f, int(bits), guide, scales, gscale if gscale is not None else gscale_out, y,
+                    int(group_rows))
 
 
 def _check_offsets(offsets: torch.Tensor, x: torch.Tensor) -> int:

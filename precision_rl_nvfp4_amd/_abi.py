@@ -15,6 +15,7 @@ OK, EINVAL, ESHAPE, EALIGN, EALIAS, EDEVICE, ELAUNCH, EBUSY = 0, -1, -2, -3, -4,
 NVFP4, MXFP4 = 0, 1
 ABI_VERSION = 8
 MISMATCH_COUNTS = 32
+NOALLOC_SCRATCH_BYTES = 4 << 20
 
 _i64 = ctypes.c_int64
 _int = ctypes.c_int
@@ -34,6 +35,8 @@ SIGNATURES = {
     "quantize_rtn": (_int, [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp]),
     # fmt, bits, rows, cols, group_rows, x_r, gscale_in, guide, scales, gscale_out, y_r, work, work_bytes, stream
     "encode_guidance": (_int, [_int, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp]),
+    # fmt, bits, rows, cols, group_rows, x_r, gscale_in, guide, scales, gscale_out, y_r, stream
+    "encode_guidance_noalloc": (_int, [_int, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     # fmt, bits, rows, cols, group_rows, x_t, guide, scales, gscale, ref_codes, stream
     "decode_guidance": (_int, [_int, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
     # fmt, bits, rows, cols, group_rows, x_t, guide, scales, gscale, y, codes, stream

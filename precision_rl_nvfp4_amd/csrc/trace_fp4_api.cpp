@@ -18,6 +18,7 @@
 #include "trace_fp4_internal.h"
 
 static_assert(TRACE_MISMATCH_COUNTS == tfp4::kMismatchCounts, "mismatch count layout");
+static_assert(TRACE_NOALLOC_SCRATCH_BYTES == tfp4::kScratchBytes, "scratch size");
 
 namespace {
 
@@ -108,11 +109,13 @@ using tfp4::check_device;
 
 int launched(hipError_t e) { return e == hipSuccess ? TRACE_OK : TRACE_ELAUNCH; }
 
-// Shared by quantize_rtn and encode_guidance. `plane_bytes` is the size of
-// the code or bit plane, `plane_align` its alignment.
+// Shared by quantize_rtn, encode_guidance and encode_guidance_noalloc.
+// `plane_bits` gives the size and alignment of the code or bit plane. With
+// use_scratch the workspace is the library's own device array instead of
+// `work` (which is then ignored), up to tfp4::kScratchBytes.
 int run_rtn(int fmt, int plane_bits, int64_t rows, int64_t cols, int64_t group_rows,
             const uint16_t* x, const float* gin, uint8_t* plane, uint8_t* scales, float* gout,
-            uint16_t* y, void* work, int64_t work_bytes, void* stream) {
+            uint16_t* y, void* work, int64_t work_bytes, void* stream, bool use_scratch = false) {
   CallShape cs;
   int st = shape_of(fmt, rows, cols, group_rows, &cs);
   if (st != TRACE_OK) return st;
@@ -125,8 +128,13 @@ int run_rtn(int fmt, int plane_bits, int64_t rows, int64_t cols, int64_t group_r
   if (n > 0 && (x == nullptr || plane == nullptr || scales == nullptr)) return TRACE_EINVAL;
   const int64_t wneed = gout != nullptr && n > 0 ? tfp4::quant_work_bytes(fmt, cs.sh) : 0;
   const bool need_work = wneed > 0;
-  if (need_work && work == nullptr) return TRACE_EINVAL;
-  if (work_bytes < wneed) return TRACE_ESHAPE;
+  if (use_scratch) {
+    work = nullptr;
+    if (wneed > tfp4::kScratchBytes) return TRACE_ESHAPE;
+  } else {
+    if (need_work && work == nullptr) return TRACE_EINVAL;
+    if (work_bytes < wneed) return TRACE_ESHAPE;
+  }
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(plane, guide_align(plane_bits)) ||
       !aligned(gin, 4) ||
       !aligned(gout, 4) || (need_work && !aligned(work, 8)))
@@ -137,6 +145,7 @@ int run_rtn(int fmt, int plane_bits, int64_t rows, int64_t cols, int64_t group_r
   if (any_alias(outs, ins)) return TRACE_EALIAS;
   st = check_device();
   if (st != TRACE_OK) return st;
+  if (use_scratch && need_work && tfp4::scratch_of_current_device(&work) != hipSuccess) return TRACE_ELAUNCH;
   return launched(tfp4::launch_quantize(fmt, plane_bits, cs.sh, x, gin, gout, plane, scales, y,
                                         need_work ? work : nullptr,
                                         static_cast<hipStream_t>(stream)));
@@ -275,6 +284,14 @@ int encode_guidance(int fmt, int bits, int64_t rows, int64_t cols, int64_t group
   if (!valid_fmt(fmt) || bits < 1 || bits > 4) return TRACE_EINVAL;
   return run_rtn(fmt, bits, rows, cols, group_rows, x_rollout, gscale_in, guide, scales,
                  gscale_out, y_rollout_opt, work, work_bytes, stream);
+}
+
+int encode_guidance_noalloc(int fmt, int bits, int64_t rows, int64_t cols, int64_t group_rows,
+                            const uint16_t* x_rollout, const float* gscale_in, uint8_t* guide,
+                            uint8_t* scales, float* gscale_out, uint16_t* y_rollout_opt, void* stream) {
+  if (!valid_fmt(fmt) || bits < 1 || bits > 4) return TRACE_EINVAL;
+  return run_rtn(fmt, bits, rows, cols, group_rows, x_rollout, gscale_in, guide, scales, gscale_out,
+                 y_rollout_opt, nullptr, 0, stream, true);
 }
 
 int decode_guidance(int fmt, int bits, int64_t rows, int64_t cols, int64_t group_rows,

@@ -94,6 +94,12 @@ int64_t set_wait_limit(int64_t polls);
 // library was loaded (a synchronous device-to-host copy).
 hipError_t read_wait_failures(uint64_t* out);
 
+// Bytes of the library's own device scratch array (one per device), the
+// workspace of encode_guidance_noalloc, and its address on the current
+// device (looked up once per device; allocates nothing).
+constexpr int64_t kScratchBytes = (int64_t)4 << 20;
+hipError_t scratch_of_current_device(void** out);
+
 // Deterministic float64 sums of discrepancy_stats into acc3.
 hipError_t launch_stats(int64_t n, const uint16_t* xt, const uint16_t* xr, const uint16_t* yt,
                         const uint16_t* yr, double* acc3, int accumulate, double* partials,

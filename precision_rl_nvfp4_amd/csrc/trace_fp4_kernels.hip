@@ -48,6 +48,15 @@
 
 #include "trace_fp4_internal.h"
 
+// Library-owned device memory: one copy per device, allocated when the code
+// object is loaded there and held until the process ends. Host code reaches it
+// only through the address hipGetSymbolAddress gives on each device (the names
+// below stand for host-side shadows in host code).
+//   g_wait_fails  count of the single-pass encode's bounded waits that gave up
+//   scratch       the workspace of encode_guidance_noalloc (no caller memory)
+static __device__ unsigned long long g_wait_fails;
+static __device__ __align__(256) uint8_t scratch[tfp4::kScratchBytes];
+
 namespace tfp4 {
 namespace {
 
@@ -1750,35 +1759,6 @@ int64_t onepass_capacity(const void* k, int dev) {
   return cap;
 }
 
-// Count of the single-pass encode's bounded waits that gave up, per device,
-// since the library was loaded (read by trace_encode_wait_failures).
-__device__ unsigned long long g_wait_fails;
-
-// Device addresses of the library's own device variables, looked up once per
-// device with that device current (in host code a __device__ variable's name
-// stands for a host-side shadow, not for its device memory).
-struct DeviceSyms {
-  bool ready = false;
-  unsigned long long* fails = nullptr;
-};
-std::mutex g_syms_mu;
-DeviceSyms g_syms[64];
-
-hipError_t device_syms(int dev, const DeviceSyms** out) {
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  std::lock_guard<std::mutex> lock(g_syms_mu);
-  DeviceSyms& d = g_syms[dev];
-  if (!d.ready) {
-    void* p = nullptr;
-    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_wait_fails));
-    if (e != hipSuccess) return e;
-    d.fails = static_cast<unsigned long long*>(p);
-    d.ready = true;
-  }
-  *out = &d;
-  return hipSuccess;
-}
-
 // Single-pass launches of one process on one device run one after another,
 // whatever their streams: each needs the whole device resident at once, so
 // two running side by side could each hold part of it and wait on the other
@@ -1792,13 +1772,48 @@ hipError_t device_syms(int dev, const DeviceSyms** out) {
 // captured into a graph (a graph runs its nodes in order).
 struct OnePassOrder {
   std::mutex mu;
-  hipEvent_t ev = nullptr;
+  hipEvent_t ev = nullptr;     // created once per device, with the device's symbols
   bool multi = false;          // launches seen on more than one stream
   bool recorded = false;       // ev holds the last launch (multi mode)
   bool any = false;            // a launch happened
   hipStream_t last = nullptr;  // stream of the last launch
 };
 OnePassOrder g_onepass_order[64];
+
+// Per-device set-up, done once with the device current: the device addresses
+// of the library's device variables, and the single-pass ordering event (so
+// no call allocates or creates anything afterwards).
+struct DeviceSyms {
+  bool ready = false;
+  unsigned long long* fails = nullptr;
+  uint8_t* scratch = nullptr;
+};
+std::mutex g_syms_mu;
+DeviceSyms g_syms[64];
+
+hipError_t device_syms(int dev, const DeviceSyms** out) {
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_syms_mu);
+  DeviceSyms& d = g_syms[dev];
+  if (!d.ready) {
+    void* p = nullptr;
+    void* q = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_wait_fails));
+    if (e != hipSuccess) return e;
+    if ((e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+    OnePassOrder& ord = g_onepass_order[dev];
+    {
+      std::lock_guard<std::mutex> olock(ord.mu);
+      if (ord.ev == nullptr && (e = hipEventCreateWithFlags(&ord.ev, hipEventDisableTiming)) != hipSuccess)
+        return e;
+    }
+    d.fails = static_cast<unsigned long long*>(p);
+    d.scratch = static_cast<uint8_t*>(q);
+    d.ready = true;
+  }
+  *out = &d;
+  return hipSuccess;
+}
 
 // Launches the single-pass encode when it applies; *used tells whether it did.
 hipError_t launch_onepass(int plane_mode, bool wy, const Shape& sh, const QuantArgs& qa, void* work,
@@ -1819,9 +1834,11 @@ hipError_t launch_onepass(int plane_mode, bool wy, const Shape& sh, const QuantA
   const int64_t Tfit = min((cap - 1) / Q, (int64_t)kOnePassTiles);
   const int64_t L = ((sh.upg + Tfit - 1) / Tfit + 63) / 64 * 64;
   const int64_t T = (sh.upg + L - 1) / L;
-  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
-  hipError_t e = hipStreamIsCapturing(stream, &capture);
+  const DeviceSyms* syms = nullptr;
+  hipError_t e = device_syms(dev, &syms);
   if (e != hipSuccess) return e;
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  if ((e = hipStreamIsCapturing(stream, &capture)) != hipSuccess) return e;
   OnePassOrder& ord = g_onepass_order[dev];
   std::unique_lock<std::mutex> lock(ord.mu, std::defer_lock);
   if (capture == hipStreamCaptureStatusNone) {
@@ -1829,8 +1846,6 @@ hipError_t launch_onepass(int plane_mode, bool wy, const Shape& sh, const QuantA
     if (ord.any && ord.last != stream && !ord.multi) {
       // first launch on a second stream: the previous launch left no event,
       // so one is recorded now on its stream (after everything enqueued there)
-      if (ord.ev == nullptr && (e = hipEventCreateWithFlags(&ord.ev, hipEventDisableTiming)) != hipSuccess)
-        return e;
       if ((e = hipEventRecord(ord.ev, ord.last)) != hipSuccess) return e;
       ord.multi = true;
       ord.recorded = true;
@@ -1845,8 +1860,6 @@ hipError_t launch_onepass(int plane_mode, bool wy, const Shape& sh, const QuantA
   a.T = (int)T;
   a.Q = (int)Q;
   a.L = (int)L;
-  const DeviceSyms* syms = nullptr;
-  if ((e = device_syms(dev, &syms)) != hipSuccess) return e;
   a.slots = static_cast<uint32_t*>(work);
   a.sword = a.slots + sh.groups * kPartMax;
   a.fails = syms->fails;
@@ -2083,6 +2096,16 @@ hipError_t launch_stats(int64_t n, const uint16_t* xt, const uint16_t* xr, const
 namespace tfp4 {
 int64_t set_encode_batch(int64_t groups) { return g_encode_batch.exchange(groups); }
 int64_t set_wait_limit(int64_t polls) { return g_wait_limit.exchange(polls); }
+
+hipError_t scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const DeviceSyms* syms = nullptr;
+  if ((e = device_syms(dev, &syms)) != hipSuccess) return e;
+  *out = syms->scratch;
+  return hipSuccess;
+}
 
 hipError_t read_wait_failures(uint64_t* out) {
   int dev = -1;

@@ -65,6 +65,26 @@ def test_encode_batch_setting(lib):
     assert lib.trace_set_encode_batch(0) == 0
 
 
+def test_noalloc_encode_limits(lib):
+    """encode_guidance_noalloc: its scratch holds 512 groups' amax workspace
+    (8192 bytes each); more is ESHAPE before any device use, at most reaches
+    the device check. Argument errors as encode_guidance."""
+    assert _abi.NOALLOC_SCRATCH_BYTES == 4 << 20
+    f = lib.encode_guidance_noalloc
+    # rows of 48 columns, one group per row (6 units: not packed, needs the workspace)
+    assert lib.trace_quant_workspace_bytes(0, 512, 48, 1) == _abi.NOALLOC_SCRATCH_BYTES
+    assert f(0, 1, 513, 48, 1, A, None, B, C, D, None, None) == _abi.ESHAPE
+    assert f(0, 1, 512, 48, 1, A, None, B, C, D, None, None) == _abi.EDEVICE
+    # the limit only counts the workspace: S supplied, packed groups, MXFP4 need none
+    assert f(0, 1, 4096, 48, 1, A, E, B, C, None, None, None) == _abi.EDEVICE
+    assert f(0, 1, 4096, 64, 1, A, None, B, C, D, None, None) == _abi.EDEVICE
+    assert f(1, 1, 4096, 64, 0, A, None, B, C, None, None, None) == _abi.EDEVICE
+    assert f(0, 5, 4, 32, 0, A, None, B, C, D, None, None) == _abi.EINVAL
+    assert f(0, 1, 4, 32, 0, A, E, B, C, D, None, None) == _abi.EINVAL      # gscale_in and out
+    assert f(0, 1, 4, 32, 0, A + 8, None, B, C, D, None, None) == _abi.EALIGN
+    assert f(0, 1, 4, 32, 0, A, None, B, C, A + 4, None, None) == _abi.EALIAS
+
+
 def test_wait_failure_query_without_a_device(lib):
     """The give-up count needs a gfx950 device; a NULL output is rejected first."""
     assert lib.trace_encode_wait_failures(None) == _abi.EINVAL
