@@ -681,6 +681,33 @@ def layered_phases(lib, tq, w, stream):
     return phases, bpe, keep
 
 
+def kv_per_tensor_phases(lib, tq, w, stream):
+    """The KV workload's K and V tensors one call each: encode_guidance
+    (bits=4, one S per tensor) and guided_fake_quant_stats, 2 x layers calls
+    of [65536, 256] per phase."""
+    R = w.rows // 2
+    C, b = w.cols, w.bits
+    qb = int(lib.trace_quant_workspace_bytes(NV, R, C, 0))
+    sb = int(lib.trace_guided_stats_workspace_bytes(NV, R, C, 0))
+    qwork = tq._workspace(qb, w.xt.device, None)
+    swork = tq._workspace(sb, w.xt.device, None)
+    enc, gst = [], []
+    for i in range(w.layers):
+        for k in (0, 1):
+            rs = slice(k * R, (k + 1) * R)
+            enc.append((NV, b, R, C, 0, w.xr[i, rs].data_ptr(), None, w.guide[i, rs].data_ptr(),
+                        w.scales[i, rs].data_ptr(), w.gscale[i, k].data_ptr(), None, qwork.data_ptr(), qb, stream))
+            gst.append((NV, b, R, C, 0, w.xt[i, rs].data_ptr(), w.xr[i, rs].data_ptr(), w.guide[i, rs].data_ptr(),
+                        w.scales[i, rs].data_ptr(), w.gscale[i, k].data_ptr(), w.yt[i, rs].data_ptr(), None,
+                        w.acc[i].data_ptr(), None, k, swork.data_ptr(), sb, stream))
+    plane = b / 8 + 1 / 16
+    phases = [("encode_guidance_per_tensor", lib.encode_guidance, enc),
+              ("guided_fake_quant_stats_per_tensor", lib.guided_fake_quant_stats, gst)]
+    bpe = {"encode_guidance_per_tensor": 2 + plane + 8 / (R * C),
+           "guided_fake_quant_stats_per_tensor": 2 + 2 + plane + 4 / (R * C) + 2}
+    return phases, bpe, [qwork, swork]
+
+
 LAYERED_KERNEL = {"encode_guidance": "quantize_kernel", "guided_fake_quant_stats": "guided_kernel",
                   "encode_guidance_grouped": "quantize_kernel", "guided_fake_quant_grouped": "guided_kernel",
                   "discrepancy_stats": "stats_partial_kernel"}
@@ -718,6 +745,19 @@ def main_layered(args, torch, syn, tq, lib, dev):
                 "avg_launch_us": d["avg_us_per_call"]}
     acc = w.acc.cpu().tolist()
     rel = [((sf - sb) / sb) if sb > 0 else math.nan for sb, sf, _ in acc]
+    variants = None
+    if args.config == "kv":
+        # The same K and V tensors one call per tensor (40 calls of [65536,
+        # 256], each its own global scale), outside the step: the calls a
+        # cache that encodes each tensor as it fills would make.
+        variants = {}
+        ph, bp, keep1 = kv_per_tensor_phases(lib, tq, w, stream.cuda_stream)
+        run_phases(ph)
+        _, per_v = timed(torch, ph, max(3, args.steps // 2))
+        for j, (name, _, calls) in enumerate(ph):
+            variants[name] = kernel_entry(name, per_v[j], len(calls), total // len(calls), bp[name])
+        del keep1
+        log("bench: per-tensor KV calls timed")
     fails = tq.encode_wait_failures() - fails0
     ceiling = copy_ceiling(torch, dev)
     cpu = None
@@ -756,6 +796,7 @@ def main_layered(args, torch, syn, tq, lib, dev):
         "step_GB_s": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "encode_wait_failures": fails,
         "rel_excess_mse_guided_per_layer": [round(r, 6) for r in rel],
+        "variants": variants,
     }
     del keep
     print(json.dumps(out), flush=True)
