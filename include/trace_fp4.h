@@ -124,7 +124,11 @@ const char* trace_status_str(int status);
  * chip while each group's amax is combined (it needs 2 resident workgroups
  * of 768 threads per CU; otherwise, for larger groups, and for a call of a
  * single group, which is faster in two launches, the two-pass schedule
- * below is used).
+ * below is used). Row-offset groups (encode_guidance_grouped, at most 4096
+ * groups) take one pass too, over a table of 32768-element tiles built on
+ * the device from the offsets; when a group has more tiles than the launch
+ * has tile workgroups, that launch reads every tile's maxima first and then
+ * quantizes (still one launch, two reads of the input).
  * n > 0 forces two passes (amax, then quantize) with n groups per batch: each
  * launch quantizes one batch while it reads the next batch for its amax
  * (n >= G: one amax pass over every group, then one quantize pass); with 0,
@@ -368,7 +372,9 @@ int64_t trace_grouped_workspace_bytes(int fmt, int64_t rows, int64_t cols, int64
 /* encode_guidance with one global scale per row-offset group: gscale_out
  * receives {S, A} of group g at [2g], [2g + 1] (required for NVFP4). Other
  * arguments as in encode_guidance (bits 1..4; bits = 4 with y_rollout_opt
- * is exactly quantize_rtn per group). */
+ * is exactly quantize_rtn per group). Scheduled as trace_set_encode_batch
+ * describes (one pass for at most 4096 groups, else two); the results are
+ * bit-identical either way. */
 int encode_guidance_grouped(int fmt, int bits, int64_t rows, int64_t cols, int64_t groups,
                             const int64_t* row_offsets, const uint16_t* x_rollout, uint8_t* guide,
                             uint8_t* scales, float* gscale_out, uint16_t* y_rollout_opt, void* work,

@@ -788,80 +788,47 @@ __global__ __launch_bounds__(quant_threads(SSRC, PACK)) void quantize_kernel(Qua
   }
 }
 
-// Single-pass NVFP4 encode with S from each group's amax. The grid never
-// exceeds the number of workgroups the device holds at once (2 per CU), so
-// all of them are resident: Q sets of T workgroups (T tiles per group, sized
-// at launch so every CU gets the same work) take groups q, q + Q, ... in
-// turn, one tile per workgroup per group, kept on chip; one more workgroup
-// combines.
-//
-// A tile workgroup is eleven data waves and one control wave (twelve waves:
-// with two workgroups per CU every SIMD holds six, at most 85 VGPRs each).
-// The data waves load, hold and quantize the tiles;
-// the control wave does every wait on other workgroups. This split matters:
-// a wait on memory is a wait on the wave's whole vector-memory counter,
-// which also covers the tile loads in flight, so a data wave that polled
-// would stall until its next tile had arrived.
-//   * Data waves: a tile's max goes to its slot, tagged (bit 31), by one
-//     store from the last of the eleven waves to reduce it (an LDS counter),
-//     as soon as the tile has arrived; no barrier is involved.
-//   * Combining workgroup (the last one): its first wave takes the groups in
-//     order, waits for each group's T slots, derives S and A, writes {S, A}
-//     to gout and publishes S (nonzero) to kSCopies words. It runs ahead of
-//     the tiles, so S is combined as soon as the last tile max of its group
-//     is in, about a round before it is needed.
-//   * Control wave: waits for one S word of the group and builds the table of
-//     block factors under S.
-//   * One barrier per group: the data waves quantize group g from its table
-//     while the control wave prepares group g + Q's in the other half of a
-//     double buffer.
-// Three tiles are on chip per data wave: the one being quantized (in LDS,
-// each thread keeping its own words), the next one (registers, max
-// published) and the one after (registers, loads in flight). The two
-// register tiles swap roles each round; within a round, unit j of the
-// stashed tile is quantized, its LDS words refilled from the next tile and
-// that register reloaded from the tile three rounds ahead, so the loads
-// leave spread over the round rather than in one burst (a burst queues
-// ahead of every other access of the CU, the slot stores and S polls
-// included). Tiles are read through a buffer resource whose range is the
-// tile, so every load instruction is issued whatever the tile's length and
-// each wait covers exactly the older tile.
-// Slots and S words are zeroed by a fill kernel before the launch. Every wait
-// is bounded: past spin_max polls the waiting wave stops waiting, counts the
-// give-up in *fails and takes what it waited for from the input itself (the
-// maxima of the tiles whose slots were not tagged, or the whole group's
-// amax), so the grid always drains and the results stay exact; only the
-// time grows.
 struct OnePassArgs {
   const uint4* x;
-  int upg;                   // units per group
+  int upg;                   // units per group (equal groups)
   int groups;
-  int T;                     // tiles (workgroups) per group
-  int Q;                     // groups in flight
+  int T;                     // equal groups: tiles (workgroups) per group; row-offset groups: tile workgroups W
+  int Q;                     // equal groups: groups in flight
   int L;                     // units per tile (a multiple of 64, <= kOPTile); a group's last tile may be shorter
-  uint32_t* slots;           // [groups][kPartMax] tagged tile maxima
-  uint32_t* sword;           // [groups][kSCopies][64]: S bits at [.][c][0], 0 until published
+  int rounds;                // row-offset groups: rounds of every tile workgroup (even)
+  int copies;                // published copies of each S (kSCopies for equal groups, 1 for row-offset groups)
+  uint32_t* slots;           // tagged tile maxima: [groups][kPartMax] (equal groups) or [entries] (row-offset groups)
+  uint32_t* sword;           // [groups][copies][64]: S bits at [.][c][0], 0 until published
   unsigned long long* fails; // bounded waits that gave up (device-wide count)
   int spin_max;              // polls before a wait gives up
   float* gout;
   uint8_t* plane;
   uint8_t* scales;
   uint4* y;
+  // row-offset groups: the tile table built on the device from the offsets
+  const int64_t* offs;       // [groups + 1] row offsets (clamped, nondecreasing)
+  const int32_t* tstart;     // [groups + 1] first table entry of each group
+  const int4* desc;          // [entries] tile descriptors {first unit (lo, hi), length, group}; group -1 past the last
+  const int32_t* big;        // nonzero when a group has more tiles than stay on chip (see below)
+  int entries;
+  int upr;                   // units per row
 };
 
 constexpr int kSpinMax = 1 << 22;      // default bound of every wait, in polls (~0.25 s)
 constexpr int kSCopies = 16;            // copies of each published S, one per 256-byte line
 constexpr int kOPDataWaves = 11;                     // data waves per workgroup
 constexpr int kOPData = kOPDataWaves * 64;           // data threads
-constexpr int kOnePassThreads = kOPData + 64;        // + the control wave: 8 waves, 2 per SIMD
+constexpr int kOnePassThreads = kOPData + 64;        // + the control wave: 12 waves, 6 per SIMD with 2 per CU
 constexpr int kOPUnits = 6;                          // units per data thread and tile
 constexpr int kOPTile = kOPData * kOPUnits;          // most units per tile (4224, a multiple of 64)
+constexpr int kOPTableTile = 4096;                   // tile of row-offset groups (a table entry)
 // Every workgroup must become resident at once. Its waves are spread over a
 // CU's 4 SIMDs, so a wave count that is not a multiple of 4 fills them
 // unevenly, and a second workgroup per CU may not fit even where the
 // occupancy query says it does (14 waves per workgroup: the launch stalls on
 // its bounded waits).
 static_assert((kOPDataWaves + 1) % 4 == 0, "single-pass workgroups must fill the 4 SIMDs of a CU evenly");
+static_assert(kOPTableTile <= kOPTile && kOPTableTile % 64 == 0, "table tiles fit a single-pass tile");
 constexpr int kSlotsPerLane = kPartMax / 64;
 constexpr int kRawBufferWord3 = 0x00020000;     // buffer descriptor word 3: untyped 32-bit data, no swizzle
 constexpr int kBufferNT = 2;                    // buffer access cache policy: nontemporal
@@ -889,49 +856,285 @@ __device__ __forceinline__ uint32_t wave_units_amax(const uint4* xg, int64_t u0,
   return wave_max_u32(m);
 }
 
-template <int PLANE, bool WY>
+// The tile a workgroup handles in round r: its group (-1 for a padding
+// round), its first unit in x, its length in units and its slot.
+//   Equal groups: workgroup (q, t) takes tile t of groups q, q + Q, q + 2Q, ...
+//   Row-offset groups: workgroup w takes table entries w, w + W, w + 2W, ...
+//     (entries are the tiles of the groups in order, kOPTableTile units each).
+struct OPTile {
+  int g;
+  int len;
+  int64_t base;
+  int64_t slot;
+};
+
+template <bool TABLE>
+__device__ __forceinline__ OPTile op_tile(const OnePassArgs& a, int q, int t, int r) {
+  OPTile d;
+  if constexpr (TABLE) {
+    const int e = t + r * a.T;
+    d.g = -1;
+    d.len = 0;
+    d.base = 0;
+    d.slot = e;
+    if (e < a.entries) {
+      const int4 td = a.desc[e];
+      if (td.w >= 0) {
+        d.g = td.w;
+        d.base = (int64_t)(((uint64_t)(uint32_t)td.y << 32) | (uint32_t)td.x);
+        d.len = td.z;
+      }
+    }
+  } else {
+    const int g = q + r * a.Q;
+    const int t0u = t * a.L;
+    const bool in = g < a.groups;
+    d.g = in ? g : -1;
+    d.len = in ? min(a.upg - t0u, a.L) : 0;
+    d.base = (int64_t)(in ? g : 0) * a.upg + t0u;
+    d.slot = (int64_t)g * kPartMax + t;
+  }
+  return d;
+}
+
+// The unit range [u0, u1) of group g in x.
+template <bool TABLE>
+__device__ __forceinline__ void op_group_range(const OnePassArgs& a, int g, int64_t& u0, int64_t& u1) {
+  if constexpr (TABLE) {
+    u0 = a.offs[g] * a.upr;
+    u1 = a.offs[g + 1] * a.upr;
+  } else {
+    u0 = (int64_t)g * a.upg;
+    u1 = u0 + a.upg;
+  }
+}
+
+// First slot and number of slots (tiles) of group g.
+template <bool TABLE>
+__device__ __forceinline__ void op_group_slots(const OnePassArgs& a, int g, int64_t& s0, int64_t& ns) {
+  if constexpr (TABLE) {
+    s0 = a.tstart[g];
+    ns = a.tstart[g + 1] - s0;
+  } else {
+    s0 = (int64_t)g * kPartMax;
+    ns = a.T;
+  }
+}
+
+// Unit range [u0, u1) of the tile behind slot `slot`, the i-th of group g.
+template <bool TABLE>
+__device__ __forceinline__ void op_slot_units(const OnePassArgs& a, int g, int64_t slot, int64_t i, int64_t& u0,
+                                              int64_t& u1) {
+  if constexpr (TABLE) {
+    const int4 td = a.desc[slot];
+    u0 = (int64_t)(((uint64_t)(uint32_t)td.y << 32) | (uint32_t)td.x);
+    u1 = u0 + td.z;
+  } else {
+    u0 = (int64_t)g * a.upg + i * a.L;
+    u1 = min(u0 + a.L, (int64_t)(g + 1) * a.upg);
+  }
+}
+
+// Max over each row of 16 lanes, returned to every lane of the row; the
+// row's lanes must be active.
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t m) {
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp((int)m, (int)m, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp((int)m, (int)m, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp((int)m, (int)m, 0x124, 0xF, 0xF, false));  // row_ror:4
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp((int)m, (int)m, 0x128, 0xF, 0xF, false));  // row_ror:8
+  return m;
+}
+
+// S and A of group g from its amax bits gm: {S, A} to gout and S to the
+// group's published words (lane l < copies stores copy l).
+template <bool TABLE>
+__device__ __forceinline__ void publish_scale(const OnePassArgs& a, int g, uint32_t gm, int lane) {
+  const float A = __uint_as_float(gm << 16);
+  const float S = global_scale(A);
+  if (lane < a.copies) store_agent(&a.sword[((int64_t)g * a.copies + lane) * 64], __float_as_uint(S));
+  if (lane == 0) {
+    a.gout[2 * (int64_t)g] = S;
+    a.gout[2 * (int64_t)g + 1] = A;
+  }
+}
+
+// Groups of at most this many tiles are combined by a 16-lane segment.
+constexpr int kSegSlots = 64;
+
+// A tile descriptor the control wave left in LDS, read into scalar registers
+// (it is the same for every lane).
+__device__ __forceinline__ OPTile uniform_tile(const OPTile& t) {
+  OPTile d;
+  d.g = __builtin_amdgcn_readfirstlane(t.g);
+  d.len = __builtin_amdgcn_readfirstlane(t.len);
+  const uint64_t b = (uint64_t)t.base, s = (uint64_t)t.slot;
+  d.base = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(b >> 32)) << 32) |
+                     (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b));
+  d.slot = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(s >> 32)) << 32) |
+                     (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)s));
+  return d;
+}
+
+// Single-pass NVFP4 encode with S from each group's amax. The grid never
+// exceeds the number of workgroups the device holds at once (2 per CU), so
+// all of them are resident. Equal groups (TABLE false): Q sets of T
+// workgroups (T tiles per group, sized at launch so every CU gets the same
+// work) take groups q, q + Q, ... in turn, one tile per workgroup per group,
+// kept on chip. Row-offset groups (TABLE true, e.g. one global scale per
+// expert): W workgroups take the table's tiles w, w + W, ... in turn. One
+// more workgroup combines.
+//
+// A tile workgroup is eleven data waves and one control wave (twelve waves:
+// with two workgroups per CU every SIMD holds six, at most 85 VGPRs each).
+// The data waves load, hold and quantize the tiles;
+// the control wave does every wait on other workgroups. This split matters:
+// a wait on memory is a wait on the wave's whole vector-memory counter,
+// which also covers the tile loads in flight, so a data wave that polled
+// would stall until its next tile had arrived.
+//   * Data waves: a tile's max goes to its slot, tagged (bit 31), by one
+//     store from the last of the eleven waves to reduce it (an LDS counter),
+//     as soon as the tile has arrived; no barrier is involved.
+//   * Combining workgroup (the last one): waits for each group's slots,
+//     derives S and A, writes {S, A} to gout and publishes S (nonzero) to
+//     `copies` words; its first wave takes the groups of many tiles in order,
+//     the other waves the small groups, 16 lanes each. It runs ahead of the
+//     tiles, so S is combined as soon as the last tile max of its group is
+//     in, about a round before it is needed.
+//   * Control wave: waits for one S word of the round's group and builds the
+//     table of block factors under S.
+//   * One barrier per round: the data waves quantize a tile from its table
+//     while the control wave prepares the next round's in the other half of
+//     a double buffer.
+// Three tiles are on chip per data wave: the one being quantized (in LDS,
+// each thread keeping its own words), the next one (registers, max
+// published) and the one after (registers, loads in flight). The two
+// register tiles swap roles each round; within a round, unit j of the
+// stashed tile is quantized, its LDS words refilled from the next tile and
+// that register reloaded from the tile three rounds ahead, so the loads
+// leave spread over the round rather than in one burst (a burst queues
+// ahead of every other access of the CU, the slot stores and S polls
+// included). Tiles are read through a buffer resource whose range is the
+// tile, so every load instruction is issued whatever the tile's length and
+// each wait covers exactly the older tile.
+// A round's group is complete (all its slots published) once every
+// workgroup has finished the round before, as long as a group spans at most
+// one tile more than there are tile workgroups: always for equal groups
+// (T <= W), and for row-offset groups whenever *big is 0. When a row-offset
+// group is larger (the prep kernel sets *big; the routing may send most rows
+// to one expert), every workgroup first reads all its tiles once to publish
+// their maxima (one barrier per round), then runs the rounds above without
+// publishing: the input is read twice, as in the two-pass schedule.
+// Slots and S words are zeroed by a fill kernel before the launch. Every wait
+// is bounded: past spin_max polls the waiting wave stops waiting, counts the
+// give-up in *fails and takes what it waited for from the input itself (the
+// maxima of the tiles whose slots were not tagged, or the whole group's
+// amax), so the grid always drains and the results stay exact; only the
+// time grows.
+template <int PLANE, bool WY, bool TABLE>
 __global__ __launch_bounds__(kOnePassThreads, 6) void onepass_encode_kernel(OnePassArgs a) {
   __shared__ float2 lut[2][128];
   __shared__ float sS[2];
+  __shared__ OPTile ring[8];       // row-offset groups: the tile of round k at [k % 8], filled 4 rounds ahead
   __shared__ uint32_t wmax[2], wcnt[2];
   __shared__ uint4 stash[kOPUnits * kOPData];   // the tile being quantized (thread-private words)
-  // Group indices fit 31 bits and a group at most kPartMax tiles (checked at
-  // launch), so the indexing here is 32-bit and mostly scalar.
-  const int G = a.groups, Q = a.Q, upg = a.upg;
-  if ((int)blockIdx.x == Q * a.T) {
-    // ---- the combining workgroup (the last one): its first wave derives S
-    // of every group, in order, as soon as the group's T slots are tagged.
-    if (threadIdx.x >= 64) return;
-    const int lane = (int)threadIdx.x;
-    for (int g = 0; g < G; ++g) {
-      const int64_t gs = (int64_t)g * kPartMax;
-      uint32_t v[kSlotsPerLane];
+  // Group and entry indices fit 31 bits (checked at launch), so the indexing
+  // here is 32-bit where it can be, and mostly scalar.
+  const int G = a.groups, Q = a.Q;
+  const int W = TABLE ? a.T : a.Q * a.T;        // tile workgroups
+  if ((int)blockIdx.x == W) {
+    // ---- the combining workgroup (the last one): derives S of every group as
+    // soon as the group's slots are tagged. Wave 0 takes the groups of more
+    // than kSegSlots tiles, in order, all 64 lanes on one group; waves 1..11
+    // take the smaller ones (e.g. the experts of a routed MoE layer) in
+    // segments of 16 lanes, one group per segment, 44 groups at a time.
+    const int cw = (int)threadIdx.x >> 6;
+    if (cw == 0) {
+      const int lane = (int)threadIdx.x;
+      for (int g = 0; g < G; ++g) {
+        int64_t s0, ns;   // first slot and number of slots of the group
+        op_group_slots<TABLE>(a, g, s0, ns);
+        if (ns <= kSegSlots) continue;   // empty (nobody waits for it), or a segment's
+        uint32_t acc = 0;   // this lane's max over the group's slots (and over tiles read after a give-up)
+        for (int64_t c0 = 0; c0 < ns; c0 += 64 * kSlotsPerLane) {
+          uint32_t v[kSlotsPerLane];
 #pragma unroll
-      for (int k2 = 0; k2 < kSlotsPerLane; ++k2) {
-        const int i = lane + 64 * k2;
-        v[k2] = i < a.T ? load_agent(&a.slots[gs + i]) : 0x80000000u;
+          for (int k2 = 0; k2 < kSlotsPerLane; ++k2) {
+            const int64_t i = c0 + lane + 64 * k2;
+            v[k2] = i < ns ? load_agent(&a.slots[s0 + i]) : 0x80000000u;
+          }
+          int spins = 0;
+          for (;;) {
+            bool all = true;
+#pragma unroll
+            for (int k2 = 0; k2 < kSlotsPerLane; ++k2) all = all && (v[k2] & 0x80000000u) != 0u;
+            if (__all(all)) break;
+            if (++spins > a.spin_max) {
+              // Some tiles' workgroups have not published (not resident beside
+              // this one): take those tiles' maxima from x. An untagged slot
+              // still holds 0 (cleared before the launch), so it adds nothing.
+              if (lane == 0) atomicAdd(a.fails, 1ull);
+#pragma unroll
+              for (int k2 = 0; k2 < kSlotsPerLane; ++k2) {
+                uint64_t miss = __ballot(c0 + lane + 64 * k2 < ns && (v[k2] & 0x80000000u) == 0u);
+                while (miss != 0u) {
+                  const int64_t i = c0 + __builtin_ctzll(miss) + 64 * k2;
+                  miss &= miss - 1u;
+                  int64_t u0, u1;
+                  op_slot_units<TABLE>(a, g, s0 + i, i, u0, u1);
+                  acc = max(acc, wave_units_amax(a.x, u0, u1));
+                }
+                v[k2] |= 0x80000000u;
+              }
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+            for (int k2 = 0; k2 < kSlotsPerLane; ++k2)
+              if ((v[k2] & 0x80000000u) == 0u) v[k2] = load_agent(&a.slots[s0 + c0 + lane + 64 * k2]);
+          }
+#pragma unroll
+          for (int k2 = 0; k2 < kSlotsPerLane; ++k2) acc = max(acc, v[k2] & 0x7FFFFFFFu);
+        }
+        publish_scale<TABLE>(a, g, wave_max_u32(acc), lane);
       }
+      return;
+    }
+    // waves 1..11: one group of at most kSegSlots tiles per 16-lane segment
+    const int seg = (cw - 1) * 4 + (((int)threadIdx.x & 63) >> 4);
+    const int sl = (int)threadIdx.x & 15;
+    const int segshift = (int)threadIdx.x & 48;   // the segment's first lane in the wave
+    constexpr int kSegs = (kOnePassThreads / 64 - 1) * 4;
+    for (int g = seg; g < G; g += kSegs) {
+      int64_t s0, ns;
+      op_group_slots<TABLE>(a, g, s0, ns);
+      if (ns == 0 || ns > kSegSlots) continue;   // uniform in the segment
+      uint32_t v[kSegSlots / 16];
+#pragma unroll
+      for (int k2 = 0; k2 < kSegSlots / 16; ++k2) {
+        const int i = sl + 16 * k2;
+        v[k2] = i < ns ? load_agent(&a.slots[s0 + i]) : 0x80000000u;
+      }
+      uint32_t late = 0;
       int spins = 0;
-      uint32_t late = 0;   // maxima of the tiles read here after a wait gave up
       for (;;) {
         bool all = true;
 #pragma unroll
-        for (int k2 = 0; k2 < kSlotsPerLane; ++k2) all = all && (v[k2] & 0x80000000u) != 0u;
-        if (__all(all)) break;
+        for (int k2 = 0; k2 < kSegSlots / 16; ++k2) all = all && (v[k2] & 0x80000000u) != 0u;
+        if (((__ballot(!all) >> segshift) & 0xFFFFu) == 0u) break;
         if (++spins > a.spin_max) {
-          // Some tiles' workgroups have not published (not resident beside
-          // this one): take those tiles' maxima from x. An untagged slot still
-          // holds 0 (cleared before the launch), so it adds nothing itself.
-          if (lane == 0) atomicAdd(a.fails, 1ull);
-          const uint4* xg = a.x + (int64_t)g * upg;
+          // as in wave 0: the untagged tiles' maxima from x, by the segment
+          if (sl == 0) atomicAdd(a.fails, 1ull);
 #pragma unroll
-          for (int k2 = 0; k2 < kSlotsPerLane; ++k2) {
-            uint64_t miss = __ballot(lane + 64 * k2 < a.T && (v[k2] & 0x80000000u) == 0u);
+          for (int k2 = 0; k2 < kSegSlots / 16; ++k2) {
+            uint32_t miss = (uint32_t)(__ballot(sl + 16 * k2 < ns && (v[k2] & 0x80000000u) == 0u) >> segshift) & 0xFFFFu;
             while (miss != 0u) {
-              const int i = __builtin_ctzll(miss) + 64 * k2;
+              const int i = __builtin_ctz(miss) + 16 * k2;
               miss &= miss - 1u;
-              const int64_t u0 = (int64_t)i * a.L;
-              late = max(late, wave_units_amax(xg, u0, min(u0 + a.L, (int64_t)upg)));
+              int64_t u0, u1;
+              op_slot_units<TABLE>(a, g, s0 + i, i, u0, u1);
+              uint32_t m = 0;
+              for (int64_t u = u0 + sl; u < u1; u += 16) m = max(m, unit_amax_bits(a.x[u]));
+              late = max(late, row_max_u32(m));
             }
             v[k2] |= 0x80000000u;
           }
@@ -939,50 +1142,57 @@ __global__ __launch_bounds__(kOnePassThreads, 6) void onepass_encode_kernel(OneP
         }
         __builtin_amdgcn_s_sleep(1);
 #pragma unroll
-        for (int k2 = 0; k2 < kSlotsPerLane; ++k2)
-          if ((v[k2] & 0x80000000u) == 0u) v[k2] = load_agent(&a.slots[gs + lane + 64 * k2]);
+        for (int k2 = 0; k2 < kSegSlots / 16; ++k2)
+          if ((v[k2] & 0x80000000u) == 0u) v[k2] = load_agent(&a.slots[s0 + sl + 16 * k2]);
       }
-      uint32_t gm = late;
+      uint32_t m = late;
 #pragma unroll
-      for (int k2 = 0; k2 < kSlotsPerLane; ++k2) gm = max(gm, v[k2] & 0x7FFFFFFFu);
-      gm = wave_max_u32(gm);
-      const float A = __uint_as_float(gm << 16);
-      const float S = global_scale(A);
-      if (lane < kSCopies) store_agent(&a.sword[((int64_t)g * kSCopies + lane) * 64], __float_as_uint(S));
-      if (lane == 0) {
-        a.gout[2 * (int64_t)g] = S;
-        a.gout[2 * (int64_t)g + 1] = A;
-      }
+      for (int k2 = 0; k2 < kSegSlots / 16; ++k2) m = max(m, v[k2] & 0x7FFFFFFFu);
+      publish_scale<TABLE>(a, g, row_max_u32(m), sl);
     }
     return;
   }
-  const int q = (int)blockIdx.x / a.T;
-  const int t = (int)blockIdx.x - q * a.T;
+  const int q = TABLE ? 0 : (int)blockIdx.x / a.T;
+  const int t = TABLE ? (int)blockIdx.x : (int)blockIdx.x - q * a.T;
+  // row-offset groups with a group larger than the grid holds: maxima first
+  const bool maxima_first = TABLE && *a.big != 0;
   if (threadIdx.x == 0) {
     wmax[0] = wmax[1] = 0u;
     wcnt[0] = wcnt[1] = 0u;
   }
   __syncthreads();
 
-  // Rounds this workgroup runs: one per group q, q + Q, ..., padded to an
-  // even number (the data waves run two rounds per iteration of a loop with
-  // one exit; a padding round quantizes nothing).
-  const int rounds = ((G - q + Q - 1) / Q + 1) & ~1;
+  // Rounds this workgroup runs, padded to an even number (the data waves
+  // run two rounds per iteration of a loop with one exit; a padding round
+  // quantizes nothing).
+  const int rounds = TABLE ? a.rounds : ((G - q + Q - 1) / Q + 1) & ~1;
   // wave index as a scalar, so the roles split without exec masking
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   if (wave == kOPDataWaves) {
     // ---- control wave
     const int lane = (int)threadIdx.x - kOPData;
+    // Row-offset groups: the data waves take each round's tiles (the one
+    // quantized, the one whose max is published, the one loaded) from a ring
+    // in LDS, which this wave fills four rounds ahead, so the table loads
+    // stay off their path. The ring slot a round writes is not read in the
+    // round before or after it.
+    if (TABLE && lane == 0)
+      for (int k = 0; k < 4; ++k) ring[k] = op_tile<TABLE>(a, q, t, k);
+    if (maxima_first)
+      for (int k = 0; k < rounds; ++k) __syncthreads();   // the data waves' first read
     int par = 0;
-    for (int k = 0, g = q; k < rounds; ++k, g += Q, par ^= 1) {
-      if (g >= G) {   // the data waves' padding round
+    for (int k = 0; k < rounds; ++k, par ^= 1) {
+      const OPTile d = TABLE ? uniform_tile(ring[k & 7]) : op_tile<TABLE>(a, q, t, k);
+      if (TABLE && lane == 0) ring[(k + 4) & 7] = op_tile<TABLE>(a, q, t, k + 4);
+      if (d.g < 0) {   // the data waves' padding round
         __syncthreads();
         continue;
       }
+      const int g = d.g;
       // S of group g, published by the combining workgroup (never 0)
       uint32_t v = 0u;
       if (lane == 0) {
-        const uint32_t* w = &a.sword[((int64_t)g * kSCopies + (int)(blockIdx.x % kSCopies)) * 64];
+        const uint32_t* w = &a.sword[((int64_t)g * a.copies + (int)(blockIdx.x % a.copies)) * 64];
         int spins = 0;
         while ((v = load_agent(w)) == 0u) {
           if (++spins > a.spin_max) {
@@ -997,7 +1207,9 @@ __global__ __launch_bounds__(kOnePassThreads, 6) void onepass_encode_kernel(OneP
         // The wait gave up (the combining workgroup is not resident yet):
         // this wave reduces the whole group's amax from x itself; the same
         // exact maximum gives the same S the combining wave publishes.
-        const uint32_t gm = wave_units_amax(a.x + (int64_t)g * upg, 0, upg);
+        int64_t u0, u1;
+        op_group_range<TABLE>(a, g, u0, u1);
+        const uint32_t gm = wave_units_amax(a.x, u0, u1);
         v = __float_as_uint(global_scale(__uint_as_float(gm << 16)));
       }
       const float S = __uint_as_float(v);
@@ -1006,55 +1218,52 @@ __global__ __launch_bounds__(kOnePassThreads, 6) void onepass_encode_kernel(OneP
       for (int h = 0; h < 2; ++h) {
         const int i = lane + 64 * h;
         const float e = e4m3_value((uint32_t)i);
-        float r = 0.0f, d = 0.0f;
+        float r = 0.0f, dd = 0.0f;
         if (e != 0.0f) {
-          d = e / S;
+          dd = e / S;
           r = fminf(S / e, kFltMax);
         }
-        lut[par][i] = make_float2(r, d);
+        lut[par][i] = make_float2(r, dd);
       }
       if (lane == 0) sS[par] = S;
-      __syncthreads();   // group g's table is ready; group g - Q's is no longer read
+      __syncthreads();   // the round's table is ready; the one two rounds back is no longer read
     }
     return;
   }
 
   // ---- data waves
-  // The tile is units t0u .. t0u + tlen - 1 of its group; unit j of this
-  // thread's share is t0u + tid + j * kOPData. Tiles are read through a buffer
-  // resource whose range is the tile (empty past the last group), so units
-  // outside it read as zero without a memory access, and every tile load is
-  // the same kOPUnits instructions.
-  const int t0u = t * a.L;
-  const int tlen = min(upg - t0u, a.L);
+  // A round's tile is units base .. base + len - 1 of x; unit j of this
+  // thread's share is base + tid + j * kOPData. Tiles are read through a
+  // buffer resource whose range is the tile (empty in a padding round), so
+  // units outside it read as zero without a memory access, and every tile
+  // load is the same kOPUnits instructions.
   uint4 r0[kOPUnits], r1[kOPUnits];
-  auto tile_rsrc = [&](int g) {
-    const bool in = g < G;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(a.x + (in ? (int64_t)g * upg + t0u : 0)), (short)0,
-                                             in ? tlen * 16 : 0, kRawBufferWord3);
+  auto tile_rsrc = [&](const OPTile& d) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(a.x + (d.g >= 0 ? d.base : 0)), (short)0, d.len * 16,
+                                             kRawBufferWord3);
   };
-  auto load_tile = [&](uint4 (&v)[kOPUnits], int g) {
-    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(g);
+  auto load_tile = [&](uint4 (&v)[kOPUnits], const OPTile& d) {
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(d);
 #pragma unroll
     for (int j = 0; j < kOPUnits; ++j)
       v[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)threadIdx.x * 16,
                                                                               j * kOPData * 16, kBufferNT));
   };
-  // Tile max of group g -> its tagged slot, stored by the last data wave to
-  // add its wave max (LDS counter `par`, reset by that wave).
-  auto publish_max = [&](const uint4 (&v)[kOPUnits], int g, int par) {
+  // Tile max of the round's tile -> its tagged slot, stored by the last data
+  // wave to add its wave max (LDS counter `par`, reset by that wave).
+  auto publish_max = [&](const uint4 (&v)[kOPUnits], const OPTile& d, int par) {
     uint32_t m = 0;
 #pragma unroll
     for (int j = 0; j < kOPUnits; ++j) m = max(m, unit_amax_bits(v[j]));
     m = wave_max_u32(m);
-    if (g < G && (threadIdx.x & 63) == 0) {
+    if (d.g >= 0 && (threadIdx.x & 63) == 0) {
       __hip_atomic_fetch_max(&wmax[par], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       const uint32_t c = __hip_atomic_fetch_add(&wcnt[par], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
       if (c == kOPDataWaves - 1) {
         const uint32_t M = __hip_atomic_load(&wmax[par], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         wmax[par] = 0u;
         wcnt[par] = 0u;
-        store_agent(&a.slots[(int64_t)g * kPartMax + t], 0x80000000u | M);
+        store_agent(&a.slots[d.slot], 0x80000000u | M);
       }
     }
   };
@@ -1062,21 +1271,24 @@ __global__ __launch_bounds__(kOnePassThreads, 6) void onepass_encode_kernel(OneP
 #pragma unroll
     for (int j = 0; j < kOPUnits; ++j) stash[j * kOPData + threadIdx.x] = v[j];
   };
-  // One round on group g (publication counter `par` for g + 2Q). On entry:
-  // stash = tile of g (max published), ra = tile of g + Q (max published),
-  // rb = loads of g + 2Q in flight. On exit ra and rb have swapped roles.
-  auto encode_round = [&](uint4 (&ra)[kOPUnits], uint4 (&rb)[kOPUnits], int g, int par) {
-    __syncthreads();   // the control wave has group g's table ready
-    const bool live = g < G;
+  // Round k (publication counter `par` for round k + 2). On entry: stash =
+  // tile of round k (max published), ra = tile of k + 1 (max published), rb
+  // = loads of k + 2 in flight. On exit ra and rb have swapped roles. With
+  // maxima_first every max is already published and none is published here.
+  auto encode_round = [&](uint4 (&ra)[kOPUnits], uint4 (&rb)[kOPUnits], int k, int par) {
+    __syncthreads();   // the control wave has the round's factor table (and row-offset tiles) ready
+    // (equal groups: the tiles are plain arithmetic on the round index)
+    const OPTile d = TABLE ? uniform_tile(ring[k & 7]) : op_tile<TABLE>(a, q, t, k);
+    const bool live = d.g >= 0;
     const float S = sS[par];
     const float2* L = lut[par];
-    // Outputs of this tile of group g, through buffer resources whose range
-    // is the tile: stores past it are dropped by the range check, and every
+    // Outputs of this tile, through buffer resources whose range is the
+    // tile: stores past it are dropped by the range check, and every
     // offset is 32-bit. The tile starts on an even unit, so a unit's parity
     // (which decides who writes the block's scale byte) is the lane's.
     constexpr int PB = PLANE == 4 ? 4 : PLANE == 3 ? 3 : PLANE == 2 ? 2 : 1;   // plane bytes per unit
-    const int64_t gb = (int64_t)(live ? g : 0) * upg + t0u;
-    const int tl = live ? tlen : 0;
+    const int64_t gb = live ? d.base : 0;
+    const int tl = live ? d.len : 0;
     const __amdgpu_buffer_rsrc_t rp =
         __builtin_amdgcn_make_buffer_rsrc(a.plane + gb * PB, (short)0, tl * PB, kRawBufferWord3);
     // 3-bit planes are stored a dword at a time where the tile's plane bytes
@@ -1087,11 +1299,11 @@ __global__ __launch_bounds__(kOnePassThreads, 6) void onepass_encode_kernel(OneP
     const __amdgpu_buffer_rsrc_t ryy =
         __builtin_amdgcn_make_buffer_rsrc(WY ? a.y + gb : a.y, (short)0, WY ? tl * 16 : 0, kRawBufferWord3);
     const int lane_u = (int)threadIdx.x;   // the thread's unit offset in the tile, for j = 0
-    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(g + 3 * Q);
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(TABLE ? uniform_tile(ring[(k + 3) & 7]) : op_tile<TABLE>(a, q, t, k + 3));
     // Unit by unit: quantize stash[j], refill it from ra[j] and reload ra[j]
-    // from group g + 3Q, so the tile's loads leave over the whole round
-    // rather than in one burst (a burst queues ahead of every other access
-    // of the CU, the slot stores and S polls included).
+    // from the tile of round k + 3, so the tile's loads leave over the whole
+    // round rather than in one burst (a burst queues ahead of every other
+    // access of the CU, the slot stores and S polls included).
 #pragma unroll
     for (int j = 0; j < kOPUnits; ++j) {
       if (live) {
@@ -1143,18 +1355,31 @@ __global__ __launch_bounds__(kOnePassThreads, 6) void onepass_encode_kernel(OneP
       __builtin_amdgcn_sched_barrier(0);
     }
     // the tile after next: its loads were issued a round ago
-    publish_max(rb, g + 2 * Q, par);
+    if (!maxima_first) publish_max(rb, TABLE ? uniform_tile(ring[(k + 2) & 7]) : op_tile<TABLE>(a, q, t, k + 2), par);
   };
 
-  load_tile(r0, q);
-  publish_max(r0, q, 0);
-  to_stash(r0);
-  load_tile(r0, q + Q);
-  load_tile(r1, q + 2 * Q);
-  publish_max(r0, q + Q, 1);
-  for (int k = 0, g = q; k < rounds; k += 2, g += 2 * Q) {
-    encode_round(r0, r1, g, 0);
-    encode_round(r1, r0, g + Q, 1);
+  if (maxima_first) {
+    // Every tile's max first: one tile at a time, one barrier per round (the
+    // LDS counters of a round are reused two rounds later).
+    for (int k = 0; k < rounds; ++k) {
+      const OPTile d = op_tile<TABLE>(a, q, t, k);
+      load_tile(r0, d);
+      publish_max(r0, d, k & 1);
+      __syncthreads();
+    }
+  }
+  {
+    const OPTile d0 = op_tile<TABLE>(a, q, t, 0), d1 = op_tile<TABLE>(a, q, t, 1), d2 = op_tile<TABLE>(a, q, t, 2);
+    load_tile(r0, d0);
+    if (!maxima_first) publish_max(r0, d0, 0);
+    to_stash(r0);
+    load_tile(r0, d1);
+    load_tile(r1, d2);
+    if (!maxima_first) publish_max(r0, d1, 1);
+  }
+  for (int k = 0; k < rounds; k += 2) {
+    encode_round(r0, r1, k, 0);
+    encode_round(r1, r0, k + 1, 1);
   }
 }
 
@@ -1263,14 +1488,21 @@ __global__ __launch_bounds__(kThreads) void tile_table_kernel(const int32_t* __r
 // launch: every workgroup derives offs and tstart in LDS from the caller's
 // offsets with the same two scans, workgroup 0 also stores them (and {1, 0}
 // for empty groups), and each workgroup writes its kThreads table entries.
+// Tiles are `tu` units. When `big` is given, workgroup 0 also stores there
+// whether some group has more than big_limit tiles.
 constexpr int kMergeGroups = 4096;
 __global__ __launch_bounds__(kThreads) void offs_table_kernel(const int64_t* __restrict__ off_in, int64_t G,
                                                              int64_t rows, int64_t upr, int64_t entries,
                                                              int64_t* offs, int32_t* tstart, float* gout,
-                                                             int2* table) {
+                                                             int2* table, int64_t tu, int32_t* big,
+                                                             int64_t big_limit, int4* desc, uint32_t* zero,
+                                                             int64_t zero_words) {
   __shared__ int64_t so[kMergeGroups + 1];
   __shared__ int32_t st[kMergeGroups + 1];
   const bool first = blockIdx.x == 0;
+  // words to clear for the kernel that follows (the single pass's slots and S words)
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < zero_words; i += (int64_t)gridDim.x * kThreads)
+    zero[i] = 0u;
   const int64_t n = G + 1;
   const int64_t per = (n + kThreads - 1) / kThreads;
   const int64_t i0 = min((int64_t)threadIdx.x * per, n), i1 = min(i0 + per, n);
@@ -1288,16 +1520,23 @@ __global__ __launch_bounds__(kThreads) void offs_table_kernel(const int64_t* __r
   // 2. tiles per group, exclusive prefix sum
   const int64_t gper = (G + kThreads - 1) / kThreads;
   const int64_t g0 = min((int64_t)threadIdx.x * gper, G), g1 = min(g0 + gper, G);
-  int64_t t = 0;
-  for (int64_t g = g0; g < g1; ++g) t += ((so[g + 1] - so[g]) * upr + kTileUnits - 1) / kTileUnits;
+  int64_t t = 0, tmax = 0;
+  for (int64_t g = g0; g < g1; ++g) {
+    const int64_t tg = ((so[g + 1] - so[g]) * upr + tu - 1) / tu;
+    t += tg;
+    tmax = max(tmax, tg);
+  }
+  int64_t most;
+  (void)block_exclusive_scan<true>(tmax, &most);
   t = block_exclusive_scan<false>(t, &total);
   if (threadIdx.x == 0) {
     st[G] = (int32_t)total;
     if (first) tstart[G] = (int32_t)total;
+    if (first && big != nullptr) *big = most > big_limit ? 1 : 0;
   }
   for (int64_t g = g0; g < g1; ++g) {
     st[g] = (int32_t)t;
-    const int64_t tg = ((so[g + 1] - so[g]) * upr + kTileUnits - 1) / kTileUnits;
+    const int64_t tg = ((so[g + 1] - so[g]) * upr + tu - 1) / tu;
     if (first) {
       tstart[g] = (int32_t)t;
       if (tg == 0 && gout != nullptr) {
@@ -1308,11 +1547,13 @@ __global__ __launch_bounds__(kThreads) void offs_table_kernel(const int64_t* __r
     t += tg;
   }
   __syncthreads();
-  // 3. this workgroup's table entries
+  // 3. this workgroup's table entries: (group, tile within the group), or
+  // with `desc` the tile descriptor {first unit (lo, hi), length, group}
   const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (e >= entries) return;
   if (e >= total) {
-    table[e] = make_int2(-1, 0);
+    if (desc != nullptr) desc[e] = make_int4(0, 0, 0, -1);
+    else table[e] = make_int2(-1, 0);
     return;
   }
   int64_t lo = 0, hi = G - 1;   // last g with tstart[g] <= e
@@ -1321,7 +1562,13 @@ __global__ __launch_bounds__(kThreads) void offs_table_kernel(const int64_t* __r
     if (st[mid] <= e) lo = mid;
     else hi = mid - 1;
   }
-  table[e] = make_int2((int)lo, (int)(e - st[lo]));
+  if (desc != nullptr) {
+    const int64_t base = so[lo] * upr + (e - st[lo]) * tu;
+    const int64_t len = min(tu, so[lo + 1] * upr - base);
+    desc[e] = make_int4((int)(uint32_t)(uint64_t)base, (int)(uint32_t)((uint64_t)base >> 32), (int)len, (int)lo);
+  } else {
+    table[e] = make_int2((int)lo, (int)(e - st[lo]));
+  }
 }
 
 // Tile maxima of row-offset groups: tpart[e] for table entry e.
@@ -1727,16 +1974,17 @@ constexpr int kOnePassTiles = kPartMax;  // most tiles per group (slot layout); 
 constexpr int kOnePassPerCU = 2;         // resident workgroups per CU it is built for
 
 template <int PLANE, bool WY>
-const void* onepass_fn() {
-  return reinterpret_cast<const void*>(&onepass_encode_kernel<PLANE, WY>);
+const void* onepass_fn(bool table) {
+  return table ? reinterpret_cast<const void*>(&onepass_encode_kernel<PLANE, WY, true>)
+               : reinterpret_cast<const void*>(&onepass_encode_kernel<PLANE, WY, false>);
 }
 
-const void* onepass_kernel(int plane_mode, bool wy) {
+const void* onepass_kernel(int plane_mode, bool wy, bool table) {
   switch (plane_mode) {
-    case 1: return wy ? onepass_fn<1, true>() : onepass_fn<1, false>();
-    case 2: return wy ? onepass_fn<2, true>() : onepass_fn<2, false>();
-    case 3: return wy ? onepass_fn<3, true>() : onepass_fn<3, false>();
-    default: return wy ? onepass_fn<4, true>() : onepass_fn<4, false>();
+    case 1: return wy ? onepass_fn<1, true>(table) : onepass_fn<1, false>(table);
+    case 2: return wy ? onepass_fn<2, true>(table) : onepass_fn<2, false>(table);
+    case 3: return wy ? onepass_fn<3, true>(table) : onepass_fn<3, false>(table);
+    default: return wy ? onepass_fn<4, true>(table) : onepass_fn<4, false>(table);
   }
 }
 
@@ -1815,30 +2063,16 @@ hipError_t device_syms(int dev, const DeviceSyms** out) {
   return hipSuccess;
 }
 
-// Launches the single-pass encode when it applies; *used tells whether it did.
-hipError_t launch_onepass(int plane_mode, bool wy, const Shape& sh, const QuantArgs& qa, void* work,
-                          hipStream_t stream, bool* used) {
-  *used = false;
-  const int64_t Tmin = (sh.upg + kOPTile - 1) / kOPTile;
-  if (Tmin > kOnePassTiles) return hipSuccess;
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipSuccess;
-  const void* k = onepass_kernel(plane_mode, wy);
-  const int64_t cap = onepass_capacity(k, dev);
-  const int64_t Q = min(sh.groups, (cap - 1) / Tmin);   // + the combining workgroup
-  // the kernel indexes groups with 32-bit ints, up to groups + 4Q
-  if (Q < 1 || sh.groups + 5 * Q > INT32_MAX) return hipSuccess;
-  // Spread each group over as many tiles as the resident grid allows (equal
-  // work per CU), in multiples of 64 units: a wave's plane and y stores then
-  // start on whole 64-byte segments, and no NVFP4 block straddles two tiles.
-  const int64_t Tfit = min((cap - 1) / Q, (int64_t)kOnePassTiles);
-  const int64_t L = ((sh.upg + Tfit - 1) / Tfit + 63) / 64 * 64;
-  const int64_t T = (sh.upg + L - 1) / L;
-  const DeviceSyms* syms = nullptr;
-  hipError_t e = device_syms(dev, &syms);
-  if (e != hipSuccess) return e;
+// Enqueues a single-pass launch: orders it after the device's previous one
+// (see OnePassOrder), clears its `words` words of slots and S words at
+// `zero` with a fill kernel when words > 0 (no memset, so the call can be
+// captured in a graph), then launches `grid` workgroups of kernel k with
+// arguments a.
+hipError_t onepass_enqueue(const void* k, OnePassArgs& a, int64_t grid, uint32_t* zero, int64_t words, int dev,
+                           const DeviceSyms* syms, hipStream_t stream) {
   hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
-  if ((e = hipStreamIsCapturing(stream, &capture)) != hipSuccess) return e;
+  hipError_t e = hipStreamIsCapturing(stream, &capture);
+  if (e != hipSuccess) return e;
   OnePassOrder& ord = g_onepass_order[dev];
   std::unique_lock<std::mutex> lock(ord.mu, std::defer_lock);
   if (capture == hipStreamCaptureStatusNone) {
@@ -1853,35 +2087,22 @@ hipError_t launch_onepass(int plane_mode, bool wy, const Shape& sh, const QuantA
     if (ord.multi && ord.recorded && ord.last != stream && (e = hipStreamWaitEvent(stream, ord.ev, 0)) != hipSuccess)
       return e;
   }
-  OnePassArgs a{};
-  a.x = qa.x;
-  a.upg = (int)sh.upg;
-  a.groups = (int)sh.groups;
-  a.T = (int)T;
-  a.Q = (int)Q;
-  a.L = (int)L;
-  a.slots = static_cast<uint32_t*>(work);
-  a.sword = a.slots + sh.groups * kPartMax;
   a.fails = syms->fails;
   const int64_t wl = g_wait_limit.load(std::memory_order_relaxed);
   a.spin_max = wl > 0 ? (int)wl : kSpinMax;
-  a.gout = qa.gout;
-  a.plane = qa.plane;
-  a.scales = qa.scales;
-  a.y = qa.y;
-  const int64_t words = sh.groups * ((int64_t)kPartMax + kSCopies * 64);
-  const int64_t zb = min((words + kThreads - 1) / kThreads, (int64_t)1024);
-  e = launch(zero_words_kernel, dim3((unsigned)zb), dim3(kThreads), stream, a.slots, words);
-  if (e != hipSuccess) return e;
+  if (words > 0) {
+    const int64_t zb = min((words + kThreads - 1) / kThreads, (int64_t)1024);
+    e = launch(zero_words_kernel, dim3((unsigned)zb), dim3(kThreads), stream, zero, words);
+    if (e != hipSuccess) return e;
+  }
   // An ordinary launch on the caller's queue: the grid is at most the
   // resident capacity, and the workgroups wait only for each other, so every
   // one of them becomes resident once earlier work on the device drains (a
   // cooperative launch would guarantee the same but goes through another
   // hardware queue, ~11 us of switching before and after the kernel).
   void* argv[] = {&a};
-  e = hipLaunchKernel(k, dim3((unsigned)(Q * T + 1)), dim3(kOnePassThreads), argv, 0, stream);
+  e = hipLaunchKernel(k, dim3((unsigned)grid), dim3(kOnePassThreads), argv, 0, stream);
   if (e != hipSuccess) return e;
-  *used = true;
   if (capture == hipStreamCaptureStatusNone) {
     if (ord.multi) {
       if ((e = hipEventRecord(ord.ev, stream)) != hipSuccess) return e;
@@ -1891,6 +2112,48 @@ hipError_t launch_onepass(int plane_mode, bool wy, const Shape& sh, const QuantA
     ord.last = stream;
   }
   return hipSuccess;
+}
+
+// Launches the single-pass encode of equal groups when it applies; *used
+// tells whether it did.
+hipError_t launch_onepass(int plane_mode, bool wy, const Shape& sh, const QuantArgs& qa, void* work,
+                          hipStream_t stream, bool* used) {
+  *used = false;
+  const int64_t Tmin = (sh.upg + kOPTile - 1) / kOPTile;
+  if (Tmin > kOnePassTiles) return hipSuccess;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipSuccess;
+  const void* k = onepass_kernel(plane_mode, wy, false);
+  const int64_t cap = onepass_capacity(k, dev);
+  const int64_t Q = min(sh.groups, (cap - 1) / Tmin);   // + the combining workgroup
+  // the kernel indexes groups with 32-bit ints, up to groups + 4Q
+  if (Q < 1 || sh.groups + 5 * Q > INT32_MAX) return hipSuccess;
+  // Spread each group over as many tiles as the resident grid allows (equal
+  // work per CU), in multiples of 64 units: a wave's plane and y stores then
+  // start on whole 64-byte segments, and no NVFP4 block straddles two tiles.
+  const int64_t Tfit = min((cap - 1) / Q, (int64_t)kOnePassTiles);
+  const int64_t L = ((sh.upg + Tfit - 1) / Tfit + 63) / 64 * 64;
+  const int64_t T = (sh.upg + L - 1) / L;
+  const DeviceSyms* syms = nullptr;
+  hipError_t e = device_syms(dev, &syms);
+  if (e != hipSuccess) return e;
+  OnePassArgs a{};
+  a.x = qa.x;
+  a.upg = (int)sh.upg;
+  a.groups = (int)sh.groups;
+  a.T = (int)T;
+  a.Q = (int)Q;
+  a.L = (int)L;
+  a.copies = kSCopies;
+  a.slots = static_cast<uint32_t*>(work);
+  a.sword = a.slots + sh.groups * kPartMax;
+  a.gout = qa.gout;
+  a.plane = qa.plane;
+  a.scales = qa.scales;
+  a.y = qa.y;
+  e = onepass_enqueue(k, a, Q * T + 1, a.slots, sh.groups * ((int64_t)kPartMax + kSCopies * 64), dev, syms, stream);
+  if (e == hipSuccess) *used = true;
+  return e;
 }
 
 template <int FMT, int BITS, bool DECODE, bool WCODES, bool STATS, bool DIAG, int MAP>
@@ -2122,8 +2385,13 @@ hipError_t read_wait_failures(uint64_t* out) {
 // ---- row-offset groups: workspace [offs | tstart | table | tile maxima]
 
 namespace {
+// [offs | tstart | table | tile maxima (slots) | published S words | flag]:
+// the table and maxima hold the two-pass schedule's entries (tiles of
+// kTileUnits), at least as many as the single pass's (kOPTableTile); the S
+// words ([G][64], one copy per group) and the flag serve the single pass,
+// which takes up to kMergeGroups groups.
 struct OffsLayout {
-  int64_t entries, b_offs, b_tstart, b_table, b_tpart, total;
+  int64_t entries, b_offs, b_tstart, b_table, b_tpart, b_sword, b_big, b_desc, total;
 };
 OffsLayout offs_layout(int64_t rows, int64_t cols, int64_t G) {
   OffsLayout L{};
@@ -2134,7 +2402,12 @@ OffsLayout offs_layout(int64_t rows, int64_t cols, int64_t G) {
   L.b_tstart = up8(8 * (G + 1));
   L.b_table = L.b_tstart + up8(4 * (G + 1));
   L.b_tpart = L.b_table + 8 * L.entries;
-  L.total = L.b_tpart + up8(4 * L.entries);
+  L.b_sword = L.b_tpart + 4 * L.entries;            // contiguous with the maxima (one fill clears both)
+  const bool single = G <= kMergeGroups;
+  L.b_big = up8(L.b_sword + (single ? 4 * 64 * G : 0));
+  // the single pass's tile descriptors (16 bytes per kOPTableTile tile)
+  L.b_desc = (L.b_big + (single ? 8 : 0) + 15) / 16 * 16;
+  L.total = L.b_desc + (single ? 16 * ((units + kOPTableTile - 1) / kOPTableTile + G) : 0);
   return L;
 }
 
@@ -2155,7 +2428,8 @@ hipError_t offs_prepare(int64_t rows, int64_t cols, int64_t G, const int64_t* of
     return launch(offs_table_kernel, dim3((unsigned)max((L.entries + kThreads - 1) / kThreads, (int64_t)1)),
                   dim3(kThreads), stream, off_in, G, rows, m->upr, L.entries,
                   reinterpret_cast<int64_t*>(w + L.b_offs), reinterpret_cast<int32_t*>(w + L.b_tstart), gout,
-                  reinterpret_cast<int2*>(w + L.b_table));
+                  reinterpret_cast<int2*>(w + L.b_table), (int64_t)kTileUnits, (int32_t*)nullptr, (int64_t)0,
+                  (int4*)nullptr, (uint32_t*)nullptr, (int64_t)0);
   hipError_t e = launch(offs_prep_kernel, dim3(1), dim3(kThreads), stream, off_in, G, rows, m->upr,
                         reinterpret_cast<int64_t*>(w + L.b_offs), reinterpret_cast<int32_t*>(w + L.b_tstart),
                         gout);
@@ -2173,9 +2447,77 @@ int64_t offs_entries(int64_t rows, int64_t cols, int64_t groups) {
   return offs_layout(rows, cols, groups).entries;
 }
 
+namespace {
+// Single-pass encode of row-offset groups (onepass_encode_kernel over the
+// device-built table of kOPTableTile-unit tiles) when the device holds the
+// grid and the groups are few enough for their S words; *used tells whether
+// it ran.
+hipError_t launch_onepass_table(int bits, int64_t rows, int64_t cols, int64_t G, const int64_t* off_in,
+                                const uint16_t* x, uint8_t* plane, uint8_t* scales, float* gout, uint16_t* y,
+                                void* work, hipStream_t stream, bool* used) {
+  *used = false;
+  if (G > kMergeGroups) return hipSuccess;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipSuccess;
+  const void* k = onepass_kernel(bits, y != nullptr, true);
+  const int64_t cap = onepass_capacity(k, dev);
+  if (cap < 2) return hipSuccess;
+  const int64_t W = cap - 1;
+  const OffsLayout L = offs_layout(rows, cols, G);
+  const int64_t upr = cols / kUnitElems;
+  const int64_t entries = (rows * upr + kOPTableTile - 1) / kOPTableTile + G;   // <= L.entries
+  const int64_t rounds = ((entries + W - 1) / W + 1) & ~(int64_t)1;
+  if (entries + 4 * W > INT32_MAX) return hipSuccess;
+  const DeviceSyms* syms = nullptr;
+  hipError_t e = device_syms(dev, &syms);
+  if (e != hipSuccess) return e;
+  uint8_t* w = static_cast<uint8_t*>(work);
+  e = launch(offs_table_kernel, dim3((unsigned)max((entries + kThreads - 1) / kThreads, (int64_t)1)), dim3(kThreads),
+             stream, off_in, G, rows, upr, entries, reinterpret_cast<int64_t*>(w + L.b_offs),
+             reinterpret_cast<int32_t*>(w + L.b_tstart), gout, reinterpret_cast<int2*>(w + L.b_table),
+             (int64_t)kOPTableTile, reinterpret_cast<int32_t*>(w + L.b_big), W + 1,
+             reinterpret_cast<int4*>(w + L.b_desc), reinterpret_cast<uint32_t*>(w + L.b_tpart),
+             L.entries + 64 * G);
+  if (e != hipSuccess) return e;
+  OnePassArgs a{};
+  a.x = reinterpret_cast<const uint4*>(x);
+  a.groups = (int)G;
+  a.T = (int)W;
+  a.Q = 1;
+  a.L = kOPTableTile;
+  a.rounds = (int)rounds;
+  a.copies = 1;
+  a.slots = reinterpret_cast<uint32_t*>(w + L.b_tpart);
+  a.sword = reinterpret_cast<uint32_t*>(w + L.b_sword);
+  a.gout = gout;
+  a.plane = plane;
+  a.scales = scales;
+  a.y = reinterpret_cast<uint4*>(y);
+  a.offs = reinterpret_cast<const int64_t*>(w + L.b_offs);
+  a.tstart = reinterpret_cast<const int32_t*>(w + L.b_tstart);
+  a.desc = reinterpret_cast<const int4*>(w + L.b_desc);
+  a.big = reinterpret_cast<const int32_t*>(w + L.b_big);
+  a.entries = (int)entries;
+  a.upr = (int)upr;
+  // (the prep kernel above cleared the slots and S words)
+  e = onepass_enqueue(k, a, W + 1, a.slots, 0, dev, syms, stream);
+  if (e == hipSuccess) *used = true;
+  return e;
+}
+}  // namespace
+
 hipError_t launch_encode_offsets(int bits, int64_t rows, int64_t cols, int64_t G, const int64_t* off_in,
                                  const uint16_t* x, uint8_t* plane, uint8_t* scales, float* gout,
                                  uint16_t* y, void* work, hipStream_t stream) {
+  // One pass over the input (unless a batch size was set to force two passes)
+  if (g_encode_batch.load(std::memory_order_relaxed) == 0) {
+    bool used = false;
+    const hipError_t e1 = launch_onepass_table(bits, rows, cols, G, off_in, x, plane, scales, gout, y, work, stream,
+                                               &used);
+    if (e1 != hipSuccess || used) return e1;
+  }
+  // Two passes: the tile maxima of every table entry, then quantize with each
+  // group's S from its tiles' maxima.
   QuantArgs a{};
   hipError_t e = offs_prepare(rows, cols, G, off_in, gout, work, &a.map, stream);
   if (e != hipSuccess) return e;

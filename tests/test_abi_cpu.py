@@ -337,10 +337,17 @@ def test_grouped_workspace_sizes(lib):
     # [offs int64 G+1 | tstart int32 G+1 | table int2 x entries | tile maxima u32 x entries],
     # entries = tiles of the call + one per group
     up8 = lambda b: (b + 7) // 8 * 8  # noqa: E731
-    for rows, cols, G in [(1000, 2048, 9), (65536, 2048, 256), (4, 32, 1)]:
+    for rows, cols, G in [(1000, 2048, 9), (65536, 2048, 256), (4, 32, 1), (64, 32, 4096), (64, 32, 4097)]:
+        # [offsets | tile starts | (group, tile) table | tile maxima | S words | flag |
+        # descriptors]: the table has the two-pass schedule's entries (2048-unit tiles);
+        # the single pass (up to 4096 groups) adds one 256-byte S line per group, an
+        # 8-byte flag and a 16-byte descriptor per 4096-unit tile (on 16 bytes)
         entries = (rows * cols // 8 + 2047) // 2048 + G
-        want = up8(8 * (G + 1)) + up8(4 * (G + 1)) + 8 * entries + up8(4 * entries)
-        assert lib.trace_grouped_workspace_bytes(0, rows, cols, G) == want
+        single = G <= 4096
+        want = up8(8 * (G + 1)) + up8(4 * (G + 1)) + 8 * entries + up8(4 * entries + (256 * G if single else 0))
+        if single:
+            want = (want + 8 + 15) // 16 * 16 + 16 * ((rows * cols // 8 + 4095) // 4096 + G)
+        assert lib.trace_grouped_workspace_bytes(0, rows, cols, G) == want, (rows, cols, G)
     assert lib.trace_grouped_workspace_bytes(1, 64, 2048, 4) == 0
     assert lib.trace_grouped_workspace_bytes(0, 64, 2048, 0) == -1
     assert lib.trace_grouped_workspace_bytes(0, 64, 24, 2) == -1

@@ -10,6 +10,7 @@ import pytest
 import torch
 
 import precision_rl_nvfp4_amd as tq
+from precision_rl_nvfp4_amd import _abi
 import synthetic as syn
 from oracle import formats, fp4 as ofp4
 from tests import _gpu as G
@@ -710,6 +711,71 @@ def _check_row_offset_groups(sizes, cols, widths):
                 _oracle_offsets(NV, bits, xt_b, xr_b, cols, offs)
             G.assert_same(G.bits_of(y), yg, f"guided y bits={gb}")
             G.assert_same(G.u8(codes), cg, f"guided codes bits={gb}")
+
+
+def _grouped_both_schedules(xr, doffs, bits, with_y):
+    """encode_guidance_grouped in one pass (the default) and in two passes
+    (forced by a batch size), plus the device's count of waits that gave up
+    during the single pass."""
+    lib = _abi.load()
+    fails0 = tq.encode_wait_failures()
+    one = tq.encode_guidance_grouped(xr, doffs, NV, bits, with_y=with_y)
+    torch.cuda.synchronize()
+    fails = tq.encode_wait_failures() - fails0
+    prev = lib.trace_set_encode_batch(1)
+    try:
+        two = tq.encode_guidance_grouped(xr, doffs, NV, bits, with_y=with_y)
+        torch.cuda.synchronize()
+    finally:
+        lib.trace_set_encode_batch(prev)
+    return one, two, fails
+
+
+@pytest.mark.parametrize("sizes,cols,bits", [
+    ([0, 37, 1, 300, 0, 0, 512, 100, 50], 2048, 1),                 # small experts, some empty
+    ([4096] * 16, 2048, 4),                                          # 16 experts of 4096 rows (2048 tiles each)
+    ([100, 60000, 0, 5436], 2048, 1),                                # one expert with most rows: tiles read twice
+    ([65536], 2048, 2),                                              # a single group larger than the grid holds
+    (np.random.default_rng(5).integers(0, 600, 256).tolist(), 2048, 1),   # a routed MoE layer's shape
+])
+def test_row_offset_single_pass_equals_two_passes(sizes, cols, bits):
+    """The single-pass encode of row-offset groups (a device-built table of
+    tiles, one pass over the input; groups larger than the resident grid
+    holds have their tiles' maxima read first) against the two-pass schedule,
+    bit for bit, every S against the oracle's scale of the exact amax, and
+    sampled rows of the largest group against the oracle."""
+    sizes = [int(v) for v in sizes]
+    rows = sum(sizes)
+    G.say(f"row-offset single pass vs two passes: {len(sizes)} groups, {rows} rows x {cols}, bits {bits}")
+    x = torch.empty((rows, cols), dtype=torch.bfloat16, device=G.DEV)
+    r0 = 0
+    for g, n in enumerate(sizes):
+        if n:
+            _, xr = syn.activation_pair(n, cols, (95, len(sizes), g), G.DEV)
+            x[r0:r0 + n] = (xr.float() * float(2.0 ** (g % 9 - 4))).to(torch.bfloat16)
+        r0 += n
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    doffs = torch.from_numpy(offs).to(G.DEV)
+    one, two, fails = _grouped_both_schedules(x, doffs, bits, True)
+    assert fails == 0
+    assert torch.equal(one.guide, two.guide) and torch.equal(one.scales, two.scales)
+    assert torch.equal(one.gscale, two.gscale)
+    assert torch.equal(one.y.view(torch.int16), two.y.view(torch.int16))
+    amax = (x.view(torch.int16) & 0x7FFF).amax(dim=1).cpu().numpy().astype(np.uint16)
+    gs = G.f32(one.gscale).reshape(-1, 2)
+    for g in range(len(sizes)):
+        a0, a1 = int(offs[g]), int(offs[g + 1])
+        A = ofp4.bf16_to_f32(amax[a0:a1]).max() if a1 > a0 else np.float32(0)
+        assert gs[g, 1] == A and gs[g, 0] == ofp4.nvfp4_global_scale(A), g
+    big = int(np.argmax(sizes))
+    a0 = int(offs[big])
+    S = gs[big, 0]
+    xb = G.bits_of(x[a0:a0 + min(64, sizes[big])])
+    o = ofp4.encode_guidance(NV, bits, xb, S)
+    n0, n1 = a0 * cols, (a0 + xb.size // cols) * cols
+    G.assert_same(G.u8(one.guide).reshape(-1)[n0 * bits // 8:n1 * bits // 8], o["guide"], "largest group guide")
+    G.assert_same(G.u8(one.scales).reshape(-1)[n0 // 16:n1 // 16], o["scales"], "largest group scales")
+    G.assert_same(G.bits_of(one.y)[n0:n1], o["y"], "largest group y")
 
 
 def test_row_offset_groups_bad_offsets_and_uncovered_rows():

@@ -60,3 +60,25 @@ def test_waits_give_up_and_results_stay_exact(group_rows, chunks, bits):
     torch.cuda.synchronize()
     assert tq.encode_wait_failures() == fails1
     assert torch.equal(g2.guide, ref.guide) and torch.equal(g2.gscale, ref.gscale)
+
+
+def test_row_offset_single_pass_gives_up_exactly():
+    """The single pass over row-offset groups (one S per expert of a routed
+    MoE layer) at a wait limit of one poll: bit-identical to the default."""
+    G.say("row-offset single pass, wait limit 1 poll")
+    lib = _abi.load()
+    _, xr, _, offsets = syn.moe_pair(21, tokens=2048, device=G.DEV)
+    ref = tq.encode_guidance_grouped(xr, offsets, NV, 1, with_y=True)
+    torch.cuda.synchronize()
+    fails0 = tq.encode_wait_failures()
+    prev = lib.trace_set_wait_limit(1)
+    try:
+        g = tq.encode_guidance_grouped(xr, offsets, NV, 1, with_y=True)
+        torch.cuda.synchronize()
+    finally:
+        assert lib.trace_set_wait_limit(prev) == 1
+    G.say(f"  waits that gave up: {tq.encode_wait_failures() - fails0}")
+    assert tq.encode_wait_failures() > fails0
+    assert torch.equal(g.guide, ref.guide) and torch.equal(g.scales, ref.scales)
+    assert torch.equal(g.gscale, ref.gscale)
+    assert torch.equal(g.y.view(torch.int16), ref.y.view(torch.int16))
