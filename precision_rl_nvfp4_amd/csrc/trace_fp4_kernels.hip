@@ -959,7 +959,7 @@ __device__ __forceinline__ void publish_scale(const OnePassArgs& a, int g, uint3
 }
 
 // Groups of at most this many tiles are combined by a 16-lane segment.
-constexpr int kSegSlots = 64;
+constexpr int kSegSlots = 128;
 
 // A tile descriptor the control wave left in LDS, read into scalar registers
 // (it is the same for every lane).
@@ -1183,8 +1183,12 @@ __global__ __launch_bounds__(kOnePassThreads, 6) void onepass_encode_kernel(OneP
     int par = 0;
     for (int k = 0; k < rounds; ++k, par ^= 1) {
       const OPTile d = TABLE ? uniform_tile(ring[k & 7]) : op_tile<TABLE>(a, q, t, k);
-      if (TABLE && lane == 0) ring[(k + 4) & 7] = op_tile<TABLE>(a, q, t, k + 4);
+      // the tile of round k + 4 for the ring: its descriptor load is issued
+      // now and written to LDS at the end of the round
+      OPTile ahead{};
+      if (TABLE && lane == 0) ahead = op_tile<TABLE>(a, q, t, k + 4);
       if (d.g < 0) {   // the data waves' padding round
+        if (TABLE && lane == 0) ring[(k + 4) & 7] = ahead;
         __syncthreads();
         continue;
       }
@@ -1226,6 +1230,7 @@ __global__ __launch_bounds__(kOnePassThreads, 6) void onepass_encode_kernel(OneP
         lut[par][i] = make_float2(r, dd);
       }
       if (lane == 0) sS[par] = S;
+      if (TABLE && lane == 0) ring[(k + 4) & 7] = ahead;
       __syncthreads();   // the round's table is ready; the one two rounds back is no longer read
     }
     return;

@@ -736,6 +736,8 @@ def _grouped_both_schedules(xr, doffs, bits, with_y):
     ([4096] * 16, 2048, 4),                                          # 16 experts of 4096 rows (2048 tiles each)
     ([100, 60000, 0, 5436], 2048, 1),                                # one expert with most rows: tiles read twice
     ([65536], 2048, 2),                                              # a single group larger than the grid holds
+    ([1040, 2048, 2064, 1500, 16, 1100] * 3, 2048, 1),               # 65, 128, 129, 94, 1, 69 tiles: both sides of the
+                                                                     # combining workgroup's small-group limit
     (np.random.default_rng(5).integers(0, 600, 256).tolist(), 2048, 1),   # a routed MoE layer's shape
 ])
 def test_row_offset_single_pass_equals_two_passes(sizes, cols, bits):
