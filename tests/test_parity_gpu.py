@@ -746,6 +746,31 @@ def test_row_offset_single_pass_equals_two_passes(sizes, cols, bits):
     holds have their tiles' maxima read first) against the two-pass schedule,
     bit for bit, every S against the oracle's scale of the exact amax, and
     sampled rows of the largest group against the oracle."""
+    _single_vs_two_passes(sizes, cols, bits)
+
+
+@pytest.mark.parametrize("extra", [1, 2])
+def test_row_offset_single_pass_group_of_grid_size(extra):
+    """A group of W + 1 tiles of 4096 units (W = tile workgroups of the
+    launch, 2 per CU less the combining one): the largest group that is
+    complete one round after its last tile, and W + 2, the smallest whose
+    tiles' maxima are read first; between small groups, against the
+    two-pass schedule and the oracle."""
+    W = 2 * torch.cuda.get_device_properties(0).multi_processor_count - 1
+    cols = 2048                              # 256 units per row: 16 rows per tile
+    _single_vs_two_passes([40, (W + extra) * 16, 300, 0, 17], cols, 1)
+
+
+@pytest.mark.parametrize("n_groups", [4096, 4097])
+def test_row_offset_group_count_limit(n_groups):
+    """Up to 4096 row-offset groups the encode takes one pass; one more group
+    takes the two-pass schedule. Both against the oracle."""
+    sizes = np.random.default_rng(n_groups + 1).integers(0, 4, n_groups).tolist()
+    G.say(f"row-offset groups: {n_groups} groups of 0..3 rows x 16")
+    _check_row_offset_groups(sizes, 16, (1,))
+
+
+def _single_vs_two_passes(sizes, cols, bits):
     sizes = [int(v) for v in sizes]
     rows = sum(sizes)
     G.say(f"row-offset single pass vs two passes: {len(sizes)} groups, {rows} rows x {cols}, bits {bits}")
