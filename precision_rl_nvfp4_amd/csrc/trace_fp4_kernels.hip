@@ -996,10 +996,10 @@ __device__ __forceinline__ OPTile uniform_tile(const OPTile& t) {
 //     as soon as the tile has arrived; no barrier is involved.
 //   * Combining workgroup (the last one): waits for each group's slots,
 //     derives S and A, writes {S, A} to gout and publishes S (nonzero) to
-//     `copies` words; its first wave takes the groups of many tiles in order,
-//     the other waves the small groups, 16 lanes each. It runs ahead of the
-//     tiles, so S is combined as soon as the last tile max of its group is
-//     in, about a round before it is needed.
+//     `copies` words; its first wave takes the groups of more than
+//     kSegSlots tiles in order, the other waves the smaller ones, 16 lanes
+//     each. It runs ahead of the tiles, so S is combined as soon as the last
+//     tile max of its group is in, about a round before it is needed.
 //   * Control wave: waits for one S word of the round's group and builds the
 //     table of block factors under S.
 //   * One barrier per round: the data waves quantize a tile from its table
@@ -1024,7 +1024,8 @@ __device__ __forceinline__ OPTile uniform_tile(const OPTile& t) {
 // to one expert), every workgroup first reads all its tiles once to publish
 // their maxima (one barrier per round), then runs the rounds above without
 // publishing: the input is read twice, as in the two-pass schedule.
-// Slots and S words are zeroed by a fill kernel before the launch. Every wait
+// Slots and S words are zeroed before the launch, by a fill kernel (equal
+// groups) or by the kernel that builds the tile table. Every wait
 // is bounded: past spin_max polls the waiting wave stops waiting, counts the
 // give-up in *fails and takes what it waited for from the input itself (the
 // maxima of the tiles whose slots were not tagged, or the whole group's
@@ -2390,11 +2391,12 @@ hipError_t read_wait_failures(uint64_t* out) {
 // ---- row-offset groups: workspace [offs | tstart | table | tile maxima]
 
 namespace {
-// [offs | tstart | table | tile maxima (slots) | published S words | flag]:
-// the table and maxima hold the two-pass schedule's entries (tiles of
-// kTileUnits), at least as many as the single pass's (kOPTableTile); the S
-// words ([G][64], one copy per group) and the flag serve the single pass,
-// which takes up to kMergeGroups groups.
+// [offs | tstart | table | tile maxima (slots) | published S words | flag |
+// tile descriptors]: the table and maxima hold the two-pass schedule's
+// entries (tiles of kTileUnits), at least as many as the single pass's
+// (kOPTableTile); the S words ([G][64], one copy per group), the flag and the
+// descriptors (one int4 per kOPTableTile tile) serve the single pass, which
+// takes up to kMergeGroups groups.
 struct OffsLayout {
   int64_t entries, b_offs, b_tstart, b_table, b_tpart, b_sword, b_big, b_desc, total;
 };
