@@ -770,6 +770,45 @@ def test_row_offset_group_count_limit(n_groups):
     _check_row_offset_groups(sizes, 16, (1,))
 
 
+def test_row_offset_random_cases():
+    """16 seeded random row-offset layouts (1 to 200 groups, runs of empty
+    groups, one dominant group in some, widths 16 to 2048 columns, every
+    record width): the default encode (one pass up to 4096 groups) against
+    the two-pass schedule bit for bit, and both against the oracle run on
+    each group's rows."""
+    rng = np.random.default_rng(2027)
+    for k in range(16):
+        cols = int(rng.choice([16, 48, 128, 256, 2048]))
+        n_groups = int(rng.integers(1, 201))
+        cap = max(1, 1_500_000 // cols)                    # elements per case stay within ~1.5M
+        sizes = rng.geometric(0.02, n_groups) - 1          # many small, some empty
+        sizes[rng.random(n_groups) < 0.2] = 0
+        if k % 4 == 3:
+            sizes[int(rng.integers(0, n_groups))] += cap // 2   # one dominant group
+        if sizes.sum() > cap:
+            sizes = (sizes * (cap / sizes.sum())).astype(np.int64)
+        sizes = [int(v) for v in sizes]
+        if sum(sizes) == 0:
+            sizes[0] = 1
+        bits = int(rng.integers(1, 5))
+        G.say(f"row-offset random case {k}: {n_groups} groups, {sum(sizes)} rows x {cols}, bits {bits}")
+        xt_b, xr_b = _offset_groups_pair(sizes, cols, 600 + k)
+        rows = sum(sizes)
+        offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+        doffs = torch.from_numpy(offs).to(G.DEV)
+        xr = G.to_dev(xr_b, rows, cols)
+        one, two, fails = _grouped_both_schedules(xr, doffs, bits, True)
+        assert fails == 0
+        assert torch.equal(one.guide, two.guide) and torch.equal(one.scales, two.scales), k
+        assert torch.equal(one.gscale, two.gscale), k
+        assert torch.equal(one.y.view(torch.int16), two.y.view(torch.int16)), k
+        guide, scales, yr, _, _, S = _oracle_offsets(NV, bits, xt_b, xr_b, cols, offs)
+        G.assert_same(G.u8(one.guide), guide, f"case {k} guide")
+        G.assert_same(G.u8(one.scales), scales, f"case {k} scales")
+        G.assert_same(G.bits_of(one.y), yr, f"case {k} rollout y")
+        G.assert_same(G.f32(one.gscale).reshape(-1, 2), np.array(S, np.float32), f"case {k} {{S, A}}")
+
+
 def _single_vs_two_passes(sizes, cols, bits):
     sizes = [int(v) for v in sizes]
     rows = sum(sizes)
