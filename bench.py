@@ -567,26 +567,43 @@ def warn_wait_failures(fails):
               file=sys.stderr, flush=True)
 
 
-def copy_ceiling(torch, dev, nbytes=1 << 30, reps=10):
-    """A plain device-to-device copy of `nbytes` (torch's copy kernel), timed
-    with events: the HBM rate a read + write stream reaches on this GPU,
-    reported beside the roofline (its `peak` stays the published 8 TB/s)."""
-    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    dst = torch.empty_like(src)
-    src.fill_(1)
+def _timed_rate(torch, fn, moved, reps):
     for _ in range(3):
-        dst.copy_(src)
+        fn()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
-        dst.copy_(src)
+        fn()
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / reps
-    gbs = 2 * nbytes / (us * 1e-6) / 1e9
-    del src, dst
-    return {"kernel": "torch copy_ (device to device)", "bytes_read_plus_written": 2 * nbytes,
-            "avg_us": round(us, 2), "GB_s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    gbs = moved / (us * 1e-6) / 1e9
+    return {"bytes_read_plus_written": moved, "avg_us": round(us, 2), "GB_s": round(gbs, 1),
+            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def copy_ceiling(torch, dev, nbytes=1 << 30, reps=10):
+    """The HBM rates plain streams reach on this GPU in this run, timed with
+    events, reported beside the roofline (whose `peak` stays the published 8
+    TB/s): the library's stream references (trace_stream_copy, one stream in
+    and one out; trace_stream_mix, two in and one out, the fused guided
+    pass's mix), which use the kernels' access policy, and torch's copy."""
+    import precision_rl_nvfp4_amd as tq
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    out = torch.empty_like(a)
+    a.fill_(1)
+    b.fill_(2)
+    res = {"kernel": "trace_stream_copy (library stream reference: one stream in, one out)"}
+    res.update(_timed_rate(torch, lambda: tq.stream_copy(a, out), 2 * nbytes, reps))
+    mix = {"kernel": "trace_stream_mix (library stream reference: two in, one out)"}
+    mix.update(_timed_rate(torch, lambda: tq.stream_mix(a, b, out), 3 * nbytes, reps))
+    tc = {"kernel": "torch copy_ (device to device)"}
+    tc.update(_timed_rate(torch, lambda: out.copy_(a), 2 * nbytes, reps))
+    res["two_in_one_out"] = mix
+    res["torch_copy"] = tc
+    del a, b, out
+    return res
 
 
 # ---------------------------------------------------------------- other workloads

@@ -88,7 +88,7 @@
 extern "C" {
 #endif
 
-#define TRACE_ABI_VERSION 8
+#define TRACE_ABI_VERSION 9
 
 /* Entries of the mismatch diagnostics of guided_fake_quant_stats. */
 #define TRACE_MISMATCH_COUNTS 32
@@ -460,6 +460,24 @@ int trace_ring_release(trace_ring* ring, int32_t slot);
 int trace_gather_pages(const uint8_t* pool, int64_t pool_pages, int64_t page_bytes,
                        const int32_t* page_ids, int64_t n, uint8_t* out, uint32_t* bad_ids,
                        void* stream);
+
+/*
+ * Measurement references, not steps of the method: plain streams of 16-byte
+ * words with the same access policy as the path's kernels (nontemporal loads
+ * and stores, 256 threads of 4 words per workgroup), so a benchmark can time,
+ * on the same device and in the same run, the HBM rates its kernels are
+ * compared with.
+ *
+ * trace_stream_copy: dst[i] = src[i]; one stream read, one written.
+ * trace_stream_mix:  out[i] = a[i] XOR b[i]; two streams read, one written
+ *                    (the mix of the fused guided pass).
+ *
+ *   src, a, b   in   bytes of device memory, 16-byte aligned
+ *   dst, out    out  bytes of device memory, 16-byte aligned, disjoint from the inputs
+ *   bytes       a multiple of 16, at most 2^44 (else ESHAPE)
+ */
+int trace_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
+int trace_stream_mix(const void* a, const void* b, void* out, int64_t bytes, void* stream);
 
 #ifdef __cplusplus
 }

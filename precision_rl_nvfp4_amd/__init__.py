@@ -37,7 +37,7 @@ __all__ = ["NVFP4", "MXFP4", "TraceError", "Quantized", "Guidance", "quantize_rt
            "guided_fake_quant_stats",
            "discrepancy_stats", "stats_workspace", "quant_workspace", "guided_stats_workspace",
            "encode_wait_failures", "encode_guidance_noalloc", "NOALLOC_SCRATCH_BYTES",
-           "grouped_workspace",
+           "grouped_workspace", "stream_copy", "stream_mix",
            "derived_metrics", "mismatch_summary", "fmt_id", "BLOCK", "MISMATCH_COUNTS"]
 
 BLOCK = {NVFP4: 16, MXFP4: 32}
@@ -360,6 +360,30 @@ def discrepancy_stats(x_t, x_r, y_t, y_r, acc: Optional[torch.Tensor] = None,
     _abi.call("discrepancy_stats", n, _ptr(x_t), _ptr(x_r), _ptr(y_t), _ptr(y_r), _ptr(acc),
               1 if accumulate else 0, _ptr(work), _nbytes(work), _stream(x_t))
     return acc
+
+
+def _stream_bytes(*ts) -> int:
+    n = ts[0].numel() * ts[0].element_size()
+    for t in ts:
+        if not t.is_contiguous() or t.device.type != "cuda" or t.numel() * t.element_size() != n:
+            raise ValueError("stream references take contiguous device tensors of one byte size")
+    return n
+
+
+def stream_copy(src: torch.Tensor, dst: torch.Tensor) -> torch.Tensor:
+    """Measurement reference (no step of the method): dst = src as a plain
+    stream with the path kernels' access policy."""
+    n = _stream_bytes(src, dst)
+    _abi.call("trace_stream_copy", _ptr(src), _ptr(dst), n, _stream(src))
+    return dst
+
+
+def stream_mix(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor) -> torch.Tensor:
+    """Measurement reference (no step of the method): out = a XOR b, bytewise,
+    two streams read and one written (the fused guided pass's mix)."""
+    n = _stream_bytes(a, b, out)
+    _abi.call("trace_stream_mix", _ptr(a), _ptr(b), _ptr(out), n, _stream(a))
+    return out
 
 
 def mismatch_summary(counts) -> dict:

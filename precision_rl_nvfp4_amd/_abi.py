@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtrace_fp
 
 OK, EINVAL, ESHAPE, EALIGN, EALIAS, EDEVICE, ELAUNCH, EBUSY = 0, -1, -2, -3, -4, -5, -6, -7
 NVFP4, MXFP4 = 0, 1
-ABI_VERSION = 8
+ABI_VERSION = 9
 MISMATCH_COUNTS = 32
 NOALLOC_SCRATCH_BYTES = 4 << 20
 
@@ -66,6 +66,8 @@ SIGNATURES = {
     "trace_ring_release": (_int, [_vp, ctypes.c_int32]),
     # pool, pool_pages, page_bytes, page_ids, n, out, bad_ids, stream
     "trace_gather_pages": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp]),
+    "trace_stream_copy": (_int, [_vp, _vp, _i64, _vp]),
+    "trace_stream_mix": (_int, [_vp, _vp, _vp, _i64, _vp]),
 }
 
 _lib = None

@@ -32,7 +32,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libtrace_fp4.so")
 SOURCES = [os.path.join(CSRC, "trace_fp4_kernels.hip"), os.path.join(CSRC, "trace_fp4_api.cpp"),
-           os.path.join(CSRC, "trace_fp4_record.hip")]
+           os.path.join(CSRC, "trace_fp4_record.hip"), os.path.join(CSRC, "trace_fp4_stream.hip")]
 ARCH = "gfx950"
 
 

@@ -65,7 +65,19 @@ typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kFltMax = 3.40282346638528859812e+38f;
 constexpr int kMidGroups = 64;          // first level of the partial-sum reduction
-constexpr int64_t kDirectTiles = 32768; // up to this many per-tile pairs are summed by one workgroup
+constexpr int64_t kDirectTiles = 65536; // up to this many per-tile pairs are summed by one workgroup
+// Tile of guided rounding and of the fused statistics (equal or packed
+// groups): half the tile of the other kernels. Measured on a streamed
+// layer: the fused pass 1-5% faster and plain guided rounding 1-5% faster
+// than with kTileUnits, while Reconstruct alone, the encode with S supplied
+// and a KV tensor's two-pass encode were 3-10% slower with the smaller tile,
+// so those keep kTileUnits. The statistics with mismatch diagnostics keep
+// the smaller tile too (2-5% slower than on kTileUnits), so that the sums
+// are bit-identical with and without the diagnostics.
+constexpr int64_t kGuidedTileUnits = kTileUnits / 2;
+// Tile of a guided_kernel launch: kGuidedTileUnits for guided rounding and
+// the fused statistics of equal or packed groups, kTileUnits otherwise.
+constexpr int64_t guided_tile(bool decode, int map) { return (decode || map == 2) ? kTileUnits : kGuidedTileUnits; }
 constexpr int kMismatchBins = 15;       // signed-grid distances 0..14
 constexpr int kPackGroups = kTileUnits / 2;  // most groups in a packed tile (NVFP4: >= 2 units each)
 
@@ -451,15 +463,16 @@ __device__ __forceinline__ double sq_diff_sum(const float (&a)[8], const float (
 
 // ------------------------------------------------------------ kernel arguments
 
-// Work split of a launch. Normally a tile of kTileUnits units lies in one
-// group (tiles = tiles per group). Packed (NVFP4 groups of a power-of-two
-// unit count below kTileUnits, e.g. one token's row): a tile holds
-// kTileUnits >> lg whole consecutive groups (tiles = tiles of the call).
+// Work split of a launch. Normally a tile of tu units lies in one group
+// (tiles = tiles per group). Packed (NVFP4 groups of a power-of-two unit
+// count below tu, e.g. one token's row): a tile holds tu >> lg whole
+// consecutive groups (tiles = tiles of the call).
 // Row-offset groups (groups of any size, e.g. the experts of a grouped MoE
 // input): a device table gives each workgroup its (group, tile); groups are
 // the row ranges [offs[g], offs[g + 1]), tiles of group g are table entries
 // tstart[g] .. tstart[g + 1] - 1, and entries past the last are (-1, 0).
 struct TileMap {
+  int64_t tu;         // units per tile
   int64_t upg;        // units per group
   int64_t tiles;      // tiles per group, or of the call when packed
   int64_t units;      // units of the call
@@ -477,7 +490,7 @@ struct TileMap {
 __device__ __forceinline__ void tile_of(const TileMap& m, int64_t& g, int64_t& tbase) {
   const int64_t b = blockIdx.x;
   g = b / m.tiles;
-  tbase = (b - g * m.tiles) * kTileUnits;
+  tbase = (b - g * m.tiles) * m.tu;
 }
 
 struct AmaxArgs {
@@ -1602,15 +1615,18 @@ __global__ __launch_bounds__(kThreads) void tile_amax_kernel(TileMap m, const ui
 // alone (DECODE: reference codes, no y), and the fused discrepancy sums
 // (STATS: SB = sum (x_t - x_r)^2 over the inputs; SF = sum (y_t - y_r)^2 with
 // y_r the rollout's RTN output under the same scales, recomputed from x_r).
-// Threads of a guided_kernel workgroup; its tile is kTileUnits units either
-// way. The fused statistics pass keeps 256 threads of 8 units (measured
-// fastest); the other modes run 512 threads of 4 units, which keeps more
-// waves per SIMD (3.7% faster for plain guided rounding of a streamed layer).
+// Threads of a guided_kernel workgroup, whose tile is guided_tile(...) units:
+// the fused statistics pass runs 256 threads (4 units each on its 1024-unit
+// tile), the other modes 512 (2 units each for guided rounding, 4 for
+// Reconstruct alone and row-offset groups), which
+// keeps more waves per SIMD (3.7% faster for plain guided rounding of a
+// streamed layer on 2048-unit tiles).
 constexpr int guided_threads(bool stats) { return stats ? kThreads : 2 * kThreads; }
 
 template <int FMT, int BITS, bool DECODE, bool WCODES, bool STATS, bool DIAG, int MAP>
 __global__ __launch_bounds__(guided_threads(STATS)) void guided_kernel(GuidedArgs a) {
-  constexpr int GT = guided_threads(STATS), GU = (int)(kTileUnits / GT);
+  constexpr int64_t TU = guided_tile(DECODE, MAP);
+  constexpr int GT = guided_threads(STATS), GU = (int)(TU / GT);
   // MAP 0: one group per tile; 1: packed small groups; 2: row-offset groups.
   constexpr bool PACK = MAP == 1;
   static_assert(!(MAP == 2 && STATS), "row-offset groups take no fused statistics");
@@ -1620,14 +1636,14 @@ __global__ __launch_bounds__(guided_threads(STATS)) void guided_kernel(GuidedArg
   int64_t g, tbase, gbase, lim;
   if constexpr (PACK) {
     g = 0;
-    tbase = (int64_t)blockIdx.x * kTileUnits;
+    tbase = (int64_t)blockIdx.x * TU;
     gbase = 0;
     lim = a.map.units;
   } else if constexpr (MAP == 2) {
     const int2 e = a.map.table[blockIdx.x];
     if (e.x < 0) return;
     g = e.x;
-    tbase = (int64_t)e.y * kTileUnits;
+    tbase = (int64_t)e.y * TU;
     gbase = a.map.offs[g] * a.map.upr;
     lim = a.map.offs[g + 1] * a.map.upr - gbase;
   } else {
@@ -1665,7 +1681,7 @@ __global__ __launch_bounds__(guided_threads(STATS)) void guided_kernel(GuidedArg
   }
   if constexpr (PACK) {
     const int64_t g0t = tbase >> a.map.lg;
-    for (int i = threadIdx.x; i < (kTileUnits >> a.map.lg); i += GT) {
+    for (int i = threadIdx.x; i < (TU >> a.map.lg); i += GT) {
       const int64_t gg = g0t + i;
       gs[i] = gg < a.map.groups ? a.gscale[2 * gg] : 1.0f;
     }
@@ -1731,7 +1747,7 @@ __global__ __launch_bounds__(guided_threads(STATS)) void guided_kernel(GuidedArg
     __syncthreads();
     if (threadIdx.x < kMismatchCounts) {
       // Distance 0 (bins 0 and 15) is the rest of the tile's elements.
-      const int64_t valid = min((int64_t)kTileUnits, lim - tbase) * kUnitElems;
+      const int64_t valid = min(TU, lim - tbase) * kUnitElems;
       const int b = threadIdx.x;
       uint32_t hv = hist[b];
       if (b == 0 || b == kMismatchBins) {
@@ -1784,10 +1800,10 @@ __global__ __launch_bounds__(kThreads) void sums_mid_kernel(const double* __rest
 
 // Fixed-order reduction of `groups` partial pairs into acc3 = {SB, SF, n}, by
 // one workgroup of kSumThreads. Thread t sums pairs t, t + kSumThreads, ... in
-// order, loading kSumBatch pairs at a time so that a streamed layer's 17,408
-// pairs (17 per thread) take one round trip to memory; the 16 wave sums are
-// then added in wave order. (Workspaces are only 8-byte aligned: a pair is
-// two loads.)
+// order, loading kSumBatch pairs at a time, so that a streamed layer's 34,816
+// pairs (34 per thread, on 1024-unit tiles) take two round trips to memory;
+// the 16 wave sums are then added in wave order. (Workspaces are only 8-byte
+// aligned: a pair is two loads.)
 constexpr int kSumThreads = 1024;
 constexpr int kSumBatch = 17;
 __global__ __launch_bounds__(kSumThreads) void sums_final_kernel(const double* __restrict__ partials,
@@ -1901,22 +1917,23 @@ Shape effective(int fmt, const Shape& sh) {
 
 // NVFP4 groups whose unit count is a power of two below a tile are packed
 // several to a tile (and their encode reads the input once).
-bool packable(int fmt, const Shape& sh) {
-  return fmt == 0 && sh.groups > 1 && sh.upg > 0 && sh.upg < kTileUnits && kTileUnits % sh.upg == 0;
+bool packable(int fmt, const Shape& sh, int64_t tu = kTileUnits) {
+  return fmt == 0 && sh.groups > 1 && sh.upg > 0 && sh.upg < tu && tu % sh.upg == 0;
 }
 
-TileMap tile_map(int fmt, const Shape& sh0) {
+TileMap tile_map(int fmt, const Shape& sh0, int64_t tu = kTileUnits) {
   const Shape sh = effective(fmt, sh0);
   TileMap m{};
+  m.tu = tu;
   m.upg = sh.upg;
   m.units = sh.groups * sh.upg;
   m.groups = sh.groups;
-  if (packable(fmt, sh)) {
-    m.tiles = (m.units + kTileUnits - 1) / kTileUnits;
+  if (packable(fmt, sh, tu)) {
+    m.tiles = (m.units + tu - 1) / tu;
     m.lg = __builtin_ctzll((unsigned long long)sh.upg);
     m.packed = 1;
   } else {
-    m.tiles = (sh.upg + kTileUnits - 1) / kTileUnits;
+    m.tiles = (sh.upg + tu - 1) / tu;
   }
   return m;
 }
@@ -2210,7 +2227,8 @@ int64_t quant_work_bytes(int fmt, const Shape& sh) {
 }
 
 int64_t guided_stats_work_bytes(int fmt, const Shape& sh) {
-  const int64_t tiles = tile_grid(tile_map(fmt, sh));
+  // sized for the smaller tile, whose count is never below the other's
+  const int64_t tiles = tile_grid(tile_map(fmt, sh, kGuidedTileUnits));
   return 2 * (int64_t)sizeof(double) * (tiles + kMidGroups) +
          (int64_t)sizeof(uint32_t) * kMismatchCounts * tiles;
 }
@@ -2313,7 +2331,7 @@ hipError_t launch_guided(int fmt, int bits, bool decode_only, const Shape& sh, c
                   (const uint32_t*)nullptr, (int64_t)0, counts, accumulate);
   }
   GuidedArgs a{};
-  a.map = tile_map(fmt, sh);
+  a.map = tile_map(fmt, sh, guided_tile(decode_only, 0));
   a.x = reinterpret_cast<const uint4*>(x);
   a.guide = guide;
   a.scales = scales;
@@ -2428,6 +2446,7 @@ hipError_t offs_prepare(int64_t rows, int64_t cols, int64_t G, const int64_t* of
   m->tstart = reinterpret_cast<const int32_t*>(w + L.b_tstart);
   m->table = reinterpret_cast<const int2*>(w + L.b_table);
   m->tpart = reinterpret_cast<const uint32_t*>(w + L.b_tpart);
+  m->tu = kTileUnits;
   m->upr = cols / kUnitElems;
   m->groups = G;
   m->units = rows * m->upr;

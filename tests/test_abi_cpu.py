@@ -51,7 +51,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.trace_abi_version() == _abi.ABI_VERSION == 8
+    assert lib.trace_abi_version() == _abi.ABI_VERSION == 9
     for code, name in [(0, "TRACE_OK"), (-1, "TRACE_EINVAL"), (-2, "TRACE_ESHAPE"),
                        (-3, "TRACE_EALIGN"), (-4, "TRACE_EALIAS"), (-5, "TRACE_EDEVICE"),
                        (-6, "TRACE_ELAUNCH"), (-7, "TRACE_EBUSY"), (7, "unknown status")]:
@@ -101,6 +101,10 @@ def test_wait_limit_setting(lib):
     assert lib.trace_set_wait_limit(0) == 0
 
 
+TILE = 2048   # units (8 bf16 each) of a workgroup tile of the quantize and two-pass kernels
+GTILE = 1024  # units of a tile of guided rounding and the fused statistics
+
+
 def test_workspace_sizes(lib):
     assert lib.trace_stats_workspace_bytes(0) == 16
     assert lib.trace_stats_workspace_bytes(8192 * 2048) == 16 * 1024
@@ -113,22 +117,24 @@ def test_workspace_sizes(lib):
     assert lib.trace_quant_workspace_bytes(1, 4, 32, 0) == 0            # MXFP4: no amax pass
     assert lib.trace_quant_workspace_bytes(0, 5, 32, 2) == -1           # 2 does not divide 5
     assert lib.trace_quant_workspace_bytes(3, 4, 32, 0) == -1           # bad format
-    # two float64 partial sums per workgroup tile of 2048 units (16384 elements),
-    # plus 64 pairs for the first level of the reduction
+    # two float64 partial sums per workgroup tile of GTILE units, plus 64 pairs for
+    # the first level of the reduction
     # packed groups (power-of-two units below a tile, G > 1) need no amax workspace
     assert lib.trace_quant_workspace_bytes(0, 8, 32, 4) == 0           # 2 groups of 16 units
     assert lib.trace_quant_workspace_bytes(0, 139264, 2048, 1) == 0    # per-token scales
     assert lib.trace_quant_workspace_bytes(0, 6, 32, 3) == qwb(2)      # 12 units: not a power of two
-    assert lib.trace_quant_workspace_bytes(0, 16, 2048, 8) == qwb(2)   # 2048 units: a whole tile
+    assert lib.trace_quant_workspace_bytes(0, 16, 2048, 8) == qwb(2)   # 2048 units: whole tiles
     assert lib.trace_quant_workspace_bytes(1, 16, 2048, 8) == 0
-    # per-token: 139264 rows x 256 units packed 8 to a tile
-    assert lib.trace_guided_stats_workspace_bytes(0, 139264, 2048, 1) == 16 * (17408 + 64) + 128 * 17408
-    # MXFP4 groups merge into one tensor: 4 groups of 300 units -> 1 tile
-    assert lib.trace_guided_stats_workspace_bytes(1, 4 * 75, 32, 75) == 16 * (1 + 64) + 128
+    # per-token: 139264 rows x 256 units packed GTILE / 256 to a tile
+    t = 139264 * 256 // GTILE
+    assert lib.trace_guided_stats_workspace_bytes(0, 139264, 2048, 1) == 16 * (t + 64) + 128 * t
+    # MXFP4 groups merge into one tensor: 4 groups of 300 units -> ceil(1200 / GTILE) tiles
+    t = (1200 + GTILE - 1) // GTILE
+    assert lib.trace_guided_stats_workspace_bytes(1, 4 * 75, 32, 75) == 16 * (t + 64) + 128 * t
     # 16 bytes of sums per tile + 64 second-level pairs, 32 uint32 counts per tile
     assert lib.trace_guided_stats_workspace_bytes(0, 4, 32, 0) == 16 * (1 + 64) + 128
-    assert lib.trace_guided_stats_workspace_bytes(0, 17 * 8192, 2048, 8192) == \
-        16 * (17 * 1024 + 64) + 128 * 17 * 1024
+    t = 17 * (8192 * 256 // GTILE)
+    assert lib.trace_guided_stats_workspace_bytes(0, 17 * 8192, 2048, 8192) == 16 * (t + 64) + 128 * t
     assert lib.trace_guided_stats_workspace_bytes(0, 4, 24, 0) == -1    # cols % 16
 
 
@@ -331,6 +337,42 @@ def test_gather_without_gpu_is_edevice(lib):
     assert lib.trace_gather_pages(A, 4, 16, B, 2, C, D, None) == _abi.EDEVICE
 
 
+# trace_stream_copy(src, dst, bytes, stream) / trace_stream_mix(a, b, out, bytes, stream)
+@pytest.mark.parametrize("args,status", [
+    ((A, B, 24, None), _abi.ESHAPE),                 # not whole 16-byte words
+    ((A, B, -16, None), _abi.ESHAPE),
+    ((A, B, 1 << 45, None), _abi.ESHAPE),            # beyond 2^44 bytes
+    ((None, B, 64, None), _abi.EINVAL),
+    ((A, None, 64, None), _abi.EINVAL),
+    ((A + 8, B, 64, None), _abi.EALIGN),
+    ((A, B + 4, 64, None), _abi.EALIGN),
+    ((A, A + 48, 64, None), _abi.EALIAS),            # dst over the source's last word
+])
+def test_stream_copy_rejects(lib, args, status):
+    assert lib.trace_stream_copy(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((A, B, C, 40, None), _abi.ESHAPE),
+    ((A, None, C, 64, None), _abi.EINVAL),           # the mix needs both sources
+    ((None, B, C, 64, None), _abi.EINVAL),
+    ((A, B + 8, C, 64, None), _abi.EALIGN),
+    ((A, B, B + 16, 64, None), _abi.EALIAS),         # out over the second source
+    ((A, A, C, 64, None), _abi.EDEVICE if torch.cuda.device_count() == 0 else _abi.OK),  # one source twice is a read
+])
+def test_stream_mix_rejects(lib, args, status):
+    if status == _abi.OK:
+        pytest.skip("a GPU is visible: the call would launch")
+    assert lib.trace_stream_mix(*args) == status
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is visible: valid calls would launch")
+def test_stream_references_without_gpu_are_edevice(lib):
+    assert lib.trace_stream_copy(A, B, 64, None) == _abi.EDEVICE
+    assert lib.trace_stream_mix(A, B, C, 64, None) == _abi.EDEVICE
+    assert lib.trace_stream_copy(None, None, 0, None) == _abi.EDEVICE   # even empty: the device is checked
+
+
 # ---------------------------------------------------------------- row-offset groups
 
 def test_grouped_workspace_sizes(lib):
@@ -339,10 +381,10 @@ def test_grouped_workspace_sizes(lib):
     up8 = lambda b: (b + 7) // 8 * 8  # noqa: E731
     for rows, cols, G in [(1000, 2048, 9), (65536, 2048, 256), (4, 32, 1), (64, 32, 4096), (64, 32, 4097)]:
         # [offsets | tile starts | (group, tile) table | tile maxima | S words | flag |
-        # descriptors]: the table has the two-pass schedule's entries (2048-unit tiles);
+        # descriptors]: the table has the two-pass schedule's entries (TILE-unit tiles);
         # the single pass (up to 4096 groups) adds one 256-byte S line per group, an
         # 8-byte flag and a 16-byte descriptor per 4096-unit tile (on 16 bytes)
-        entries = (rows * cols // 8 + 2047) // 2048 + G
+        entries = (rows * cols // 8 + TILE - 1) // TILE + G
         single = G <= 4096
         want = up8(8 * (G + 1)) + up8(4 * (G + 1)) + 8 * entries + up8(4 * entries + (256 * G if single else 0))
         if single:

@@ -49,8 +49,10 @@ def test_bench_json_line_small():
     # no bounded wait of the single-pass encode gave up; a measured copy rate
     assert d["encode_wait_failures"] == 0
     c = d["copy_ceiling"]
-    assert 0 < c["frac_of_peak"] < 1 and abs(c["GB_s"] - c["bytes_read_plus_written"] / (c["avg_us"] * 1e3)) \
-        <= 0.01 * c["GB_s"]
+    for r in (c, c["two_in_one_out"], c["torch_copy"]):
+        assert 0 < r["frac_of_peak"] < 1 and abs(r["GB_s"] - r["bytes_read_plus_written"] / (r["avg_us"] * 1e3)) \
+            <= 0.01 * r["GB_s"]
+    assert c["two_in_one_out"]["bytes_read_plus_written"] == 3 * c["bytes_read_plus_written"] // 2
 
 
 @pytest.mark.parametrize("config,n_layer", [("kv", 2 * 65536 * 256), ("mxfp4", 65536 * 2048),

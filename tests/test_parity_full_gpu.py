@@ -149,9 +149,9 @@ def test_stream_layer_bench_configuration():
 
 def test_guided_stats_two_layers_in_one_call():
     """guided_fake_quant_stats over two streamed layers in one call (34
-    chunks of [8192, 2048]: 34,816 tiles, past the 32,768 that one reduction
-    workgroup sums, so the per-tile sums go through the two-level
-    reduction). SB and SF against the oracle's float64 sums over the inputs
+    chunks of [8192, 2048]: 69,632 tiles of 1024 units, past the 65,536 that
+    one reduction workgroup sums, so the per-tile sums go through the
+    two-level reduction). SB and SF against the oracle's float64 sums over the inputs
     and the (row-sampled) outputs; the same sums from the two per-layer calls,
     which take the one-level reduction."""
     G.say("full size: guided_fake_quant_stats over 2 streamed layers in one call")
