@@ -70,6 +70,10 @@
  * the tensor, and then `work` must hold trace_quant_workspace_bytes(...)
  * bytes. For MXFP4 both must be NULL (and work may be NULL).
  *
+ * Sizes. A call takes at most 2^35 elements (N = rows * cols) and, with
+ * row offsets, at most 2^22 groups; beyond that it returns TRACE_ESHAPE. These
+ * keep every launch within the 32-bit work-item count of a dispatch.
+ *
  * Streams and errors. Every call validates its arguments on the host before
  * any HIP call, then enqueues its kernels on `stream` (a hipStream_t; NULL is
  * the null stream) and returns without synchronizing. Calls allocate no
@@ -101,7 +105,7 @@ enum trace_fmt { TRACE_FMT_NVFP4 = 0, TRACE_FMT_MXFP4 = 1 };
 enum trace_status {
   TRACE_OK = 0,
   TRACE_EINVAL = -1,  /* NULL required pointer, bad fmt/bits/flag, bad gscale combination */
-  TRACE_ESHAPE = -2,  /* negative size, cols % B != 0, group_rows not dividing rows, N overflow,
+  TRACE_ESHAPE = -2,  /* negative size, cols % B != 0, group_rows not dividing rows, N above 2^35,
                          workspace too small */
   TRACE_EALIGN = -3,  /* a pointer misses its alignment */
   TRACE_EALIAS = -4,  /* an output overlaps an input or another output */
@@ -362,7 +366,7 @@ int discrepancy_stats(int64_t n, const uint16_t* x_t, const uint16_t* x_r,
  * group gets {S, A} = {1, 0}. Results equal separate calls on each group's
  * rows. NVFP4 only matters here: for MXFP4 (no global scale) the offsets are
  * not read and the call equals the ungrouped one (gscale pointers NULL).
- * groups in [1, 2^24]; otherwise ESHAPE.
+ * groups in [1, 2^22]; otherwise ESHAPE.
  */
 
 /* Workspace bytes of the two calls below; 0 for MXFP4, -1 for an invalid
@@ -474,7 +478,8 @@ int trace_gather_pages(const uint8_t* pool, int64_t pool_pages, int64_t page_byt
  *
  *   src, a, b   in   bytes of device memory, 16-byte aligned
  *   dst, out    out  bytes of device memory, 16-byte aligned, disjoint from the inputs
- *   bytes       a multiple of 16, at most 2^44 (else ESHAPE)
+ *   bytes       a multiple of 16, at most 2^37 (else ESHAPE; one launch of up to 2^23
+ *               workgroups)
  */
 int trace_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
 int trace_stream_mix(const void* a, const void* b, void* out, int64_t bytes, void* stream);

@@ -51,7 +51,7 @@ int block_of(int fmt) { return fmt == TRACE_FMT_NVFP4 ? 16 : 32; }
 
 bool valid_fmt(int fmt) { return fmt == TRACE_FMT_NVFP4 || fmt == TRACE_FMT_MXFP4; }
 
-constexpr int64_t kMaxOffsetGroups = (int64_t)1 << 24;  // row-offset groups per call
+constexpr int64_t kMaxOffsetGroups = (int64_t)1 << 22;  // row-offset groups per call
 
 // Guidance planes: bits 1..3 keep the low bits of each magnitude index (N*bits/8
 // bytes), 4 the full codes (N/2). Units of 8 elements are read whole, so a
@@ -65,13 +65,17 @@ struct CallShape {
   tfp4::Shape sh;
 };
 
-// N = rows * cols with cols % B == 0, group_rows dividing rows, and every
-// launch grid (tiles of kTileUnits units; amax partials) inside 2^31 workgroups.
+// N = rows * cols with cols % B == 0, group_rows dividing rows, N at most
+// 2^35 and G * (tiles + kPartMax) below 2^31 (tiles of kTileUnits units per
+// group). Together they bound every launch: the guided pass's 1024-unit tiles
+// number at most 2^22 + G <= 2^22 + 2^21 workgroups of 512 threads, below the
+// 2^32 work-items a dispatch packet can describe, and the quantize and amax
+// launches less.
 int shape_of(int fmt, int64_t rows, int64_t cols, int64_t group_rows, CallShape* out) {
   if (rows < 0 || cols < 0 || group_rows < 0) return TRACE_ESHAPE;
   if (cols % block_of(fmt) != 0) return TRACE_ESHAPE;
   if (group_rows > 0 && rows % group_rows != 0) return TRACE_ESHAPE;
-  const int64_t kMaxElems = (int64_t)1 << 44;
+  const int64_t kMaxElems = (int64_t)1 << 35;
   if (cols != 0 && rows > kMaxElems / cols) return TRACE_ESHAPE;
   const int64_t grows = group_rows > 0 ? group_rows : rows;
   out->n = rows * cols;

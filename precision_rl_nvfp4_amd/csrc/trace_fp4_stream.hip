@@ -18,7 +18,7 @@ namespace {
 constexpr int kStreamThreads = 256;
 constexpr int kStreamWords = 4;                        // 16-byte words per thread
 constexpr int64_t kStreamTile = (int64_t)kStreamThreads * kStreamWords;
-constexpr int64_t kMaxStreamBytes = (int64_t)1 << 44;   // 2^29 workgroups at most
+constexpr int64_t kMaxStreamBytes = (int64_t)1 << 37;   // 2^23 workgroups, 2^31 work-items at most
 
 typedef unsigned int v4u_t __attribute__((ext_vector_type(4)));
 

@@ -151,6 +151,7 @@ WB = 8192               # quantize workspace bytes for one group
     ((0, 4, 32, -2, A, None, B, C, D, None, W, WB, None), _abi.ESHAPE),         # negative group_rows
     ((0, 4, 32, 3, A, None, B, C, D, None, W, WB, None), _abi.ESHAPE),          # 3 does not divide 4
     ((0, 2 ** 40, 2 ** 20, 0, A, None, B, C, D, None, W, WB, None), _abi.ESHAPE),  # N limit
+    ((0, 2 ** 20, 2 ** 15 + 16, 0, A, None, B, C, D, None, W, WB, None), _abi.ESHAPE),  # N just above 2^35
     ((0, 4, 32, 0, A, None, B, C, None, None, W, WB, None), _abi.EINVAL),       # NVFP4 needs a gscale
     ((0, 4, 32, 0, A, E, B, C, D, None, W, WB, None), _abi.EINVAL),             # both gscale_in and out
     ((1, 4, 32, 0, A, E, B, C, None, None, None, 0, None), _abi.EINVAL),        # MXFP4 takes no gscale
@@ -341,7 +342,8 @@ def test_gather_without_gpu_is_edevice(lib):
 @pytest.mark.parametrize("args,status", [
     ((A, B, 24, None), _abi.ESHAPE),                 # not whole 16-byte words
     ((A, B, -16, None), _abi.ESHAPE),
-    ((A, B, 1 << 45, None), _abi.ESHAPE),            # beyond 2^44 bytes
+    ((A, B, (1 << 37) + 16, None), _abi.ESHAPE),     # beyond 2^37 bytes
+    ((A, B, 1 << 45, None), _abi.ESHAPE),
     ((None, B, 64, None), _abi.EINVAL),
     ((A, None, 64, None), _abi.EINVAL),
     ((A + 8, B, 64, None), _abi.EALIGN),
@@ -393,6 +395,22 @@ def test_grouped_workspace_sizes(lib):
     assert lib.trace_grouped_workspace_bytes(1, 64, 2048, 4) == 0
     assert lib.trace_grouped_workspace_bytes(0, 64, 2048, 0) == -1
     assert lib.trace_grouped_workspace_bytes(0, 64, 24, 2) == -1
+    # at most 2^22 groups and 2^35 elements per call
+    assert lib.trace_grouped_workspace_bytes(0, 2 ** 22, 16, 2 ** 22) > 0
+    assert lib.trace_grouped_workspace_bytes(0, 2 ** 22, 16, 2 ** 22 + 1) == -1
+    assert lib.trace_grouped_workspace_bytes(0, 2 ** 20, 2 ** 15, 4) > 0
+    assert lib.trace_grouped_workspace_bytes(0, 2 ** 20, 2 ** 15 + 16, 4) == -1
+
+
+def test_size_limits_keep_launches_in_32_bit_grids(lib):
+    """2^35 elements is the largest call: its workspaces are defined there and
+    not one block beyond (every launch then stays below 2^32 work-items)."""
+    assert lib.trace_quant_workspace_bytes(0, 2 ** 20, 2 ** 15, 0) > 0
+    assert lib.trace_quant_workspace_bytes(0, 2 ** 20, 2 ** 15 + 16, 0) == -1
+    assert lib.trace_guided_stats_workspace_bytes(0, 2 ** 20, 2 ** 15, 0) > 0
+    assert lib.trace_guided_stats_workspace_bytes(0, 2 ** 20, 2 ** 15 + 16, 0) == -1
+    # 2^35 elements in 1024-unit tiles of 512 threads: 2^22 workgroups, 2^31 work-items
+    assert (2 ** 35 // 8 // GTILE) * 512 < 2 ** 32
 
 
 GW = 0x900000   # fake workspace for the grouped calls
