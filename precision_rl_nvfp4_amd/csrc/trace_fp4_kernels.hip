@@ -1654,29 +1654,71 @@ __global__ __launch_bounds__(guided_threads(STATS)) void guided_kernel(GuidedArg
   if constexpr (DIAG) {
     if (threadIdx.x < kMismatchCounts) hist[threadIdx.x] = 0u;
   }
+  // Equal groups (WRUN): each wave takes 64 * GU consecutive units (unit j
+  // of lane l at j * 64 + l), so the wave's scale bytes (one per block: two
+  // units for NVFP4, four for MXFP4) and, for 1-bit records, its record bytes
+  // (one per unit) are one contiguous run each. A wave whose runs lie inside
+  // the group and start on a dword reads them as one dword per lane and hands
+  // each lane its bytes with ds_bpermute (a load or two per lane instead of
+  // one or two per unit); any other wave reads them per unit, as wider
+  // records always are. The x, x_r and y accesses stay one contiguous KiB per
+  // wave instruction either way.
+  constexpr bool WRUN = MAP == 0;
+  constexpr int SU = FMT == 0 ? 1 : 2;   // log2 of the units per block
+  const int wl = (int)threadIdx.x & 63;
+  const int64_t wb = tbase + (int64_t)((int)threadIdx.x >> 6) * (GU * 64);   // the wave's first unit (WRUN)
+  bool words = false;
+  uint32_t sdw = 0u, gdw = 0u;
+  if constexpr (WRUN) {
+    const uint32_t* sp = reinterpret_cast<const uint32_t*>(a.scales + ((gbase + wb) >> SU));
+    const uint32_t* gp = BITS == 1 ? reinterpret_cast<const uint32_t*>(a.guide + gbase + wb) : nullptr;
+    words = wb + GU * 64 <= lim && (reinterpret_cast<uintptr_t>(sp) & 3u) == 0 &&
+            (reinterpret_cast<uintptr_t>(gp) & 3u) == 0;
+    if (words) {
+      if (wl < (16 >> SU) * GU) sdw = __builtin_nontemporal_load(sp + wl);
+      if (BITS == 1 && wl < 16 * GU) gdw = __builtin_nontemporal_load(gp + wl);
+    }
+  }
   // Issue the tile's loads first; the factor table is built while they fly.
   uint4 v[GU];
   uint4 vr[STATS ? GU : 1];
   uint32_t sbv[GU], gv[GU];
 #pragma unroll
   for (int j = 0; j < GU; ++j) {
-    const int64_t u = tbase + j * GT + threadIdx.x;
+    const int64_t u = WRUN ? wb + j * 64 + wl : tbase + j * GT + threadIdx.x;
     const bool ok = u < lim;
     const int64_t gu = gbase + u;
     v[j] = ok ? load_stream(a.x + gu) : make_uint4(0u, 0u, 0u, 0u);
     if constexpr (STATS) vr[j] = ok ? load_stream(a.xr + gu) : make_uint4(0u, 0u, 0u, 0u);
-    sbv[j] = ok ? (uint32_t)__builtin_nontemporal_load(a.scales + (FMT == 0 ? (gu >> 1) : (gu >> 2))) : 0u;
-    if constexpr (BITS == 1) {
-      gv[j] = ok ? (uint32_t)__builtin_nontemporal_load(a.guide + gu) : 0u;
-    } else if constexpr (BITS == 2) {
+    sbv[j] = 0u;
+    gv[j] = 0u;
+    if (WRUN && words) {
+      if constexpr (BITS <= 1) continue;   // scale and record bytes from the dwords below
+    } else {
+      sbv[j] = ok ? (uint32_t)__builtin_nontemporal_load(a.scales + (FMT == 0 ? (gu >> 1) : (gu >> 2))) : 0u;
+      if constexpr (BITS == 1) gv[j] = ok ? (uint32_t)__builtin_nontemporal_load(a.guide + gu) : 0u;
+    }
+    if constexpr (BITS == 2) {
       gv[j] = ok ? (uint32_t)__builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(a.guide) + gu) : 0u;
     } else if constexpr (BITS == 3) {
       const uint8_t* q = a.guide + 3 * gu;
       gv[j] = ok ? (uint32_t)q[0] | ((uint32_t)q[1] << 8) | ((uint32_t)q[2] << 16) : 0u;
     } else if constexpr (BITS == 4) {
       gv[j] = ok ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(a.guide) + gu) : 0u;
-    } else {
-      gv[j] = 0u;
+    }
+  }
+  if constexpr (WRUN) {
+    if (words) {   // uniform in the wave, so every lane takes part in the permutes
+#pragma unroll
+      for (int j = 0; j < GU; ++j) {
+        // unit o = j * 64 + wl of the run: scale byte o >> SU, record byte o
+        const uint32_t sw = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (j * (16 >> SU) + (wl >> (SU + 2))), (int)sdw);
+        sbv[j] = (sw >> (8 * ((wl >> SU) & 3))) & 0xFFu;
+        if constexpr (BITS == 1) {
+          const uint32_t gw = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (j * 16 + (wl >> 2)), (int)gdw);
+          gv[j] = (gw >> (8 * (wl & 3))) & 0xFFu;
+        }
+      }
     }
   }
   if constexpr (PACK) {
@@ -1692,7 +1734,7 @@ __global__ __launch_bounds__(guided_threads(STATS)) void guided_kernel(GuidedArg
   double acc_b = 0.0, acc_f = 0.0;
 #pragma unroll
   for (int j = 0; j < GU; ++j) {
-    const int64_t u = tbase + j * GT + threadIdx.x;
+    const int64_t u = WRUN ? wb + j * 64 + wl : tbase + j * GT + threadIdx.x;
     float r, d = 0.0f, dsc = 0.0f;
     if constexpr (PACK) {
       nv_factors_pair(sbv[j], gs[(j * GT + threadIdx.x) >> a.map.lg], r, d);

@@ -388,6 +388,51 @@ def test_guided_fake_quant_stats(fmt, bits, rows, cols):
 
 
 @pytest.mark.parametrize("fmt", [NV, MX])
+@pytest.mark.parametrize("bits", [0, 1, 2, 4])
+@pytest.mark.parametrize("shift", [0, 1, 3])
+def test_guided_wave_runs_unaligned_and_ragged(fmt, bits, shift):
+    """Guided rounding over equal groups reads a wave's scale bytes (and
+    1-bit record bytes) as dwords when the wave's run lies inside its group
+    and starts on a dword, and per unit otherwise. NVFP4 groups of 37 rows x
+    2064 columns (9,546 units) start off a dword in both planes and end in a
+    ragged run (MXFP4, whose groups form one tensor: 111 x 2080); the planes
+    are also moved to byte offsets 1 and 3. Plain and fused passes and
+    Reconstruct, GPU vs oracle."""
+    G.say(f"guided wave runs fmt={fmt} bits={bits} shift={shift}")
+    G_, gr = 3, 37
+    cols = 2064 if fmt == NV else 2080
+    xt, xr = _grouped_pair(G_, gr, cols, 5, mx=(fmt == MX))
+    rows = G_ * gr
+    rec_bits = 4 if bits == 0 else bits
+    t, r = G.to_dev(xt, rows, cols), G.to_dev(xr, rows, cols)
+    g = tq.encode_guidance(r, fmt, rec_bits, group_rows=gr)
+
+    def moved(p, step):
+        raw = torch.zeros(p.numel() + 64, dtype=torch.uint8, device=G.DEV)
+        v = raw[step:step + p.numel()].view(p.shape)
+        v.copy_(p)
+        return v
+
+    # records of 2 and 4 bits keep their 2- and 4-byte alignment
+    g = g._replace(scales=moved(g.scales, shift), guide=moved(g.guide, shift * {1: 1, 2: 2, 4: 4}[rec_bits]))
+    y, codes = tq.guided_fake_quant(t, g, bits=bits, with_codes=True)
+    y2, codes2, acc = tq.guided_fake_quant_stats(t, r, g, bits=bits, with_codes=True)
+    o_enc = G.oracle_encode(fmt, rec_bits, xr, rows, gr)
+    o = G.oracle_guided(fmt, bits, xt, o_enc, rows, gr)
+    what = f"fmt={fmt} bits={bits} shift={shift}"
+    G.assert_same(G.bits_of(y), o["y"], f"guided y {what}")
+    G.assert_same(G.u8(codes), o["codes"], f"guided codes {what}")
+    G.assert_same(G.bits_of(y2), o["y"], f"guided y (stats) {what}")
+    G.assert_same(G.u8(codes2), o["codes"], f"guided codes (stats) {what}")
+    sb, sf, n = ofp4.discrepancy_stats(xt, xr, o["y"], o_enc["y"])
+    a = acc.cpu().numpy()
+    assert a[2] == n and G.rel_close(a[0], sb) and G.rel_close(a[1], sf), (a, sb, sf, n)
+    if bits in (1, 2):
+        ref = tq.decode_guidance(t, g)
+        G.assert_same(G.u8(ref), G.oracle_decode(fmt, xt, o_enc, rows, gr, bits), f"reference codes {what}")
+
+
+@pytest.mark.parametrize("fmt", [NV, MX])
 def test_guided_fake_quant_stats_grouped_and_accumulated(fmt):
     G.say(f"guided_fake_quant_stats grouped fmt={fmt}")
     xt, xr = _grouped_pair(3, 37, 2048, 3, mx=(fmt == MX))
