@@ -1654,16 +1654,18 @@ __global__ __launch_bounds__(guided_threads(STATS)) void guided_kernel(GuidedArg
   if constexpr (DIAG) {
     if (threadIdx.x < kMismatchCounts) hist[threadIdx.x] = 0u;
   }
-  // Equal groups (WRUN): each wave takes 64 * GU consecutive units (unit j
-  // of lane l at j * 64 + l), so the wave's scale bytes (one per block: two
-  // units for NVFP4, four for MXFP4) and, for 1-bit records, its record bytes
-  // (one per unit) are one contiguous run each. A wave whose runs lie inside
-  // the group and start on a dword reads them as one dword per lane and hands
-  // each lane its bytes with ds_bpermute (a load or two per lane instead of
-  // one or two per unit); any other wave reads them per unit, as wider
-  // records always are. The x, x_r and y accesses stay one contiguous KiB per
-  // wave instruction either way.
-  constexpr bool WRUN = MAP == 0;
+  // The fused statistics pass over equal groups and the row-offset passes,
+  // with no record or a 1-bit one (WRUN): each wave takes 64 * GU
+  // consecutive units (unit j of lane l at j * 64 + l), so the wave's scale
+  // bytes (one per block: two units for NVFP4, four for MXFP4) and record
+  // bytes (one per unit) are one contiguous run each. A wave whose runs lie
+  // inside the group and start on a dword reads them as one dword per lane
+  // and hands each lane its bytes with ds_bpermute (two loads per lane
+  // instead of two per unit); any other wave reads them per unit. The x, x_r
+  // and y accesses stay one contiguous KiB per wave instruction either way.
+  // Elsewhere unit j of thread t is at j * GT + t: there this layout measured
+  // slower (plain guided rounding by 0.6%, 2- and 3-bit records by 2-6%).
+  constexpr bool WRUN = ((STATS && MAP == 0) || MAP == 2) && BITS <= 1;
   constexpr int SU = FMT == 0 ? 1 : 2;   // log2 of the units per block
   const int wl = (int)threadIdx.x & 63;
   const int64_t wb = tbase + (int64_t)((int)threadIdx.x >> 6) * (GU * 64);   // the wave's first unit (WRUN)

@@ -391,13 +391,13 @@ def test_guided_fake_quant_stats(fmt, bits, rows, cols):
 @pytest.mark.parametrize("bits", [0, 1, 2, 4])
 @pytest.mark.parametrize("shift", [0, 1, 3])
 def test_guided_wave_runs_unaligned_and_ragged(fmt, bits, shift):
-    """Guided rounding over equal groups reads a wave's scale bytes (and
-    1-bit record bytes) as dwords when the wave's run lies inside its group
-    and starts on a dword, and per unit otherwise. NVFP4 groups of 37 rows x
-    2064 columns (9,546 units) start off a dword in both planes and end in a
+    """The fused pass with no record or a 1-bit one reads a wave's scale and
+    record bytes as dwords when the wave's run lies inside its group and
+    starts on a dword, and per unit otherwise. NVFP4 groups of 37 rows x 2064
+    columns (9,546 units) start off a dword in both planes and end in a
     ragged run (MXFP4, whose groups form one tensor: 111 x 2080); the planes
-    are also moved to byte offsets 1 and 3. Plain and fused passes and
-    Reconstruct, GPU vs oracle."""
+    are also moved to byte offsets 1 and 3. The plain pass, wider records and
+    Reconstruct (per-unit reads) on the same inputs. GPU vs oracle."""
     G.say(f"guided wave runs fmt={fmt} bits={bits} shift={shift}")
     G_, gr = 3, 37
     cols = 2064 if fmt == NV else 2080
