@@ -65,7 +65,7 @@ typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kFltMax = 3.40282346638528859812e+38f;
 constexpr int kMidGroups = 64;          // first level of the partial-sum reduction
-constexpr int64_t kDirectTiles = 65536; // up to this many per-tile pairs are summed by one workgroup
+constexpr int64_t kDirectTiles = 65536; // up to this many per-tile pairs are summed in one level
 // Tile of guided rounding and of the fused statistics (equal or packed
 // groups): half the tile of the other kernels. Measured on a streamed
 // layer: the fused pass 1-5% faster and plain guided rounding 1-5% faster
@@ -527,6 +527,7 @@ struct GuidedArgs {
   const uint4* xr;           // rollout input (stats)
   double* partials;          // 2 per workgroup (stats)
   uint32_t* cpart;           // [kMismatchCounts][tiles] mismatch counts (diagnostics)
+  uint32_t* ticket;          // counter of the split final sum, zeroed here (stats; or NULL)
 };
 
 
@@ -1654,6 +1655,10 @@ __global__ __launch_bounds__(guided_threads(STATS)) void guided_kernel(GuidedArg
   if constexpr (DIAG) {
     if (threadIdx.x < kMismatchCounts) hist[threadIdx.x] = 0u;
   }
+  if constexpr (STATS) {
+    if (a.ticket != nullptr && blockIdx.x == 0 && threadIdx.x == 0)
+      __hip_atomic_store(a.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   // The fused statistics pass over equal groups and the row-offset passes,
   // with no record or a 1-bit one (WRUN): each wave takes 64 * GU
   // consecutive units (unit j of lane l at j * 64 + l), so the wave's scale
@@ -1844,22 +1849,21 @@ __global__ __launch_bounds__(kThreads) void sums_mid_kernel(const double* __rest
 
 // Fixed-order reduction of `groups` partial pairs into acc3 = {SB, SF, n}, by
 // one workgroup of kSumThreads. Thread t sums pairs t, t + kSumThreads, ... in
-// order, loading kSumBatch pairs at a time, so that a streamed layer's 34,816
-// pairs (34 per thread, on 1024-unit tiles) take two round trips to memory;
-// the 16 wave sums are then added in wave order. (Workspaces are only 8-byte
-// aligned: a pair is two loads.)
+// order, loading kSumBatch pairs at a time (two round trips to memory for
+// 34 pairs per thread); the 16 wave sums are then added in wave order.
+// (Workspaces are only 8-byte aligned: a pair is two loads.)
 constexpr int kSumThreads = 1024;
 constexpr int kSumBatch = 17;
-__global__ __launch_bounds__(kSumThreads) void sums_final_kernel(const double* __restrict__ partials,
-                                                                 int64_t groups, int64_t n, double* acc3,
-                                                                 int accumulate) {
-  double sb = 0.0, sf = 0.0;
-  for (int64_t base = threadIdx.x; base < groups; base += (int64_t)kSumBatch * kSumThreads) {
+
+// This thread's share of pairs [lo, hi): lo + t, lo + t + kSumThreads, ...
+__device__ __forceinline__ void pair_range_sum(const double* __restrict__ p, int64_t lo, int64_t hi, double& sb,
+                                               double& sf) {
+  for (int64_t base = lo + threadIdx.x; base < hi; base += (int64_t)kSumBatch * kSumThreads) {
     double2 v[kSumBatch];
 #pragma unroll
     for (int k = 0; k < kSumBatch; ++k) {
       const int64_t i = base + (int64_t)k * kSumThreads;
-      v[k] = i < groups ? make_double2(partials[2 * i], partials[2 * i + 1]) : make_double2(0.0, 0.0);
+      v[k] = i < hi ? make_double2(p[2 * i], p[2 * i + 1]) : make_double2(0.0, 0.0);
     }
 #pragma unroll
     for (int k = 0; k < kSumBatch; ++k) {
@@ -1867,6 +1871,10 @@ __global__ __launch_bounds__(kSumThreads) void sums_final_kernel(const double* _
       sf += v[k].y;
     }
   }
+}
+
+// The kSumThreads threads' sums added in wave order; valid in thread 0.
+__device__ __forceinline__ void pair_block_sum(double& sb, double& sf) {
   __shared__ double wb[kSumThreads / 64], wf[kSumThreads / 64];
   sb = wave_sum(sb);
   sf = wave_sum(sf);
@@ -1882,16 +1890,60 @@ __global__ __launch_bounds__(kSumThreads) void sums_final_kernel(const double* _
       sb += wb[w];
       sf += wf[w];
     }
-    if (accumulate) {
-      acc3[0] += sb;
-      acc3[1] += sf;
-      acc3[2] += (double)n;
-    } else {
-      acc3[0] = sb;
-      acc3[1] = sf;
-      acc3[2] = (double)n;
-    }
   }
+}
+
+__device__ __forceinline__ void put_acc3(double* acc3, double sb, double sf, int64_t n, int accumulate) {
+  if (accumulate) {
+    acc3[0] += sb;
+    acc3[1] += sf;
+    acc3[2] += (double)n;
+  } else {
+    acc3[0] = sb;
+    acc3[1] = sf;
+    acc3[2] = (double)n;
+  }
+}
+
+__global__ __launch_bounds__(kSumThreads) void sums_final_kernel(const double* __restrict__ partials,
+                                                                 int64_t groups, int64_t n, double* acc3,
+                                                                 int accumulate) {
+  double sb = 0.0, sf = 0.0;
+  pair_range_sum(partials, 0, groups, sb, sf);
+  pair_block_sum(sb, sf);
+  if (threadIdx.x == 0) put_acc3(acc3, sb, sf, n, accumulate);
+}
+
+// The same reduction over kSplitGroups workgroups, one per XCD, for the
+// fused pass's per-tile pairs (one workgroup reads them at one CU's rate:
+// 7.6 µs for a streamed layer's 34,816; eight take 5.7). Workgroup w sums pairs
+// [w * per, (w + 1) * per) as above and stores its pair to mid[w] with
+// agent-scope stores; once they are complete it takes a ticket from an
+// agent-scope counter that the guided kernel zeroed, and the workgroup with
+// the last ticket adds the kSplitGroups pairs in index order into acc3. The
+// result does not depend on which workgroup finishes last; nothing waits.
+constexpr int kSplitGroups = 8;
+constexpr int64_t kSplitMin = 8192;   // pairs from which the final sum is split
+static_assert(2 * kSplitGroups < 2 * kMidGroups - 1, "the split pairs and the counter fit the second-level area");
+__global__ __launch_bounds__(kSumThreads) void sums_split_kernel(const double* __restrict__ partials, int64_t count,
+                                                                 int64_t per, double* mid, uint32_t* ticket,
+                                                                 int64_t n, double* acc3, int accumulate) {
+  const int64_t lo = min((int64_t)blockIdx.x * per, count), hi = min(lo + per, count);
+  double sb = 0.0, sf = 0.0;
+  pair_range_sum(partials, lo, hi, sb, sf);
+  pair_block_sum(sb, sf);
+  if (threadIdx.x != 0) return;
+  __hip_atomic_store(&mid[2 * blockIdx.x], sb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(&mid[2 * blockIdx.x + 1], sf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0);   // the pair is stored before the ticket is taken
+  const uint32_t t = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (t != gridDim.x - 1) return;
+  double ab = 0.0, af = 0.0;
+  for (int w = 0; w < (int)gridDim.x; ++w) {
+    ab += __hip_atomic_load(&mid[2 * w], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    af += __hip_atomic_load(&mid[2 * w + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  put_acc3(acc3, ab, af, n, accumulate);
 }
 
 // ------------------------------------------------------------ discrepancy_stats
@@ -2386,6 +2438,11 @@ hipError_t launch_guided(int fmt, int bits, bool decode_only, const Shape& sh, c
   a.partials = static_cast<double*>(work);
   const int64_t tiles = tile_grid(a.map);
   if (stats) a.cpart = reinterpret_cast<uint32_t*>(a.partials + 2 * (tiles + kMidGroups));
+  // The split final sum keeps its pairs and counter in the second-level area
+  // (unused below kDirectTiles): pairs at [0, kSplitGroups), the counter in
+  // the area's last word.
+  const bool split = stats && tiles >= kSplitMin && tiles <= kDirectTiles;
+  if (split) a.ticket = reinterpret_cast<uint32_t*>(a.partials + 2 * (tiles + kMidGroups) - 1);
   const bool wc = codes != nullptr;
   hipError_t e;
   if (fmt == 1) e = guided_pack<1, 0>(bits, decode_only, wc, stats, diag, a, tiles, stream);
@@ -2397,8 +2454,14 @@ hipError_t launch_guided(int fmt, int bits, bool decode_only, const Shape& sh, c
                (const uint32_t*)a.cpart, tiles, counts, accumulate);
     if (e != hipSuccess) return e;
   }
-  // Per-tile pairs -> acc3 in one workgroup (up to kDirectTiles pairs), else
-  // per-tile pairs -> kMidGroups pairs -> acc3; each level in a fixed order.
+  // Per-tile pairs -> acc3 in one workgroup (below kSplitMin pairs), in
+  // kSplitGroups workgroups (up to kDirectTiles), else per-tile pairs ->
+  // kMidGroups pairs -> acc3; each level in a fixed order.
+  if (split) {
+    const int64_t per = (tiles + kSplitGroups - 1) / kSplitGroups;
+    return launch(sums_split_kernel, dim3(kSplitGroups), dim3(kSumThreads), stream, (const double*)a.partials,
+                  tiles, per, a.partials + 2 * tiles, a.ticket, units * kUnitElems, acc3, accumulate);
+  }
   if (tiles <= kDirectTiles)
     return launch(sums_final_kernel, dim3(1), dim3(kSumThreads), stream, (const double*)a.partials, tiles,
                   units * kUnitElems, acc3, accumulate);

@@ -147,6 +147,43 @@ def test_stream_layer_bench_configuration():
     assert a[2] == n and G.rel_close(a[0], sb) and G.rel_close(a[1], sf), (a, (sb, sf, n))
 
 
+@pytest.mark.parametrize("rows", [32764, 32768, 32772])
+def test_guided_stats_reduction_split_boundary(rows):
+    """guided_fake_quant_stats reduces its per-tile sums in one workgroup
+    below 8,192 tiles and in eight from there (each a fixed slice, the last to
+    finish adding the eight in order): 8,191, 8,192 and 8,193 tiles of 1024
+    units over [rows, 2048] with one global scale. SB and SF against the
+    oracle's float64 sums over the inputs and the (row-sampled) outputs; with
+    accumulate=True a second call adds the same sums; the result is the same
+    bits on a repeat."""
+    G.say(f"full size: stats reduction at the split boundary, rows={rows}")
+    dev = G.DEV
+    CH = syn.STREAM_CHUNK
+    sigma = syn.stream_sigma(3, dev)
+    xt = torch.empty((4 * CH + CH, syn.HIDDEN), dtype=torch.bfloat16, device=dev)
+    xr = torch.empty_like(xt)
+    for c in range(5):
+        a, b = syn.stream_pair(3, c, dev, sigma=sigma)
+        xt[c * CH:(c + 1) * CH].copy_(a)
+        xr[c * CH:(c + 1) * CH].copy_(b)
+        del a, b
+    xt, xr = xt[:rows].contiguous(), xr[:rows].contiguous()
+    g = tq.encode_guidance(xr, NV, 1, with_y=True)
+    y, codes, acc = tq.guided_fake_quant_stats(xt, xr, g, with_codes=True)
+    _, _, acc_again = tq.guided_fake_quant_stats(xt, xr, g)
+    tq.guided_fake_quant_stats(xt, xr, g, acc=acc_again, accumulate=True)
+    torch.cuda.synchronize()
+    xt_b, xr_b = _bits(xt), _bits(xr)
+    S = _group_S(NV, xr_b)
+    for r0, r1 in _samples(rows):
+        _check_rows(NV, 1, xt_b, xr_b, syn.HIDDEN, r0, r1, S, g, y_g=y, codes_g=codes, y_r=g.y)
+    a = acc.cpu().numpy()
+    sb, sf, n = G.oracle_plane_sums(xt, xr, y, g.y)
+    assert a[2] == n == rows * syn.HIDDEN and G.rel_close(a[0], sb) and G.rel_close(a[1], sf), (a, (sb, sf, n))
+    b = acc_again.cpu().numpy()
+    assert b[2] == 2 * a[2] and b[0] == 2 * a[0] and b[1] == 2 * a[1], (a, b)
+
+
 def test_guided_stats_two_layers_in_one_call():
     """guided_fake_quant_stats over two streamed layers in one call (34
     chunks of [8192, 2048]: 69,632 tiles of 1024 units, past the 65,536 that
