@@ -71,12 +71,15 @@ def test_guided_calls_on_two_streams():
     assert torch.equal(acc_a, ref_acc)
 
 
-def test_step_captured_in_a_graph():
+@pytest.mark.parametrize("n_chunks", [2, 5])
+def test_step_captured_in_a_graph(n_chunks):
     """encode (single pass) + guided_fake_quant_stats with mismatch counts on
-    2 chunks, captured once, replayed 4 times with eager work in between;
-    every replay equals the eager results."""
-    G.say("graph capture of the step")
-    xt, xr = _chunks(23, 2)
+    2 chunks (4,096 tiles: the final sum in one workgroup) and 5 (10,240
+    tiles: split over eight, whose ticket counter the guided kernel zeroes on
+    every replay), captured once, replayed 4 times with eager work in
+    between; every replay equals the eager results."""
+    G.say(f"graph capture of the step, {n_chunks} chunks")
+    xt, xr = _chunks(23, n_chunks)
     rows, cols = xt.shape
     eager_g = tq.encode_guidance(xr, "nvfp4", 1, group_rows=CH)
     eager = tq.guided_fake_quant_stats(xt, xr, eager_g, with_codes=True, mismatch=True)
