@@ -52,9 +52,14 @@ def test_single_pass_encodes_on_two_streams():
     assert tq.encode_wait_failures() == fails0
 
 
-def test_guided_calls_on_two_streams():
-    G.say("two streams: guided calls")
-    xt, xr = _chunks(22, 1)
+@pytest.mark.parametrize("n_chunks", [1, 4])
+def test_guided_calls_on_two_streams(n_chunks):
+    """Guided calls on two streams at once, each with its own workspace: a
+    fused pass and a plain one, then two fused passes (4 chunks: 8,192
+    tiles, so each call's final sum is split over eight workgroups with its
+    own ticket counter). Every result equals the sequential one."""
+    G.say(f"two streams: guided calls, {n_chunks} chunks")
+    xt, xr = _chunks(22, n_chunks)
     g = tq.encode_guidance(xr, "nvfp4", 1, group_rows=CH)
     ref_y, ref_c, ref_acc = tq.guided_fake_quant_stats(xt, xr, g, with_codes=True)
     torch.cuda.synchronize()
@@ -65,10 +70,12 @@ def test_guided_calls_on_two_streams():
         ya, ca, acc_a = tq.guided_fake_quant_stats(xt, xr, g, with_codes=True)
     with torch.cuda.stream(sb):
         yb, cb = tq.guided_fake_quant(xt, g, with_codes=True)
+        yc, cc, acc_c = tq.guided_fake_quant_stats(xt, xr, g, with_codes=True)
     torch.cuda.synchronize()
     assert torch.equal(ya.view(torch.int16), ref_y.view(torch.int16)) and torch.equal(ca, ref_c)
     assert torch.equal(yb.view(torch.int16), ref_y.view(torch.int16)) and torch.equal(cb, ref_c)
-    assert torch.equal(acc_a, ref_acc)
+    assert torch.equal(yc.view(torch.int16), ref_y.view(torch.int16)) and torch.equal(cc, ref_c)
+    assert torch.equal(acc_a, ref_acc) and torch.equal(acc_c, ref_acc)
 
 
 @pytest.mark.parametrize("n_chunks", [2, 5])
