@@ -4,15 +4,17 @@
 Workload: the long-trajectory stream. 20 guided (deepest) MoE layers x 17
 chunks of 8,192 tokens x 2,048 hidden, bf16 train/rollout pairs (8K prompt +
 128K response = 139,264 tokens per layer), NVFP4 with one FP32 global scale
-per chunk. A step is one pass of the whole path over that batch, one call per
-layer and side (the 17 chunks of a layer are the call's global-scale groups):
+per chunk. A step is one pass of the whole path over that batch:
 
-  rollout side   encode_guidance(bits=1): per-chunk amax -> global scale,
-                 E4M3 block scales, RTN codes, the packed mantissa-bit plane
-  training side  guided_fake_quant_stats(bits=1): Reconstruct + BracketFP4 +
-                 selection + bf16 dequantization -> y_t, and in the same pass
-                 the layer's sums of (x_t - x_r)^2 and (y_t - y_r)^2 (y_r the
-                 rollout's RTN output, recomputed from x_r)
+  rollout side   encode_guidance(bits=1), one call over the whole stream (its
+                 340 chunks are the call's global-scale groups): per-chunk
+                 amax -> global scale, E4M3 block scales, RTN codes, the
+                 packed mantissa-bit plane
+  training side  guided_fake_quant_stats(bits=1), one call per layer:
+                 Reconstruct + BracketFP4 + selection + bf16 dequantization
+                 -> y_t, and in the same pass the layer's sums of
+                 (x_t - x_r)^2 and (y_t - y_r)^2 (y_r the rollout's RTN
+                 output, recomputed from x_r)
 
 Inputs are seeded synthetic tensors drawn on the GPU (no model, no dataset);
 they are resident in HBM before the timed region starts. Every kernel runs
@@ -22,9 +24,12 @@ Prints one JSON line. ``roofline`` covers the call with the largest share of
 step time, from HIP events recorded on the launch stream around each phase;
 ``kernels`` also reports plain guided_fake_quant (no statistics) and the
 statistics pass with mismatch counts, each timed the same way outside the
-step; ``mismatch`` summarizes those counts (code distances between the
-training and rollout sides, per layer); ``cpu_baseline`` times the CPU oracle
-on a bounded sample of the same workload in a process pool.
+step, and the per-layer encode call; ``mismatch`` summarizes those counts
+(code distances between the training and rollout sides, per layer);
+``copy_ceiling`` times the library's stream references (and torch's copy) on
+the same device as the HBM rates the kernels are compared with;
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same
+workload in a process pool.
 """
 
 from __future__ import annotations
