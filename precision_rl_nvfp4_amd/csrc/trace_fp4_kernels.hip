@@ -1957,6 +1957,7 @@ __device__ __forceinline__ void accum_unit(const uint4& a, const uint4& b, doubl
 
 __device__ __forceinline__ double bf16_f64(uint32_t b) { return (double)__uint_as_float(b << 16); }
 
+constexpr int kStatsUnits = 4;   // units per thread and array in a discrepancy_stats tile
 __global__ __launch_bounds__(kThreads) void stats_partial_kernel(const uint16_t* __restrict__ xt,
                                                                  const uint16_t* __restrict__ xr,
                                                                  const uint16_t* __restrict__ yt,
@@ -1967,11 +1968,29 @@ __global__ __launch_bounds__(kThreads) void stats_partial_kernel(const uint16_t*
   const uint4* xr4 = reinterpret_cast<const uint4*>(xr);
   const uint4* yt4 = reinterpret_cast<const uint4*>(yt);
   const uint4* yr4 = reinterpret_cast<const uint4*>(yr);
+  // Workgroup tiles of kStatsUnits * kThreads consecutive units (unit k of
+  // thread t at k * kThreads + t), the workgroups striding over the arrays
+  // tile by tile; every load of a tile is issued before its sums. Against
+  // one unit per thread and stride: 337 against 370 µs for four arrays of a
+  // streamed layer (84% of the HBM peak against 77%); 6 or 8 units tie.
   double sb = 0.0, sf = 0.0;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < units; u += stride) {
-    accum_unit(load_stream(xt4 + u), load_stream(xr4 + u), sb);
-    accum_unit(load_stream(yt4 + u), load_stream(yr4 + u), sf);
+  const int64_t tstride = (int64_t)gridDim.x * kThreads * kStatsUnits;
+  for (int64_t tb = (int64_t)blockIdx.x * kThreads * kStatsUnits; tb < units; tb += tstride) {
+    uint4 a[kStatsUnits], b[kStatsUnits], c[kStatsUnits], d[kStatsUnits];
+#pragma unroll
+    for (int k = 0; k < kStatsUnits; ++k) {
+      const int64_t u = tb + k * kThreads + threadIdx.x;
+      const bool ok = u < units;
+      a[k] = ok ? load_stream(xt4 + u) : make_uint4(0u, 0u, 0u, 0u);
+      b[k] = ok ? load_stream(xr4 + u) : make_uint4(0u, 0u, 0u, 0u);
+      c[k] = ok ? load_stream(yt4 + u) : make_uint4(0u, 0u, 0u, 0u);
+      d[k] = ok ? load_stream(yr4 + u) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int k = 0; k < kStatsUnits; ++k) {   // zero units add nothing
+      accum_unit(a[k], b[k], sb);
+      accum_unit(c[k], d[k], sf);
+    }
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     for (int64_t i = units * kUnitElems; i < n; ++i) {
@@ -2331,7 +2350,7 @@ int64_t guided_stats_work_bytes(int fmt, const Shape& sh) {
 
 int64_t stats_groups(int64_t n) {
   int64_t units = n / kUnitElems;
-  int64_t g = (units + (int64_t)kThreads * 4 - 1) / ((int64_t)kThreads * 4);
+  int64_t g = (units + (int64_t)kThreads * kStatsUnits - 1) / ((int64_t)kThreads * kStatsUnits);   // tiles
   if (g < 1) g = 1;
   if (g > 1024) g = 1024;
   return g;
