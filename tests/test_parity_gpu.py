@@ -681,6 +681,35 @@ def test_random_shapes():
         G.check_guided(xtb, xrb, rows, cols, fmt, gbits, group_rows=gr)
 
 
+def test_random_shapes_fused_pass():
+    """24 seeded random shapes through guided_fake_quant_stats (with and
+    without mismatch counts), records of 0 to 4 bits weighted to 0 and 1
+    (whose waves read their scale and record bytes as dwords where a run is
+    whole and aligned): group sizes, ragged runs and group starts as the
+    shapes fall, each group with its own magnitude, against the oracle."""
+    rng = np.random.default_rng(2027)
+    done = 0
+    while done < 24:
+        fmt = NV if rng.random() < 0.7 else MX
+        cols = int(rng.choice([16, 48, 64, 96, 208, 256, 1040, 2048, 2064]))
+        if fmt == MX and cols % 32:
+            continue
+        rows = int(rng.integers(1, min(2048, 1_000_000 // cols) + 1))
+        divs = [d for d in range(1, rows + 1) if rows % d == 0]
+        gr = 0 if rng.random() < 0.3 else int(rng.choice(divs))
+        bits = int(rng.choice([0, 1, 1, 0, 2, 4]))
+        seed = int(rng.integers(1 << 30))
+        G.say(f"random fused case {done}: fmt {fmt} [{rows}, {cols}] group_rows {gr} bits {bits}")
+        xt, xr = syn.activation_pair(rows, cols, (98, seed))
+        n_g = rows // gr if gr else 1
+        mag = 2.0 ** np.random.default_rng(seed).integers(-8, 9, n_g).astype(np.float32)
+        scale = torch.from_numpy(np.repeat(mag, rows // n_g)).reshape(-1, 1)
+        xtb = syn.bits_u16((xt.float() * scale).to(torch.bfloat16)).reshape(-1)
+        xrb = syn.bits_u16((xr.float() * scale).to(torch.bfloat16)).reshape(-1)
+        G.check_guided_stats(xtb, xrb, rows, cols, fmt, bits, group_rows=gr)
+        done += 1
+
+
 # ---------------------------------------------------------------- row-offset groups
 
 def _offset_groups_pair(sizes, cols, seed):
