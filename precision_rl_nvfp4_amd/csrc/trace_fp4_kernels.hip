@@ -1621,9 +1621,7 @@ __global__ __launch_bounds__(kThreads) void tile_amax_kernel(TileMap m, const ui
 // tile), the other modes 512 (2 units each for guided rounding, 4 for
 // Reconstruct alone and row-offset groups), which
 // keeps more waves per SIMD (3.7% faster for plain guided rounding of a
-// streamed layer on 2048-unit tiles; on 1024-unit tiles 256 threads of 4
-// units, with or without the wave runs below, were 1-5% slower for every
-// record width and MXFP4).
+// streamed layer on 2048-unit tiles).
 constexpr int guided_threads(bool stats) { return stats ? kThreads : 2 * kThreads; }
 
 template <int FMT, int BITS, bool DECODE, bool WCODES, bool STATS, bool DIAG, int MAP>
